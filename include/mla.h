@@ -1,0 +1,173 @@
+/*
+ * mla.h — C ABI of the MI355X (gfx950) Multi-head Latent Attention library (libmla.so).
+ *
+ * The operation is the MLA layer of DeepSeek-V2 as written out on the page
+ * "DeepSeek-V2 paper summary" (7shi.hateblo.jp), App. C "Full Formulas of MLA",
+ * with the definitions of section 2.1.2 (joint KV compression) and section 2.1.3
+ * (decoupled RoPE: per-head rope query, one rope key shared by all heads):
+ *
+ *   c^q_t  = W_DQ h_t                      (c^q_t := h_t when d_cq == 0: App. B.1, V2-Lite)
+ *   q^C_t  = W_UQ c^q_t,   q^R_t = RoPE_t(W_QR c^q_t)      (head i = rows i*d_h.., i*d_hr..)
+ *   c^KV_t = W_DKV h_t,    k^R_t = RoPE_t(W_KR h_t)        (the cached vectors)
+ *   k^C_{t,i} = W_UK_i c^KV_t,   v_{t,i} = W_UV_i c^KV_t
+ *   o_{t,i} = sum_{j<=t} softmax_j(scale * ([q^C;q^R]_{t,i} . [k^C_{j,i};k^R_j])) v_{j,i}
+ *   u_t    = W_O [o_{t,1}; ...; o_{t,n_h}]
+ *
+ * RoPE rotates interleaved pairs (x_2k, x_2k+1) by angle pos * rope_base^(-2k/d_hr), pos = the
+ * token's 0-based index in its sequence.  The page only names "the RoPE matrix"; this is the
+ * RoFormer rotation it cites.
+ *
+ * Conventions for every entry point
+ *   - Weights are row-major [out][in] (y = W x), in dims->dtype, device memory, 16-byte aligned.
+ *   - The cache pool is [num_blocks][block_size][d_c + d_hr] in dims->dtype; each token's entry is
+ *     [c^KV | k^R] (d_c + d_hr = 576 values at DeepSeek-V2 sizes).  block_table[b][k] is the
+ *     physical block holding logical block k of sequence b (int32, device).
+ *   - Every pointer argument is a device pointer unless marked "host".
+ *   - The caller owns all memory (weights, cache, tables, inputs, outputs, workspace).  The
+ *     library never allocates or frees device memory and keeps no state between calls; calls on
+ *     different streams are independent as long as their output and workspace buffers differ.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued asynchronously; the
+ *     call returns without synchronising.
+ *   - Host-side validation runs before anything is enqueued and returns a negative mla_status;
+ *     on error nothing has been launched.  Device-side preconditions (block ids < num_blocks,
+ *     ctx_lens[b] <= max_ctx_len, positions inside the block table) are the caller's duty.
+ *   - Accumulation is always fp32.  In MLA_BF16 mode the intermediates handed between kernels
+ *     (c^q, q^C, the absorbed query, attention outputs) are stored as bf16.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = -1, /* NULL pointer, non-positive or inconsistent size */
+  MLA_ERR_UNSUPPORTED = -2, /* valid MLA sizes this build has no kernel for */
+  MLA_ERR_WORKSPACE = -3,   /* workspace NULL or smaller than mla_workspace_size() */
+  MLA_ERR_HIP = -4          /* a HIP call or kernel launch failed */
+} mla_status;
+
+typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
+
+typedef enum { MLA_OP_CACHE_APPEND = 0, MLA_OP_PREFILL = 1, MLA_OP_DECODE = 2 } mla_op;
+
+/* Layer sizes, in the pages' notation (section 3.1.2; App. B.1). */
+typedef struct {
+  int32_t d_model;     /* d: hidden size */
+  int32_t n_h;         /* attention heads */
+  int32_t d_h;         /* per-head content dimension (query/key/value) */
+  int32_t d_c;         /* KV compression dimension (latent width) */
+  int32_t d_cq;        /* query compression dimension d'_q; 0 = no query compression */
+  int32_t d_hr;        /* per-head decoupled rope dimension d_e (d_h^R); even */
+  float softmax_scale; /* 0 => 1/sqrt(d_h + d_hr) (App. C) */
+  float rope_base;     /* RoPE frequency base (10000 for DeepSeek-V2) */
+  int32_t dtype;       /* mla_dtype: storage of weights, h, cache, u */
+} mla_dims;
+
+/* Device pointers, row-major [out][in].  W_DQ is NULL iff d_cq == 0. */
+typedef struct {
+  const void *W_DQ;  /* [d_cq][d_model] */
+  const void *W_UQ;  /* [n_h*d_h][q_in], q_in = d_cq or d_model */
+  const void *W_QR;  /* [n_h*d_hr][q_in] */
+  const void *W_DKV; /* [d_c][d_model] */
+  const void *W_KR;  /* [d_hr][d_model] */
+  const void *W_UK;  /* [n_h*d_h][d_c] */
+  const void *W_UV;  /* [n_h*d_h][d_c] */
+  const void *W_O;   /* [d_model][n_h*d_h] */
+} mla_weights;
+
+/* Paged latent cache (the App. C cached vectors, in pages of block_size tokens). */
+typedef struct {
+  void *pool;                 /* [num_blocks][block_size][d_c + d_hr], dims->dtype */
+  int32_t num_blocks;
+  int32_t block_size;         /* tokens per block (64 at DeepSeek-V2 sizes); >= 1 */
+  int32_t max_blocks_per_seq; /* columns of block_table */
+  const int32_t *block_table; /* [batch][max_blocks_per_seq] */
+} mla_paged_cache;
+
+/*
+ * Bytes of workspace that `op` needs for the given sizes (written to *bytes, host).
+ *   MLA_OP_CACHE_APPEND: batch ignored, max_tokens = n (tokens appended in one call).
+ *   MLA_OP_PREFILL:      batch sequences of max_tokens tokens each.
+ *   MLA_OP_DECODE:       batch sequences, max_ctx_len = largest ctx_lens[b] the call may see,
+ *                        num_splits = the value that will be passed to mla_decode (0 = auto).
+ * Pass the same sizes to the entry point.  Returns MLA_OK or MLA_ERR_INVALID_ARG/UNSUPPORTED.
+ */
+int mla_workspace_size(const mla_dims *dims, int op, int32_t batch, int32_t max_tokens,
+                       int32_t max_ctx_len, int32_t num_splits, size_t *bytes);
+
+/*
+ * Cache writer (section 2.1.2 compression, section 2.1.3 shared rope key, App. C cached
+ * vectors): for each of n tokens r, entry = [W_DKV h_r | RoPE_{pos[r]}(W_KR h_r)] is stored at
+ * pool[block_table[seq_idx[r]][pos[r] / block_size]][pos[r] % block_size][:].
+ *   h        [n][d_model], dims->dtype
+ *   seq_idx  [n] int32 (row of block_table), pos [n] int32 (0-based position in that sequence)
+ * Tokens with the same (seq_idx, pos) write the same slot (last writer unspecified).
+ */
+int mla_cache_append(const mla_dims *dims, const mla_weights *w, const mla_paged_cache *cache,
+                     const void *h, int32_t n, const int32_t *seq_idx, const int32_t *pos,
+                     void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Causal prefill (App. C, o_t sums over j = 1..t) of `batch` sequences of T tokens each,
+ * starting at position 0.  Writes every token's cache entry (as mla_cache_append, sequence b =
+ * block_table row b) and u.  Attention uses the un-absorbed form: per-head keys
+ * [W_UK_i c^KV | k^R] and values W_UV_i c^KV are built in the workspace.
+ *   h  [batch][T][d_model], u [batch][T][d_model] (dims->dtype)
+ *   o_heads: NULL, or fp32 [batch][T][n_h][d_h] receiving the per-head attention outputs o_{t,i}.
+ */
+int mla_prefill(const mla_dims *dims, const mla_weights *w, const mla_paged_cache *cache,
+                const void *h, int32_t batch, int32_t T, void *u, float *o_heads,
+                void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * One decode step for `batch` sequences (App. C with the absorption that the page derives
+ * from associativity: W_UK_i folds into the query, q_hat_i = W_UK_i^T q^C_i, and W_UV_i is
+ * applied after the softmax, o_i = W_UV_i sum_j p_ij c^KV_j, so attention reads only the
+ * cached [c^KV | k^R] entries, shared by all heads).
+ *   h         [batch][d_model] hidden state of the new token of each sequence
+ *   ctx_lens  [batch] int32: tokens already cached before this step.  The new token's entry is
+ *             written at position ctx_lens[b] and the token attends over ctx_lens[b] + 1 entries.
+ *             The library does not modify ctx_lens.
+ *   max_ctx_len (host) >= every ctx_lens[b]; sizes the grid.  Requires
+ *             max_ctx_len + 1 <= max_blocks_per_seq * block_size.
+ *   num_splits (host): KV partitions per sequence (split-KV, combined by a log-sum-exp
+ *             reduction); 0 = chosen from the sizes and the device's compute-unit count.
+ *   u         [batch][d_model] output
+ *   o_heads   NULL, or fp32 [batch][n_h][d_h] receiving o_{t,i}.
+ */
+int mla_decode(const mla_dims *dims, const mla_weights *w, const mla_paged_cache *cache,
+               const void *h, int32_t batch, const int32_t *ctx_lens, int32_t max_ctx_len,
+               int32_t num_splits, void *u, float *o_heads, void *workspace, size_t ws_bytes,
+               void *stream);
+
+/*
+ * Decode attention core only (the split-KV latent attention and its reduction), for timing and
+ * kernel-level tests.  Inputs are the absorbed queries already formed:
+ *   q        [batch][n_h][d_c + d_hr], dims->dtype: [q_hat_i | RoPE'd q^R_i] per head
+ *   kv_lens  [batch] int32: entries to attend over (positions 0..kv_lens[b]-1 of the cache)
+ *   max_kv_len (host) >= every kv_lens[b]
+ *   o_hat    [batch][n_h][d_c] output, dims->dtype: sum_j softmax_j(scale * q . entry_j) c^KV_j
+ *   lse      NULL or fp32 [batch][n_h]: natural-log log-sum-exp of the scaled scores
+ * Workspace: mla_workspace_size(MLA_OP_DECODE, batch, 0, max_kv_len - 1, num_splits).
+ */
+int mla_decode_attention(const mla_dims *dims, const mla_paged_cache *cache, const void *q,
+                         int32_t batch, const int32_t *kv_lens, int32_t max_kv_len,
+                         int32_t num_splits, void *o_hat, float *lse, void *workspace,
+                         size_t ws_bytes, void *stream);
+
+/* The split count mla_decode uses for num_splits == 0 (host query; -1 on invalid sizes). */
+int32_t mla_decode_auto_splits(const mla_dims *dims, int32_t batch, int32_t max_ctx_len);
+
+/* Static text for a status code. */
+const char *mla_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MLA_H_ */

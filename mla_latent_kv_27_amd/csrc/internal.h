@@ -1,0 +1,111 @@
+// Host-side launch interfaces between the C ABI (mla_api.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mla {
+
+enum class DType { F32 = 0, BF16 = 1 };
+
+inline size_t dsize(DType t) { return t == DType::BF16 ? 2 : 4; }
+
+// Where a GEMM result element (row, col) of batch z is stored, and what happens on the way.
+//   address = z*batch_stride + rowbase(row) + (col/group)*group_stride + group_off + col%group
+//   rowbase = row*ldc, or, when block_table is set, slot(row)*ldc with
+//             slot = block_table[row_seq[row]][row_pos[row]/block_size]*block_size
+//                    + row_pos[row] % block_size    (paged cache rows)
+//   columns >= rope_col0 are rotated as interleaved pairs in groups of d_hr by the angles
+//   rope_tab[row][k] = (cos, sin) of pair k.
+struct Epilogue {
+  void* C = nullptr;
+  bool c_f32 = false;  // C holds fp32 instead of the GEMM's element type
+  int64_t ldc = 0, batch_stride = 0;
+  int group = 1 << 30;
+  int64_t group_stride = 0, group_off = 0;
+  int rope_col0 = 1 << 30;
+  int d_hr = 0;
+  const float2* rope_tab = nullptr;
+  const int32_t* row_seq = nullptr;
+  const int32_t* row_pos = nullptr;
+  const int32_t* block_table = nullptr;
+  int max_blocks = 0, block_size = 1;
+  float* C2 = nullptr;  // optional fp32 copy at the same indices
+};
+
+// C[z] (M x N) = A[z] (M x K) * op(B[z]),  op(B) = B^T with B [N][K] ("NT", weights in y = W x
+// form) or B with B [K][N] ("NN").  For NT, rows n >= N0 are taken from B1 (row n - N0).
+struct GemmParams {
+  const void* A = nullptr;
+  int64_t lda = 0, strideA = 0;
+  const void* B0 = nullptr;
+  const void* B1 = nullptr;
+  int N0 = 1 << 30;
+  int64_t ldb = 0, strideB = 0;
+  bool nn = false;
+  int M = 0, N = 0, K = 0, batch = 1;
+  Epilogue epi;
+};
+
+struct GemmPlan {
+  int cfg = 0;      // tile configuration id
+  int bm = 0, bn = 0;
+  int splits = 1;   // split-K factor
+  int k_per_split = 0;
+  size_t partial_bytes = 0;  // workspace for fp32 partials (0 when splits == 1)
+};
+
+GemmPlan gemm_plan(int M, int N, int K, int batch, int cus);
+// Launches the GEMM (and its split-K reduction).  `partial` must hold plan.partial_bytes.
+hipError_t gemm_run(DType t, const GemmParams& p, const GemmPlan& plan, float* partial,
+                    hipStream_t s);
+
+// rope_tab[r][k] = (cos, sin)(pos[r] * base^(-2k/d_hr)), r < n; angles formed in fp64.
+hipError_t rope_table(const int32_t* pos, int n, int d_hr, float base, float2* tab, hipStream_t s);
+// pos[r] = r % T, seq[r] = r / T for r < n.
+hipError_t prefill_rows(int n, int T, int32_t* seq, int32_t* pos, hipStream_t s);
+// Copies dense rows src[r][0..width) into paged cache slots (row_seq/row_pos/block_table).
+hipError_t scatter_rows(DType t, const void* src, int n, int width, void* pool,
+                        const int32_t* row_seq, const int32_t* row_pos, const int32_t* block_table,
+                        int max_blocks, int block_size, hipStream_t s);
+
+struct DecodeAttnParams {
+  const void* q;          // [B][n_h][d_c + d_hr]
+  const void* pool;       // [num_blocks][block_size][d_c + d_hr]
+  const int32_t* block_table;
+  int max_blocks, block_size;
+  const int32_t* lens;    // [B] entries to attend over (or ctx_lens when lens_plus_one)
+  bool lens_plus_one;
+  int B, n_h, d_c, d_hr;
+  float scale_log2;       // softmax scale * log2(e)
+  int splits;
+  int tiles_per_split;    // in units of the kernel's token tile
+  float* part_m;          // [B][splits][n_h]   (log2 domain running max)
+  float* part_l;          // [B][splits][n_h]
+  float* part_o;          // [B][splits][n_h][d_c]
+  void* o_hat;            // [B][n_h][d_c] output (element type)
+  float* lse;             // optional [B][n_h], natural log
+};
+
+int decode_tile_tokens();
+int decode_heads_per_block(int n_h);
+bool decode_supported(int d_c, int d_hr);
+hipError_t decode_attention(DType t, const DecodeAttnParams& p, hipStream_t s);
+
+struct PrefillAttnParams {
+  const void* q;      // [S*T][n_h][d_h + d_hr]   ([q^C | q^R])
+  const void* k;      // [n_h][S*T][d_h]          (W_UK_i c^KV)
+  const void* kr;     // [S*T] rows of ld_kr elements; k^R at column kr_off
+  int64_t ld_kr;
+  int kr_off;
+  const void* vt;     // [n_h][d_h][S*T]          (W_UV_i c^KV, token-contiguous)
+  void* o;            // [S*T][n_h][d_h]
+  float* o_f32;       // optional fp32 copy
+  int S, T, n_h, d_h, d_hr;
+  float scale_log2;
+};
+bool prefill_supported(int d_h, int d_hr);
+hipError_t prefill_attention(DType t, const PrefillAttnParams& p, hipStream_t s);
+
+}  // namespace mla

@@ -1,0 +1,526 @@
+// C ABI of libmla: argument validation, workspace carving and the launch sequence of each
+// entry point.  The operations are those of App. C ("Full Formulas of MLA") on the DeepSeek-V2
+// summary page; see include/mla.h for the contract of every call.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+
+#include "../../include/mla.h"
+#include "internal.h"
+
+using namespace mla;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Bump allocator over the caller's workspace (or a null base, for sizing).
+struct Carve {
+  char* base;
+  size_t off = 0;
+  explicit Carve(void* b) : base(reinterpret_cast<char*>(b)) {}
+  template <typename P>
+  P* take(size_t bytes) {
+    P* p = base ? reinterpret_cast<P*>(base + off) : nullptr;
+    off += align_up(bytes);
+    return p;
+  }
+};
+
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return 256;
+  return cus;
+}
+
+int validate_dims(const mla_dims* d) {
+  if (!d) return MLA_ERR_INVALID_ARG;
+  if (d->d_model <= 0 || d->n_h <= 0 || d->d_h <= 0 || d->d_c <= 0 || d->d_hr <= 0 || d->d_cq < 0)
+    return MLA_ERR_INVALID_ARG;
+  if (d->d_hr % 2 != 0) return MLA_ERR_INVALID_ARG;
+  if (d->dtype != MLA_F32 && d->dtype != MLA_BF16) return MLA_ERR_INVALID_ARG;
+  if (!(d->softmax_scale >= 0.f) || !std::isfinite(d->softmax_scale)) return MLA_ERR_INVALID_ARG;
+  if (!(d->rope_base > 0.f) || !std::isfinite(d->rope_base)) return MLA_ERR_INVALID_ARG;
+  // every contraction and row is moved in 16-byte chunks
+  const int epc = d->dtype == MLA_BF16 ? 8 : 4;
+  if (d->d_model % epc || d->d_h % epc || d->d_c % epc || d->d_cq % epc || d->d_hr % 8)
+    return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
+inline DType dt(const mla_dims* d) { return d->dtype == MLA_BF16 ? DType::BF16 : DType::F32; }
+inline int q_in(const mla_dims* d) { return d->d_cq > 0 ? d->d_cq : d->d_model; }
+inline int entry(const mla_dims* d) { return d->d_c + d->d_hr; }
+inline float scale_of(const mla_dims* d) {
+  return d->softmax_scale > 0.f ? d->softmax_scale : 1.0f / std::sqrt((float)(d->d_h + d->d_hr));
+}
+
+int validate_cache(const mla_dims* d, const mla_paged_cache* c) {
+  if (!c || !c->pool || !c->block_table) return MLA_ERR_INVALID_ARG;
+  if (c->num_blocks <= 0 || c->block_size <= 0 || c->max_blocks_per_seq <= 0) return MLA_ERR_INVALID_ARG;
+  (void)d;
+  return MLA_OK;
+}
+
+int auto_splits(const mla_dims* d, int batch, int max_ctx_len, int cus) {
+  const int hpb = decode_heads_per_block(d->n_h);
+  const int hg = (d->n_h + hpb - 1) / hpb;
+  const int tiles = (max_ctx_len + 1 + decode_tile_tokens() - 1) / decode_tile_tokens();
+  const int units = batch * hg;
+  int s = (cus + units - 1) / units;
+  s = std::min(s, std::max(1, tiles / 8));
+  return std::max(1, std::min(s, 64));
+}
+
+// ----------------------------------------------------------------------------- workspace plans
+struct AppendWs {
+  float2* rope;
+  float* partial;
+  GemmPlan plan;
+};
+AppendWs carve_append(Carve& cv, const mla_dims* d, int n, int cus) {
+  AppendWs w;
+  w.plan = gemm_plan(n, entry(d), d->d_model, 1, cus);
+  w.rope = cv.take<float2>((size_t)n * (d->d_hr / 2) * sizeof(float2));
+  w.partial = cv.take<float>(w.plan.partial_bytes);
+  return w;
+}
+
+struct DecodeGemms {
+  GemmPlan cq, qc, qr, kv, absorb, uv, out;
+  size_t max_partial() const {
+    return std::max({cq.partial_bytes, qc.partial_bytes, qr.partial_bytes, kv.partial_bytes, absorb.partial_bytes,
+                     uv.partial_bytes, out.partial_bytes});
+  }
+};
+DecodeGemms decode_gemms(const mla_dims* d, int B, int cus) {
+  DecodeGemms g;
+  g.cq = d->d_cq > 0 ? gemm_plan(B, d->d_cq, d->d_model, 1, cus) : GemmPlan{};
+  g.qc = gemm_plan(B, d->n_h * d->d_h, q_in(d), 1, cus);
+  g.qr = gemm_plan(B, d->n_h * d->d_hr, q_in(d), 1, cus);
+  g.kv = gemm_plan(B, entry(d), d->d_model, 1, cus);
+  g.absorb = gemm_plan(B, d->d_c, d->d_h, d->n_h, cus);
+  g.uv = gemm_plan(B, d->d_h, d->d_c, d->n_h, cus);
+  g.out = gemm_plan(B, d->d_model, d->n_h * d->d_h, 1, cus);
+  return g;
+}
+
+struct AttnWs {
+  float *pm, *pl, *po;
+  int splits, tps;
+};
+AttnWs carve_attn(Carve& cv, const mla_dims* d, int B, int max_kv_len, int splits) {
+  AttnWs a;
+  const int tiles = (max_kv_len + decode_tile_tokens() - 1) / decode_tile_tokens();
+  a.tps = std::max(1, (tiles + splits - 1) / splits);
+  a.splits = std::max(1, (tiles + a.tps - 1) / a.tps);
+  const size_t n = (size_t)B * a.splits * d->n_h;
+  a.pm = cv.take<float>(a.splits > 1 ? n * sizeof(float) : 0);
+  a.pl = cv.take<float>(a.splits > 1 ? n * sizeof(float) : 0);
+  a.po = cv.take<float>(a.splits > 1 ? n * d->d_c * sizeof(float) : 0);
+  return a;
+}
+
+struct DecodeWs {
+  int32_t* iota;
+  int32_t* dummy;
+  float2* rope;
+  void *cq, *qc, *qcat, *ohat, *o;
+  AttnWs attn;
+  float* partial;
+  DecodeGemms gm;
+};
+DecodeWs carve_decode(Carve& cv, const mla_dims* d, int B, int max_ctx_len, int splits, int cus) {
+  DecodeWs w;
+  const size_t es = dsize(dt(d));
+  w.gm = decode_gemms(d, B, cus);
+  w.iota = cv.take<int32_t>((size_t)B * 4);
+  w.dummy = cv.take<int32_t>((size_t)B * 4);
+  w.rope = cv.take<float2>((size_t)B * (d->d_hr / 2) * sizeof(float2));
+  w.cq = cv.take<char>((size_t)B * d->d_cq * es);
+  w.qc = cv.take<char>((size_t)B * d->n_h * d->d_h * es);
+  w.qcat = cv.take<char>((size_t)B * d->n_h * entry(d) * es);
+  w.ohat = cv.take<char>((size_t)B * d->n_h * d->d_c * es);
+  w.o = cv.take<char>((size_t)B * d->n_h * d->d_h * es);
+  w.attn = carve_attn(cv, d, B, max_ctx_len + 1, splits);
+  w.partial = cv.take<float>(w.gm.max_partial());
+  return w;
+}
+
+struct PrefillWs {
+  int32_t *seq, *pos;
+  float2* rope;
+  void *cq, *qp, *kvd, *kp, *vt, *o;
+  float* partial;
+  GemmPlan cq_p, qc_p, qr_p, kv_p, k_p, v_p, out_p;
+  int Tp;
+};
+PrefillWs carve_prefill(Carve& cv, const mla_dims* d, int S, int T, int cus) {
+  PrefillWs w;
+  const size_t es = dsize(dt(d));
+  const int M = S * T;
+  w.Tp = (T + 63) / 64 * 64;
+  const int qw = d->n_h * (d->d_h + d->d_hr);
+  w.cq_p = d->d_cq > 0 ? gemm_plan(M, d->d_cq, d->d_model, 1, cus) : GemmPlan{};
+  w.qc_p = gemm_plan(M, d->n_h * d->d_h, q_in(d), 1, cus);
+  w.qr_p = gemm_plan(M, d->n_h * d->d_hr, q_in(d), 1, cus);
+  w.kv_p = gemm_plan(M, entry(d), d->d_model, 1, cus);
+  w.k_p = gemm_plan(M, d->n_h * d->d_h, d->d_c, 1, cus);
+  w.v_p = gemm_plan(d->n_h * d->d_h, M, d->d_c, 1, cus);
+  w.out_p = gemm_plan(M, d->d_model, d->n_h * d->d_h, 1, cus);
+  w.seq = cv.take<int32_t>((size_t)M * 4);
+  w.pos = cv.take<int32_t>((size_t)M * 4);
+  w.rope = cv.take<float2>((size_t)M * (d->d_hr / 2) * sizeof(float2));
+  w.cq = cv.take<char>((size_t)M * d->d_cq * es);
+  w.qp = cv.take<char>((size_t)M * qw * es);
+  w.kvd = cv.take<char>((size_t)M * entry(d) * es);
+  w.kp = cv.take<char>((size_t)M * d->n_h * d->d_h * es);
+  w.vt = cv.take<char>((size_t)d->n_h * d->d_h * S * w.Tp * es);
+  w.o = cv.take<char>((size_t)M * d->n_h * d->d_h * es);
+  const size_t mp = std::max({w.cq_p.partial_bytes, w.qc_p.partial_bytes, w.qr_p.partial_bytes, w.kv_p.partial_bytes,
+                              w.k_p.partial_bytes, w.v_p.partial_bytes, w.out_p.partial_bytes});
+  w.partial = cv.take<float>(mp);
+  return w;
+}
+
+#define MLA_HIP(x)                                  \
+  do {                                              \
+    if ((x) != hipSuccess) return MLA_ERR_HIP;      \
+  } while (0)
+
+// Plain row-major output epilogue.
+Epilogue dense(void* C, int64_t ldc) {
+  Epilogue e;
+  e.C = C;
+  e.ldc = ldc;
+  return e;
+}
+
+int run_cache_writer(const mla_dims* d, const mla_weights* w, const mla_paged_cache* c, const void* h, int n,
+                     const int32_t* seq, const int32_t* pos, const float2* rope, const GemmPlan& plan,
+                     float* partial, hipStream_t s) {
+  GemmParams g;
+  g.A = h;
+  g.lda = d->d_model;
+  g.B0 = w->W_DKV;
+  g.B1 = w->W_KR;
+  g.N0 = d->d_c;
+  g.ldb = d->d_model;
+  g.M = n;
+  g.N = entry(d);
+  g.K = d->d_model;
+  g.epi.C = c->pool;
+  g.epi.ldc = entry(d);
+  g.epi.rope_col0 = d->d_c;
+  g.epi.d_hr = d->d_hr;
+  g.epi.rope_tab = rope;
+  g.epi.row_seq = seq;
+  g.epi.row_pos = pos;
+  g.epi.block_table = c->block_table;
+  g.epi.max_blocks = c->max_blocks_per_seq;
+  g.epi.block_size = c->block_size;
+  MLA_HIP(gemm_run(dt(d), g, plan, partial, s));
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(int status) {
+  switch (status) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG: null pointer, non-positive or inconsistent size";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: sizes without a kernel in this build";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace missing or too small";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP: a HIP call or kernel launch failed";
+    default: return "unknown mla_status";
+  }
+}
+
+int32_t mla_decode_auto_splits(const mla_dims* d, int32_t batch, int32_t max_ctx_len) {
+  if (validate_dims(d) != MLA_OK || batch <= 0 || max_ctx_len < 0) return -1;
+  return auto_splits(d, batch, max_ctx_len, device_cus());
+}
+
+int mla_workspace_size(const mla_dims* d, int op, int32_t batch, int32_t max_tokens, int32_t max_ctx_len,
+                       int32_t num_splits, size_t* bytes) {
+  int st = validate_dims(d);
+  if (st != MLA_OK) return st;
+  if (!bytes) return MLA_ERR_INVALID_ARG;
+  const int cus = device_cus();
+  Carve cv(nullptr);
+  switch (op) {
+    case MLA_OP_CACHE_APPEND:
+      if (max_tokens < 0) return MLA_ERR_INVALID_ARG;
+      carve_append(cv, d, max_tokens, cus);
+      break;
+    case MLA_OP_PREFILL:
+      if (batch <= 0 || max_tokens <= 0) return MLA_ERR_INVALID_ARG;
+      carve_prefill(cv, d, batch, max_tokens, cus);
+      break;
+    case MLA_OP_DECODE: {
+      if (batch <= 0 || max_ctx_len < 0 || num_splits < 0) return MLA_ERR_INVALID_ARG;
+      const int sp = num_splits > 0 ? num_splits : auto_splits(d, batch, max_ctx_len, cus);
+      carve_decode(cv, d, batch, max_ctx_len, sp, cus);
+      break;
+    }
+    default: return MLA_ERR_INVALID_ARG;
+  }
+  *bytes = cv.off;
+  return MLA_OK;
+}
+
+int mla_cache_append(const mla_dims* d, const mla_weights* w, const mla_paged_cache* c, const void* h, int32_t n,
+                     const int32_t* seq_idx, const int32_t* pos, void* workspace, size_t ws_bytes, void* stream) {
+  int st = validate_dims(d);
+  if (st != MLA_OK) return st;
+  if ((st = validate_cache(d, c)) != MLA_OK) return st;
+  if (!w || !w->W_DKV || !w->W_KR || n < 0) return MLA_ERR_INVALID_ARG;
+  if (n == 0) return MLA_OK;
+  if (!h || !seq_idx || !pos) return MLA_ERR_INVALID_ARG;
+  const int cus = device_cus();
+  Carve sz(nullptr);
+  carve_append(sz, d, n, cus);
+  if (!workspace || ws_bytes < sz.off) return MLA_ERR_WORKSPACE;
+  Carve cv(workspace);
+  AppendWs ws = carve_append(cv, d, n, cus);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  MLA_HIP(rope_table(pos, n, d->d_hr, d->rope_base, ws.rope, s));
+  return run_cache_writer(d, w, c, h, n, seq_idx, pos, ws.rope, ws.plan, ws.partial, s);
+}
+
+int mla_decode_attention(const mla_dims* d, const mla_paged_cache* c, const void* q, int32_t batch,
+                         const int32_t* kv_lens, int32_t max_kv_len, int32_t num_splits, void* o_hat, float* lse,
+                         void* workspace, size_t ws_bytes, void* stream) {
+  int st = validate_dims(d);
+  if (st != MLA_OK) return st;
+  if ((st = validate_cache(d, c)) != MLA_OK) return st;
+  if (!q || !kv_lens || !o_hat || batch <= 0 || max_kv_len <= 0 || num_splits < 0) return MLA_ERR_INVALID_ARG;
+  if ((int64_t)max_kv_len > (int64_t)c->max_blocks_per_seq * c->block_size) return MLA_ERR_INVALID_ARG;
+  if (!decode_supported(d->d_c, d->d_hr)) return MLA_ERR_UNSUPPORTED;
+  const int cus = device_cus();
+  const int sp = num_splits > 0 ? num_splits : auto_splits(d, batch, max_kv_len - 1, cus);
+  Carve sz(nullptr);
+  carve_decode(sz, d, batch, max_kv_len - 1, sp, cus);
+  if (!workspace || ws_bytes < sz.off) return MLA_ERR_WORKSPACE;
+  Carve cv(workspace);
+  DecodeWs ws = carve_decode(cv, d, batch, max_kv_len - 1, sp, cus);
+  DecodeAttnParams a{};
+  a.q = q;
+  a.pool = c->pool;
+  a.block_table = c->block_table;
+  a.max_blocks = c->max_blocks_per_seq;
+  a.block_size = c->block_size;
+  a.lens = kv_lens;
+  a.lens_plus_one = false;
+  a.B = batch;
+  a.n_h = d->n_h;
+  a.d_c = d->d_c;
+  a.d_hr = d->d_hr;
+  a.scale_log2 = scale_of(d) * 1.4426950408889634f;
+  a.splits = ws.attn.splits;
+  a.tiles_per_split = ws.attn.tps;
+  a.part_m = ws.attn.pm;
+  a.part_l = ws.attn.pl;
+  a.part_o = ws.attn.po;
+  a.o_hat = o_hat;
+  a.lse = lse;
+  MLA_HIP(decode_attention(dt(d), a, reinterpret_cast<hipStream_t>(stream)));
+  return MLA_OK;
+}
+
+int mla_decode(const mla_dims* d, const mla_weights* w, const mla_paged_cache* c, const void* h, int32_t batch,
+               const int32_t* ctx_lens, int32_t max_ctx_len, int32_t num_splits, void* u, float* o_heads,
+               void* workspace, size_t ws_bytes, void* stream) {
+  int st = validate_dims(d);
+  if (st != MLA_OK) return st;
+  if ((st = validate_cache(d, c)) != MLA_OK) return st;
+  if (!w || !w->W_UQ || !w->W_QR || !w->W_DKV || !w->W_KR || !w->W_UK || !w->W_UV || !w->W_O)
+    return MLA_ERR_INVALID_ARG;
+  if ((d->d_cq > 0) != (w->W_DQ != nullptr)) return MLA_ERR_INVALID_ARG;
+  if (!h || !ctx_lens || !u || batch <= 0 || max_ctx_len < 0 || num_splits < 0) return MLA_ERR_INVALID_ARG;
+  if ((int64_t)max_ctx_len + 1 > (int64_t)c->max_blocks_per_seq * c->block_size) return MLA_ERR_INVALID_ARG;
+  if (!decode_supported(d->d_c, d->d_hr)) return MLA_ERR_UNSUPPORTED;
+  const int cus = device_cus();
+  const int sp = num_splits > 0 ? num_splits : auto_splits(d, batch, max_ctx_len, cus);
+  Carve sz(nullptr);
+  carve_decode(sz, d, batch, max_ctx_len, sp, cus);
+  if (!workspace || ws_bytes < sz.off) return MLA_ERR_WORKSPACE;
+  Carve cv(workspace);
+  DecodeWs ws = carve_decode(cv, d, batch, max_ctx_len, sp, cus);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const DType t = dt(d);
+  const int B = batch, E = entry(d), qw = q_in(d);
+
+  // positions of the new tokens are ctx_lens[b]; rows are sequences 0..B-1
+  MLA_HIP(prefill_rows(B, 1, ws.iota, ws.dummy, s));
+  MLA_HIP(rope_table(ctx_lens, B, d->d_hr, d->rope_base, ws.rope, s));
+  const void* qin = h;
+  if (d->d_cq > 0) {  // c^q = W_DQ h
+    GemmParams g;
+    g.A = h; g.lda = d->d_model; g.B0 = w->W_DQ; g.ldb = d->d_model;
+    g.M = B; g.N = d->d_cq; g.K = d->d_model;
+    g.epi = dense(ws.cq, d->d_cq);
+    MLA_HIP(gemm_run(t, g, ws.gm.cq, ws.partial, s));
+    qin = ws.cq;
+  }
+  {  // q^C = W_UQ c^q
+    GemmParams g;
+    g.A = qin; g.lda = qw; g.B0 = w->W_UQ; g.ldb = qw;
+    g.M = B; g.N = d->n_h * d->d_h; g.K = qw;
+    g.epi = dense(ws.qc, (int64_t)d->n_h * d->d_h);
+    MLA_HIP(gemm_run(t, g, ws.gm.qc, ws.partial, s));
+  }
+  {  // q^R = RoPE(W_QR c^q) -> columns [d_c, d_c + d_hr) of each head's absorbed query row
+    GemmParams g;
+    g.A = qin; g.lda = qw; g.B0 = w->W_QR; g.ldb = qw;
+    g.M = B; g.N = d->n_h * d->d_hr; g.K = qw;
+    g.epi = dense(ws.qcat, (int64_t)d->n_h * E);
+    g.epi.group = d->d_hr; g.epi.group_stride = E; g.epi.group_off = d->d_c;
+    g.epi.rope_col0 = 0; g.epi.d_hr = d->d_hr; g.epi.rope_tab = ws.rope;
+    MLA_HIP(gemm_run(t, g, ws.gm.qr, ws.partial, s));
+  }
+  // the new token's cache entry at position ctx_lens[b]
+  if ((st = run_cache_writer(d, w, c, h, B, ws.iota, ctx_lens, ws.rope, ws.gm.kv, ws.partial, s)) != MLA_OK)
+    return st;
+  {  // q_hat_i = W_UK_i^T q^C_i -> columns [0, d_c) of each head's row
+    GemmParams g;
+    g.A = ws.qc; g.lda = (int64_t)d->n_h * d->d_h; g.strideA = d->d_h;
+    g.B0 = w->W_UK; g.ldb = d->d_c; g.strideB = (int64_t)d->d_h * d->d_c; g.nn = true;
+    g.M = B; g.N = d->d_c; g.K = d->d_h; g.batch = d->n_h;
+    g.epi = dense(ws.qcat, (int64_t)d->n_h * E);
+    g.epi.batch_stride = E;
+    MLA_HIP(gemm_run(t, g, ws.gm.absorb, ws.partial, s));
+  }
+  {  // latent attention over ctx_lens[b] + 1 entries
+    DecodeAttnParams a{};
+    a.q = ws.qcat; a.pool = c->pool; a.block_table = c->block_table;
+    a.max_blocks = c->max_blocks_per_seq; a.block_size = c->block_size;
+    a.lens = ctx_lens; a.lens_plus_one = true;
+    a.B = B; a.n_h = d->n_h; a.d_c = d->d_c; a.d_hr = d->d_hr;
+    a.scale_log2 = scale_of(d) * 1.4426950408889634f;
+    a.splits = ws.attn.splits; a.tiles_per_split = ws.attn.tps;
+    a.part_m = ws.attn.pm; a.part_l = ws.attn.pl; a.part_o = ws.attn.po;
+    a.o_hat = ws.ohat; a.lse = nullptr;
+    MLA_HIP(decode_attention(t, a, s));
+  }
+  {  // o_i = W_UV_i o_hat_i
+    GemmParams g;
+    g.A = ws.ohat; g.lda = (int64_t)d->n_h * d->d_c; g.strideA = d->d_c;
+    g.B0 = w->W_UV; g.ldb = d->d_c; g.strideB = (int64_t)d->d_h * d->d_c;
+    g.M = B; g.N = d->d_h; g.K = d->d_c; g.batch = d->n_h;
+    g.epi = dense(ws.o, (int64_t)d->n_h * d->d_h);
+    g.epi.batch_stride = d->d_h;
+    g.epi.C2 = o_heads;
+    MLA_HIP(gemm_run(t, g, ws.gm.uv, ws.partial, s));
+  }
+  {  // u = W_O [o_1; ...; o_n_h]
+    GemmParams g;
+    g.A = ws.o; g.lda = (int64_t)d->n_h * d->d_h; g.B0 = w->W_O; g.ldb = (int64_t)d->n_h * d->d_h;
+    g.M = B; g.N = d->d_model; g.K = d->n_h * d->d_h;
+    g.epi = dense(u, d->d_model);
+    MLA_HIP(gemm_run(t, g, ws.gm.out, ws.partial, s));
+  }
+  return MLA_OK;
+}
+
+int mla_prefill(const mla_dims* d, const mla_weights* w, const mla_paged_cache* c, const void* h, int32_t batch,
+                int32_t T, void* u, float* o_heads, void* workspace, size_t ws_bytes, void* stream) {
+  int st = validate_dims(d);
+  if (st != MLA_OK) return st;
+  if ((st = validate_cache(d, c)) != MLA_OK) return st;
+  if (!w || !w->W_UQ || !w->W_QR || !w->W_DKV || !w->W_KR || !w->W_UK || !w->W_UV || !w->W_O)
+    return MLA_ERR_INVALID_ARG;
+  if ((d->d_cq > 0) != (w->W_DQ != nullptr)) return MLA_ERR_INVALID_ARG;
+  if (!h || !u || batch <= 0 || T <= 0) return MLA_ERR_INVALID_ARG;
+  if ((int64_t)T > (int64_t)c->max_blocks_per_seq * c->block_size) return MLA_ERR_INVALID_ARG;
+  if ((int64_t)batch * T > (1LL << 30)) return MLA_ERR_UNSUPPORTED;
+  if (!prefill_supported(d->d_h, d->d_hr)) return MLA_ERR_UNSUPPORTED;
+  const int cus = device_cus();
+  Carve sz(nullptr);
+  carve_prefill(sz, d, batch, T, cus);
+  if (!workspace || ws_bytes < sz.off) return MLA_ERR_WORKSPACE;
+  Carve cv(workspace);
+  PrefillWs ws = carve_prefill(cv, d, batch, T, cus);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const DType t = dt(d);
+  const int M = batch * T, E = entry(d), qw = q_in(d), QD = d->d_h + d->d_hr;
+
+  MLA_HIP(prefill_rows(M, T, ws.seq, ws.pos, s));
+  MLA_HIP(rope_table(ws.pos, M, d->d_hr, d->rope_base, ws.rope, s));
+  const void* qin = h;
+  if (d->d_cq > 0) {
+    GemmParams g;
+    g.A = h; g.lda = d->d_model; g.B0 = w->W_DQ; g.ldb = d->d_model;
+    g.M = M; g.N = d->d_cq; g.K = d->d_model;
+    g.epi = dense(ws.cq, d->d_cq);
+    MLA_HIP(gemm_run(t, g, ws.cq_p, ws.partial, s));
+    qin = ws.cq;
+  }
+  {  // q^C -> columns [0, d_h) of each head's [q^C | q^R] row
+    GemmParams g;
+    g.A = qin; g.lda = qw; g.B0 = w->W_UQ; g.ldb = qw;
+    g.M = M; g.N = d->n_h * d->d_h; g.K = qw;
+    g.epi = dense(ws.qp, (int64_t)d->n_h * QD);
+    g.epi.group = d->d_h; g.epi.group_stride = QD; g.epi.group_off = 0;
+    MLA_HIP(gemm_run(t, g, ws.qc_p, ws.partial, s));
+  }
+  {  // RoPE(q^R) -> columns [d_h, d_h + d_hr)
+    GemmParams g;
+    g.A = qin; g.lda = qw; g.B0 = w->W_QR; g.ldb = qw;
+    g.M = M; g.N = d->n_h * d->d_hr; g.K = qw;
+    g.epi = dense(ws.qp, (int64_t)d->n_h * QD);
+    g.epi.group = d->d_hr; g.epi.group_stride = QD; g.epi.group_off = d->d_h;
+    g.epi.rope_col0 = 0; g.epi.d_hr = d->d_hr; g.epi.rope_tab = ws.rope;
+    MLA_HIP(gemm_run(t, g, ws.qr_p, ws.partial, s));
+  }
+  {  // dense [c^KV | RoPE(k^R)] rows, then copied into the paged cache
+    GemmParams g;
+    g.A = h; g.lda = d->d_model; g.B0 = w->W_DKV; g.B1 = w->W_KR; g.N0 = d->d_c; g.ldb = d->d_model;
+    g.M = M; g.N = E; g.K = d->d_model;
+    g.epi = dense(ws.kvd, E);
+    g.epi.rope_col0 = d->d_c; g.epi.d_hr = d->d_hr; g.epi.rope_tab = ws.rope;
+    MLA_HIP(gemm_run(t, g, ws.kv_p, ws.partial, s));
+    MLA_HIP(scatter_rows(t, ws.kvd, M, E, c->pool, ws.seq, ws.pos, c->block_table, c->max_blocks_per_seq,
+                         c->block_size, s));
+  }
+  {  // k^C_i = W_UK_i c^KV, stored head-major [n_h][M][d_h]
+    GemmParams g;
+    g.A = ws.kvd; g.lda = E; g.B0 = w->W_UK; g.ldb = d->d_c;
+    g.M = M; g.N = d->n_h * d->d_h; g.K = d->d_c;
+    g.epi = dense(ws.kp, d->d_h);
+    g.epi.group = d->d_h; g.epi.group_stride = (int64_t)M * d->d_h;
+    MLA_HIP(gemm_run(t, g, ws.k_p, ws.partial, s));
+  }
+  {  // v^T: rows (head, dim) of W_UV times c^KV^T, token-contiguous [n_h][d_h][S][Tp]
+    GemmParams g;
+    g.A = w->W_UV; g.lda = d->d_c; g.B0 = ws.kvd; g.ldb = E;
+    g.M = d->n_h * d->d_h; g.N = M; g.K = d->d_c;
+    g.epi = dense(ws.vt, (int64_t)batch * ws.Tp);
+    g.epi.group = T; g.epi.group_stride = ws.Tp;
+    MLA_HIP(gemm_run(t, g, ws.v_p, ws.partial, s));
+  }
+  {
+    PrefillAttnParams a{};
+    a.q = ws.qp; a.k = ws.kp; a.kr = ws.kvd; a.ld_kr = E; a.kr_off = d->d_c; a.vt = ws.vt;
+    a.o = ws.o; a.o_f32 = o_heads;
+    a.S = batch; a.T = T; a.n_h = d->n_h; a.d_h = d->d_h; a.d_hr = d->d_hr;
+    a.scale_log2 = scale_of(d) * 1.4426950408889634f;
+    MLA_HIP(prefill_attention(t, a, s));
+  }
+  {
+    GemmParams g;
+    g.A = ws.o; g.lda = (int64_t)d->n_h * d->d_h; g.B0 = w->W_O; g.ldb = (int64_t)d->n_h * d->d_h;
+    g.M = M; g.N = d->d_model; g.K = d->n_h * d->d_h;
+    g.epi = dense(u, d->d_model);
+    MLA_HIP(gemm_run(t, g, ws.out_p, ws.partial, s));
+  }
+  return MLA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,75 @@
+// Small helper kernels: RoPE angle tables, prefill row bookkeeping, paged row scatter.
+//
+// RoPE follows the reading of the DeepSeek-V2 summary page's App. C ("RoPE(.)", the RoFormer
+// rotation it cites): interleaved pairs (x_2k, x_2k+1) rotate by pos * base^(-2k/d_hr).  The
+// angle is formed and reduced modulo 2*pi in fp64 so that positions near 1.3e5 keep full fp32
+// accuracy in cos/sin.
+#include "common.h"
+#include "internal.h"
+
+namespace mla {
+
+__global__ void __launch_bounds__(256)
+    rope_table_kernel(const int32_t* __restrict__ pos, int n, int half, double log_base, float2* tab) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= (int64_t)n * half) return;
+  const int r = (int)(i / half), k = (int)(i % half);
+  const double theta = exp(-(2.0 * k / (2.0 * half)) * log_base);
+  double a = (double)pos[r] * theta;
+  const double two_pi = 6.283185307179586476925286766559;
+  a = a - floor(a / two_pi) * two_pi;
+  double sn, cs;
+  sincos(a, &sn, &cs);
+  tab[i] = make_float2((float)cs, (float)sn);
+}
+
+hipError_t rope_table(const int32_t* pos, int n, int d_hr, float base, float2* tab, hipStream_t s) {
+  const int half = d_hr / 2;
+  const int64_t total = (int64_t)n * half;
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, pos, n,
+                     half, log((double)base), tab);
+  return hipGetLastError();
+}
+
+__global__ void __launch_bounds__(256) prefill_rows_kernel(int n, int T, int32_t* seq, int32_t* pos) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r < n) {
+    seq[r] = r / T;
+    pos[r] = r % T;
+  }
+}
+
+hipError_t prefill_rows(int n, int T, int32_t* seq, int32_t* pos, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(prefill_rows_kernel, dim3((n + 255) / 256), dim3(256), 0, s, n, T, seq, pos);
+  return hipGetLastError();
+}
+
+// One thread per 16-byte chunk of a row.
+__global__ void __launch_bounds__(256)
+    scatter_rows_kernel(const char* __restrict__ src, int n, int row_bytes, char* __restrict__ pool,
+                        const int32_t* __restrict__ row_seq, const int32_t* __restrict__ row_pos,
+                        const int32_t* __restrict__ bt, int max_blocks, int block_size) {
+  const int cpr = row_bytes / 16;
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= (int64_t)n * cpr) return;
+  const int r = (int)(i / cpr), c = (int)(i % cpr);
+  const int sq = row_seq[r], ps = row_pos[r];
+  const int64_t slot = (int64_t)bt[(int64_t)sq * max_blocks + ps / block_size] * block_size + ps % block_size;
+  st16(pool + slot * row_bytes + c * 16, ld16(src + (int64_t)r * row_bytes + c * 16));
+}
+
+hipError_t scatter_rows(DType t, const void* src, int n, int width, void* pool, const int32_t* row_seq,
+                        const int32_t* row_pos, const int32_t* block_table, int max_blocks, int block_size,
+                        hipStream_t s) {
+  const int row_bytes = width * (int)dsize(t);
+  const int64_t total = (int64_t)n * (row_bytes / 16);
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(scatter_rows_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
+                     reinterpret_cast<const char*>(src), n, row_bytes, reinterpret_cast<char*>(pool), row_seq,
+                     row_pos, block_table, max_blocks, block_size);
+  return hipGetLastError();
+}
+
+}  // namespace mla

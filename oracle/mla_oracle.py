@@ -125,23 +125,36 @@ def attend_unabsorbed(W: dict, dims, qc, qr, cache: np.ndarray, kv_len) -> tuple
     return o, lse
 
 
+def latent_attention(qcat: np.ndarray, cache: np.ndarray, kv_len, scale: float, d_c: int) -> tuple:
+    """The attention step of the absorbed form (App. C, associativity): every head attends over
+    the cached entries themselves.  qcat [n, n_h, d_c + d_hr] = [q_hat_i | q^R_i] per head,
+    cache [L, d_c + d_hr] = [c_KV | k_R]; query r sees rows 0..kv_len[r]-1.
+    s_ij = scale * (qcat_i . entry_j), o_hat_i = sum_j softmax_j(s_ij) c_KV,j.
+    Returns o_hat [n, n_h, d_c] and lse [n, n_h]."""
+    cache = np.asarray(cache, dtype=np.float64)
+    qcat = np.asarray(qcat, dtype=np.float64)
+    L = cache.shape[0]
+    kv_len = np.asarray(kv_len)
+    mask = np.arange(L)[None, :] < kv_len[:, None]
+    s = np.einsum("nie,le->nil", qcat, cache) * scale
+    s = np.where(mask[:, None, :], s, -np.inf)
+    p, lse = softmax_rows(s)
+    return np.einsum("nil,lc->nic", p, cache[:, :d_c]), lse
+
+
+def absorb_query(W: dict, dims, qc, qr) -> np.ndarray:
+    """[q_hat_i | q^R_i] per head with q_hat_i = W_UK_i^T q^C_i (App. C, associativity)."""
+    WUK = _w(W, "W_UK").reshape(dims.n_h, dims.d_h, dims.d_c)
+    qhat = np.einsum("nik,ikc->nic", qc, WUK)  # [n, n_h, d_c]
+    return np.concatenate([qhat, qr], axis=-1)
+
+
 def attend_absorbed(W: dict, dims, qc, qr, cache: np.ndarray, kv_len) -> tuple:
     """Absorbed form (App. C, associativity): q_hat_i = W_UK_i^T q^C_i in R^{d_c},
     s = scale * (q_hat_i . c_j + q^R_i . k_R,j), o_hat_i = sum_j p_ij c_j,
     o_i = W_UV_i o_hat_i.  Same outputs as attend_unabsorbed in exact arithmetic."""
-    cache = np.asarray(cache, dtype=np.float64)
-    c, kr = cache[:, : dims.d_c], cache[:, dims.d_c:]
-    n = qc.shape[0]
-    L = cache.shape[0]
-    kv_len = np.asarray(kv_len)
-    mask = np.arange(L)[None, :] < kv_len[:, None]
-    WUK = _w(W, "W_UK").reshape(dims.n_h, dims.d_h, dims.d_c)
+    ohat, lse = latent_attention(absorb_query(W, dims, qc, qr), cache, kv_len, dims.scale, dims.d_c)
     WUV = _w(W, "W_UV").reshape(dims.n_h, dims.d_h, dims.d_c)
-    qhat = np.einsum("nik,ikc->nic", qc, WUK)  # [n, n_h, d_c]
-    s = (np.einsum("nic,lc->nil", qhat, c) + np.einsum("nir,lr->nil", qr, kr)) * dims.scale
-    s = np.where(mask[:, None, :], s, -np.inf)
-    p, lse = softmax_rows(s)
-    ohat = np.einsum("nil,lc->nic", p, c)
     o = np.einsum("nic,idc->nid", ohat, WUV)
     return o, lse
 
