@@ -1,0 +1,224 @@
+"""Benchmark of the MLA decode hot path on one MI355X.
+
+A step is one full `mla_decode` call over the whole batch: query projections and RoPE, the
+cache writer for the new tokens, the W_UK absorption, split-KV latent attention and its
+reduction, W_UV and W_O.  Default workload: DeepSeek-V2 dims, batch 64, 8192 cached tokens per
+sequence in a paged bf16 latent cache (block 64), decode at position 8192.
+
+Inputs are seeded and synthetic and already resident in HBM when the timed region starts.
+Steps rotate over independent replicas of the weights and the cache so that no step is served
+from the previous step's cache lines.  The dominant kernel (decode attention) is timed in a
+second loop of the attention-core entry point with HIP events on the stream it runs on.  The
+fp64 oracle is timed on the host cores on a bounded sample as a CPU baseline.
+
+Prints one JSON line.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+FP32_PEAK_TFLOPS = 157.3
+METRIC = "MLA decode tokens/s + achieved GB/s & %roofline, DeepSeek-V2 shape, 1 GPU"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="v2_decode_b64_ctx8192")
+    ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--replicas", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def decode_bytes(dims, lens, B):
+    """Algorithmic HBM bytes of one decode step: each cached entry once, each weight once, h in,
+    u out, the new entries written."""
+    es = 2 if dims.dtype == "bf16" else 4
+    cache = sum(int(L) + 1 for L in lens) * dims.entry * es
+    weights = dims.param_count() * es
+    io = B * 2 * dims.d_model * es + B * dims.entry * es
+    return cache, weights, io
+
+
+def decode_flops(dims, lens, B):
+    attn = sum(int(L) + 1 for L in lens) * 2 * dims.n_h * (dims.entry + dims.d_c)
+    proj = 2 * B * dims.param_count()
+    return attn, proj
+
+
+def attn_core_bytes(dims, lens, B):
+    """Algorithmic bytes of the attention core: cached entries, the absorbed queries and o_hat."""
+    es = 2 if dims.dtype == "bf16" else 4
+    return sum(int(L) + 1 for L in lens) * dims.entry * es + B * dims.n_h * (dims.entry + dims.d_c) * es
+
+
+def counters_for(kernel_file, workload):
+    """HBM traffic per dispatch from a committed rocprofv3 counter summary, if it was taken on the
+    current source of the kernel; else None."""
+    path = os.path.join(ROOT, "profiles", f"decode_attn_{workload}.counters.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    src = open(os.path.join(ROOT, "mla_latent_kv_27_amd", "csrc", kernel_file), "rb").read()
+    if kv.get("kernel_source_sha256") != hashlib.sha256(src).hexdigest():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_dispatch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(dims, W_np, lens, recipe, budget_s):
+    """The fp64 oracle, un-absorbed, on whole sequences of the same workload until the budget is
+    spent (at least one sequence); tokens/s = sequences decoded per second."""
+    import numpy as np
+    import mla_synth as S
+    import oracle.mla_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    h = S.hidden_step(dims, len(lens), recipe)
+    done, spent = 0, 0.0
+    while done < len(lens) and (done == 0 or spent < budget_s):
+        b = done
+        cache = O.latent_entries(W_np, dims, S.hidden_history(dims, b, int(lens[b]), recipe), np.arange(int(lens[b])))
+        t0 = time.perf_counter()
+        O.mla_decode(W_np, dims, h[b:b + 1], [cache])
+        spent += time.perf_counter() - t0
+        done += 1
+    return {"value": done / spent, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {len(lens)} sequences of the same decode step (each over {int(lens[0]) + 1} "
+                      f"cached tokens), un-absorbed fp64 numpy, {spent:.1f} s; cache entries precomputed untimed"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build "
+              f"(sharding across GPUs is described in DESIGN.md but not implemented)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import mla_synth as S
+    import mla_latent_kv_27_amd as M
+    from mla_latent_kv_27_amd import workload as WL
+
+    w = S.WORKLOADS[args.workload]
+    if w.kind != "decode":
+        print("bench.py times the decode hot path; choose a decode workload", file=sys.stderr)
+        sys.exit(2)
+    dims = w.dims
+    torch.cuda.set_device(0)
+    lens = S.context_lengths(w)
+    B = w.batch
+    max_ctx = int(max(lens))
+    W_np = S.make_weights(dims, std=w.weight_std)
+    layer = WL.DeviceLayer(dims, W_np)
+    pool = WL.PagedPool(dims, [int(L) + 1 for L in lens], block_size=w.block_size)
+    t0 = time.perf_counter()
+    WL.build_context(layer, pool, lens, w.hidden)
+    setup_s = time.perf_counter() - t0
+    h = WL.to_device(S.hidden_step(dims, B, w.hidden), dims)
+    ctx = torch.tensor(np.asarray(lens, dtype=np.int32), device="cuda")
+    splits = args.splits if args.splits > 0 else M.auto_splits(layer.cdims, B, max_ctx)
+    reps = [(layer, pool)] + [(layer.clone(), pool.clone()) for _ in range(max(0, args.replicas - 1))]
+    outs = [torch.empty((B, dims.d_model), dtype=WL.torch_dtype(dims), device="cuda") for _ in reps]
+    wss = [WL.decode_workspace(layer, B, max_ctx, splits) for _ in reps]
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        ly, pl = reps[i % len(reps)]
+        M.decode(ly.cdims, ly.cweights, pl.ccache, h, ctx, max_ctx, outs[i % len(reps)], wss[i % len(reps)],
+                 num_splits=splits, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    value = B / (ms / 1e3)
+
+    # dominant kernel: the latent attention core, timed on the same stream
+    q = WL.to_device(S.to_dtype((np.random.default_rng(9).standard_normal((B, dims.n_h, dims.entry)) * 0.05)
+                                .astype(np.float32), dims.dtype), dims)
+    kv = ctx + 1
+    ohat = torch.empty((B, dims.n_h, dims.d_c), dtype=WL.torch_dtype(dims), device="cuda")
+    for i in range(args.warmup):
+        M.decode_attention(layer.cdims, reps[i % len(reps)][1].ccache, q, kv, max_ctx + 1, ohat, wss[0],
+                           num_splits=splits, stream=stream)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(args.steps):
+        M.decode_attention(layer.cdims, reps[i % len(reps)][1].ccache, q, kv, max_ctx + 1, ohat, wss[0],
+                           num_splits=splits, stream=stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    attn_ms = ev0.elapsed_time(ev1) / args.steps
+    core_bytes = attn_core_bytes(dims, lens, B)
+    achieved = core_bytes / (attn_ms / 1e3) / 1e9
+    traffic = counters_for("decode_attn.hip", args.workload)
+
+    cache_b, weight_b, io_b = decode_bytes(dims, lens, B)
+    step_bytes = cache_b + weight_b + io_b
+    attn_f, proj_f = decode_flops(dims, lens, B)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(dims, W_np, lens, w.hidden, args.cpu_seconds)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dims.dtype,
+        "data": "synthetic (seeded weights N(0,0.02), RMS-normalised N(0,1) hidden states, random page order)",
+        "config": {"workload": w.name, "batch": B, "ctx_tokens": [int(min(lens)), int(max(lens))],
+                   "d_model": dims.d_model, "n_h": dims.n_h, "d_h": dims.d_h, "d_c": dims.d_c, "d_cq": dims.d_cq,
+                   "d_hr": dims.d_hr, "block_size": w.block_size, "num_splits": splits, "replicas": len(reps)},
+        "step_GBps": round(step_bytes / (ms / 1e3) / 1e9, 1),
+        "step_hbm_frac": round(step_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "step_bytes": step_bytes,
+        "step_TFLOPs": round((attn_f + proj_f) / (ms / 1e3) / 1e12, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "kernel": "decode latent attention (+ split-KV combine when num_splits > 1)",
+                     "kernel_ms": round(attn_ms, 5), "algorithmic_bytes": core_bytes,
+                     "mfma_TFLOPs": round(attn_f / (attn_ms / 1e3) / 1e12, 1),
+                     "mfma_frac": round(attn_f / (attn_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
+        "cpu_baseline": cpu,
+        "setup_s": round(setup_s, 1),
+    }
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()

@@ -136,10 +136,10 @@ def latent_attention(qcat: np.ndarray, cache: np.ndarray, kv_len, scale: float, 
     L = cache.shape[0]
     kv_len = np.asarray(kv_len)
     mask = np.arange(L)[None, :] < kv_len[:, None]
-    s = np.einsum("nie,le->nil", qcat, cache) * scale
+    s = (qcat @ cache.T) * scale  # [n, n_h, L]
     s = np.where(mask[:, None, :], s, -np.inf)
     p, lse = softmax_rows(s)
-    return np.einsum("nil,lc->nic", p, cache[:, :d_c]), lse
+    return p @ cache[:, :d_c], lse
 
 
 def absorb_query(W: dict, dims, qc, qr) -> np.ndarray:
@@ -209,10 +209,17 @@ def mla_decode(W: dict, dims, h_new: np.ndarray, caches, absorbed: bool = False)
     return {"u": u, "o": o, "entry": entry, "lse": lse}
 
 
-def mla_decode_rows(W: dict, dims, h_new: np.ndarray, caches, rows) -> dict:
-    """mla_decode for the batch rows in `rows` only (sampled checks at large sizes)."""
-    sub = mla_decode(W, dims, np.asarray(h_new)[list(rows)], [caches[r] for r in rows])
-    return sub
+def mla_prefill_rows(W: dict, dims, h: np.ndarray, rows, cache=None) -> dict:
+    """mla_prefill's u, o and lse for the query rows `rows` of one sequence only (positions
+    0..T-1), through the absorbed form so that no per-head key/value rebuild over all T tokens is
+    needed (sampled checks at large sizes).  cache: the sequence's entries if already known."""
+    h = np.asarray(h)
+    rows = np.asarray(rows)
+    if cache is None:
+        cache = latent_entries(W, dims, h[: int(rows.max()) + 1], np.arange(int(rows.max()) + 1))
+    qc, qr = query(W, dims, h[rows], rows)
+    o, lse = attend_absorbed(W, dims, qc, qr, cache, rows + 1)
+    return {"u": output(W, dims, o), "o": o, "lse": lse}
 
 
 def cache_values_per_token(dims) -> int:

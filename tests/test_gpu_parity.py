@@ -162,3 +162,72 @@ def test_tiny_prefill_then_four_decode_steps():
         torch.cuda.synchronize()
         check(ud.cpu().numpy()[0], ref["u"][t], dims.dtype, f"decode step t={t}")
     check(pool.read_entries(0, 20), ref["cache"], dims.dtype, "cache after 4 steps")
+
+
+# ----------------------------------------------------------------------------- properties
+def _decode_u(layer, pool, h, lens, splits):
+    dims = layer.dims
+    B = len(lens)
+    u = torch.empty((B, dims.d_model), dtype=WL.torch_dtype(dims), device="cuda")
+    ctx = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    M.decode(layer.cdims, layer.cweights, pool.ccache, WL.to_device(h, dims), ctx, max(lens), u,
+             WL.decode_workspace(layer, B, max(lens), splits), num_splits=splits)
+    torch.cuda.synchronize()
+    return u.float().cpu().numpy()
+
+
+def test_split_count_invariance_and_page_permutation_invariance():
+    """Splitting the context into 1, 2, 7 or the automatic number of partitions changes only
+    fp32 rounding; placing the same logical context in other physical pages changes nothing."""
+    dims, recipe = SMALL["v2"]
+    W = S.make_weights(dims)
+    layer = WL.DeviceLayer(dims, W)
+    lens = [300, 77, 511]
+    pool = WL.PagedPool(dims, [L + 1 for L in lens])
+    WL.build_context(layer, pool, lens, recipe)
+    h = S.hidden_step(dims, len(lens), recipe)
+    base = _decode_u(layer, pool.clone(), h, lens, 1)
+    for sp in (2, 7, 0):
+        got = _decode_u(layer, pool.clone(), h, lens, sp)
+        assert np.max(np.abs(got - base)) <= 2e-3 * np.max(np.abs(base)), sp
+    pool2 = WL.PagedPool(dims, [L + 1 for L in lens], seed=99)
+    WL.build_context(layer, pool2, lens, recipe)
+    assert not np.array_equal(pool2.table_np, pool.table_np)
+    for sp in (1, 0):
+        assert np.array_equal(_decode_u(layer, pool2.clone(), h, lens, sp), _decode_u(layer, pool.clone(), h, lens, sp))
+
+
+def test_checkpoint_restore_continues_bit_identically():
+    """The caller-owned cache is the only state: copy pool and table to the host, restore them
+    into fresh device buffers and keep decoding; outputs equal the uninterrupted run bit for bit."""
+    dims, recipe = SMALL["v2lite"]
+    layer = WL.DeviceLayer(dims, S.make_weights(dims))
+    lens = [100, 37]
+    pool = WL.PagedPool(dims, [L + 3 for L in lens])
+    WL.build_context(layer, pool, lens, recipe)
+    snap = (pool.pool.cpu(), pool.block_table.cpu())
+    hs = [S.hidden_step(dims, 2, recipe, step=k) for k in range(3)]
+    ref = [_decode_u(layer, pool, hs[k], [L + k for L in lens], 0) for k in range(3)]
+    restored = WL.PagedPool(dims, [L + 3 for L in lens])
+    restored.pool.copy_(snap[0].cuda())
+    restored.block_table.copy_(snap[1].cuda())
+    got = [_decode_u(layer, restored, hs[k], [L + k for L in lens], 0) for k in range(3)]
+    for k in range(3):
+        assert np.array_equal(got[k], ref[k]), k
+
+
+@pytest.mark.parametrize("name", ["tiny", "v2"])
+def test_decode_step_equals_prefill_row(name):
+    """Decoding token t over the t entries a prefill wrote reproduces prefill row t."""
+    dims, recipe = SMALL[name]
+    layer = WL.DeviceLayer(dims, S.make_weights(dims))
+    T = 97
+    h = S.hidden_history(dims, 0, T + 1, recipe)
+    pool = WL.PagedPool(dims, [T + 1], block_size=64)
+    u = torch.empty((1, T + 1, dims.d_model), dtype=WL.torch_dtype(dims), device="cuda")
+    M.prefill(layer.cdims, layer.cweights, pool.ccache, WL.to_device(h[None], dims), u,
+              WL.prefill_workspace(layer, 1, T + 1))
+    torch.cuda.synchronize()
+    row = u[0, T].float().cpu().numpy()
+    got = _decode_u(layer, pool, h[T:T + 1], [T], 0)[0]
+    check(got, row, dims.dtype, f"{name} decode vs prefill row")

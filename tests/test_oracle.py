@@ -273,6 +273,19 @@ def test_decode_step_equals_prefill_row(dims):
         assert _rel(dec["entry"][0], pre["cache"][t]) < 1e-14
 
 
+def test_prefill_rows_equals_prefill():
+    dims = S.TINY
+    W = _rand_weights(dims, 24, std=0.3)
+    h = np.random.default_rng(25).standard_normal((11, dims.d_model))
+    whole = O.mla_prefill(W, dims, h)
+    rows = np.array([0, 3, 10])
+    sub = O.mla_prefill_rows(W, dims, h, rows)
+    assert _rel(sub["u"], whole["u"][rows]) < 1e-12
+    assert _rel(sub["o"], whole["o"][rows]) < 1e-12
+    sub2 = O.mla_prefill_rows(W, dims, h, rows, cache=whole["cache"])
+    assert _rel(sub2["u"], whole["u"][rows]) < 1e-12
+
+
 def test_chunked_prefill_equals_whole():
     dims = S.TINY
     W = _rand_weights(dims, 21, std=0.3)
