@@ -96,7 +96,8 @@ typedef struct {
  *   MLA_OP_PREFILL:      batch sequences of max_tokens tokens each.
  *   MLA_OP_DECODE:       batch sequences, max_ctx_len = largest ctx_lens[b] the call may see,
  *                        num_splits = the value that will be passed to mla_decode (0 = auto).
- * Pass the same sizes to the entry point.  Returns MLA_OK or MLA_ERR_INVALID_ARG/UNSUPPORTED.
+ * The size is an upper bound for every call whose sizes (batch, tokens, context) do not exceed
+ * these, with the same num_splits.  Returns MLA_OK or MLA_ERR_INVALID_ARG/UNSUPPORTED.
  */
 int mla_workspace_size(const mla_dims *dims, int op, int32_t batch, int32_t max_tokens,
                        int32_t max_ctx_len, int32_t num_splits, size_t *bytes);

@@ -232,6 +232,17 @@ GemmPlan gemm_plan(int M, int N, int K, int batch, int cus) {
   return pl;
 }
 
+size_t gemm_partial_bound(int M, int N, int K, int batch, int cus) {
+  // every tile height is a multiple of 32, so within a 32-row bucket the split count is fixed
+  // and the partial size grows with M: the bucket tops (and M itself) are the only candidates
+  size_t best = 0;
+  for (int m = 32; m < M + 32; m += 32) {
+    const int mm = std::min(m, M);
+    best = std::max(best, gemm_plan(mm, N, K, batch, cus).partial_bytes);
+  }
+  return best;
+}
+
 hipError_t gemm_run(DType t, const GemmParams& p, const GemmPlan& plan, float* partial, hipStream_t s) {
   if (p.M == 0 || p.N == 0 || p.batch == 0) return hipSuccess;
   return t == DType::BF16 ? run_t<bf16>(p, plan, partial, s) : run_t<float>(p, plan, partial, s);

@@ -57,6 +57,9 @@ struct GemmPlan {
 };
 
 GemmPlan gemm_plan(int M, int N, int K, int batch, int cus);
+// Largest partial_bytes of gemm_plan(m, ...) over 1 <= m <= M (workspace sized for M then also
+// serves every smaller call).
+size_t gemm_partial_bound(int M, int N, int K, int batch, int cus);
 // Launches the GEMM (and its split-K reduction).  `partial` must hold plan.partial_bytes.
 hipError_t gemm_run(DType t, const GemmParams& p, const GemmPlan& plan, float* partial,
                     hipStream_t s);

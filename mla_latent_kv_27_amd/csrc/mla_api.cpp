@@ -86,17 +86,24 @@ AppendWs carve_append(Carve& cv, const mla_dims* d, int n, int cus) {
   AppendWs w;
   w.plan = gemm_plan(n, entry(d), d->d_model, 1, cus);
   w.rope = cv.take<float2>((size_t)n * (d->d_hr / 2) * sizeof(float2));
-  w.partial = cv.take<float>(w.plan.partial_bytes);
+  w.partial = cv.take<float>(gemm_partial_bound(n, entry(d), d->d_model, 1, cus));
   return w;
 }
 
 struct DecodeGemms {
   GemmPlan cq, qc, qr, kv, absorb, uv, out;
-  size_t max_partial() const {
-    return std::max({cq.partial_bytes, qc.partial_bytes, qr.partial_bytes, kv.partial_bytes, absorb.partial_bytes,
-                     uv.partial_bytes, out.partial_bytes});
-  }
 };
+// partial workspace serving every batch <= B
+size_t decode_partial_bound(const mla_dims* d, int B, int cus) {
+  size_t b = std::max({gemm_partial_bound(B, d->n_h * d->d_h, q_in(d), 1, cus),
+                       gemm_partial_bound(B, d->n_h * d->d_hr, q_in(d), 1, cus),
+                       gemm_partial_bound(B, entry(d), d->d_model, 1, cus),
+                       gemm_partial_bound(B, d->d_c, d->d_h, d->n_h, cus),
+                       gemm_partial_bound(B, d->d_h, d->d_c, d->n_h, cus),
+                       gemm_partial_bound(B, d->d_model, d->n_h * d->d_h, 1, cus)});
+  if (d->d_cq > 0) b = std::max(b, gemm_partial_bound(B, d->d_cq, d->d_model, 1, cus));
+  return b;
+}
 DecodeGemms decode_gemms(const mla_dims* d, int B, int cus) {
   DecodeGemms g;
   g.cq = d->d_cq > 0 ? gemm_plan(B, d->d_cq, d->d_model, 1, cus) : GemmPlan{};
@@ -113,15 +120,30 @@ struct AttnWs {
   float *pm, *pl, *po;
   int splits, tps;
 };
-AttnWs carve_attn(Carve& cv, const mla_dims* d, int B, int max_kv_len, int splits) {
-  AttnWs a;
+int split_count(int max_kv_len, int splits, int* tps) {
   const int tiles = (max_kv_len + decode_tile_tokens() - 1) / decode_tile_tokens();
-  a.tps = std::max(1, (tiles + splits - 1) / splits);
-  a.splits = std::max(1, (tiles + a.tps - 1) / a.tps);
-  const size_t n = (size_t)B * a.splits * d->n_h;
-  a.pm = cv.take<float>(a.splits > 1 ? n * sizeof(float) : 0);
-  a.pl = cv.take<float>(a.splits > 1 ? n * sizeof(float) : 0);
-  a.po = cv.take<float>(a.splits > 1 ? n * d->d_c * sizeof(float) : 0);
+  *tps = std::max(1, (tiles + splits - 1) / splits);
+  return std::max(1, (tiles + *tps - 1) / *tps);
+}
+// Partial rows serving every batch <= B and context <= max_kv_len.  split_count never exceeds
+// the requested count, and the automatic count grows with the context, so the request at
+// max_kv_len bounds every smaller call.  splits_raw == 0: automatic choice.
+size_t attn_rows_bound(const mla_dims* d, int B, int max_kv_len, int splits_raw, int cus) {
+  size_t best = 0;
+  for (int b = 1; b <= B; ++b) {
+    const int req = splits_raw > 0 ? splits_raw : auto_splits(d, b, max_kv_len - 1, cus);
+    if (req > 1) best = std::max(best, (size_t)b * req * d->n_h);
+  }
+  return best;
+}
+AttnWs carve_attn(Carve& cv, const mla_dims* d, int B, int max_kv_len, int splits_raw, int cus) {
+  AttnWs a;
+  const int req = splits_raw > 0 ? splits_raw : auto_splits(d, B, max_kv_len - 1, cus);
+  a.splits = split_count(max_kv_len, req, &a.tps);
+  const size_t n = attn_rows_bound(d, B, max_kv_len, splits_raw, cus);
+  a.pm = cv.take<float>(n * sizeof(float));
+  a.pl = cv.take<float>(n * sizeof(float));
+  a.po = cv.take<float>(n * d->d_c * sizeof(float));
   return a;
 }
 
@@ -134,6 +156,7 @@ struct DecodeWs {
   float* partial;
   DecodeGemms gm;
 };
+// splits: the caller's num_splits (0 = automatic)
 DecodeWs carve_decode(Carve& cv, const mla_dims* d, int B, int max_ctx_len, int splits, int cus) {
   DecodeWs w;
   const size_t es = dsize(dt(d));
@@ -146,8 +169,8 @@ DecodeWs carve_decode(Carve& cv, const mla_dims* d, int B, int max_ctx_len, int 
   w.qcat = cv.take<char>((size_t)B * d->n_h * entry(d) * es);
   w.ohat = cv.take<char>((size_t)B * d->n_h * d->d_c * es);
   w.o = cv.take<char>((size_t)B * d->n_h * d->d_h * es);
-  w.attn = carve_attn(cv, d, B, max_ctx_len + 1, splits);
-  w.partial = cv.take<float>(w.gm.max_partial());
+  w.attn = carve_attn(cv, d, B, max_ctx_len + 1, splits, cus);
+  w.partial = cv.take<float>(decode_partial_bound(d, B, cus));
   return w;
 }
 
@@ -181,8 +204,13 @@ PrefillWs carve_prefill(Carve& cv, const mla_dims* d, int S, int T, int cus) {
   w.kp = cv.take<char>((size_t)M * d->n_h * d->d_h * es);
   w.vt = cv.take<char>((size_t)d->n_h * d->d_h * S * w.Tp * es);
   w.o = cv.take<char>((size_t)M * d->n_h * d->d_h * es);
-  const size_t mp = std::max({w.cq_p.partial_bytes, w.qc_p.partial_bytes, w.qr_p.partial_bytes, w.kv_p.partial_bytes,
-                              w.k_p.partial_bytes, w.v_p.partial_bytes, w.out_p.partial_bytes});
+  size_t mp = std::max({gemm_partial_bound(M, d->n_h * d->d_h, q_in(d), 1, cus),
+                        gemm_partial_bound(M, d->n_h * d->d_hr, q_in(d), 1, cus),
+                        gemm_partial_bound(M, entry(d), d->d_model, 1, cus),
+                        gemm_partial_bound(M, d->n_h * d->d_h, d->d_c, 1, cus),
+                        gemm_partial_bound(d->n_h * d->d_h, M, d->d_c, 1, cus),
+                        gemm_partial_bound(M, d->d_model, d->n_h * d->d_h, 1, cus)});
+  if (d->d_cq > 0) mp = std::max(mp, gemm_partial_bound(M, d->d_cq, d->d_model, 1, cus));
   w.partial = cv.take<float>(mp);
   return w;
 }
@@ -265,8 +293,7 @@ int mla_workspace_size(const mla_dims* d, int op, int32_t batch, int32_t max_tok
       break;
     case MLA_OP_DECODE: {
       if (batch <= 0 || max_ctx_len < 0 || num_splits < 0) return MLA_ERR_INVALID_ARG;
-      const int sp = num_splits > 0 ? num_splits : auto_splits(d, batch, max_ctx_len, cus);
-      carve_decode(cv, d, batch, max_ctx_len, sp, cus);
+      carve_decode(cv, d, batch, max_ctx_len, num_splits, cus);
       break;
     }
     default: return MLA_ERR_INVALID_ARG;
@@ -304,12 +331,11 @@ int mla_decode_attention(const mla_dims* d, const mla_paged_cache* c, const void
   if ((int64_t)max_kv_len > (int64_t)c->max_blocks_per_seq * c->block_size) return MLA_ERR_INVALID_ARG;
   if (!decode_supported(d->d_c, d->d_hr)) return MLA_ERR_UNSUPPORTED;
   const int cus = device_cus();
-  const int sp = num_splits > 0 ? num_splits : auto_splits(d, batch, max_kv_len - 1, cus);
   Carve sz(nullptr);
-  carve_decode(sz, d, batch, max_kv_len - 1, sp, cus);
+  carve_decode(sz, d, batch, max_kv_len - 1, num_splits, cus);
   if (!workspace || ws_bytes < sz.off) return MLA_ERR_WORKSPACE;
   Carve cv(workspace);
-  DecodeWs ws = carve_decode(cv, d, batch, max_kv_len - 1, sp, cus);
+  DecodeWs ws = carve_decode(cv, d, batch, max_kv_len - 1, num_splits, cus);
   DecodeAttnParams a{};
   a.q = q;
   a.pool = c->pool;
@@ -347,12 +373,11 @@ int mla_decode(const mla_dims* d, const mla_weights* w, const mla_paged_cache* c
   if ((int64_t)max_ctx_len + 1 > (int64_t)c->max_blocks_per_seq * c->block_size) return MLA_ERR_INVALID_ARG;
   if (!decode_supported(d->d_c, d->d_hr)) return MLA_ERR_UNSUPPORTED;
   const int cus = device_cus();
-  const int sp = num_splits > 0 ? num_splits : auto_splits(d, batch, max_ctx_len, cus);
   Carve sz(nullptr);
-  carve_decode(sz, d, batch, max_ctx_len, sp, cus);
+  carve_decode(sz, d, batch, max_ctx_len, num_splits, cus);
   if (!workspace || ws_bytes < sz.off) return MLA_ERR_WORKSPACE;
   Carve cv(workspace);
-  DecodeWs ws = carve_decode(cv, d, batch, max_ctx_len, sp, cus);
+  DecodeWs ws = carve_decode(cv, d, batch, max_ctx_len, num_splits, cus);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const DType t = dt(d);
   const int B = batch, E = entry(d), qw = q_in(d);

@@ -120,3 +120,17 @@ def test_workspace_sizes_grow_with_work():
     assert 0 < p1 < p2
     with pytest.raises(M.MlaError):
         M.workspace_size(d, 9)
+
+
+def test_workspace_for_max_sizes_serves_every_smaller_call():
+    """A workspace sized for (n, batch, context) also fits every call with smaller sizes."""
+    d = M.make_dims(5120, 128, 128, 512, 1536, 64, "bf16")
+    big = M.workspace_size(d, M.OP_CACHE_APPEND, max_tokens=8192)
+    assert all(M.workspace_size(d, M.OP_CACHE_APPEND, max_tokens=n) <= big for n in range(1, 8193, 97))
+    big = M.workspace_size(d, M.OP_DECODE, batch=64, max_ctx_len=8192)
+    for b in (1, 3, 5, 6, 17, 63, 64):
+        for ctx in (0, 100, 4095, 8192):
+            assert M.workspace_size(d, M.OP_DECODE, batch=b, max_ctx_len=ctx) <= big, (b, ctx)
+    big = M.workspace_size(d, M.OP_DECODE, batch=4, max_ctx_len=131072, num_splits=7)
+    for ctx in (1, 700, 22 * 32, 21 * 32, 131071):
+        assert M.workspace_size(d, M.OP_DECODE, batch=4, max_ctx_len=ctx, num_splits=7) <= big
