@@ -144,7 +144,9 @@ __global__ void __launch_bounds__(64 * NW) decode_attn_kernel(DecodeAttnParams p
     for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float e = exp2f(s[tb][j] - m_new);
+        // the sum uses the probabilities as rounded for the PV product, so the weights applied
+        // to the latent rows sum to exactly the normaliser
+        const float e = to_f32(from_f32<T>(exp2f(s[tb][j] - m_new)));
         sum += e;
         set8(pf, tb * 4 + j, e);
       }

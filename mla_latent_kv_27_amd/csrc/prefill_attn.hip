@@ -132,7 +132,7 @@ __global__ void __launch_bounds__(256) prefill_attn_kernel(PrefillAttnParams p) 
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float e = exp2f(sc[kb][r] - m_use);
+        const float e = to_f32(from_f32<T>(exp2f(sc[kb][r] - m_use)));  // as rounded for PV
         sc[kb][r] = e;
         sum += e;
       }

@@ -202,11 +202,15 @@ def test_split_count_invariance_and_page_permutation_invariance():
         torch.cuda.synchronize()
         return o.float().cpu().numpy(), lse.cpu().numpy()
 
+    # probabilities enter the PV product rounded to bf16 relative to each partition's running
+    # max, so two split counts differ by at most ~2^-8 of the largest latent value, plus a
+    # rounding step of o_hat itself
+    cmax = max(float(np.max(np.abs(pool.read_entries(b, L)[:, :dims.d_c]))) for b, L in enumerate(lens))
     o1, l1 = core(1)
     for sp in (2, 7, 0):
         o2, l2 = core(sp)
         assert np.max(np.abs(l2 - l1)) <= 1e-5 * np.max(np.abs(l1)), sp
-        assert np.all(np.abs(o2 - o1) <= 2.0 ** -8 * np.abs(o1) + 1e-6), sp
+        assert np.all(np.abs(o2 - o1) <= 2.0 ** -8 * cmax + 2.0 ** -7 * np.abs(o1)), sp
         check(_decode_u(layer, pool.clone(), h, lens, sp), base, dims.dtype, f"u with {sp} splits")
     pool2 = WL.PagedPool(dims, [L + 1 for L in lens], seed=99)
     WL.build_context(layer, pool2, lens, recipe)
