@@ -178,9 +178,10 @@ def _decode_u(layer, pool, h, lens, splits):
 
 def test_split_count_invariance_and_page_permutation_invariance():
     """Splitting the context into 1, 2, 7 or the automatic number of partitions changes only
-    fp32 rounding: the attention core's log-sum-exp agrees to fp32 accuracy and o_hat to one bf16
-    rounding step; the full step agrees to the parity tolerance (o_hat is stored as bf16 before
-    W_UV).  Placing the same logical context in other physical pages changes nothing at all."""
+    rounding: probabilities enter the PV product as bf16 relative to each partition's running
+    max, so the core's log-sum-exp and o_hat agree to that rounding, and the full step agrees to
+    the parity tolerance.  Placing the same logical context in other physical pages changes
+    nothing at all."""
     dims, recipe = SMALL["v2"]
     W = S.make_weights(dims)
     layer = WL.DeviceLayer(dims, W)
@@ -209,7 +210,9 @@ def test_split_count_invariance_and_page_permutation_invariance():
     o1, l1 = core(1)
     for sp in (2, 7, 0):
         o2, l2 = core(sp)
-        assert np.max(np.abs(l2 - l1)) <= 1e-5 * np.max(np.abs(l1)), sp
+        # the normaliser sums the rounded probabilities: each within 2^-9 relative, so the two
+        # log-sum-exps differ by at most 2 * 2^-9 in natural-log units
+        assert np.max(np.abs(l2 - l1)) <= 2.0 ** -8, sp
         assert np.all(np.abs(o2 - o1) <= 2.0 ** -8 * cmax + 2.0 ** -7 * np.abs(o1)), sp
         check(_decode_u(layer, pool.clone(), h, lens, sp), base, dims.dtype, f"u with {sp} splits")
     pool2 = WL.PagedPool(dims, [L + 1 for L in lens], seed=99)
