@@ -63,8 +63,9 @@ __global__ void __launch_bounds__(64 * NW) decode_attn_kernel(DecodeAttnParams p
 
   const int kv_len = p.lens[b] + (p.lens_plus_one ? 1 : 0);
   const int ntiles = (kv_len + kTile - 1) / kTile;
-  const int t_begin = split * p.tiles_per_split;
-  const int t_end = min(ntiles, t_begin + p.tiles_per_split);
+  const int tps = p.tokens_per_split / kTile;
+  const int t_begin = split * tps;
+  const int t_end = min(ntiles, t_begin + tps);
 
   // Q^T fragments (B operand): head = hl, k = 8g..8g+7 of every 32-chunk.
   Frag8<T> q[Sh::KCH];
@@ -185,6 +186,258 @@ __global__ void __launch_bounds__(64 * NW) decode_attn_kernel(DecodeAttnParams p
   for (int d = 0; d < Sh::DB; ++d) *reinterpret_cast<floatx4*>(po + d * 16 + 4 * g) = o[d];
 }
 
+// ----------------------------------------------------------------------------- tiled kernel
+// The DeepSeek-V2-sized bf16 case (d_c = 512, d_hr = 64): eight waves of 16 heads share 64-token
+// tiles that arrive by direct global->LDS copies, double-buffered so that the next tile streams
+// in while the current one is multiplied.
+//   * LDS row of a token = its 1152-byte cache entry as 72 16-byte chunks; chunk c of token t is
+//     stored at chunk slot t*72 + (c ^ (t & 7)) so that the 16 tokens of an MFMA operand read
+//     fall on different banks.
+//   * S^T = K Q^T with 16x16x32 MFMA: A = 16 tokens x 32 latent dims (ds_read_b128),
+//     B = Q^T held in registers for the whole kernel (18 k-chunks x 8 values).
+//   * O^T = V^T P^T: the A operand (16 latent dims x 32 tokens) is read straight from the
+//     token-major tile with the gfx950 LDS transpose read (ds_read_b64_tr_b16): within each
+//     16-lane group, source lane s supplies 4 consecutive dims of token 4j + s/4 and lane i
+//     receives dim i of those four tokens.
+//   * softmax scaling is lazy: the running max is only raised (and O rescaled) when a tile's
+//     max exceeds it by more than 2^8, which keeps every probability <= 256.
+namespace tiled {
+constexpr int kT = 64;                    // tokens per tile
+constexpr int kD = 576, kDC = 512;        // entry width, latent width
+constexpr int kCPR = kD * 2 / 16;         // 72 chunks per entry
+constexpr int kRow = kCPR * 16;           // 1152 bytes per entry
+constexpr int kBytes = kT * kRow;         // 73728
+constexpr int kWaves = 8;
+constexpr int kDmaPerWave = kT * kCPR / (64 * kWaves);  // 9
+constexpr float kLazy = 8.f;              // log2 headroom before a rescale
+}  // namespace tiled
+
+__shared__ __attribute__((aligned(1024))) char g_kv0[tiled::kBytes];
+__shared__ __attribute__((aligned(1024))) char g_kv1[tiled::kBytes];
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) shortx4 lds_shortx4_t;
+
+template <int BUF>
+__device__ __forceinline__ char* kv_buf() { return BUF ? g_kv1 : g_kv0; }
+
+// s_waitcnt immediates (gfx9 encoding): vmcnt in bits [3:0] and [15:14], expcnt [6:4],
+// lgkmcnt [11:8]; the unused counters are left at their maximum.
+constexpr int waitcnt_vm(int n) { return ((n >> 4) << 14) | (0xF << 8) | (0x7 << 4) | (n & 0xF); }
+constexpr int kWaitLgkm0 = (0x3 << 14) | (0x7 << 4) | 0xF;
+
+// Workgroup barrier for the double-buffered pipeline: waits only on what the caller asked for
+// (unlike __syncthreads, whose release fence would also wait for the prefetch in flight), and
+// compiler-only fences keep LDS accesses from being moved across it.
+#define MLA_TILE_BARRIER(waitcnt_imm)            \
+  do {                                           \
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);     \
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm);     \
+    __builtin_amdgcn_s_barrier();                \
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);     \
+  } while (0)
+
+struct TiledCtx {
+  const char* pool;
+  const int32_t* bt;
+  int bs, kv_len;
+};
+
+// This wave's 9 direct-to-LDS copies of tile `tile` into buffer BUF.  block_size is a multiple
+// of 64, so a tile lies inside one block: one uniform block-table lookup, and every row copied
+// is a row of an allocated block (rows past the context are zeroed once the copies land).
+template <int BUF>
+__device__ __forceinline__ void issue_tile(const TiledCtx& c, int tile, int w, int lane) {
+  using namespace tiled;
+  char* dst = kv_buf<BUF>();
+  const int tok0 = tile * kT;
+  const int blk = tok0 / c.bs;
+  const char* base = c.pool + ((int64_t)c.bt[blk] * c.bs + (tok0 - blk * c.bs)) * kRow;
+  int ln = lane;
+  asm volatile("" : "+v"(ln));  // recompute the lane offsets here instead of keeping 9 live
+#pragma unroll
+  for (int i = 0; i < kDmaPerWave; ++i) {
+    const int P = (w * kDmaPerWave + i) * 64 + ln;
+    const int t = P / kCPR;
+    const int ch = (P - t * kCPR) ^ (t & 7);
+    __builtin_amdgcn_global_load_lds((const void*)(base + (uint32_t)(t * kRow + ch * 16)),
+                                     (lds_void_t*)(dst + (w * kDmaPerWave + i) * 1024), 16, 0, 0);
+  }
+}
+
+template <int BUF>
+__device__ __forceinline__ void tiled_compute(const Frag8<bf16> (&q)[18], floatx4 (&o)[32], float& m_run,
+                                              float& l_run, int t, int kv_len, float scale_log2, int lane) {
+  using namespace tiled;
+  const char* buf = kv_buf<BUF>();
+  const int g = lane >> 4, l16 = lane & 15;
+  // ---- S^T = K Q^T : four 16-token blocks; lane holds head l16, tokens 16*tb + 4g + j
+  floatx4 sc[4];
+  {
+    // chunk (4kc + g) of token l16 sits at slot (4kc + g) ^ (l16 & 7): two lane-constant bases
+    // (kc parity); 128 bytes per kc pair and 16 rows per token block are immediates
+    const int x = l16 & 7;
+    const char* rb[2];
+#pragma unroll
+    for (int par = 0; par < 2; ++par) rb[par] = buf + l16 * kRow + ((4 * par + g) ^ x) * 16;
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) sc[tb] = floatx4{0, 0, 0, 0};
+#pragma unroll
+    for (int kc = 0; kc < 18; ++kc) {
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        Frag8<bf16> a;
+        a.v = *reinterpret_cast<const bf16x8*>(rb[kc & 1] + 128 * (kc >> 1) + tb * 16 * kRow);
+        sc[tb] = mma16(a, q[kc], sc[tb]);
+      }
+    }
+  }
+  // ---- online softmax over the 64 tokens (the 4 lane groups sharing a head exchange via xor)
+  float mx = -INFINITY;
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int tok = t * kT + tb * 16 + 4 * g + j;
+      const float v = tok < kv_len ? sc[tb][j] * scale_log2 : -INFINITY;
+      sc[tb][j] = v;
+      mx = fmaxf(mx, v);
+    }
+  mx = wave_max_xor(mx, 16);
+  mx = wave_max_xor(mx, 32);
+  if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazy) != 0) {  // wave-uniform rescale
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = exp2f(m_run - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int d = 0; d < 32; ++d) o[d] *= alpha;
+    m_run = m_new;
+  }
+  float sum = 0.f;
+  Frag8<bf16> pf[2];  // k-chunk kc2: slot s = token 32 kc2 + 16 (s/4) + 4g + s%4
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bf16 e = (bf16)exp2f(sc[tb][j] - m_run);
+      sum += (float)e;
+      pf[tb >> 1].v[(tb & 1) * 4 + j] = e;
+    }
+  sum = wave_sum_xor(sum, 16);
+  sum = wave_sum_xor(sum, 32);
+  l_run += sum;
+  // ---- O^T += V^T P^T : 32 blocks of 16 latent dims, 2 k-chunks of 32 tokens
+  // lane group g reads tokens 4g + s/4 (+16 for the second read) of each 32-token chunk; source
+  // lane s supplies dims 16 d + 4 (s % 4) .. +3 = chunk 2d + (s%4)/2, byte (s % 2) * 8
+  const int s4 = lane & 15;
+  const int x = (4 * g + (s4 >> 2)) & 7;
+  const int clo = (s4 & 3) >> 1;
+  const char* vb[4];
+#pragma unroll
+  for (int par = 0; par < 4; ++par)
+    vb[par] = buf + (4 * g + (s4 >> 2)) * kRow + (s4 & 1) * 8 + ((2 * par + clo) ^ x) * 16;
+#pragma unroll
+  for (int kc2 = 0; kc2 < 2; ++kc2)
+#pragma unroll
+    for (int d = 0; d < 32; ++d) {
+      const char* pv = vb[d & 3] + 128 * (d >> 2) + kc2 * 32 * kRow;
+      const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)pv);
+      const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)(pv + 16 * kRow));
+      Frag8<bf16> a;
+      a.v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      o[d] = mma16(a, pf[kc2], o[d]);
+    }
+}
+
+template <int CUR>
+__device__ __forceinline__ void tiled_step(const TiledCtx& c, const Frag8<bf16> (&q)[18], floatx4 (&o)[32],
+                                           float& m_run, float& l_run, int t, bool has_next, float scale_log2,
+                                           int w, int lane, int tid) {
+  using namespace tiled;
+  if (has_next) {
+    issue_tile<CUR ^ 1>(c, t + 1, w, lane);
+    MLA_TILE_BARRIER(waitcnt_vm(kDmaPerWave));  // this tile's copies have landed, the next's fly
+  } else {
+    MLA_TILE_BARRIER(waitcnt_vm(0));
+  }
+  const int valid = c.kv_len - t * kT;
+  if (valid < kT) {  // zero the rows past the end of the context (uniform branch)
+    char* buf = kv_buf<CUR>();
+    for (int i = tid; i < (kT - valid) * kCPR; i += 64 * kWaves) st16(buf + (valid * kCPR + i) * 16, zero16());
+    MLA_TILE_BARRIER(kWaitLgkm0);
+  }
+  tiled_compute<CUR>(q, o, m_run, l_run, t, c.kv_len, scale_log2, lane);
+  MLA_TILE_BARRIER(kWaitLgkm0);  // every wave is done reading before the buffer is refilled
+}
+
+__global__ void __launch_bounds__(512)
+    decode_attn_tiled_kernel(DecodeAttnParams p, int HG, const int32_t* __restrict__ block_table) {
+  using namespace tiled;
+  const int units = p.B * p.splits;
+  const int unit = blockIdx.x / HG, hg = blockIdx.x % HG;
+  if (unit >= units) return;
+  const int b = unit / p.splits, split = unit % p.splits;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4;
+  const int head = hg * (16 * kWaves) + w * 16 + (lane & 15);
+  const bool valid_head = head < p.n_h;
+
+  TiledCtx c;
+  c.pool = reinterpret_cast<const char*>(p.pool);
+  c.bt = block_table + (int64_t)b * p.max_blocks;  // read-only: block ids load as scalars
+  c.bs = p.block_size;
+  c.kv_len = p.lens[b] + (p.lens_plus_one ? 1 : 0);
+  const int ntiles = (c.kv_len + kT - 1) / kT;
+  const int tps = p.tokens_per_split / kT;
+  const int t_begin = split * tps;
+  const int t_end = min(ntiles, t_begin + tps);
+
+  Frag8<bf16> q[18];
+  {
+    const bf16* qrow = reinterpret_cast<const bf16*>(p.q) + ((int64_t)b * p.n_h + (valid_head ? head : 0)) * kD;
+#pragma unroll
+    for (int kc = 0; kc < 18; ++kc) {
+      if (valid_head) load8(q[kc], qrow + kc * 32 + 8 * g);
+      else zero8(q[kc]);
+    }
+  }
+  floatx4 o[32];
+#pragma unroll
+  for (int d = 0; d < 32; ++d) o[d] = floatx4{0, 0, 0, 0};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  if (t_begin < t_end) issue_tile<0>(c, t_begin, w, lane);
+  for (int t = t_begin; t < t_end; t += 2) {
+    tiled_step<0>(c, q, o, m_run, l_run, t, t + 1 < t_end, p.scale_log2, w, lane, tid);
+    if (t + 1 < t_end) tiled_step<1>(c, q, o, m_run, l_run, t + 1, t + 2 < t_end, p.scale_log2, w, lane, tid);
+  }
+
+  if (!valid_head) return;
+  if (p.splits == 1) {
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    bf16* out = reinterpret_cast<bf16*>(p.o_hat) + ((int64_t)b * p.n_h + head) * kDC;
+#pragma unroll
+    for (int d = 0; d < 32; ++d) {
+      bf16x4 v;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = (bf16)(o[d][r] * inv);
+      *reinterpret_cast<bf16x4*>(out + d * 16 + 4 * g) = v;
+    }
+    if (p.lse && g == 0) p.lse[(int64_t)b * p.n_h + head] = (m_run + log2f(l_run)) * 0.69314718055994531f;
+    return;
+  }
+  const int64_t pi = ((int64_t)b * p.splits + split) * p.n_h + head;
+  if (g == 0) {
+    p.part_m[pi] = m_run;
+    p.part_l[pi] = l_run;
+  }
+  float* po = p.part_o + pi * kDC;
+#pragma unroll
+  for (int d = 0; d < 32; ++d) *reinterpret_cast<floatx4*>(po + d * 16 + 4 * g) = o[d];
+}
+
 // Log-sum-exp combination of the partitions: M = max_s m_s, w_s = 2^(m_s - M),
 // o_hat = sum_s w_s O_s / sum_s w_s l_s.
 template <typename T, int DC>
@@ -214,16 +467,20 @@ __global__ void __launch_bounds__(128) decode_combine_kernel(DecodeAttnParams p)
 }
 
 // ----------------------------------------------------------------------------- host side
-int decode_tile_tokens() { return kTile; }
+bool decode_tiled(DType t, int d_c, int d_hr, int block_size) {
+  return t == DType::BF16 && d_c == 512 && d_hr == 64 && block_size % tiled::kT == 0;
+}
 
-int decode_heads_per_block(int n_h) { return n_h >= 128 ? 128 : (n_h >= 64 ? 64 : 16); }
+
+
+static int v1_heads_per_block(int n_h) { return n_h >= 128 ? 128 : (n_h >= 64 ? 64 : 16); }
 
 bool decode_supported(int d_c, int d_hr) { return (d_c == 512 && d_hr == 64) || (d_c == 32 && d_hr == 8); }
 
 namespace {
 template <typename T, int DC, int DR>
 hipError_t launch(const DecodeAttnParams& p, hipStream_t s) {
-  const int hpb = decode_heads_per_block(p.n_h);
+  const int hpb = v1_heads_per_block(p.n_h);
   const int HG = (p.n_h + hpb - 1) / hpb;
   const int units = p.B * p.splits;
   const int blocks = (units + 7) / 8 * 8 * HG;
@@ -241,6 +498,17 @@ hipError_t launch(const DecodeAttnParams& p, hipStream_t s) {
 }  // namespace
 
 hipError_t decode_attention(DType t, const DecodeAttnParams& p, hipStream_t s) {
+  if (decode_tiled(t, p.d_c, p.d_hr, p.block_size)) {
+    const int HG = (p.n_h + 16 * tiled::kWaves - 1) / (16 * tiled::kWaves);
+    const int units = p.B * p.splits;
+    if (units == 0) return hipSuccess;
+    hipLaunchKernelGGL(decode_attn_tiled_kernel, dim3(units * HG), dim3(64 * tiled::kWaves), 0, s, p, HG,
+                       p.block_table);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.splits == 1) return e;
+    hipLaunchKernelGGL((decode_combine_kernel<bf16, 512>), dim3(p.B * p.n_h), dim3(128), 0, s, p);
+    return hipGetLastError();
+  }
   if (p.d_c == 512 && p.d_hr == 64)
     return t == DType::BF16 ? launch<bf16, 512, 64>(p, s) : launch<float, 512, 64>(p, s);
   if (p.d_c == 32 && p.d_hr == 8)

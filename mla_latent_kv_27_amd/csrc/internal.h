@@ -83,7 +83,7 @@ struct DecodeAttnParams {
   int B, n_h, d_c, d_hr;
   float scale_log2;       // softmax scale * log2(e)
   int splits;
-  int tiles_per_split;    // in units of the kernel's token tile
+  int tokens_per_split;   // a multiple of 64
   float* part_m;          // [B][splits][n_h]   (log2 domain running max)
   float* part_l;          // [B][splits][n_h]
   float* part_o;          // [B][splits][n_h][d_c]
@@ -91,8 +91,6 @@ struct DecodeAttnParams {
   float* lse;             // optional [B][n_h], natural log
 };
 
-int decode_tile_tokens();
-int decode_heads_per_block(int n_h);
 bool decode_supported(int d_c, int d_hr);
 hipError_t decode_attention(DType t, const DecodeAttnParams& p, hipStream_t s);
 

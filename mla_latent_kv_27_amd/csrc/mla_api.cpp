@@ -66,13 +66,17 @@ int validate_cache(const mla_dims* d, const mla_paged_cache* c) {
   return MLA_OK;
 }
 
+// KV partitions are whole multiples of 64 tokens (a common multiple of every decode kernel's
+// tile), so the partition count, and with it the workspace, does not depend on which kernel
+// runs.
+constexpr int kSplitQuantum = 64;
+
 int auto_splits(const mla_dims* d, int batch, int max_ctx_len, int cus) {
-  const int hpb = decode_heads_per_block(d->n_h);
-  const int hg = (d->n_h + hpb - 1) / hpb;
-  const int tiles = (max_ctx_len + 1 + decode_tile_tokens() - 1) / decode_tile_tokens();
+  const int hg = (d->n_h + 127) / 128;
+  const int chunks = (max_ctx_len + 1 + kSplitQuantum - 1) / kSplitQuantum;
   const int units = batch * hg;
   int s = (cus + units - 1) / units;
-  s = std::min(s, std::max(1, tiles / 8));
+  s = std::min(s, std::max(1, chunks / 4));  // at least 256 tokens per partition
   return std::max(1, std::min(s, 64));
 }
 
@@ -120,10 +124,12 @@ struct AttnWs {
   float *pm, *pl, *po;
   int splits, tps;
 };
+// Partition count for a request of `splits`; *tps = tokens per partition.
 int split_count(int max_kv_len, int splits, int* tps) {
-  const int tiles = (max_kv_len + decode_tile_tokens() - 1) / decode_tile_tokens();
-  *tps = std::max(1, (tiles + splits - 1) / splits);
-  return std::max(1, (tiles + *tps - 1) / *tps);
+  const int chunks = (max_kv_len + kSplitQuantum - 1) / kSplitQuantum;
+  const int per = std::max(1, (chunks + splits - 1) / splits);
+  *tps = per * kSplitQuantum;
+  return std::max(1, (chunks + per - 1) / per);
 }
 // Partial rows serving every batch <= B and context <= max_kv_len.  split_count never exceeds
 // the requested count, and the automatic count grows with the context, so the request at
@@ -350,7 +356,7 @@ int mla_decode_attention(const mla_dims* d, const mla_paged_cache* c, const void
   a.d_hr = d->d_hr;
   a.scale_log2 = scale_of(d) * 1.4426950408889634f;
   a.splits = ws.attn.splits;
-  a.tiles_per_split = ws.attn.tps;
+  a.tokens_per_split = ws.attn.tps;
   a.part_m = ws.attn.pm;
   a.part_l = ws.attn.pl;
   a.part_o = ws.attn.po;
@@ -429,7 +435,7 @@ int mla_decode(const mla_dims* d, const mla_weights* w, const mla_paged_cache* c
     a.lens = ctx_lens; a.lens_plus_one = true;
     a.B = B; a.n_h = d->n_h; a.d_c = d->d_c; a.d_hr = d->d_hr;
     a.scale_log2 = scale_of(d) * 1.4426950408889634f;
-    a.splits = ws.attn.splits; a.tiles_per_split = ws.attn.tps;
+    a.splits = ws.attn.splits; a.tokens_per_split = ws.attn.tps;
     a.part_m = ws.attn.pm; a.part_l = ws.attn.pl; a.part_o = ws.attn.po;
     a.o_hat = ws.ohat; a.lse = nullptr;
     MLA_HIP(decode_attention(t, a, s));

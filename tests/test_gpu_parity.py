@@ -58,17 +58,19 @@ def test_cache_append_matches_oracle(name):
 
 
 # ----------------------------------------------------------------------------- decode core
-@pytest.mark.parametrize("name,lens,splits", [("tiny", [1, 17, 64, 100], 0), ("v2lite", [1, 33, 200, 64], 0),
-                                              ("v2lite", [300, 31], 3), ("v2", [1, 95, 257], 0),
-                                              ("v2", [257, 40], 2)])
-def test_decode_attention_core_matches_oracle(name, lens, splits):
+@pytest.mark.parametrize("name,lens,splits,block", [("tiny", [1, 17, 64, 100], 0, 16), ("v2lite", [1, 33, 200, 64], 0, 64),
+                                                    ("v2lite", [300, 31], 3, 64), ("v2", [1, 95, 257], 0, 64),
+                                                    ("v2", [257, 40], 2, 64), ("v2", [130, 3, 700], 0, 16),
+                                                    ("v2", [130, 3, 700], 4, 128), ("v2lite", [64, 128, 1], 0, 256)])
+def test_decode_attention_core_matches_oracle(name, lens, splits, block):
     """Kernel-isolated: queries and cache entries are random device values; the oracle reads the
-    same values back."""
+    same values back.  Block sizes that are multiples of 64 take the tiled kernel, others the
+    general one."""
     dims = SMALL[name][0]
     layer = WL.DeviceLayer(dims, S.make_weights(dims))
     B = len(lens)
     rng = np.random.default_rng(5)
-    pool = WL.PagedPool(dims, lens, block_size=64 if name != "tiny" else 16)
+    pool = WL.PagedPool(dims, lens, block_size=block)
     ent = S.to_dtype(rng.standard_normal((pool.pool.shape[0] * pool.pool.shape[1], dims.entry)).astype(np.float32),
                      dims.dtype)
     pool.pool.copy_(WL.to_device(ent, dims).view(pool.pool.shape))
