@@ -187,9 +187,12 @@ __global__ void __launch_bounds__(64 * NW) decode_attn_kernel(DecodeAttnParams p
 }
 
 // ----------------------------------------------------------------------------- tiled kernel
-// The DeepSeek-V2-sized bf16 case (d_c = 512, d_hr = 64): eight waves of 16 heads share 64-token
-// tiles that arrive by direct global->LDS copies, double-buffered so that the next tile streams
-// in while the current one is multiplied.
+// The DeepSeek-V2-sized bf16 case (d_c = 512, d_hr = 64).  A workgroup is eight waves of 16 heads
+// (two waves per SIMD hide each other's LDS and copy latency); with more than 128 heads the other
+// head groups' workgroups read the same tiles and get block ids on the same XCD, so their repeat
+// reads come from its L2.
+//   * Tiles of 32 tokens arrive by direct global->LDS copies into a ring of four buffers, three
+//     tiles ahead of the one being multiplied.
 //   * LDS row of a token = its 1152-byte cache entry as 72 16-byte chunks; chunk c of token t is
 //     stored at chunk slot t*72 + (c ^ (t & 7)) so that the 16 tokens of an MFMA operand read
 //     fall on different banks.
@@ -199,36 +202,44 @@ __global__ void __launch_bounds__(64 * NW) decode_attn_kernel(DecodeAttnParams p
 //     token-major tile with the gfx950 LDS transpose read (ds_read_b64_tr_b16): within each
 //     16-lane group, source lane s supplies 4 consecutive dims of token 4j + s/4 and lane i
 //     receives dim i of those four tokens.
-//   * softmax scaling is lazy: the running max is only raised (and O rescaled) when a tile's
-//     max exceeds it by more than 2^8, which keeps every probability <= 256.
+//   * Softmax scaling is lazy: all lanes of a head share a reference max that is only raised (and
+//     O rescaled) when some score exceeds it by more than 2^8, so the common tile needs no
+//     cross-lane exchange; every lane keeps a partial sum that is combined once at the end.
 namespace tiled {
-constexpr int kT = 64;                    // tokens per tile
+constexpr int kT = 32;                    // tokens per tile
+constexpr int kNBuf = 4;                  // ring depth
 constexpr int kD = 576, kDC = 512;        // entry width, latent width
 constexpr int kCPR = kD * 2 / 16;         // 72 chunks per entry
 constexpr int kRow = kCPR * 16;           // 1152 bytes per entry
-constexpr int kBytes = kT * kRow;         // 73728
+constexpr int kBytes = kT * kRow;         // 36864 per buffer
 constexpr int kWaves = 8;
-constexpr int kDmaPerWave = kT * kCPR / (64 * kWaves);  // 9
+constexpr int kDmaTotal = kT * kCPR / 64;  // 36 one-KiB copies per tile: waves 0-3 issue 5, 4-7 issue 4
+__device__ __forceinline__ int dma_count(int w) { return w < 4 ? 5 : 4; }
+__device__ __forceinline__ int dma_first(int w) { return w < 4 ? 5 * w : 20 + 4 * (w - 4); }
 constexpr float kLazy = 8.f;              // log2 headroom before a rescale
 }  // namespace tiled
 
 __shared__ __attribute__((aligned(1024))) char g_kv0[tiled::kBytes];
 __shared__ __attribute__((aligned(1024))) char g_kv1[tiled::kBytes];
+__shared__ __attribute__((aligned(1024))) char g_kv2[tiled::kBytes];
+__shared__ __attribute__((aligned(1024))) char g_kv3[tiled::kBytes];
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4_t;
 
 template <int BUF>
-__device__ __forceinline__ char* kv_buf() { return BUF ? g_kv1 : g_kv0; }
+__device__ __forceinline__ char* kv_buf() {
+  return BUF == 0 ? g_kv0 : (BUF == 1 ? g_kv1 : (BUF == 2 ? g_kv2 : g_kv3));
+}
 
 // s_waitcnt immediates (gfx9 encoding): vmcnt in bits [3:0] and [15:14], expcnt [6:4],
 // lgkmcnt [11:8]; the unused counters are left at their maximum.
 constexpr int waitcnt_vm(int n) { return ((n >> 4) << 14) | (0xF << 8) | (0x7 << 4) | (n & 0xF); }
 constexpr int kWaitLgkm0 = (0x3 << 14) | (0x7 << 4) | 0xF;
 
-// Workgroup barrier for the double-buffered pipeline: waits only on what the caller asked for
-// (unlike __syncthreads, whose release fence would also wait for the prefetch in flight), and
+// Workgroup barrier for the pipeline: waits only on what the caller asked for (unlike
+// __syncthreads, whose release fence would also wait for the copies in flight), and
 // compiler-only fences keep LDS accesses from being moved across it.
 #define MLA_TILE_BARRIER(waitcnt_imm)            \
   do {                                           \
@@ -244,7 +255,7 @@ struct TiledCtx {
   int bs, kv_len;
 };
 
-// This wave's 9 direct-to-LDS copies of tile `tile` into buffer BUF.  block_size is a multiple
+// This wave's share (5 or 4) of the 36 direct-to-LDS copies of tile `tile` into buffer BUF.  block_size is a multiple
 // of 64, so a tile lies inside one block: one uniform block-table lookup, and every row copied
 // is a row of an allocated block (rows past the context are zeroed once the copies land).
 template <int BUF>
@@ -255,127 +266,146 @@ __device__ __forceinline__ void issue_tile(const TiledCtx& c, int tile, int w, i
   const int blk = tok0 / c.bs;
   const char* base = c.pool + ((int64_t)c.bt[blk] * c.bs + (tok0 - blk * c.bs)) * kRow;
   int ln = lane;
-  asm volatile("" : "+v"(ln));  // recompute the lane offsets here instead of keeping 9 live
+  asm volatile("" : "+v"(ln));  // recompute the lane offsets here instead of keeping them live
+  const int first = dma_first(w), cnt = dma_count(w);
 #pragma unroll
-  for (int i = 0; i < kDmaPerWave; ++i) {
-    const int P = (w * kDmaPerWave + i) * 64 + ln;
-    const int t = P / kCPR;
-    const int ch = (P - t * kCPR) ^ (t & 7);
-    __builtin_amdgcn_global_load_lds((const void*)(base + (uint32_t)(t * kRow + ch * 16)),
-                                     (lds_void_t*)(dst + (w * kDmaPerWave + i) * 1024), 16, 0, 0);
+  for (int i = 0; i < 5; ++i) {
+    if (i < cnt) {
+      const int P = (first + i) * 64 + ln;
+      const int t = P / kCPR;
+      const int ch = (P - t * kCPR) ^ (t & 7);
+      __builtin_amdgcn_global_load_lds((const void*)(base + (uint32_t)(t * kRow + ch * 16)),
+                                       (lds_void_t*)(dst + (first + i) * 1024), 16, 0, 0);
+    }
   }
 }
 
+struct TiledState {
+  floatx4 o[32];   // O^T: 32 blocks of 16 latent dims; lane: head l16, dims 16 d + 4 g + j
+  float m_ref;     // shared reference max of this lane's head (log2 domain)
+  float l_part;    // this lane's partial normaliser
+};
+
 template <int BUF>
-__device__ __forceinline__ void tiled_compute(const Frag8<bf16> (&q)[18], floatx4 (&o)[32], float& m_run,
-                                              float& l_run, int t, int kv_len, float scale_log2, int lane) {
+__device__ __forceinline__ void tiled_compute(const Frag8<bf16> (&q)[18], TiledState& st, int t, int kv_len,
+                                              float scale_log2, int lane) {
   using namespace tiled;
   const char* buf = kv_buf<BUF>();
   const int g = lane >> 4, l16 = lane & 15;
-  // ---- S^T = K Q^T : four 16-token blocks; lane holds head l16, tokens 16*tb + 4g + j
-  floatx4 sc[4];
+  // ---- S^T = K Q^T : two 16-token blocks; lane holds head l16, tokens 16*tb + 4g + j
+  floatx4 sc[2] = {floatx4{0, 0, 0, 0}, floatx4{0, 0, 0, 0}};
   {
     // chunk (4kc + g) of token l16 sits at slot (4kc + g) ^ (l16 & 7): two lane-constant bases
     // (kc parity); 128 bytes per kc pair and 16 rows per token block are immediates
     const int x = l16 & 7;
-    const char* rb[2];
-#pragma unroll
-    for (int par = 0; par < 2; ++par) rb[par] = buf + l16 * kRow + ((4 * par + g) ^ x) * 16;
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) sc[tb] = floatx4{0, 0, 0, 0};
+    const char* rb0 = buf + l16 * kRow + ((g) ^ x) * 16;
+    const char* rb1 = buf + l16 * kRow + ((4 + g) ^ x) * 16;
+    Frag8<bf16> a[2][2];  // [stage][tb]
+    a[0][0].v = *reinterpret_cast<const bf16x8*>(rb0);
+    a[0][1].v = *reinterpret_cast<const bf16x8*>(rb0 + 16 * kRow);
 #pragma unroll
     for (int kc = 0; kc < 18; ++kc) {
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        Frag8<bf16> a;
-        a.v = *reinterpret_cast<const bf16x8*>(rb[kc & 1] + 128 * (kc >> 1) + tb * 16 * kRow);
-        sc[tb] = mma16(a, q[kc], sc[tb]);
+      const int cur = kc & 1, nxt = cur ^ 1;
+      if (kc + 1 < 18) {  // prefetch the next k-chunk's two fragments
+        const char* pn = ((kc + 1) & 1 ? rb1 : rb0) + 128 * ((kc + 1) >> 1);
+        a[nxt][0].v = *reinterpret_cast<const bf16x8*>(pn);
+        a[nxt][1].v = *reinterpret_cast<const bf16x8*>(pn + 16 * kRow);
       }
+      sc[0] = mma16(a[cur][0], q[kc], sc[0]);
+      sc[1] = mma16(a[cur][1], q[kc], sc[1]);
     }
   }
-  // ---- online softmax over the 64 tokens (the 4 lane groups sharing a head exchange via xor)
-  float mx = -INFINITY;
+  // ---- lazy online softmax
+  float lmax = -INFINITY;
+  const bool full = (t + 1) * kT <= kv_len;
 #pragma unroll
-  for (int tb = 0; tb < 4; ++tb)
+  for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int tok = t * kT + tb * 16 + 4 * g + j;
-      const float v = tok < kv_len ? sc[tb][j] * scale_log2 : -INFINITY;
+      float v = sc[tb][j] * scale_log2;
+      if (!full && t * kT + tb * 16 + 4 * g + j >= kv_len) v = -INFINITY;
       sc[tb][j] = v;
-      mx = fmaxf(mx, v);
+      lmax = fmaxf(lmax, v);
     }
-  mx = wave_max_xor(mx, 16);
-  mx = wave_max_xor(mx, 32);
-  if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazy) != 0) {  // wave-uniform rescale
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f(m_run - m_new);
-    l_run *= alpha;
+  if (__builtin_amdgcn_ballot_w64(lmax > st.m_ref + kLazy) != 0) {  // rare: raise the reference
+    float hmax = wave_max_xor(lmax, 16);
+    hmax = wave_max_xor(hmax, 32);
+    const float m_new = fmaxf(st.m_ref, hmax);
+    const float alpha = __builtin_amdgcn_exp2f(st.m_ref - m_new);  // -inf -> 0
+    st.l_part *= alpha;
 #pragma unroll
-    for (int d = 0; d < 32; ++d) o[d] *= alpha;
-    m_run = m_new;
+    for (int d = 0; d < 32; ++d) st.o[d] *= alpha;
+    st.m_ref = m_new;
   }
-  float sum = 0.f;
-  Frag8<bf16> pf[2];  // k-chunk kc2: slot s = token 32 kc2 + 16 (s/4) + 4g + s%4
+  Frag8<bf16> pf;  // slot s = token 16 (s/4) + 4g + s%4
 #pragma unroll
-  for (int tb = 0; tb < 4; ++tb)
+  for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const bf16 e = (bf16)exp2f(sc[tb][j] - m_run);
-      sum += (float)e;
-      pf[tb >> 1].v[(tb & 1) * 4 + j] = e;
+      const bf16 e = (bf16)__builtin_amdgcn_exp2f(sc[tb][j] - st.m_ref);  // argument <= 8
+      st.l_part += (float)e;
+      pf.v[tb * 4 + j] = e;
     }
-  sum = wave_sum_xor(sum, 16);
-  sum = wave_sum_xor(sum, 32);
-  l_run += sum;
-  // ---- O^T += V^T P^T : 32 blocks of 16 latent dims, 2 k-chunks of 32 tokens
-  // lane group g reads tokens 4g + s/4 (+16 for the second read) of each 32-token chunk; source
-  // lane s supplies dims 16 d + 4 (s % 4) .. +3 = chunk 2d + (s%4)/2, byte (s % 2) * 8
-  const int s4 = lane & 15;
-  const int x = (4 * g + (s4 >> 2)) & 7;
-  const int clo = (s4 & 3) >> 1;
+  // ---- O^T += V^T P^T : 32 blocks of 16 latent dims over the tile's 32 tokens
+  // lane group g reads tokens 4g + s/4 (+16 for the second read); source lane s supplies dims
+  // 16 d + 4 (s % 4) .. +3 = chunk 2d + (s%4)/2, byte (s % 2) * 8
+  const int x = (4 * g + (l16 >> 2)) & 7;
+  const int clo = (l16 & 3) >> 1;
   const char* vb[4];
 #pragma unroll
   for (int par = 0; par < 4; ++par)
-    vb[par] = buf + (4 * g + (s4 >> 2)) * kRow + (s4 & 1) * 8 + ((2 * par + clo) ^ x) * 16;
+    vb[par] = buf + (4 * g + (l16 >> 2)) * kRow + (l16 & 1) * 8 + ((2 * par + clo) ^ x) * 16;
+  shortx4 vlo[2], vhi[2];
+  vlo[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)vb[0]);
+  vhi[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)(vb[0] + 16 * kRow));
 #pragma unroll
-  for (int kc2 = 0; kc2 < 2; ++kc2)
-#pragma unroll
-    for (int d = 0; d < 32; ++d) {
-      const char* pv = vb[d & 3] + 128 * (d >> 2) + kc2 * 32 * kRow;
-      const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)pv);
-      const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)(pv + 16 * kRow));
-      Frag8<bf16> a;
-      a.v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      o[d] = mma16(a, pf[kc2], o[d]);
+  for (int d = 0; d < 32; ++d) {
+    const int cur = d & 1, nxt = cur ^ 1;
+    if (d + 1 < 32) {  // prefetch the next block's fragment
+      const char* pv = vb[(d + 1) & 3] + 128 * ((d + 1) >> 2);
+      vlo[nxt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)pv);
+      vhi[nxt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)(pv + 16 * kRow));
     }
+    Frag8<bf16> a;
+    a.v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vlo[cur], vhi[cur], 0, 1, 2, 3, 4, 5, 6, 7));
+    st.o[d] = mma16(a, pf, st.o[d]);
+  }
 }
 
-template <int CUR>
-__device__ __forceinline__ void tiled_step(const TiledCtx& c, const Frag8<bf16> (&q)[18], floatx4 (&o)[32],
-                                           float& m_run, float& l_run, int t, bool has_next, float scale_log2,
-                                           int w, int lane, int tid) {
+// One pipeline step on ring buffer BUF (= t % 4): wait for tile t, publish it to the workgroup,
+// refill the buffer of tile t-1 with tile t+3, multiply tile t.
+template <int BUF>
+__device__ __forceinline__ void tiled_step(const TiledCtx& c, const Frag8<bf16> (&q)[18], TiledState& st, int t,
+                                           int t_end, float scale_log2, int w, int lane, int tid) {
   using namespace tiled;
-  if (has_next) {
-    issue_tile<CUR ^ 1>(c, t + 1, w, lane);
-    MLA_TILE_BARRIER(waitcnt_vm(kDmaPerWave));  // this tile's copies have landed, the next's fly
+  const int ahead = min(t_end - 1 - t, kNBuf - 2);  // tiles issued after t and still in flight
+  if (ahead >= 2) {
+    if (w < 4) MLA_TILE_BARRIER(waitcnt_vm(10));
+    else MLA_TILE_BARRIER(waitcnt_vm(8));
+  } else if (ahead == 1) {
+    if (w < 4) MLA_TILE_BARRIER(waitcnt_vm(5));
+    else MLA_TILE_BARRIER(waitcnt_vm(4));
   } else {
     MLA_TILE_BARRIER(waitcnt_vm(0));
   }
+  if (t + kNBuf - 1 < t_end) issue_tile<(BUF + kNBuf - 1) % kNBuf>(c, t + kNBuf - 1, w, lane);
   const int valid = c.kv_len - t * kT;
   if (valid < kT) {  // zero the rows past the end of the context (uniform branch)
-    char* buf = kv_buf<CUR>();
+    char* buf = kv_buf<BUF>();
     for (int i = tid; i < (kT - valid) * kCPR; i += 64 * kWaves) st16(buf + (valid * kCPR + i) * 16, zero16());
     MLA_TILE_BARRIER(kWaitLgkm0);
   }
-  tiled_compute<CUR>(q, o, m_run, l_run, t, c.kv_len, scale_log2, lane);
-  MLA_TILE_BARRIER(kWaitLgkm0);  // every wave is done reading before the buffer is refilled
+  tiled_compute<BUF>(q, st, t, c.kv_len, scale_log2, lane);
 }
 
 __global__ void __launch_bounds__(512)
     decode_attn_tiled_kernel(DecodeAttnParams p, int HG, const int32_t* __restrict__ block_table) {
   using namespace tiled;
+  // block id -> (unit = (sequence, partition), head group): the HG head groups of a unit sit 8
+  // ids apart, i.e. on the same XCD (ids are dealt to the 8 XCDs round robin)
   const int units = p.B * p.splits;
-  const int unit = blockIdx.x / HG, hg = blockIdx.x % HG;
+  const int grp = blockIdx.x / (8 * HG), rem = blockIdx.x % (8 * HG);
+  const int hg = rem / 8, unit = grp * 8 + rem % 8;
   if (unit >= units) return;
   const int b = unit / p.splits, split = unit % p.splits;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -403,16 +433,25 @@ __global__ void __launch_bounds__(512)
       else zero8(q[kc]);
     }
   }
-  floatx4 o[32];
+  TiledState st;
 #pragma unroll
-  for (int d = 0; d < 32; ++d) o[d] = floatx4{0, 0, 0, 0};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int d = 0; d < 32; ++d) st.o[d] = floatx4{0, 0, 0, 0};
+  st.m_ref = -INFINITY;
+  st.l_part = 0.f;
 
   if (t_begin < t_end) issue_tile<0>(c, t_begin, w, lane);
-  for (int t = t_begin; t < t_end; t += 2) {
-    tiled_step<0>(c, q, o, m_run, l_run, t, t + 1 < t_end, p.scale_log2, w, lane, tid);
-    if (t + 1 < t_end) tiled_step<1>(c, q, o, m_run, l_run, t + 1, t + 2 < t_end, p.scale_log2, w, lane, tid);
+  if (t_begin + 1 < t_end) issue_tile<1>(c, t_begin + 1, w, lane);
+  if (t_begin + 2 < t_end) issue_tile<2>(c, t_begin + 2, w, lane);
+  for (int t = t_begin; t < t_end; t += kNBuf) {
+    tiled_step<0>(c, q, st, t, t_end, p.scale_log2, w, lane, tid);
+    if (t + 1 < t_end) tiled_step<1>(c, q, st, t + 1, t_end, p.scale_log2, w, lane, tid);
+    if (t + 2 < t_end) tiled_step<2>(c, q, st, t + 2, t_end, p.scale_log2, w, lane, tid);
+    if (t + 3 < t_end) tiled_step<3>(c, q, st, t + 3, t_end, p.scale_log2, w, lane, tid);
   }
+  // the four lane groups of a head hold partial sums over different tokens
+  float l_run = wave_sum_xor(st.l_part, 16);
+  l_run = wave_sum_xor(l_run, 32);
+  const float m_run = st.m_ref;
 
   if (!valid_head) return;
   if (p.splits == 1) {
@@ -422,7 +461,7 @@ __global__ void __launch_bounds__(512)
     for (int d = 0; d < 32; ++d) {
       bf16x4 v;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = (bf16)(o[d][r] * inv);
+      for (int r = 0; r < 4; ++r) v[r] = (bf16)(st.o[d][r] * inv);
       *reinterpret_cast<bf16x4*>(out + d * 16 + 4 * g) = v;
     }
     if (p.lse && g == 0) p.lse[(int64_t)b * p.n_h + head] = (m_run + log2f(l_run)) * 0.69314718055994531f;
@@ -435,7 +474,7 @@ __global__ void __launch_bounds__(512)
   }
   float* po = p.part_o + pi * kDC;
 #pragma unroll
-  for (int d = 0; d < 32; ++d) *reinterpret_cast<floatx4*>(po + d * 16 + 4 * g) = o[d];
+  for (int d = 0; d < 32; ++d) *reinterpret_cast<floatx4*>(po + d * 16 + 4 * g) = st.o[d];
 }
 
 // Log-sum-exp combination of the partitions: M = max_s m_s, w_s = 2^(m_s - M),
@@ -502,7 +541,8 @@ hipError_t decode_attention(DType t, const DecodeAttnParams& p, hipStream_t s) {
     const int HG = (p.n_h + 16 * tiled::kWaves - 1) / (16 * tiled::kWaves);
     const int units = p.B * p.splits;
     if (units == 0) return hipSuccess;
-    hipLaunchKernelGGL(decode_attn_tiled_kernel, dim3(units * HG), dim3(64 * tiled::kWaves), 0, s, p, HG,
+    const int blocks = (units + 7) / 8 * 8 * HG;
+    hipLaunchKernelGGL(decode_attn_tiled_kernel, dim3(blocks), dim3(64 * tiled::kWaves), 0, s, p, HG,
                        p.block_table);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;

@@ -6,7 +6,7 @@
 #include <algorithm>
 #include <cmath>
 
-#include "../../include/mla.h"
+#include "mla.h"
 #include "internal.h"
 
 using namespace mla;
@@ -72,7 +72,7 @@ int validate_cache(const mla_dims* d, const mla_paged_cache* c) {
 constexpr int kSplitQuantum = 64;
 
 int auto_splits(const mla_dims* d, int batch, int max_ctx_len, int cus) {
-  const int hg = (d->n_h + 127) / 128;
+  const int hg = (d->n_h + 127) / 128;  // workgroups per (sequence, partition)
   const int chunks = (max_ctx_len + 1 + kSplitQuantum - 1) / kSplitQuantum;
   const int units = batch * hg;
   int s = (cus + units - 1) / units;
