@@ -178,6 +178,148 @@ __global__ void __launch_bounds__(256)
   }
 }
 
+// ----------------------------------------------------------------------------- skinny kernel
+// Decode-sized products (M <= 64 rows, bf16, y = W x with W [N][K]) stream the weights once and
+// are bound by HBM.  Each wave owns 32 output columns for all M rows:
+//   * its weight rows come straight from global memory into registers, 64 contiguous bytes per
+//     lane and k-step of 64 (two lanes per row cover the row's 128-byte line), three k-steps ahead;
+//   * the activation slice of a k-step (M x 64) is copied once per workgroup into LDS by direct
+//     global->LDS copies (four-stage ring, 16-byte chunks XOR-swizzled by row);
+//   * the 32x32x16 MFMA k-slots are permuted so that lane group g owns k = 32g + 8j .. +7 in
+//     sub-step j, which makes both operands' per-lane data contiguous.
+namespace skinny {
+constexpr int kKS = 64;      // k per step
+constexpr int kWaves = 4;
+constexpr int kBN = 32 * kWaves;
+constexpr int kAStages = 4;
+constexpr int kBStages = 4;  // register ring: steps s+1..s+3 in flight while s is multiplied
+}  // namespace skinny
+
+typedef __attribute__((address_space(3))) void lds_void_g;
+
+template <int MB>
+__device__ __forceinline__ void skinny_issue_a(const bf16* A, int64_t lda, int M, int k0, char* stage, int w,
+                                               int lane) {
+  // stage layout: row m (64 k = 128 bytes = 8 chunks), chunk c at slot c ^ (m & 7)
+  constexpr int kInst = MB * 32 * 8 / 64;  // 1 KiB copies per workgroup (4 or 8)
+#pragma unroll
+  for (int i = 0; i < kInst / skinny::kWaves; ++i) {
+    const int inst = w * (kInst / skinny::kWaves) + i;
+    const int P = inst * 64 + lane;
+    const int m = P >> 3, slot = P & 7;
+    const int c = slot ^ (m & 7);
+    const int mr = min(m, M - 1);  // rows past M copy a valid row; their results are dropped
+    __builtin_amdgcn_global_load_lds((const void*)(A + (int64_t)mr * lda + k0 + c * 8),
+                                     (lds_void_g*)(stage + inst * 1024), 16, 0, 0);
+  }
+}
+
+template <int MB>
+__global__ void __launch_bounds__(256)
+    gemm_skinny_kernel(GemmParams p, int splits, int k_per_split, float* __restrict__ partial) {
+  using namespace skinny;
+  constexpr int kAStageBytes = MB * 32 * 128;
+  constexpr int kAInstPerWave = MB * 32 * 8 / 64 / kWaves;  // 1 or 2
+  __shared__ __attribute__((aligned(1024))) char As[kAStages][kAStageBytes];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, l32 = lane & 31;
+  const int n0 = blockIdx.x * kBN;
+  const int z = blockIdx.y / splits, sp = blockIdx.y % splits;
+  const int kb = sp * k_per_split, ke = min(p.K, kb + k_per_split);
+  const int nsteps = (ke - kb) / kKS;
+
+  const bf16* A = reinterpret_cast<const bf16*>(p.A) + (int64_t)z * p.strideA;
+  // this lane's weight row (rows past N read row N-1; their columns are dropped)
+  const int n = min(n0 + w * 32 + l32, p.N - 1);
+  const bf16* brow = n < p.N0 ? reinterpret_cast<const bf16*>(p.B0) + (int64_t)z * p.strideB + (int64_t)n * p.ldb
+                              : reinterpret_cast<const bf16*>(p.B1) + (int64_t)z * p.strideB + (int64_t)(n - p.N0) * p.ldb;
+  brow += 32 * g;
+
+  floatx16 acc[MB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+
+  bf16x8 bq[kBStages][4];
+  // prologue: steps 0..2, each issued as [A copies, B loads] like every later step, so that the
+  // wait for step t always leaves exactly the copies and loads of steps t+1 and t+2 in flight
+#pragma unroll
+  for (int s0 = 0; s0 < kBStages - 1; ++s0)
+    if (s0 < nsteps) {
+      skinny_issue_a<MB>(A, p.lda, p.M, kb + s0 * kKS, As[s0], w, lane);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bq[s0][j] = *reinterpret_cast<const bf16x8*>(brow + kb + s0 * kKS + 8 * j);
+    }
+
+  for (int s = 0; s < nsteps; s += kBStages) {
+#pragma unroll
+    for (int u = 0; u < kBStages; ++u) {
+      const int st = s + u;
+      if (st < nsteps) {
+        // every step is issued as [A copies, B loads]; waiting until only the later steps'
+        // (st+1, st+2, if they exist) copies and loads are outstanding completes step st
+        const int later = min(nsteps - 1 - st, kBStages - 2);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (later >= 2) __builtin_amdgcn_s_waitcnt(((2 * (kAInstPerWave + 4)) & 0xF) | (((2 * (kAInstPerWave + 4)) >> 4) << 14) | (0xF << 8) | (0x7 << 4));
+        else if (later == 1) __builtin_amdgcn_s_waitcnt(((kAInstPerWave + 4) & 0xF) | (((kAInstPerWave + 4) >> 4) << 14) | (0xF << 8) | (0x7 << 4));
+        else __builtin_amdgcn_s_waitcnt((0xF << 8) | (0x7 << 4));
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        // refill: the A stage of step st-1 (everyone is past it) and B slot of step st-1
+        if (st + 3 < nsteps) {
+          skinny_issue_a<MB>(A, p.lda, p.M, kb + (st + 3) * kKS, As[(u + 3) % kAStages], w, lane);
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            bq[(u + 3) % kBStages][j] = *reinterpret_cast<const bf16x8*>(brow + kb + (st + 3) * kKS + 8 * j);
+        }
+        const char* as = As[u % kAStages];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          Frag8<bf16> bf;
+          bf.v = bq[u][j];
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            const int m = mb * 32 + l32;
+            Frag8<bf16> af;
+            af.v = *reinterpret_cast<const bf16x8*>(as + m * 128 + (((4 * g + j) ^ (m & 7)) * 16));
+            acc[mb] = mma32(af, bf, acc[mb]);
+          }
+        }
+      }
+    }
+  }
+
+  // C layout: lane col = n0 + w*32 + l32; value r at row mb*32 + 8*(r/4) + 4*g + r%4
+  const int col = n0 + w * 32 + l32;
+  if (splits > 1) {
+    float* P = partial + ((int64_t)(sp * p.batch + z) * p.M) * p.N;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = mb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+        if (row < p.M && col < p.N) P[(int64_t)row * p.N + col] = acc[mb][r];
+      }
+    return;
+  }
+  const bool tile_rope = n0 + kBN > p.epi.rope_col0;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = mb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+      float v = acc[mb][r];
+      if (tile_rope) {
+        const float partner = __shfl_xor(v, 1, 64);
+        if (row < p.M && col < p.N) rope_pair(p.epi, row, col, v, partner);
+      }
+      if (row < p.M && col < p.N) epi_store<bf16>(p.epi, z, row, col, v);
+    }
+}
+
 // ----------------------------------------------------------------------------- host side
 namespace {
 struct Cfg {
@@ -201,6 +343,16 @@ hipError_t run_t(const GemmParams& p, const GemmPlan& plan, float* partial, hipS
   switch (plan.cfg) {
     case 0: err = launch_cfg<T, 0>(p, plan, partial, s); break;
     case 1: err = launch_cfg<T, 1>(p, plan, partial, s); break;
+    case 3:
+    case 4: {
+      dim3 grid((p.N + skinny::kBN - 1) / skinny::kBN, p.batch * plan.splits);
+      if (plan.cfg == 3)
+        hipLaunchKernelGGL(gemm_skinny_kernel<1>, grid, dim3(256), 0, s, p, plan.splits, plan.k_per_split, partial);
+      else
+        hipLaunchKernelGGL(gemm_skinny_kernel<2>, grid, dim3(256), 0, s, p, plan.splits, plan.k_per_split, partial);
+      err = hipGetLastError();
+      break;
+    }
     default: err = launch_cfg<T, 2>(p, plan, partial, s); break;
   }
   if (err != hipSuccess || plan.splits == 1) return err;
@@ -211,7 +363,30 @@ hipError_t run_t(const GemmParams& p, const GemmPlan& plan, float* partial, hipS
 }
 }  // namespace
 
-GemmPlan gemm_plan(int M, int N, int K, int batch, int cus) {
+bool gemm_skinny_ok(DType t, const GemmParams& p) {
+  return t == DType::BF16 && !p.nn && p.M <= 64 && p.K % skinny::kKS == 0 && p.N % 2 == 0 && p.lda % 8 == 0 &&
+         p.ldb % 8 == 0 && p.strideA % 8 == 0 && p.strideB % 8 == 0;
+}
+
+GemmPlan gemm_plan_skinny(int M, int N, int K, int batch, int cus) {
+  GemmPlan pl;
+  pl.cfg = M <= 32 ? 3 : 4;
+  pl.bm = M <= 32 ? 32 : 64;
+  pl.bn = skinny::kBN;
+  const int64_t tiles = (int64_t)((N + pl.bn - 1) / pl.bn) * batch;
+  const int ksteps = K / skinny::kKS;
+  // about two workgroups per CU, each streaming at least 8 k-steps
+  int splits = (int)std::max<int64_t>(1, (2LL * cus + tiles - 1) / tiles);
+  splits = std::min(splits, std::max(1, ksteps / 8));
+  const int per = (ksteps + splits - 1) / splits;
+  pl.splits = (ksteps + per - 1) / per;
+  pl.k_per_split = per * skinny::kKS;
+  pl.partial_bytes = pl.splits > 1 ? (size_t)pl.splits * batch * M * N * sizeof(float) : 0;
+  return pl;
+}
+
+GemmPlan gemm_plan(int M, int N, int K, int batch, int cus, bool skinny_ok) {
+  if (skinny_ok && M <= 64 && K % skinny::kKS == 0 && N % 2 == 0) return gemm_plan_skinny(M, N, K, batch, cus);
   GemmPlan pl;
   pl.cfg = M <= 32 ? 0 : (M <= 64 ? 1 : 2);
   pl.bm = kCfgs[pl.cfg].bm;
@@ -232,19 +407,20 @@ GemmPlan gemm_plan(int M, int N, int K, int batch, int cus) {
   return pl;
 }
 
-size_t gemm_partial_bound(int M, int N, int K, int batch, int cus) {
+size_t gemm_partial_bound(int M, int N, int K, int batch, int cus, bool skinny_ok) {
   // every tile height is a multiple of 32, so within a 32-row bucket the split count is fixed
   // and the partial size grows with M: the bucket tops (and M itself) are the only candidates
   size_t best = 0;
   for (int m = 32; m < M + 32; m += 32) {
     const int mm = std::min(m, M);
-    best = std::max(best, gemm_plan(mm, N, K, batch, cus).partial_bytes);
+    best = std::max(best, gemm_plan(mm, N, K, batch, cus, skinny_ok).partial_bytes);
   }
   return best;
 }
 
 hipError_t gemm_run(DType t, const GemmParams& p, const GemmPlan& plan, float* partial, hipStream_t s) {
   if (p.M == 0 || p.N == 0 || p.batch == 0) return hipSuccess;
+  if ((plan.cfg == 3 || plan.cfg == 4) && (t != DType::BF16 || !gemm_skinny_ok(t, p))) return hipErrorInvalidValue;
   return t == DType::BF16 ? run_t<bf16>(p, plan, partial, s) : run_t<float>(p, plan, partial, s);
 }
 

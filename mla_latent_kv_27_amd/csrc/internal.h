@@ -56,10 +56,12 @@ struct GemmPlan {
   size_t partial_bytes = 0;  // workspace for fp32 partials (0 when splits == 1)
 };
 
-GemmPlan gemm_plan(int M, int N, int K, int batch, int cus);
+// skinny_ok: the product is bf16, "NT" and 16-byte aligned, so rows M <= 64 may take the
+// weight-streaming kernel.
+GemmPlan gemm_plan(int M, int N, int K, int batch, int cus, bool skinny_ok);
 // Largest partial_bytes of gemm_plan(m, ...) over 1 <= m <= M (workspace sized for M then also
 // serves every smaller call).
-size_t gemm_partial_bound(int M, int N, int K, int batch, int cus);
+size_t gemm_partial_bound(int M, int N, int K, int batch, int cus, bool skinny_ok);
 // Launches the GEMM (and its split-K reduction).  `partial` must hold plan.partial_bytes.
 hipError_t gemm_run(DType t, const GemmParams& p, const GemmPlan& plan, float* partial,
                     hipStream_t s);

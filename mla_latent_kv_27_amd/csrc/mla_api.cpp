@@ -55,6 +55,8 @@ int validate_dims(const mla_dims* d) {
 inline DType dt(const mla_dims* d) { return d->dtype == MLA_BF16 ? DType::BF16 : DType::F32; }
 inline int q_in(const mla_dims* d) { return d->d_cq > 0 ? d->d_cq : d->d_model; }
 inline int entry(const mla_dims* d) { return d->d_c + d->d_hr; }
+// bf16 "NT" products may take the weight-streaming kernel for small row counts
+inline bool sk(const mla_dims* d) { return d->dtype == MLA_BF16; }
 inline float scale_of(const mla_dims* d) {
   return d->softmax_scale > 0.f ? d->softmax_scale : 1.0f / std::sqrt((float)(d->d_h + d->d_hr));
 }
@@ -88,9 +90,9 @@ struct AppendWs {
 };
 AppendWs carve_append(Carve& cv, const mla_dims* d, int n, int cus) {
   AppendWs w;
-  w.plan = gemm_plan(n, entry(d), d->d_model, 1, cus);
+  w.plan = gemm_plan(n, entry(d), d->d_model, 1, cus, sk(d));
   w.rope = cv.take<float2>((size_t)n * (d->d_hr / 2) * sizeof(float2));
-  w.partial = cv.take<float>(gemm_partial_bound(n, entry(d), d->d_model, 1, cus));
+  w.partial = cv.take<float>(gemm_partial_bound(n, entry(d), d->d_model, 1, cus, sk(d)));
   return w;
 }
 
@@ -99,24 +101,24 @@ struct DecodeGemms {
 };
 // partial workspace serving every batch <= B
 size_t decode_partial_bound(const mla_dims* d, int B, int cus) {
-  size_t b = std::max({gemm_partial_bound(B, d->n_h * d->d_h, q_in(d), 1, cus),
-                       gemm_partial_bound(B, d->n_h * d->d_hr, q_in(d), 1, cus),
-                       gemm_partial_bound(B, entry(d), d->d_model, 1, cus),
-                       gemm_partial_bound(B, d->d_c, d->d_h, d->n_h, cus),
-                       gemm_partial_bound(B, d->d_h, d->d_c, d->n_h, cus),
-                       gemm_partial_bound(B, d->d_model, d->n_h * d->d_h, 1, cus)});
-  if (d->d_cq > 0) b = std::max(b, gemm_partial_bound(B, d->d_cq, d->d_model, 1, cus));
+  size_t b = std::max({gemm_partial_bound(B, d->n_h * d->d_h, q_in(d), 1, cus, sk(d)),
+                       gemm_partial_bound(B, d->n_h * d->d_hr, q_in(d), 1, cus, sk(d)),
+                       gemm_partial_bound(B, entry(d), d->d_model, 1, cus, sk(d)),
+                       gemm_partial_bound(B, d->d_c, d->d_h, d->n_h, cus, false),
+                       gemm_partial_bound(B, d->d_h, d->d_c, d->n_h, cus, sk(d)),
+                       gemm_partial_bound(B, d->d_model, d->n_h * d->d_h, 1, cus, sk(d))});
+  if (d->d_cq > 0) b = std::max(b, gemm_partial_bound(B, d->d_cq, d->d_model, 1, cus, sk(d)));
   return b;
 }
 DecodeGemms decode_gemms(const mla_dims* d, int B, int cus) {
   DecodeGemms g;
-  g.cq = d->d_cq > 0 ? gemm_plan(B, d->d_cq, d->d_model, 1, cus) : GemmPlan{};
-  g.qc = gemm_plan(B, d->n_h * d->d_h, q_in(d), 1, cus);
-  g.qr = gemm_plan(B, d->n_h * d->d_hr, q_in(d), 1, cus);
-  g.kv = gemm_plan(B, entry(d), d->d_model, 1, cus);
-  g.absorb = gemm_plan(B, d->d_c, d->d_h, d->n_h, cus);
-  g.uv = gemm_plan(B, d->d_h, d->d_c, d->n_h, cus);
-  g.out = gemm_plan(B, d->d_model, d->n_h * d->d_h, 1, cus);
+  g.cq = d->d_cq > 0 ? gemm_plan(B, d->d_cq, d->d_model, 1, cus, sk(d)) : GemmPlan{};
+  g.qc = gemm_plan(B, d->n_h * d->d_h, q_in(d), 1, cus, sk(d));
+  g.qr = gemm_plan(B, d->n_h * d->d_hr, q_in(d), 1, cus, sk(d));
+  g.kv = gemm_plan(B, entry(d), d->d_model, 1, cus, sk(d));
+  g.absorb = gemm_plan(B, d->d_c, d->d_h, d->n_h, cus, false);
+  g.uv = gemm_plan(B, d->d_h, d->d_c, d->n_h, cus, sk(d));
+  g.out = gemm_plan(B, d->d_model, d->n_h * d->d_h, 1, cus, sk(d));
   return g;
 }
 
@@ -194,13 +196,13 @@ PrefillWs carve_prefill(Carve& cv, const mla_dims* d, int S, int T, int cus) {
   const int M = S * T;
   w.Tp = (T + 63) / 64 * 64;
   const int qw = d->n_h * (d->d_h + d->d_hr);
-  w.cq_p = d->d_cq > 0 ? gemm_plan(M, d->d_cq, d->d_model, 1, cus) : GemmPlan{};
-  w.qc_p = gemm_plan(M, d->n_h * d->d_h, q_in(d), 1, cus);
-  w.qr_p = gemm_plan(M, d->n_h * d->d_hr, q_in(d), 1, cus);
-  w.kv_p = gemm_plan(M, entry(d), d->d_model, 1, cus);
-  w.k_p = gemm_plan(M, d->n_h * d->d_h, d->d_c, 1, cus);
-  w.v_p = gemm_plan(d->n_h * d->d_h, M, d->d_c, 1, cus);
-  w.out_p = gemm_plan(M, d->d_model, d->n_h * d->d_h, 1, cus);
+  w.cq_p = d->d_cq > 0 ? gemm_plan(M, d->d_cq, d->d_model, 1, cus, sk(d)) : GemmPlan{};
+  w.qc_p = gemm_plan(M, d->n_h * d->d_h, q_in(d), 1, cus, sk(d));
+  w.qr_p = gemm_plan(M, d->n_h * d->d_hr, q_in(d), 1, cus, sk(d));
+  w.kv_p = gemm_plan(M, entry(d), d->d_model, 1, cus, sk(d));
+  w.k_p = gemm_plan(M, d->n_h * d->d_h, d->d_c, 1, cus, sk(d));
+  w.v_p = gemm_plan(d->n_h * d->d_h, M, d->d_c, 1, cus, sk(d));
+  w.out_p = gemm_plan(M, d->d_model, d->n_h * d->d_h, 1, cus, sk(d));
   w.seq = cv.take<int32_t>((size_t)M * 4);
   w.pos = cv.take<int32_t>((size_t)M * 4);
   w.rope = cv.take<float2>((size_t)M * (d->d_hr / 2) * sizeof(float2));
@@ -210,13 +212,13 @@ PrefillWs carve_prefill(Carve& cv, const mla_dims* d, int S, int T, int cus) {
   w.kp = cv.take<char>((size_t)M * d->n_h * d->d_h * es);
   w.vt = cv.take<char>((size_t)d->n_h * d->d_h * S * w.Tp * es);
   w.o = cv.take<char>((size_t)M * d->n_h * d->d_h * es);
-  size_t mp = std::max({gemm_partial_bound(M, d->n_h * d->d_h, q_in(d), 1, cus),
-                        gemm_partial_bound(M, d->n_h * d->d_hr, q_in(d), 1, cus),
-                        gemm_partial_bound(M, entry(d), d->d_model, 1, cus),
-                        gemm_partial_bound(M, d->n_h * d->d_h, d->d_c, 1, cus),
-                        gemm_partial_bound(d->n_h * d->d_h, M, d->d_c, 1, cus),
-                        gemm_partial_bound(M, d->d_model, d->n_h * d->d_h, 1, cus)});
-  if (d->d_cq > 0) mp = std::max(mp, gemm_partial_bound(M, d->d_cq, d->d_model, 1, cus));
+  size_t mp = std::max({gemm_partial_bound(M, d->n_h * d->d_h, q_in(d), 1, cus, sk(d)),
+                        gemm_partial_bound(M, d->n_h * d->d_hr, q_in(d), 1, cus, sk(d)),
+                        gemm_partial_bound(M, entry(d), d->d_model, 1, cus, sk(d)),
+                        gemm_partial_bound(M, d->n_h * d->d_h, d->d_c, 1, cus, sk(d)),
+                        gemm_partial_bound(d->n_h * d->d_h, M, d->d_c, 1, cus, sk(d)),
+                        gemm_partial_bound(M, d->d_model, d->n_h * d->d_h, 1, cus, sk(d))});
+  if (d->d_cq > 0) mp = std::max(mp, gemm_partial_bound(M, d->d_cq, d->d_model, 1, cus, sk(d)));
   w.partial = cv.take<float>(mp);
   return w;
 }
