@@ -291,6 +291,9 @@ __device__ __forceinline__ void tiled_compute(const Frag8<bf16> (&q)[18], TiledS
                                               float scale_log2, int lane) {
   using namespace tiled;
   const char* buf = kv_buf<BUF>();
+  // the lane's LDS offsets are recomputed in every step (a few integer ops) rather than kept live
+  // for all four ring buffers across the loop
+  asm volatile("" : "+v"(lane));
   const int g = lane >> 4, l16 = lane & 15;
   // ---- S^T = K Q^T : two 16-token blocks; lane holds head l16, tokens 16*tb + 4g + j
   floatx4 sc[2] = {floatx4{0, 0, 0, 0}, floatx4{0, 0, 0, 0}};
@@ -300,19 +303,22 @@ __device__ __forceinline__ void tiled_compute(const Frag8<bf16> (&q)[18], TiledS
     const int x = l16 & 7;
     const char* rb0 = buf + l16 * kRow + ((g) ^ x) * 16;
     const char* rb1 = buf + l16 * kRow + ((4 + g) ^ x) * 16;
-    Frag8<bf16> a[2][2];  // [stage][tb]
-    a[0][0].v = *reinterpret_cast<const bf16x8*>(rb0);
-    a[0][1].v = *reinterpret_cast<const bf16x8*>(rb0 + 16 * kRow);
+    Frag8<bf16> a[3][2];  // [stage][tb]: fragments two k-chunks ahead are in flight
+#pragma unroll
+    for (int k0 = 0; k0 < 2; ++k0) {
+      const char* pn = (k0 & 1 ? rb1 : rb0);
+      a[k0][0].v = *reinterpret_cast<const bf16x8*>(pn);
+      a[k0][1].v = *reinterpret_cast<const bf16x8*>(pn + 16 * kRow);
+    }
 #pragma unroll
     for (int kc = 0; kc < 18; ++kc) {
-      const int cur = kc & 1, nxt = cur ^ 1;
-      if (kc + 1 < 18) {  // prefetch the next k-chunk's two fragments
-        const char* pn = ((kc + 1) & 1 ? rb1 : rb0) + 128 * ((kc + 1) >> 1);
-        a[nxt][0].v = *reinterpret_cast<const bf16x8*>(pn);
-        a[nxt][1].v = *reinterpret_cast<const bf16x8*>(pn + 16 * kRow);
+      if (kc + 2 < 18) {
+        const char* pn = ((kc + 2) & 1 ? rb1 : rb0) + 128 * ((kc + 2) >> 1);
+        a[(kc + 2) % 3][0].v = *reinterpret_cast<const bf16x8*>(pn);
+        a[(kc + 2) % 3][1].v = *reinterpret_cast<const bf16x8*>(pn + 16 * kRow);
       }
-      sc[0] = mma16(a[cur][0], q[kc], sc[0]);
-      sc[1] = mma16(a[cur][1], q[kc], sc[1]);
+      sc[0] = mma16(a[kc % 3][0], q[kc], sc[0]);
+      sc[1] = mma16(a[kc % 3][1], q[kc], sc[1]);
     }
   }
   // ---- lazy online softmax
@@ -355,19 +361,21 @@ __device__ __forceinline__ void tiled_compute(const Frag8<bf16> (&q)[18], TiledS
 #pragma unroll
   for (int par = 0; par < 4; ++par)
     vb[par] = buf + (4 * g + (l16 >> 2)) * kRow + (l16 & 1) * 8 + ((2 * par + clo) ^ x) * 16;
-  shortx4 vlo[2], vhi[2];
-  vlo[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)vb[0]);
-  vhi[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)(vb[0] + 16 * kRow));
+  shortx4 vlo[3], vhi[3];  // fragments two blocks ahead are in flight
+#pragma unroll
+  for (int d0 = 0; d0 < 2; ++d0) {
+    vlo[d0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)vb[d0]);
+    vhi[d0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)(vb[d0] + 16 * kRow));
+  }
 #pragma unroll
   for (int d = 0; d < 32; ++d) {
-    const int cur = d & 1, nxt = cur ^ 1;
-    if (d + 1 < 32) {  // prefetch the next block's fragment
-      const char* pv = vb[(d + 1) & 3] + 128 * ((d + 1) >> 2);
-      vlo[nxt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)pv);
-      vhi[nxt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)(pv + 16 * kRow));
+    if (d + 2 < 32) {
+      const char* pv = vb[(d + 2) & 3] + 128 * ((d + 2) >> 2);
+      vlo[(d + 2) % 3] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)pv);
+      vhi[(d + 2) % 3] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)(pv + 16 * kRow));
     }
     Frag8<bf16> a;
-    a.v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vlo[cur], vhi[cur], 0, 1, 2, 3, 4, 5, 6, 7));
+    a.v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vlo[d % 3], vhi[d % 3], 0, 1, 2, 3, 4, 5, 6, 7));
     st.o[d] = mma16(a, pf, st.o[d]);
   }
 }
