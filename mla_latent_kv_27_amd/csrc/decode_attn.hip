@@ -288,7 +288,7 @@ struct TiledState {
 
 template <int BUF>
 __device__ __forceinline__ void tiled_compute(const Frag8<bf16> (&q)[18], TiledState& st, int t, int kv_len,
-                                              float scale_log2, int lane) {
+                                              float scale_log2, int lane, const TiledCtx& c, bool issue_next, int w) {
   using namespace tiled;
   const char* buf = kv_buf<BUF>();
   // the lane's LDS offsets are recomputed in every step (a few integer ops) rather than kept live
@@ -321,6 +321,7 @@ __device__ __forceinline__ void tiled_compute(const Frag8<bf16> (&q)[18], TiledS
       sc[1] = mma16(a[kc % 3][1], q[kc], sc[1]);
     }
   }
+  if (issue_next) issue_tile<(BUF + kNBuf - 1) % kNBuf>(c, t + kNBuf - 1, w, lane);
   // ---- lazy online softmax
   float lmax = -INFINITY;
   const bool full = (t + 1) * kT <= kv_len;
@@ -381,7 +382,7 @@ __device__ __forceinline__ void tiled_compute(const Frag8<bf16> (&q)[18], TiledS
 }
 
 // One pipeline step on ring buffer BUF (= t % 4): wait for tile t, publish it to the workgroup,
-// refill the buffer of tile t-1 with tile t+3, multiply tile t.
+// multiply tile t (refilling the buffer of tile t-1 with tile t+3 on the way).
 template <int BUF>
 __device__ __forceinline__ void tiled_step(const TiledCtx& c, const Frag8<bf16> (&q)[18], TiledState& st, int t,
                                            int t_end, float scale_log2, int w, int lane, int tid) {
@@ -396,14 +397,15 @@ __device__ __forceinline__ void tiled_step(const TiledCtx& c, const Frag8<bf16> 
   } else {
     MLA_TILE_BARRIER(waitcnt_vm(0));
   }
-  if (t + kNBuf - 1 < t_end) issue_tile<(BUF + kNBuf - 1) % kNBuf>(c, t + kNBuf - 1, w, lane);
   const int valid = c.kv_len - t * kT;
   if (valid < kT) {  // zero the rows past the end of the context (uniform branch)
     char* buf = kv_buf<BUF>();
     for (int i = tid; i < (kT - valid) * kCPR; i += 64 * kWaves) st16(buf + (valid * kCPR + i) * 16, zero16());
     MLA_TILE_BARRIER(kWaitLgkm0);
   }
-  tiled_compute<BUF>(q, st, t, c.kv_len, scale_log2, lane);
+  // multiply tile t; the copies of tile t+3 into the buffer of tile t-1 (free since the barrier)
+  // are issued inside, after the S^T products, which overlaps them best with the arithmetic
+  tiled_compute<BUF>(q, st, t, c.kv_len, scale_log2, lane, c, t + kNBuf - 1 < t_end, w);
 }
 
 __global__ void __launch_bounds__(512)
@@ -486,29 +488,32 @@ __global__ void __launch_bounds__(512)
 }
 
 // Log-sum-exp combination of the partitions: M = max_s m_s, w_s = 2^(m_s - M),
-// o_hat = sum_s w_s O_s / sum_s w_s l_s.
+// o_hat = sum_s w_s O_s / sum_s w_s l_s.  One workgroup per (sequence, head); each thread owns
+// 4 consecutive latent dims, loaded as float4.
 template <typename T, int DC>
-__global__ void __launch_bounds__(128) decode_combine_kernel(DecodeAttnParams p) {
+__global__ void __launch_bounds__(DC / 4 >= 64 ? DC / 4 : 64) decode_combine_kernel(DecodeAttnParams p) {
   const int bh = blockIdx.x;  // b * n_h + head
   const int b = bh / p.n_h, head = bh % p.n_h;
+  const int64_t base = (int64_t)b * p.splits * p.n_h + head;  // partition s at base + s * n_h
   float M = -INFINITY;
-  for (int s = 0; s < p.splits; ++s) M = fmaxf(M, p.part_m[((int64_t)b * p.splits + s) * p.n_h + head]);
+  for (int s = 0; s < p.splits; ++s) M = fmaxf(M, p.part_m[base + (int64_t)s * p.n_h]);
   float L = 0.f;
   for (int s = 0; s < p.splits; ++s) {
-    const int64_t pi = ((int64_t)b * p.splits + s) * p.n_h + head;
-    const float ms = p.part_m[pi];
-    if (ms > -INFINITY) L += exp2f(ms - M) * p.part_l[pi];
+    const float ms = p.part_m[base + (int64_t)s * p.n_h];
+    if (ms > -INFINITY) L += exp2f(ms - M) * p.part_l[base + (int64_t)s * p.n_h];
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  T* out = reinterpret_cast<T*>(p.o_hat) + (int64_t)bh * DC;
-  for (int d = threadIdx.x; d < DC; d += blockDim.x) {
-    float acc = 0.f;
+  const int d = 4 * threadIdx.x;
+  if (d < DC) {
+    floatx4 acc = {0, 0, 0, 0};
     for (int s = 0; s < p.splits; ++s) {
-      const int64_t pi = ((int64_t)b * p.splits + s) * p.n_h + head;
+      const int64_t pi = base + (int64_t)s * p.n_h;
       const float ms = p.part_m[pi];
-      if (ms > -INFINITY) acc += exp2f(ms - M) * p.part_o[pi * DC + d];
+      if (ms > -INFINITY) acc += exp2f(ms - M) * *reinterpret_cast<const floatx4*>(p.part_o + pi * DC + d);
     }
-    out[d] = from_f32<T>(acc * inv);
+    T* out = reinterpret_cast<T*>(p.o_hat) + (int64_t)bh * DC + d;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) out[r] = from_f32<T>(acc[r] * inv);
   }
   if (p.lse && threadIdx.x == 0) p.lse[bh] = (M + log2f(L)) * 0.69314718055994531f;
 }
@@ -539,7 +544,7 @@ hipError_t launch(const DecodeAttnParams& p, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<T, DC>), dim3(p.B * p.n_h), dim3(128), 0, s, p);
+  hipLaunchKernelGGL((decode_combine_kernel<T, DC>), dim3(p.B * p.n_h), dim3(DC / 4 >= 64 ? DC / 4 : 64), 0, s, p);
   return hipGetLastError();
 }
 }  // namespace
@@ -554,7 +559,7 @@ hipError_t decode_attention(DType t, const DecodeAttnParams& p, hipStream_t s) {
                        p.block_table);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
-    hipLaunchKernelGGL((decode_combine_kernel<bf16, 512>), dim3(p.B * p.n_h), dim3(128), 0, s, p);
+    hipLaunchKernelGGL((decode_combine_kernel<bf16, 512>), dim3(p.B * p.n_h), dim3(128), 0, s, p);  // 4 dims/thread
     return hipGetLastError();
   }
   if (p.d_c == 512 && p.d_hr == 64)
