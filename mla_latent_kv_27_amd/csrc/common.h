@@ -109,4 +109,31 @@ __device__ __forceinline__ float wave_sum_xor(float v, int mask) { return v + __
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// ---- direct-to-LDS copies and the waits that go with them
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// s_waitcnt immediates (gfx9 encoding): vmcnt in bits [3:0] and [15:14], expcnt [6:4],
+// lgkmcnt [11:8]; the unused counters are left at their maximum.
+constexpr int waitcnt_vm(int n) { return ((n >> 4) << 14) | (0xF << 8) | (0x7 << 4) | (n & 0xF); }
+constexpr int kWaitLgkm0 = (0x3 << 14) | (0x7 << 4) | 0xF;
+
+// Workgroup barrier for the pipeline: waits only on what the caller asked for (unlike
+// __syncthreads, whose release fence would also wait for the copies in flight), and
+// compiler-only fences keep LDS accesses from being moved across it.
+#define MLA_TILE_BARRIER(waitcnt_imm)            \
+  do {                                           \
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);     \
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm);     \
+    __builtin_amdgcn_s_barrier();                \
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);     \
+  } while (0)
+
+// The same wait without the barrier: for copies into LDS that only the issuing wave reads.
+#define MLA_WAVE_WAIT(waitcnt_imm)               \
+  do {                                           \
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);     \
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm);     \
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);     \
+  } while (0)
+
 }  // namespace mla

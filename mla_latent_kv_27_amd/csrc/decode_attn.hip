@@ -224,7 +224,6 @@ __shared__ __attribute__((aligned(1024))) char g_kv1[tiled::kBytes];
 __shared__ __attribute__((aligned(1024))) char g_kv2[tiled::kBytes];
 __shared__ __attribute__((aligned(1024))) char g_kv3[tiled::kBytes];
 
-typedef __attribute__((address_space(3))) void lds_void_t;
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4_t;
 
@@ -232,22 +231,6 @@ template <int BUF>
 __device__ __forceinline__ char* kv_buf() {
   return BUF == 0 ? g_kv0 : (BUF == 1 ? g_kv1 : (BUF == 2 ? g_kv2 : g_kv3));
 }
-
-// s_waitcnt immediates (gfx9 encoding): vmcnt in bits [3:0] and [15:14], expcnt [6:4],
-// lgkmcnt [11:8]; the unused counters are left at their maximum.
-constexpr int waitcnt_vm(int n) { return ((n >> 4) << 14) | (0xF << 8) | (0x7 << 4) | (n & 0xF); }
-constexpr int kWaitLgkm0 = (0x3 << 14) | (0x7 << 4) | 0xF;
-
-// Workgroup barrier for the pipeline: waits only on what the caller asked for (unlike
-// __syncthreads, whose release fence would also wait for the copies in flight), and
-// compiler-only fences keep LDS accesses from being moved across it.
-#define MLA_TILE_BARRIER(waitcnt_imm)            \
-  do {                                           \
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);     \
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm);     \
-    __builtin_amdgcn_s_barrier();                \
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);     \
-  } while (0)
 
 struct TiledCtx {
   const char* pool;

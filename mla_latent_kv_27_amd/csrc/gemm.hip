@@ -10,6 +10,7 @@
 // when K is split across workgroups for small M, writes fp32 partials that a second kernel
 // sums before running the same epilogue.
 #include <algorithm>
+#include <numeric>
 
 #include "common.h"
 #include "internal.h"
@@ -47,6 +48,34 @@ __device__ __forceinline__ void epi_store(const Epilogue& e, int z, int row, int
   if (e.C2) e.C2[idx] = v;
 }
 
+// The element (row, col) of the product through whichever epilogue owns the column; partner is
+// the value of column col ^ 1 (RoPE pairs).
+template <typename T>
+__device__ __forceinline__ void out_elem(const GemmParams& p, int z, int row, int col, float v, float partner) {
+  if (col >= p.E0) {
+    rope_pair(p.epi2, row, col - p.E0, v, partner);
+    epi_store<T>(p.epi2, z, row, col - p.E0, v);
+  } else {
+    rope_pair(p.epi, row, col, v, partner);
+    epi_store<T>(p.epi, z, row, col, v);
+  }
+}
+
+// Whether any column of [c0, c1) is rotated (so that partners must be exchanged).
+__device__ __forceinline__ bool cols_have_rope(const GemmParams& p, int c0, int c1) {
+  const int64_t lo_end = std::min<int64_t>(c1, p.E0);
+  if (lo_end > std::max<int64_t>(c0, p.epi.rope_col0)) return true;
+  return (int64_t)c1 > (int64_t)p.E0 + p.epi2.rope_col0;
+}
+
+// Row n of the stacked B operand ("NT" form).
+template <typename T>
+__device__ __forceinline__ const T* b_row(const GemmParams& p, int z, int n) {
+  const void* base = n < p.N0 ? p.B0 : (n < p.N1 ? p.B1 : p.B2);
+  const int r = n < p.N0 ? n : (n < p.N1 ? n - p.N0 : n - p.N1);
+  return reinterpret_cast<const T*>(base) + (int64_t)z * p.strideB + (int64_t)r * p.ldb;
+}
+
 template <typename T, int BM, int BN, int WM, int WN>
 __global__ void __launch_bounds__(64 * WM * WN)
     gemm_kernel(GemmParams p, int splits, int k_per_split, float* __restrict__ partial) {
@@ -67,7 +96,6 @@ __global__ void __launch_bounds__(64 * WM * WN)
 
   const T* A = reinterpret_cast<const T*>(p.A) + (int64_t)z * p.strideA;
   const T* B0 = reinterpret_cast<const T*>(p.B0) + (int64_t)z * p.strideB;
-  const T* B1 = p.B1 ? reinterpret_cast<const T*>(p.B1) + (int64_t)z * p.strideB : nullptr;
 
   floatx16 acc[FM][FN];
   for (int i = 0; i < FM; ++i)
@@ -90,8 +118,7 @@ __global__ void __launch_bounds__(64 * WM * WN)
         const int gn = n0 + r, gk = k0 + kc;
         Chunk16 v = zero16();
         if (gn < p.N && gk < ke) {
-          const T* src = gn < p.N0 ? B0 + (int64_t)gn * p.ldb : B1 + (int64_t)(gn - p.N0) * p.ldb;
-          v = ld16(src + gk);
+          v = ld16(b_row<T>(p, z, gn) + gk);
         }
         st16(&Bs[r * LDK + kc], v);
       }
@@ -134,83 +161,227 @@ __global__ void __launch_bounds__(64 * WM * WN)
       }
     return;
   }
-  const bool tile_rope = n0 + BN > p.epi.rope_col0;  // uniform across the workgroup
+  const bool tile_rope = cols_have_rope(p, n0, n0 + BN);  // uniform across the workgroup
   for (int i = 0; i < FM; ++i)
     for (int j = 0; j < FN; ++j) {
       const int col = n0 + wn * FN * 32 + j * 32 + (lane & 31);
       for (int r = 0; r < 16; ++r) {
         const int row = m0 + wm * FM * 32 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        float v = acc[i][j][r];
-        if (tile_rope) {
-          const float partner = __shfl_xor(v, 1, 64);
-          if (row < p.M && col < p.N) rope_pair(p.epi, row, col, v, partner);
-        }
-        if (row < p.M && col < p.N) epi_store<T>(p.epi, z, row, col, v);
+        const float v = acc[i][j][r];
+        const float partner = tile_rope ? __shfl_xor(v, 1, 64) : 0.f;
+        if (row < p.M && col < p.N) out_elem<T>(p, z, row, col, v, partner);
       }
     }
 }
 
-// Sums the split-K partials [splits][batch][M][N] and runs the epilogue; one thread per
-// column pair so that RoPE pairs stay together.
-template <typename T>
+// Sums the split-K partials [splits][batch][M][N] and runs the epilogue; a thread owns an even
+// number of consecutive columns so that RoPE pairs stay together.
+template <typename T, int V>
 __global__ void __launch_bounds__(256)
     splitk_reduce_kernel(GemmParams p, int splits, const float* __restrict__ partial) {
-  const int64_t pairs = (int64_t)p.batch * p.M * (p.N / 2);
+  // one thread per V consecutive columns of one row; the splits are summed in order, eight
+  // partial loads in flight at a time
+  typedef float vec_t __attribute__((ext_vector_type(V)));
+  const int64_t groups = (int64_t)p.batch * p.M * (p.N / V);
   const int64_t stride = (int64_t)p.M * p.N * p.batch;
-  for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < pairs;
+  for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < groups;
        t += (int64_t)gridDim.x * blockDim.x) {
-    const int cp = (int)(t % (p.N / 2));
-    const int64_t zr = t / (p.N / 2);
+    const int cg = (int)(t % (p.N / V));
+    const int64_t zr = t / (p.N / V);
     const int row = (int)(zr % p.M), z = (int)(zr / p.M);
-    const int col = 2 * cp;
+    const int col = V * cg;
     const float* src = partial + ((int64_t)z * p.M + row) * p.N + col;
-    float v0 = 0.f, v1 = 0.f;
-    for (int s = 0; s < splits; ++s) {
-      const float2 v = *reinterpret_cast<const float2*>(src + s * stride);
-      v0 += v.x;
-      v1 += v.y;
+    vec_t acc = {};
+    int s = 0;
+    for (; s + 8 <= splits; s += 8) {
+      vec_t v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = *reinterpret_cast<const vec_t*>(src + (s + i) * stride);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc += v[i];
     }
-    const float e0 = v0, e1 = v1;
-    rope_pair(p.epi, row, col, v0, e1);
-    rope_pair(p.epi, row, col + 1, v1, e0);
-    epi_store<T>(p.epi, z, row, col, v0);
-    epi_store<T>(p.epi, z, row, col + 1, v1);
+    for (; s < splits; ++s) acc += *reinterpret_cast<const vec_t*>(src + s * stride);
+#pragma unroll
+    for (int i = 0; i < V; i += 2) {
+      out_elem<T>(p, z, row, col + i, acc[i], acc[i + 1]);
+      out_elem<T>(p, z, row, col + i + 1, acc[i + 1], acc[i]);
+    }
   }
 }
 
 // ----------------------------------------------------------------------------- skinny kernel
-// Decode-sized products (M <= 64 rows, bf16, y = W x with W [N][K]) stream the weights once and
-// are bound by HBM.  Each wave owns 32 output columns for all M rows:
-//   * its weight rows come straight from global memory into registers, 64 contiguous bytes per
-//     lane and k-step of 64 (two lanes per row cover the row's 128-byte line), three k-steps ahead;
-//   * the activation slice of a k-step (M x 64) is copied once per workgroup into LDS by direct
-//     global->LDS copies (four-stage ring, 16-byte chunks XOR-swizzled by row);
-//   * the 32x32x16 MFMA k-slots are permuted so that lane group g owns k = 32g + 8j .. +7 in
-//     sub-step j, which makes both operands' per-lane data contiguous.
+// Decode-sized products (M <= 64 rows, bf16, y = W x with W [N][K]) read every weight byte once
+// and are bound by HBM.  A workgroup of four waves owns 128 output columns and one k range;
+// each wave owns 32 of the columns.
+//   Weights: each wave copies its own 32 rows straight into a private LDS ring of kNS 64-k
+//     stages (kNS steps in flight), with a coalesced pattern: one copy instruction covers
+//     eight whole 128-byte row segments.  Only the issuing wave reads a stage, so no barrier
+//     is needed for them.  Reading weights with MFMA-fragment-shaped per-lane loads instead
+//     touches four times as many cache lines per instruction and needs several times more
+//     waves in flight to reach the same bandwidth.
+//   Activations: shared by the four waves, copied in chunks of kChunk steps into a double
+//     buffer, with one barrier per chunk.
+// The LDS footprint (80 KiB) lets two workgroups share a compute unit.
+// Both LDS images swizzle 16-byte chunks (slot = chunk ^ (row & 7)) so that fragment reads,
+// 32 rows at one chunk, spread over all banks.  In sub-step j (16 k) of a step, lane group g
+// supplies k-chunk 2j + g of the step to the 32x32x16 MFMA for both operands.
+// The copies of steps and chunks past the end re-read the last one (in bounds, never used),
+// so every wait below counts the same number of copies in flight.
 namespace skinny {
-constexpr int kKS = 64;      // k per step
+constexpr int kKS = 64;                    // k per step: 128 bytes of a weight row
 constexpr int kWaves = 4;
-constexpr int kBN = 32 * kWaves;
-constexpr int kAStages = 4;
-constexpr int kBStages = 4;  // register ring: steps s+1..s+3 in flight while s is multiplied
+constexpr int kBN = 32 * kWaves;           // columns per workgroup
+constexpr int kNS = 3;                     // weight stages per wave
+constexpr int kChunk = 2;                  // steps per activation chunk
+constexpr int kStage = 32 * 128;           // bytes of one wave's weight stage
+constexpr int kBI = kStage / 1024;         // weight copy instructions per step (4)
+constexpr int kAChunkRow = kChunk * kKS * 2;  // bytes of one activation row in a chunk
+constexpr int kARowsPerCopy = 1024 / kAChunkRow;
+constexpr int kPeriod = kNS * 2 * kChunk / std::gcd(kNS, 2 * kChunk);  // steps unrolled
+// the step waits below assume the ring never holds steps of more than two chunks
+static_assert(kNS - 1 <= kChunk, "ring deeper than a chunk");
+static_assert(kPeriod % kNS == 0 && kPeriod % (2 * kChunk) == 0, "unroll period");
+// activation copies per wave per chunk for MB row blocks
+template <int MB>
+constexpr int a_copies() { return MB * 32 * kAChunkRow / (1024 * kWaves); }
+// activation chunks issued after weight step s (position q in its chunk) was issued and before
+// step s waits for it: multiples of kChunk in (s - kNS + 1, s]
+constexpr int a_after_b(int q) {
+  return (q >= 0 ? q / kChunk : -((-q + kChunk - 1) / kChunk)) -
+         ((q - kNS + 1) >= 0 ? (q - kNS + 1) / kChunk : -((-(q - kNS + 1) + kChunk - 1) / kChunk));
+}
 }  // namespace skinny
 
-typedef __attribute__((address_space(3))) void lds_void_g;
+__shared__ __attribute__((aligned(1024))) char g_sk_a0[64 * skinny::kAChunkRow];
+__shared__ __attribute__((aligned(1024))) char g_sk_a1[64 * skinny::kAChunkRow];
+__shared__ __attribute__((aligned(1024))) char g_sk_b0[skinny::kWaves * skinny::kStage];
+__shared__ __attribute__((aligned(1024))) char g_sk_b1[skinny::kWaves * skinny::kStage];
+__shared__ __attribute__((aligned(1024))) char g_sk_b2[skinny::kWaves * skinny::kStage];
+static_assert(skinny::kNS == 3, "one LDS array per stage");
 
-template <int MB>
-__device__ __forceinline__ void skinny_issue_a(const bf16* A, int64_t lda, int M, int k0, char* stage, int w,
-                                               int lane) {
-  // stage layout: row m (64 k = 128 bytes = 8 chunks), chunk c at slot c ^ (m & 7)
-  constexpr int kInst = MB * 32 * 8 / 64;  // 1 KiB copies per workgroup (4 or 8)
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+template <int AB>
+__device__ __forceinline__ char* sk_abuf() { return AB == 0 ? g_sk_a0 : g_sk_a1; }
+template <int ST>
+__device__ __forceinline__ char* sk_bbuf() { return ST == 0 ? g_sk_b0 : (ST == 1 ? g_sk_b1 : g_sk_b2); }
+
+struct SkinnyCtx {
+  const bf16* a;        // activation row 0 of this batch at k = kb
+  int64_t lda;
+  int M, nsteps, nchunks;
+  const bf16* brow[skinny::kBI];  // this lane's weight row of copy i, at k = kb + its chunk
+  int w, lane;
+};
+
+// Activation chunk c (clamped to the last one) into buffer AB: MB*32 rows x kAChunkRow bytes;
+// copy instruction p of the workgroup covers kARowsPerCopy whole row segments.
+template <int MB, int AB>
+__device__ __forceinline__ void sk_issue_a(const SkinnyCtx& x, int c) {
+  using namespace skinny;
+  constexpr int CPR = kAChunkRow / 16;  // 16-byte chunks per row segment
+  c = min(c, x.nchunks - 1);
+  char* dst = sk_abuf<AB>();
+  const int slot = x.lane % CPR;
 #pragma unroll
-  for (int i = 0; i < kInst / skinny::kWaves; ++i) {
-    const int inst = w * (kInst / skinny::kWaves) + i;
-    const int P = inst * 64 + lane;
-    const int m = P >> 3, slot = P & 7;
-    const int c = slot ^ (m & 7);
-    const int mr = min(m, M - 1);  // rows past M copy a valid row; their results are dropped
-    __builtin_amdgcn_global_load_lds((const void*)(A + (int64_t)mr * lda + k0 + c * 8),
-                                     (lds_void_g*)(stage + inst * 1024), 16, 0, 0);
+  for (int i = 0; i < a_copies<MB>(); ++i) {
+    const int p = i * kWaves + x.w;
+    const int row = p * kARowsPerCopy + x.lane / CPR;
+    const int ch = slot ^ (row & 7);                  // 16-byte chunk of the row segment
+    // the last chunk may hold fewer steps: clamp its k inside the k range
+    const int kk = min(c * (kChunk * kKS) + ch * 8, (x.nsteps - 1) * kKS + (ch & 7) * 8);
+    const bf16* src = x.a + (int64_t)min(row, x.M - 1) * x.lda + kk;
+    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(dst + p * 1024), 16, 0, 0);
+  }
+}
+
+// Weight step s (clamped to the last one) into this wave's part of stage ST.
+template <int ST>
+__device__ __forceinline__ void sk_issue_b(const SkinnyCtx& x, int s) {
+  using namespace skinny;
+  s = min(s, x.nsteps - 1);
+  char* dst = sk_bbuf<ST>() + x.w * kStage;
+#pragma unroll
+  for (int i = 0; i < kBI; ++i)
+    __builtin_amdgcn_global_load_lds((const void*)(x.brow[i] + s * kKS), (lds_void_t*)(dst + i * 1024), 16, 0, 0);
+}
+
+// One step (s = position U of the unrolled period): the copies that refill the ring, waits,
+// and 4 x MB MFMAs.
+//   At a chunk's first step, activation chunk c must have landed for every wave: after it this
+//   wave issued kNS - 1 weight steps (prologue, c = 0) or the kChunk weight steps of chunk c-1.
+//   Step s's weight copy is followed by the kNS - 1 later weight steps and a_after_b(q)
+//   activation chunks.
+template <int MB, int U>
+__device__ __forceinline__ void sk_step(const SkinnyCtx& x, int s, floatx16 (&acc)[MB]) {
+  using namespace skinny;
+  constexpr int ST = U % kNS, AB = (U / kChunk) % 2, Q = U % kChunk;
+  if (Q == 0) {
+    if (s == 0) MLA_TILE_BARRIER(waitcnt_vm((kNS - 1) * kBI));
+    else MLA_TILE_BARRIER(waitcnt_vm(kChunk * kBI));
+    sk_issue_a<MB, 1 - AB>(x, s / kChunk + 1);
+  }
+  // stage (ST + kNS - 1) % kNS was last read in step s - 1, whose reads have completed
+  sk_issue_b<(ST + kNS - 1) % kNS>(x, s + kNS - 1);
+  MLA_WAVE_WAIT(waitcnt_vm((kNS - 1) * kBI + a_after_b(Q) * a_copies<MB>()));
+
+  // Fragment reads.  The compiler would make every LDS read that follows a direct-to-LDS copy
+  // wait for all copies in flight, which serialises the ring; the reads and their wait are one
+  // asm block instead, ordered after the waits above (outputs early-clobber: every read is in
+  // flight before the first result lands).
+  int lane = x.lane;
+  asm volatile("" : "+v"(lane));
+  const int g = lane >> 5, l32 = lane & 31, x7 = l32 & 7;
+  const uint32_t bb = lds_addr(sk_bbuf<ST>()) + x.w * kStage + l32 * 128;
+  const uint32_t ab = lds_addr(sk_abuf<AB>()) + l32 * kAChunkRow + Q * 128;
+  uint32_t sw[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) sw[j] = ((2 * j + g) ^ x7) * 16;
+  bf16x8 bq[4], aq[MB][4];
+  if constexpr (MB == 1) {
+    asm volatile(
+        "ds_read_b128 %0, %8\n\tds_read_b128 %1, %9\n\tds_read_b128 %2, %10\n\tds_read_b128 %3, %11\n\t"
+        "ds_read_b128 %4, %12\n\tds_read_b128 %5, %13\n\tds_read_b128 %6, %14\n\tds_read_b128 %7, %15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(bq[0]), "=&v"(bq[1]), "=&v"(bq[2]), "=&v"(bq[3]), "=&v"(aq[0][0]), "=&v"(aq[0][1]), "=&v"(aq[0][2]),
+          "=&v"(aq[0][3])
+        : "v"(bb + sw[0]), "v"(bb + sw[1]), "v"(bb + sw[2]), "v"(bb + sw[3]), "v"(ab + sw[0]), "v"(ab + sw[1]),
+          "v"(ab + sw[2]), "v"(ab + sw[3]));
+  } else {
+    // rows 32 + l32 of the activation chunk share (row & 7) with l32: same swizzle, 32 rows on
+    asm volatile(
+        "ds_read_b128 %0, %12\n\tds_read_b128 %1, %13\n\tds_read_b128 %2, %14\n\tds_read_b128 %3, %15\n\t"
+        "ds_read_b128 %4, %16\n\tds_read_b128 %5, %17\n\tds_read_b128 %6, %18\n\tds_read_b128 %7, %19\n\t"
+        "ds_read_b128 %8, %16 offset:%20\n\tds_read_b128 %9, %17 offset:%20\n\t"
+        "ds_read_b128 %10, %18 offset:%20\n\tds_read_b128 %11, %19 offset:%20\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(bq[0]), "=&v"(bq[1]), "=&v"(bq[2]), "=&v"(bq[3]), "=&v"(aq[0][0]), "=&v"(aq[0][1]), "=&v"(aq[0][2]),
+          "=&v"(aq[0][3]), "=&v"(aq[1][0]), "=&v"(aq[1][1]), "=&v"(aq[1][2]), "=&v"(aq[1][3])
+        : "v"(bb + sw[0]), "v"(bb + sw[1]), "v"(bb + sw[2]), "v"(bb + sw[3]), "v"(ab + sw[0]), "v"(ab + sw[1]),
+          "v"(ab + sw[2]), "v"(ab + sw[3]), "n"(32 * kAChunkRow));
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    Frag8<bf16> bf;
+    bf.v = bq[j];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      Frag8<bf16> af;
+      af.v = aq[mb][j];
+      acc[mb] = mma32(af, bf, acc[mb]);
+    }
+  }
+}
+
+// Steps s .. s + kPeriod - 1 with compile-time ring, buffer and chunk positions.
+template <int MB, int U>
+__device__ __forceinline__ void sk_period(const SkinnyCtx& x, int s, floatx16 (&acc)[MB]) {
+  if constexpr (U < skinny::kPeriod) {
+    if (s + U < x.nsteps) {
+      sk_step<MB, U>(x, s + U, acc);
+      sk_period<MB, U + 1>(x, s, acc);
+    }
   }
 }
 
@@ -218,24 +389,30 @@ template <int MB>
 __global__ void __launch_bounds__(256)
     gemm_skinny_kernel(GemmParams p, int splits, int k_per_split, float* __restrict__ partial) {
   using namespace skinny;
-  constexpr int kAStageBytes = MB * 32 * 128;
-  constexpr int kAInstPerWave = MB * 32 * 8 / 64 / kWaves;  // 1 or 2
-  __shared__ __attribute__((aligned(1024))) char As[kAStages][kAStageBytes];
-
   const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = lane >> 5, l32 = lane & 31;
+  const int w = tid >> 6;
   const int n0 = blockIdx.x * kBN;
   const int z = blockIdx.y / splits, sp = blockIdx.y % splits;
   const int kb = sp * k_per_split, ke = min(p.K, kb + k_per_split);
-  const int nsteps = (ke - kb) / kKS;
 
-  const bf16* A = reinterpret_cast<const bf16*>(p.A) + (int64_t)z * p.strideA;
-  // this lane's weight row (rows past N read row N-1; their columns are dropped)
-  const int n = min(n0 + w * 32 + l32, p.N - 1);
-  const bf16* brow = n < p.N0 ? reinterpret_cast<const bf16*>(p.B0) + (int64_t)z * p.strideB + (int64_t)n * p.ldb
-                              : reinterpret_cast<const bf16*>(p.B1) + (int64_t)z * p.strideB + (int64_t)(n - p.N0) * p.ldb;
-  brow += 32 * g;
+  SkinnyCtx x;
+  x.a = reinterpret_cast<const bf16*>(p.A) + (int64_t)z * p.strideA + kb;
+  x.lda = p.lda;
+  x.M = p.M;
+  x.nsteps = (ke - kb) / kKS;
+  x.nchunks = (x.nsteps + kChunk - 1) / kChunk;
+  x.w = w;
+  x.lane = lane;
+  {
+    const int r8 = lane >> 3;                      // row within the copy's 8 rows
+    const int ch = (lane & 7) ^ r8;                // 16-byte chunk this lane copies
+#pragma unroll
+    for (int i = 0; i < kBI; ++i) {
+      // rows past N copy row N - 1; their columns are dropped
+      const int n = min(n0 + w * 32 + 8 * i + r8, p.N - 1);
+      x.brow[i] = b_row<bf16>(p, z, n) + kb + ch * 8;
+    }
+  }
 
   floatx16 acc[MB];
 #pragma unroll
@@ -243,57 +420,19 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
 
-  bf16x8 bq[kBStages][4];
-  // prologue: steps 0..2, each issued as [A copies, B loads] like every later step, so that the
-  // wait for step t always leaves exactly the copies and loads of steps t+1 and t+2 in flight
-#pragma unroll
-  for (int s0 = 0; s0 < kBStages - 1; ++s0)
-    if (s0 < nsteps) {
-      skinny_issue_a<MB>(A, p.lda, p.M, kb + s0 * kKS, As[s0], w, lane);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bq[s0][j] = *reinterpret_cast<const bf16x8*>(brow + kb + s0 * kKS + 8 * j);
-    }
-
-  for (int s = 0; s < nsteps; s += kBStages) {
-#pragma unroll
-    for (int u = 0; u < kBStages; ++u) {
-      const int st = s + u;
-      if (st < nsteps) {
-        // every step is issued as [A copies, B loads]; waiting until only the later steps'
-        // (st+1, st+2, if they exist) copies and loads are outstanding completes step st
-        const int later = min(nsteps - 1 - st, kBStages - 2);
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        if (later >= 2) __builtin_amdgcn_s_waitcnt(((2 * (kAInstPerWave + 4)) & 0xF) | (((2 * (kAInstPerWave + 4)) >> 4) << 14) | (0xF << 8) | (0x7 << 4));
-        else if (later == 1) __builtin_amdgcn_s_waitcnt(((kAInstPerWave + 4) & 0xF) | (((kAInstPerWave + 4) >> 4) << 14) | (0xF << 8) | (0x7 << 4));
-        else __builtin_amdgcn_s_waitcnt((0xF << 8) | (0x7 << 4));
-        __builtin_amdgcn_s_barrier();
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        // refill: the A stage of step st-1 (everyone is past it) and B slot of step st-1
-        if (st + 3 < nsteps) {
-          skinny_issue_a<MB>(A, p.lda, p.M, kb + (st + 3) * kKS, As[(u + 3) % kAStages], w, lane);
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            bq[(u + 3) % kBStages][j] = *reinterpret_cast<const bf16x8*>(brow + kb + (st + 3) * kKS + 8 * j);
-        }
-        const char* as = As[u % kAStages];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          Frag8<bf16> bf;
-          bf.v = bq[u][j];
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb) {
-            const int m = mb * 32 + l32;
-            Frag8<bf16> af;
-            af.v = *reinterpret_cast<const bf16x8*>(as + m * 128 + (((4 * g + j) ^ (m & 7)) * 16));
-            acc[mb] = mma32(af, bf, acc[mb]);
-          }
-        }
-      }
-    }
+  if (x.nsteps > 0) {
+    sk_issue_a<MB, 0>(x, 0);
+    sk_issue_b<0>(x, 0);
+    sk_issue_b<1>(x, 1);
+    static_assert(kNS == 3, "prologue fills kNS - 1 stages");
+    for (int s = 0; s < x.nsteps; s += kPeriod) sk_period<MB, 0>(x, s, acc);
+    // the ring's last copies (re-reads past the end) must land before the LDS is released
+    MLA_WAVE_WAIT(waitcnt_vm(0));
   }
 
   // C layout: lane col = n0 + w*32 + l32; value r at row mb*32 + 8*(r/4) + 4*g + r%4
-  const int col = n0 + w * 32 + l32;
+  const int g = lane >> 5;
+  const int col = n0 + w * 32 + (lane & 31);
   if (splits > 1) {
     float* P = partial + ((int64_t)(sp * p.batch + z) * p.M) * p.N;
 #pragma unroll
@@ -305,18 +444,15 @@ __global__ void __launch_bounds__(256)
       }
     return;
   }
-  const bool tile_rope = n0 + kBN > p.epi.rope_col0;
+  const bool tile_rope = cols_have_rope(p, n0, n0 + kBN);
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = mb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-      float v = acc[mb][r];
-      if (tile_rope) {
-        const float partner = __shfl_xor(v, 1, 64);
-        if (row < p.M && col < p.N) rope_pair(p.epi, row, col, v, partner);
-      }
-      if (row < p.M && col < p.N) epi_store<bf16>(p.epi, z, row, col, v);
+      const float v = acc[mb][r];
+      const float partner = tile_rope ? __shfl_xor(v, 1, 64) : 0.f;
+      if (row < p.M && col < p.N) out_elem<bf16>(p, z, row, col, v, partner);
     }
 }
 
@@ -356,9 +492,15 @@ hipError_t run_t(const GemmParams& p, const GemmPlan& plan, float* partial, hipS
     default: err = launch_cfg<T, 2>(p, plan, partial, s); break;
   }
   if (err != hipSuccess || plan.splits == 1) return err;
-  const int64_t pairs = (int64_t)p.batch * p.M * (p.N / 2);
-  const int blocks = (int)std::min<int64_t>((pairs + 255) / 256, 8192);
-  hipLaunchKernelGGL(splitk_reduce_kernel<T>, dim3(blocks), dim3(256), 0, s, p, plan.splits, partial);
+  if (p.N % 4 == 0) {
+    const int64_t groups = (int64_t)p.batch * p.M * (p.N / 4);
+    const int blocks = (int)std::min<int64_t>((groups + 255) / 256, 8192);
+    hipLaunchKernelGGL((splitk_reduce_kernel<T, 4>), dim3(blocks), dim3(256), 0, s, p, plan.splits, partial);
+  } else {
+    const int64_t groups = (int64_t)p.batch * p.M * (p.N / 2);
+    const int blocks = (int)std::min<int64_t>((groups + 255) / 256, 8192);
+    hipLaunchKernelGGL((splitk_reduce_kernel<T, 2>), dim3(blocks), dim3(256), 0, s, p, plan.splits, partial);
+  }
   return hipGetLastError();
 }
 }  // namespace
@@ -375,9 +517,10 @@ GemmPlan gemm_plan_skinny(int M, int N, int K, int batch, int cus) {
   pl.bn = skinny::kBN;
   const int64_t tiles = (int64_t)((N + pl.bn - 1) / pl.bn) * batch;
   const int ksteps = K / skinny::kKS;
-  // about two workgroups per CU, each streaming at least 8 k-steps
-  int splits = (int)std::max<int64_t>(1, (2LL * cus + tiles - 1) / tiles);
-  splits = std::min(splits, std::max(1, ksteps / 8));
+  // two workgroups fit per compute unit: split k so that the grid fills them once, each split
+  // streaming at least four steps
+  int splits = (int)std::max<int64_t>(1, 2LL * cus / tiles);
+  splits = std::min(splits, std::max(1, ksteps / 4));
   const int per = (ksteps + splits - 1) / splits;
   pl.splits = (ksteps + per - 1) / per;
   pl.k_per_split = per * skinny::kKS;

@@ -35,17 +35,23 @@ struct Epilogue {
 };
 
 // C[z] (M x N) = A[z] (M x K) * op(B[z]),  op(B) = B^T with B [N][K] ("NT", weights in y = W x
-// form) or B with B [K][N] ("NN").  For NT, rows n >= N0 are taken from B1 (row n - N0).
+// form) or B with B [K][N] ("NN").  For NT the rows of B may come from up to three matrices
+// stacked along N: rows n < N0 from B0, N0 <= n < N1 from B1 (row n - N0), n >= N1 from B2
+// (row n - N1).  Output columns col >= E0 go through epi2 as column col - E0 (two products that
+// share the input A in one launch); E0 is even, so RoPE pairs never straddle it.
 struct GemmParams {
   const void* A = nullptr;
   int64_t lda = 0, strideA = 0;
   const void* B0 = nullptr;
   const void* B1 = nullptr;
-  int N0 = 1 << 30;
+  const void* B2 = nullptr;
+  int N0 = 1 << 30, N1 = 1 << 30;
   int64_t ldb = 0, strideB = 0;
   bool nn = false;
   int M = 0, N = 0, K = 0, batch = 1;
   Epilogue epi;
+  Epilogue epi2;
+  int E0 = 1 << 30;
 };
 
 struct GemmPlan {

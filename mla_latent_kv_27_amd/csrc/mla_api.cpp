@@ -96,26 +96,26 @@ AppendWs carve_append(Carve& cv, const mla_dims* d, int n, int cus) {
   return w;
 }
 
+// Decode products; those sharing an input run as one launch with stacked weights:
+//   kvq = h [W_DQ; W_DKV; W_KR]   (c^q and the new cache entry; W_DKV; W_KR alone when d_cq == 0)
+//   q   = q_in [W_UQ; W_QR]       (q^C and the rotated q^R)
 struct DecodeGemms {
-  GemmPlan cq, qc, qr, kv, absorb, uv, out;
+  GemmPlan kvq, q, absorb, uv, out;
 };
+inline int kvq_cols(const mla_dims* d) { return d->d_cq + entry(d); }
+inline int q_cols(const mla_dims* d) { return d->n_h * (d->d_h + d->d_hr); }
 // partial workspace serving every batch <= B
 size_t decode_partial_bound(const mla_dims* d, int B, int cus) {
-  size_t b = std::max({gemm_partial_bound(B, d->n_h * d->d_h, q_in(d), 1, cus, sk(d)),
-                       gemm_partial_bound(B, d->n_h * d->d_hr, q_in(d), 1, cus, sk(d)),
-                       gemm_partial_bound(B, entry(d), d->d_model, 1, cus, sk(d)),
-                       gemm_partial_bound(B, d->d_c, d->d_h, d->n_h, cus, false),
-                       gemm_partial_bound(B, d->d_h, d->d_c, d->n_h, cus, sk(d)),
-                       gemm_partial_bound(B, d->d_model, d->n_h * d->d_h, 1, cus, sk(d))});
-  if (d->d_cq > 0) b = std::max(b, gemm_partial_bound(B, d->d_cq, d->d_model, 1, cus, sk(d)));
-  return b;
+  return std::max({gemm_partial_bound(B, kvq_cols(d), d->d_model, 1, cus, sk(d)),
+                   gemm_partial_bound(B, q_cols(d), q_in(d), 1, cus, sk(d)),
+                   gemm_partial_bound(B, d->d_c, d->d_h, d->n_h, cus, false),
+                   gemm_partial_bound(B, d->d_h, d->d_c, d->n_h, cus, sk(d)),
+                   gemm_partial_bound(B, d->d_model, d->n_h * d->d_h, 1, cus, sk(d))});
 }
 DecodeGemms decode_gemms(const mla_dims* d, int B, int cus) {
   DecodeGemms g;
-  g.cq = d->d_cq > 0 ? gemm_plan(B, d->d_cq, d->d_model, 1, cus, sk(d)) : GemmPlan{};
-  g.qc = gemm_plan(B, d->n_h * d->d_h, q_in(d), 1, cus, sk(d));
-  g.qr = gemm_plan(B, d->n_h * d->d_hr, q_in(d), 1, cus, sk(d));
-  g.kv = gemm_plan(B, entry(d), d->d_model, 1, cus, sk(d));
+  g.kvq = gemm_plan(B, kvq_cols(d), d->d_model, 1, cus, sk(d));
+  g.q = gemm_plan(B, q_cols(d), q_in(d), 1, cus, sk(d));
   g.absorb = gemm_plan(B, d->d_c, d->d_h, d->n_h, cus, false);
   g.uv = gemm_plan(B, d->d_h, d->d_c, d->n_h, cus, sk(d));
   g.out = gemm_plan(B, d->d_model, d->n_h * d->d_h, 1, cus, sk(d));
@@ -236,6 +236,23 @@ Epilogue dense(void* C, int64_t ldc) {
   return e;
 }
 
+// Stores rows of [c^KV | k^R] into their paged cache slots, rotating the k^R columns.
+Epilogue cache_epilogue(const mla_dims* d, const mla_paged_cache* c, const float2* rope, const int32_t* seq,
+                        const int32_t* pos) {
+  Epilogue e;
+  e.C = c->pool;
+  e.ldc = entry(d);
+  e.rope_col0 = d->d_c;
+  e.d_hr = d->d_hr;
+  e.rope_tab = rope;
+  e.row_seq = seq;
+  e.row_pos = pos;
+  e.block_table = c->block_table;
+  e.max_blocks = c->max_blocks_per_seq;
+  e.block_size = c->block_size;
+  return e;
+}
+
 int run_cache_writer(const mla_dims* d, const mla_weights* w, const mla_paged_cache* c, const void* h, int n,
                      const int32_t* seq, const int32_t* pos, const float2* rope, const GemmPlan& plan,
                      float* partial, hipStream_t s) {
@@ -249,16 +266,7 @@ int run_cache_writer(const mla_dims* d, const mla_weights* w, const mla_paged_ca
   g.M = n;
   g.N = entry(d);
   g.K = d->d_model;
-  g.epi.C = c->pool;
-  g.epi.ldc = entry(d);
-  g.epi.rope_col0 = d->d_c;
-  g.epi.d_hr = d->d_hr;
-  g.epi.rope_tab = rope;
-  g.epi.row_seq = seq;
-  g.epi.row_pos = pos;
-  g.epi.block_table = c->block_table;
-  g.epi.max_blocks = c->max_blocks_per_seq;
-  g.epi.block_size = c->block_size;
+  g.epi = cache_epilogue(d, c, rope, seq, pos);
   MLA_HIP(gemm_run(dt(d), g, plan, partial, s));
   return MLA_OK;
 }
@@ -394,33 +402,40 @@ int mla_decode(const mla_dims* d, const mla_weights* w, const mla_paged_cache* c
   MLA_HIP(prefill_rows(B, 1, ws.iota, ws.dummy, s));
   MLA_HIP(rope_table(ctx_lens, B, d->d_hr, d->rope_base, ws.rope, s));
   const void* qin = h;
-  if (d->d_cq > 0) {  // c^q = W_DQ h
+  {  // [c^q | c^KV | k^R] = [W_DQ; W_DKV; W_KR] h: c^q to the workspace, the new token's cache
+     // entry to position ctx_lens[b] of its sequence
     GemmParams g;
-    g.A = h; g.lda = d->d_model; g.B0 = w->W_DQ; g.ldb = d->d_model;
-    g.M = B; g.N = d->d_cq; g.K = d->d_model;
-    g.epi = dense(ws.cq, d->d_cq);
-    MLA_HIP(gemm_run(t, g, ws.gm.cq, ws.partial, s));
-    qin = ws.cq;
+    g.A = h; g.lda = d->d_model; g.ldb = d->d_model;
+    g.M = B; g.N = kvq_cols(d); g.K = d->d_model;
+    if (d->d_cq > 0) {
+      g.B0 = w->W_DQ; g.N0 = d->d_cq;
+      g.B1 = w->W_DKV; g.N1 = d->d_cq + d->d_c;
+      g.B2 = w->W_KR;
+      g.epi = dense(ws.cq, d->d_cq);
+      g.E0 = d->d_cq;
+      g.epi2 = cache_epilogue(d, c, ws.rope, ws.iota, ctx_lens);
+      qin = ws.cq;
+    } else {
+      g.B0 = w->W_DKV; g.N0 = d->d_c;
+      g.B1 = w->W_KR;
+      g.epi = cache_epilogue(d, c, ws.rope, ws.iota, ctx_lens);
+    }
+    MLA_HIP(gemm_run(t, g, ws.gm.kvq, ws.partial, s));
   }
-  {  // q^C = W_UQ c^q
+  {  // [q^C | q^R] = [W_UQ; W_QR] c^q: q^C to the workspace, RoPE'd q^R into columns
+     // [d_c, d_c + d_hr) of each head's absorbed query row
     GemmParams g;
-    g.A = qin; g.lda = qw; g.B0 = w->W_UQ; g.ldb = qw;
-    g.M = B; g.N = d->n_h * d->d_h; g.K = qw;
+    g.A = qin; g.lda = qw; g.ldb = qw;
+    g.B0 = w->W_UQ; g.N0 = d->n_h * d->d_h;
+    g.B1 = w->W_QR;
+    g.M = B; g.N = q_cols(d); g.K = qw;
     g.epi = dense(ws.qc, (int64_t)d->n_h * d->d_h);
-    MLA_HIP(gemm_run(t, g, ws.gm.qc, ws.partial, s));
+    g.E0 = d->n_h * d->d_h;
+    g.epi2 = dense(ws.qcat, (int64_t)d->n_h * E);
+    g.epi2.group = d->d_hr; g.epi2.group_stride = E; g.epi2.group_off = d->d_c;
+    g.epi2.rope_col0 = 0; g.epi2.d_hr = d->d_hr; g.epi2.rope_tab = ws.rope;
+    MLA_HIP(gemm_run(t, g, ws.gm.q, ws.partial, s));
   }
-  {  // q^R = RoPE(W_QR c^q) -> columns [d_c, d_c + d_hr) of each head's absorbed query row
-    GemmParams g;
-    g.A = qin; g.lda = qw; g.B0 = w->W_QR; g.ldb = qw;
-    g.M = B; g.N = d->n_h * d->d_hr; g.K = qw;
-    g.epi = dense(ws.qcat, (int64_t)d->n_h * E);
-    g.epi.group = d->d_hr; g.epi.group_stride = E; g.epi.group_off = d->d_c;
-    g.epi.rope_col0 = 0; g.epi.d_hr = d->d_hr; g.epi.rope_tab = ws.rope;
-    MLA_HIP(gemm_run(t, g, ws.gm.qr, ws.partial, s));
-  }
-  // the new token's cache entry at position ctx_lens[b]
-  if ((st = run_cache_writer(d, w, c, h, B, ws.iota, ctx_lens, ws.rope, ws.gm.kv, ws.partial, s)) != MLA_OK)
-    return st;
   {  // q_hat_i = W_UK_i^T q^C_i -> columns [0, d_c) of each head's row
     GemmParams g;
     g.A = ws.qc; g.lda = (int64_t)d->n_h * d->d_h; g.strideA = d->d_h;
