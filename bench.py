@@ -39,7 +39,30 @@ def parse():
     ap.add_argument("--replicas", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["attn", "copy"], default=None,
+                    help="profiling runs: only the attention core of the workload, or only a plain "
+                         "device copy of 1 GiB (the reference for HBM byte counters); prints one line")
     return ap.parse_args()
+
+
+def copy_only(args):
+    """A plain 1 GiB device-to-device copy, --warmup + --steps times (counter reference)."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    print(json.dumps({"only": "copy", "bytes_read": n, "bytes_written": n, "ms": round(ms, 5),
+                      "GBps": round(2 * n / (ms / 1e3) / 1e9, 1)}))
 
 
 def decode_bytes(dims, lens, B):
@@ -111,6 +134,9 @@ def cpu_baseline(dims, W_np, lens, recipe, budget_s):
 
 def main():
     args = parse()
+    if args.only == "copy":
+        copy_only(args)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build "
               f"(sharding across GPUs is described in DESIGN.md but not implemented)", file=sys.stderr)
@@ -143,40 +169,42 @@ def main():
     outs = [torch.empty((B, dims.d_model), dtype=WL.torch_dtype(dims), device="cuda") for _ in reps]
     wss = [WL.decode_workspace(layer, B, max_ctx, splits) for _ in reps]
     stream = torch.cuda.current_stream()
+    q = WL.to_device(S.to_dtype((np.random.default_rng(9).standard_normal((B, dims.n_h, dims.entry)) * 0.05)
+                                .astype(np.float32), dims.dtype), dims)
+    kv = ctx + 1
+    ohat = torch.empty((B, dims.n_h, dims.d_c), dtype=WL.torch_dtype(dims), device="cuda")
+
+    def attn(i):
+        M.decode_attention(layer.cdims, reps[i % len(reps)][1].ccache, q, kv, max_ctx + 1, ohat, wss[0],
+                           num_splits=splits, stream=stream)
+
+    def timed(fn):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.steps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    if args.only == "attn":
+        attn_ms = timed(attn)
+        print(json.dumps({"only": "attn", "workload": w.name, "num_splits": splits, "ms": round(attn_ms, 5),
+                          "algorithmic_bytes": attn_core_bytes(dims, lens, B)}))
+        return
 
     def step(i):
         ly, pl = reps[i % len(reps)]
         M.decode(ly.cdims, ly.cweights, pl.ccache, h, ctx, max_ctx, outs[i % len(reps)], wss[i % len(reps)],
                  num_splits=splits, stream=stream)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / args.steps
+    ms = timed(step)
     value = B / (ms / 1e3)
-
     # dominant kernel: the latent attention core, timed on the same stream
-    q = WL.to_device(S.to_dtype((np.random.default_rng(9).standard_normal((B, dims.n_h, dims.entry)) * 0.05)
-                                .astype(np.float32), dims.dtype), dims)
-    kv = ctx + 1
-    ohat = torch.empty((B, dims.n_h, dims.d_c), dtype=WL.torch_dtype(dims), device="cuda")
-    for i in range(args.warmup):
-        M.decode_attention(layer.cdims, reps[i % len(reps)][1].ccache, q, kv, max_ctx + 1, ohat, wss[0],
-                           num_splits=splits, stream=stream)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for i in range(args.steps):
-        M.decode_attention(layer.cdims, reps[i % len(reps)][1].ccache, q, kv, max_ctx + 1, ohat, wss[0],
-                           num_splits=splits, stream=stream)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    attn_ms = ev0.elapsed_time(ev1) / args.steps
+    attn_ms = timed(attn)
     core_bytes = attn_core_bytes(dims, lens, B)
     achieved = core_bytes / (attn_ms / 1e3) / 1e9
     traffic = counters_for("decode_attn.hip", args.workload)

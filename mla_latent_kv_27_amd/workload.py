@@ -73,6 +73,15 @@ class PagedPool:
         off = torch.from_numpy((pos % self.block_size).astype(np.int64)).to(self.pool.device)
         return self.pool[blk, off].float().cpu().numpy()
 
+    def write_entries(self, b: int, entries: torch.Tensor) -> None:
+        """Stores device entries [n, d_c + d_hr] at positions 0..n-1 of sequence b (a test input
+        path that bypasses the cache writer)."""
+        n = entries.shape[0]
+        pos = np.arange(n)
+        blk = torch.from_numpy(self.table_np[b, pos // self.block_size].astype(np.int64)).to(self.pool.device)
+        off = torch.from_numpy((pos % self.block_size).astype(np.int64)).to(self.pool.device)
+        self.pool[blk, off] = entries.to(self.pool.dtype)
+
 
 def ws_tensor(nbytes: int, device="cuda") -> torch.Tensor:
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)

@@ -44,11 +44,7 @@ class Dims:
     d_hr: int
     dtype: str = BF16
     rope_base: float = 10000.0
-    softmax_scale: float = 0.0  # 0 -> 1/sqrt(d_h + d_hr)
-
-    @property
-    def scale(self) -> float:
-        return self.softmax_scale if self.softmax_scale > 0 else 1.0 / np.sqrt(self.d_h + self.d_hr)
+    softmax_scale: float = 0.0  # 0: the layer's default scale
 
     @property
     def entry(self) -> int:

@@ -98,6 +98,13 @@ def softmax_rows(s: np.ndarray):
 
 
 # ----------------------------------------------------------------------------- attention
+def softmax_scale(dims) -> float:
+    """The logit scale of App. C, 1/sqrt(d_h + d_e), unless the layer fixes another value."""
+    if dims.softmax_scale > 0:
+        return float(dims.softmax_scale)
+    return 1.0 / np.sqrt(np.float64(dims.d_h + dims.d_hr))
+
+
 def attend_unabsorbed(W: dict, dims, qc, qr, cache: np.ndarray, kv_len) -> tuple:
     """Un-absorbed attention of queries against cached entries.
     qc [n, n_h, d_h], qr [n, n_h, d_hr]; cache [L, d_c + d_hr] ([c_KV | k_R]);
@@ -118,7 +125,7 @@ def attend_unabsorbed(W: dict, dims, qc, qr, cache: np.ndarray, kv_len) -> tuple
         rows = slice(i * dims.d_h, (i + 1) * dims.d_h)
         Kc = c @ WUK[rows].T  # [L, d_h]
         V = c @ WUV[rows].T  # [L, d_h]
-        s = (qc[:, i, :] @ Kc.T + qr[:, i, :] @ kr.T) * dims.scale  # [n, L]
+        s = (qc[:, i, :] @ Kc.T + qr[:, i, :] @ kr.T) * softmax_scale(dims)  # [n, L]
         s = np.where(mask, s, -np.inf)
         p, lse[:, i] = softmax_rows(s)
         o[:, i, :] = p @ V
@@ -153,7 +160,7 @@ def attend_absorbed(W: dict, dims, qc, qr, cache: np.ndarray, kv_len) -> tuple:
     """Absorbed form (App. C, associativity): q_hat_i = W_UK_i^T q^C_i in R^{d_c},
     s = scale * (q_hat_i . c_j + q^R_i . k_R,j), o_hat_i = sum_j p_ij c_j,
     o_i = W_UV_i o_hat_i.  Same outputs as attend_unabsorbed in exact arithmetic."""
-    ohat, lse = latent_attention(absorb_query(W, dims, qc, qr), cache, kv_len, dims.scale, dims.d_c)
+    ohat, lse = latent_attention(absorb_query(W, dims, qc, qr), cache, kv_len, softmax_scale(dims), dims.d_c)
     WUV = _w(W, "W_UV").reshape(dims.n_h, dims.d_h, dims.d_c)
     o = np.einsum("nic,idc->nid", ohat, WUV)
     return o, lse

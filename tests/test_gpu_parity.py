@@ -85,14 +85,51 @@ def test_decode_attention_core_matches_oracle(name, lens, splits, block):
     torch.cuda.synchronize()
     for b in range(B):
         cache = pool.read_entries(b, lens[b])
-        ref, ref_lse = O.latent_attention(q[b:b + 1], cache, [lens[b]], dims.scale, dims.d_c)
+        ref, ref_lse = O.latent_attention(q[b:b + 1], cache, [lens[b]], O.softmax_scale(dims), dims.d_c)
         check(ohat[b].float().cpu().numpy(), ref[0], dims.dtype, f"{name} o_hat b={b}")
         assert np.max(np.abs(lse[b].cpu().numpy() - ref_lse[0])) < 2e-3 * max(1.0, np.max(np.abs(ref_lse)))
 
 
+@pytest.mark.parametrize("name,lens,splits", [("v2", [300, 1000], 0), ("v2", [1000, 70], 3), ("v2lite", [130, 64], 0)])
+def test_decode_attention_core_sharp_softmax(name, lens, splits):
+    """Each head's query is a multiple (0.5 .. 24) of one cached entry of its sequence plus noise,
+    so the aligned key's logit reaches ~1e3 above the others: a softmax dominated by one entry,
+    which exercises the max subtraction and the deferred rescaling.  The pool around the
+    contexts holds NaN, so any read outside a context also fails the check."""
+    dims = SMALL[name][0]
+    layer = WL.DeviceLayer(dims, S.make_weights(dims))
+    B = len(lens)
+    rng = np.random.default_rng(11)
+    pool = WL.PagedPool(dims, lens, block_size=64)
+    for b, L in enumerate(lens):
+        e = S.to_dtype(rng.standard_normal((L, dims.entry)).astype(np.float32), dims.dtype)
+        pool.write_entries(b, WL.to_device(e, dims))
+    q = np.empty((B, dims.n_h, dims.entry), np.float32)
+    factors = np.geomspace(0.5, 24.0, dims.n_h)
+    for b, L in enumerate(lens):
+        cache = pool.read_entries(b, L)
+        pick = rng.integers(0, L, dims.n_h)
+        q[b] = factors[:, None] * cache[pick] + 0.1 * rng.standard_normal((dims.n_h, dims.entry))
+    q = S.to_dtype(q, dims.dtype)
+    kv = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    ws = WL.ws_tensor(M.workspace_size(layer.cdims, M.OP_DECODE, batch=B, max_ctx_len=max(lens) - 1,
+                                       num_splits=splits))
+    ohat = torch.empty((B, dims.n_h, dims.d_c), dtype=WL.torch_dtype(dims), device="cuda")
+    lse = torch.empty((B, dims.n_h), dtype=torch.float32, device="cuda")
+    M.decode_attention(layer.cdims, pool.ccache, WL.to_device(q, dims), kv, max(lens), ohat, ws, num_splits=splits,
+                       lse=lse)
+    torch.cuda.synchronize()
+    for b in range(B):
+        ref, ref_lse = O.latent_attention(q[b:b + 1], pool.read_entries(b, lens[b]), [lens[b]], O.softmax_scale(dims), dims.d_c)
+        assert np.max(ref_lse) > 500.0  # the sharpest heads really are sharp
+        check(ohat[b].float().cpu().numpy(), ref[0], dims.dtype, f"{name} sharp o_hat b={b}")
+        assert np.max(np.abs(lse[b].cpu().numpy() - ref_lse[0])) < 2e-3 * np.max(np.abs(ref_lse))
+
+
 # ----------------------------------------------------------------------------- full decode
-def _decode_case(name, lens, splits=0, block_size=64, std=0.02):
-    dims, recipe = SMALL[name]
+def _decode_case(name, lens, splits=0, block_size=64, std=0.02, recipe=None):
+    dims, default_recipe = SMALL[name]
+    recipe = recipe or default_recipe
     W = S.make_weights(dims, std=std)
     layer = WL.DeviceLayer(dims, W)
     B = len(lens)
@@ -112,8 +149,19 @@ def _decode_case(name, lens, splits=0, block_size=64, std=0.02):
 @pytest.mark.parametrize("name,lens,splits", [("tiny", [16, 3, 0, 40], 0), ("tiny", [70], 3),
                                               ("v2lite", [0, 100, 64, 257], 0), ("v2", [0, 63, 200], 0)])
 def test_decode_end_to_end_matches_oracle(name, lens, splits):
+    _end_to_end(name, lens, splits)
+
+
+def test_decode_end_to_end_sharp_weights():
+    """Tiny layer with weights N(0, 1/sqrt(fan_in)) and N(0,1) RMS-normalised hidden states:
+    logits of order one instead of ~0, so the softmax is far from uniform."""
+    _end_to_end("tiny", [16, 3, 0, 40], 0, std=0.125, recipe="rmsnorm")
+
+
+def _end_to_end(name, lens, splits, std=0.02, recipe=None):
     dims, W, recipe, layer, pool, h, u, oh = _decode_case(name, lens, splits,
-                                                          block_size=4 if name == "tiny" else 64)
+                                                          block_size=4 if name == "tiny" else 64, std=std,
+                                                          recipe=recipe)
     caches = [O.latent_entries(W, dims, S.hidden_history(dims, b, L, recipe), np.arange(L))
               for b, L in enumerate(lens)]
     ref = O.mla_decode(W, dims, h, caches)

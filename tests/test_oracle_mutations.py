@@ -1,7 +1,7 @@
 """Plants plausible mistakes in a copy of the oracle (on the CPU) and checks that the
 pins in test_oracle.py reject every one of them: a wrong sign, a dropped term, a
-transposed or swapped operand, a wrong head split, an off-by-one causal bound and a
-wrong RoPE frequency."""
+transposed or swapped operand, a wrong head split, an off-by-one causal bound, a wrong
+RoPE frequency or position, a wrong logit scale and a softmax without max subtraction."""
 import inspect
 import types
 
@@ -24,6 +24,9 @@ MUTATIONS = {
                           "o, lse = attend(W, dims, qc, qr, cache, np.maximum(idx, 1))"),
     "rope_on_wrong_position": ("kr = apply_rope(h @ _w(W, \"W_KR\").T, np.asarray(pos), dims.rope_base)",
                                "kr = apply_rope(h @ _w(W, \"W_KR\").T, np.asarray(pos) + 1, dims.rope_base)"),
+    "wrong_scale": ("return 1.0 / np.sqrt(np.float64(dims.d_h + dims.d_hr))",
+                    "return 1.0 / np.sqrt(np.float64(dims.d_h))"),
+    "no_max_subtraction": ("    e = np.exp(s - m)\n", "    e = np.exp(s - m * 0.0)\n    e = e * np.exp(-m)\n"),
     "value_from_rope_part": ("c, kr = cache[:, : dims.d_c], cache[:, dims.d_c:]\n    n = qc.shape[0]\n    L = cache.shape[0]\n    kv_len = np.asarray(kv_len)\n    mask = np.arange(L)[None, :] < kv_len[:, None]  # [n, L]",
                              "c, kr = cache[:, : dims.d_c], cache[:, dims.d_c:]\n    c = np.roll(c, 1, axis=1)\n    n = qc.shape[0]\n    L = cache.shape[0]\n    kv_len = np.asarray(kv_len)\n    mask = np.arange(L)[None, :] < kv_len[:, None]  # [n, L]"),
 }
@@ -46,6 +49,7 @@ def _pins_pass(mod, monkeypatch):
         T.test_reduces_to_textbook_mha()
         T.test_attention_matches_torch_sdpa_fp64()
         T.test_rope_complex_closed_form()
+        T.test_softmax_rows_sum_to_one_and_overflow()
     except AssertionError:
         return False
     return True
