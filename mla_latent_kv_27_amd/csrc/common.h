@@ -111,6 +111,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 // ---- direct-to-LDS copies and the waits that go with them
 typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) shortx4 lds_shortx4_t;
 
 // s_waitcnt immediates (gfx9 encoding): vmcnt in bits [3:0] and [15:14], expcnt [6:4],
 // lgkmcnt [11:8]; the unused counters are left at their maximum.

@@ -224,8 +224,6 @@ __shared__ __attribute__((aligned(1024))) char g_kv1[tiled::kBytes];
 __shared__ __attribute__((aligned(1024))) char g_kv2[tiled::kBytes];
 __shared__ __attribute__((aligned(1024))) char g_kv3[tiled::kBytes];
 
-typedef short shortx4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) shortx4 lds_shortx4_t;
 
 template <int BUF>
 __device__ __forceinline__ char* kv_buf() {
@@ -371,10 +369,11 @@ __device__ __forceinline__ void tiled_step(const TiledCtx& c, const Frag8<bf16> 
                                            int t_end, float scale_log2, int w, int lane, int tid) {
   using namespace tiled;
   const int ahead = min(t_end - 1 - t, kNBuf - 2);  // tiles issued after t and still in flight
-  if (ahead >= 2) {
+  static_assert(kNBuf == 2 || kNBuf == 4, "waits below");
+  if (kNBuf == 4 && ahead >= 2) {
     if (w < 4) MLA_TILE_BARRIER(waitcnt_vm(10));
     else MLA_TILE_BARRIER(waitcnt_vm(8));
-  } else if (ahead == 1) {
+  } else if (kNBuf == 4 && ahead == 1) {
     if (w < 4) MLA_TILE_BARRIER(waitcnt_vm(5));
     else MLA_TILE_BARRIER(waitcnt_vm(4));
   } else {
@@ -433,13 +432,13 @@ __global__ void __launch_bounds__(512)
   st.l_part = 0.f;
 
   if (t_begin < t_end) issue_tile<0>(c, t_begin, w, lane);
-  if (t_begin + 1 < t_end) issue_tile<1>(c, t_begin + 1, w, lane);
-  if (t_begin + 2 < t_end) issue_tile<2>(c, t_begin + 2, w, lane);
+  if (kNBuf > 2 && t_begin + 1 < t_end) issue_tile<1 % kNBuf>(c, t_begin + 1, w, lane);
+  if (kNBuf > 3 && t_begin + 2 < t_end) issue_tile<2 % kNBuf>(c, t_begin + 2, w, lane);
   for (int t = t_begin; t < t_end; t += kNBuf) {
     tiled_step<0>(c, q, st, t, t_end, p.scale_log2, w, lane, tid);
-    if (t + 1 < t_end) tiled_step<1>(c, q, st, t + 1, t_end, p.scale_log2, w, lane, tid);
-    if (t + 2 < t_end) tiled_step<2>(c, q, st, t + 2, t_end, p.scale_log2, w, lane, tid);
-    if (t + 3 < t_end) tiled_step<3>(c, q, st, t + 3, t_end, p.scale_log2, w, lane, tid);
+    if (t + 1 < t_end) tiled_step<1 % kNBuf>(c, q, st, t + 1, t_end, p.scale_log2, w, lane, tid);
+    if (kNBuf > 2 && t + 2 < t_end) tiled_step<2 % kNBuf>(c, q, st, t + 2, t_end, p.scale_log2, w, lane, tid);
+    if (kNBuf > 3 && t + 3 < t_end) tiled_step<3 % kNBuf>(c, q, st, t + 3, t_end, p.scale_log2, w, lane, tid);
   }
   // the four lane groups of a head hold partial sums over different tokens
   float l_run = wave_sum_xor(st.l_part, 16);

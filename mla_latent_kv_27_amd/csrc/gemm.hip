@@ -31,7 +31,7 @@ template <typename T>
 __device__ __forceinline__ void epi_store(const Epilogue& e, int z, int row, int col, float v) {
   int64_t rbase;
   if (e.block_table) {
-    const int sq = e.row_seq[row], ps = e.row_pos[row];
+    const int sq = e.row_seq ? e.row_seq[row] : row, ps = e.row_pos[row];
     const int64_t slot =
         (int64_t)e.block_table[(int64_t)sq * e.max_blocks + ps / e.block_size] * e.block_size +
         ps % e.block_size;
@@ -517,9 +517,13 @@ GemmPlan gemm_plan_skinny(int M, int N, int K, int batch, int cus) {
   pl.bn = skinny::kBN;
   const int64_t tiles = (int64_t)((N + pl.bn - 1) / pl.bn) * batch;
   const int ksteps = K / skinny::kKS;
-  // two workgroups fit per compute unit: split k so that the grid fills them once, each split
-  // streaming at least four steps
-  int splits = (int)std::max<int64_t>(1, 2LL * cus / tiles);
+  // A compute unit streams at most ~20 GB/s, about 1/256 of the chip's HBM rate (measured), so
+  // the grid should put one workgroup on as many compute units as possible without doubling up
+  // on some: floor(cus / tiles) splits; when that is 1 (tiles in (cus/2, cus]) two splits still
+  // beat leaving compute units idle (two workgroups fit per compute unit).  Each split streams at
+  // least four steps.
+  int splits = (int)std::max<int64_t>(1, cus / tiles);
+  if (splits == 1 && 2 * tiles <= 2LL * cus && tiles * 2 > cus) splits = 2;
   splits = std::min(splits, std::max(1, ksteps / 4));
   const int per = (ksteps + splits - 1) / splits;
   pl.splits = (ksteps + per - 1) / per;

@@ -14,8 +14,9 @@ inline size_t dsize(DType t) { return t == DType::BF16 ? 2 : 4; }
 // Where a GEMM result element (row, col) of batch z is stored, and what happens on the way.
 //   address = z*batch_stride + rowbase(row) + (col/group)*group_stride + group_off + col%group
 //   rowbase = row*ldc, or, when block_table is set, slot(row)*ldc with
-//             slot = block_table[row_seq[row]][row_pos[row]/block_size]*block_size
-//                    + row_pos[row] % block_size    (paged cache rows)
+//             slot = block_table[seq][row_pos[row]/block_size]*block_size
+//                    + row_pos[row] % block_size    (paged cache rows),
+//             seq = row_seq[row], or row itself when row_seq is null
 //   columns >= rope_col0 are rotated as interleaved pairs in groups of d_hr by the angles
 //   rope_tab[row][k] = (cos, sin) of pair k.
 struct Epilogue {

@@ -156,8 +156,6 @@ AttnWs carve_attn(Carve& cv, const mla_dims* d, int B, int max_kv_len, int split
 }
 
 struct DecodeWs {
-  int32_t* iota;
-  int32_t* dummy;
   float2* rope;
   void *cq, *qc, *qcat, *ohat, *o;
   AttnWs attn;
@@ -169,8 +167,6 @@ DecodeWs carve_decode(Carve& cv, const mla_dims* d, int B, int max_ctx_len, int 
   DecodeWs w;
   const size_t es = dsize(dt(d));
   w.gm = decode_gemms(d, B, cus);
-  w.iota = cv.take<int32_t>((size_t)B * 4);
-  w.dummy = cv.take<int32_t>((size_t)B * 4);
   w.rope = cv.take<float2>((size_t)B * (d->d_hr / 2) * sizeof(float2));
   w.cq = cv.take<char>((size_t)B * d->d_cq * es);
   w.qc = cv.take<char>((size_t)B * d->n_h * d->d_h * es);
@@ -399,7 +395,6 @@ int mla_decode(const mla_dims* d, const mla_weights* w, const mla_paged_cache* c
   const int B = batch, E = entry(d), qw = q_in(d);
 
   // positions of the new tokens are ctx_lens[b]; rows are sequences 0..B-1
-  MLA_HIP(prefill_rows(B, 1, ws.iota, ws.dummy, s));
   MLA_HIP(rope_table(ctx_lens, B, d->d_hr, d->rope_base, ws.rope, s));
   const void* qin = h;
   {  // [c^q | c^KV | k^R] = [W_DQ; W_DKV; W_KR] h: c^q to the workspace, the new token's cache
@@ -413,12 +408,12 @@ int mla_decode(const mla_dims* d, const mla_weights* w, const mla_paged_cache* c
       g.B2 = w->W_KR;
       g.epi = dense(ws.cq, d->d_cq);
       g.E0 = d->d_cq;
-      g.epi2 = cache_epilogue(d, c, ws.rope, ws.iota, ctx_lens);
+      g.epi2 = cache_epilogue(d, c, ws.rope, nullptr, ctx_lens);
       qin = ws.cq;
     } else {
       g.B0 = w->W_DKV; g.N0 = d->d_c;
       g.B1 = w->W_KR;
-      g.epi = cache_epilogue(d, c, ws.rope, ws.iota, ctx_lens);
+      g.epi = cache_epilogue(d, c, ws.rope, nullptr, ctx_lens);
     }
     MLA_HIP(gemm_run(t, g, ws.gm.kvq, ws.partial, s));
   }
