@@ -181,9 +181,10 @@ __global__ void __launch_bounds__(64 * NW) decode_attn_kernel(DecodeAttnParams p
     p.part_m[pi] = m_run;
     p.part_l[pi] = l_run;
   }
-  float* po = p.part_o + pi * DC;
+  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  float* po = reinterpret_cast<float*>(p.part_o) + pi * DC;
 #pragma unroll
-  for (int d = 0; d < Sh::DB; ++d) *reinterpret_cast<floatx4*>(po + d * 16 + 4 * g) = o[d];
+  for (int d = 0; d < Sh::DB; ++d) *reinterpret_cast<floatx4*>(po + d * 16 + 4 * g) = o[d] * inv;
 }
 
 // ----------------------------------------------------------------------------- tiled kernel
@@ -464,40 +465,68 @@ __global__ void __launch_bounds__(512)
     p.part_m[pi] = m_run;
     p.part_l[pi] = l_run;
   }
-  float* po = p.part_o + pi * kDC;
+  // the partition's normalised output O_s / l_s (a convex combination of latent values) in bf16:
+  // half the partial traffic of fp32 for one more rounding of 2^-9 relative
+  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  bf16* po = reinterpret_cast<bf16*>(p.part_o) + pi * kDC;
 #pragma unroll
-  for (int d = 0; d < 32; ++d) *reinterpret_cast<floatx4*>(po + d * 16 + 4 * g) = st.o[d];
+  for (int d = 0; d < 32; ++d) {
+    bf16x4 v;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = (bf16)(st.o[d][r] * inv);
+    *reinterpret_cast<bf16x4*>(po + d * 16 + 4 * g) = v;
+  }
 }
 
-// Log-sum-exp combination of the partitions: M = max_s m_s, w_s = 2^(m_s - M),
-// o_hat = sum_s w_s O_s / sum_s w_s l_s.  One workgroup per (sequence, head); each thread owns
-// 4 consecutive latent dims, loaded as float4.
-template <typename T, int DC>
-__global__ void __launch_bounds__(DC / 4 >= 64 ? DC / 4 : 64) decode_combine_kernel(DecodeAttnParams p) {
-  const int bh = blockIdx.x;  // b * n_h + head
+// Log-sum-exp combination of the partitions: M = max_s m_s, w_s = 2^(m_s - M) l_s,
+// o_hat = sum_s w_s o_s / sum_s w_s with o_s = O_s / l_s the partition's normalised output (PT:
+// fp32 or bf16).  A 256-thread workgroup combines four (sequence, head) rows; each thread owns
+// DC/64 consecutive latent dims, and the partitions' loads are issued four at a time before any
+// of them is used.
+template <typename T, typename PT, int DC>
+__global__ void __launch_bounds__(256) decode_combine_kernel(DecodeAttnParams p) {
+  constexpr int V = DC >= 64 ? DC / 64 : 1;  // dims per thread
+  const int bh = blockIdx.x * 4 + (threadIdx.x >> 6);  // b * n_h + head
+  if (bh >= p.B * p.n_h || V * (threadIdx.x & 63) >= DC) return;
   const int b = bh / p.n_h, head = bh % p.n_h;
   const int64_t base = (int64_t)b * p.splits * p.n_h + head;  // partition s at base + s * n_h
+  const int d = V * (threadIdx.x & 63);
   float M = -INFINITY;
   for (int s = 0; s < p.splits; ++s) M = fmaxf(M, p.part_m[base + (int64_t)s * p.n_h]);
   float L = 0.f;
-  for (int s = 0; s < p.splits; ++s) {
-    const float ms = p.part_m[base + (int64_t)s * p.n_h];
-    if (ms > -INFINITY) L += exp2f(ms - M) * p.part_l[base + (int64_t)s * p.n_h];
+  float acc[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) acc[i] = 0.f;
+  for (int s0 = 0; s0 < p.splits; s0 += 4) {
+    float ms[4], ls[4];
+    PT v[4][V];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      ms[u] = -INFINITY;
+      if (s0 + u < p.splits) {
+        const int64_t pi = base + (int64_t)(s0 + u) * p.n_h;
+        ms[u] = p.part_m[pi];
+        ls[u] = p.part_l[pi];
+        const PT* src = reinterpret_cast<const PT*>(p.part_o) + pi * DC + d;
+#pragma unroll
+        for (int i = 0; i < V; ++i) v[u][i] = src[i];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (ms[u] > -INFINITY) {
+        const float ws = exp2f(ms[u] - M) * ls[u];
+        L += ws;
+#pragma unroll
+        for (int i = 0; i < V; ++i) acc[i] += ws * to_f32(v[u][i]);
+      }
+    }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  const int d = 4 * threadIdx.x;
-  if (d < DC) {
-    floatx4 acc = {0, 0, 0, 0};
-    for (int s = 0; s < p.splits; ++s) {
-      const int64_t pi = base + (int64_t)s * p.n_h;
-      const float ms = p.part_m[pi];
-      if (ms > -INFINITY) acc += exp2f(ms - M) * *reinterpret_cast<const floatx4*>(p.part_o + pi * DC + d);
-    }
-    T* out = reinterpret_cast<T*>(p.o_hat) + (int64_t)bh * DC + d;
+  T* out = reinterpret_cast<T*>(p.o_hat) + (int64_t)bh * DC + d;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) out[r] = from_f32<T>(acc[r] * inv);
-  }
-  if (p.lse && threadIdx.x == 0) p.lse[bh] = (M + log2f(L)) * 0.69314718055994531f;
+  for (int i = 0; i < V; ++i) out[i] = from_f32<T>(acc[i] * inv);
+  if (p.lse && d == 0) p.lse[bh] = (M + log2f(L)) * 0.69314718055994531f;
 }
 
 // ----------------------------------------------------------------------------- host side
@@ -526,7 +555,7 @@ hipError_t launch(const DecodeAttnParams& p, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<T, DC>), dim3(p.B * p.n_h), dim3(DC / 4 >= 64 ? DC / 4 : 64), 0, s, p);
+  hipLaunchKernelGGL((decode_combine_kernel<T, float, DC>), dim3((p.B * p.n_h + 3) / 4), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 }  // namespace
@@ -541,7 +570,7 @@ hipError_t decode_attention(DType t, const DecodeAttnParams& p, hipStream_t s) {
                        p.block_table);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
-    hipLaunchKernelGGL((decode_combine_kernel<bf16, 512>), dim3(p.B * p.n_h), dim3(128), 0, s, p);  // 4 dims/thread
+    hipLaunchKernelGGL((decode_combine_kernel<bf16, bf16, 512>), dim3((p.B * p.n_h + 3) / 4), dim3(256), 0, s, p);
     return hipGetLastError();
   }
   if (p.d_c == 512 && p.d_hr == 64)

@@ -95,7 +95,7 @@ struct DecodeAttnParams {
   int tokens_per_split;   // a multiple of 64
   float* part_m;          // [B][splits][n_h]   (log2 domain running max)
   float* part_l;          // [B][splits][n_h]
-  float* part_o;          // [B][splits][n_h][d_c]
+  void* part_o;           // [B][splits][n_h][d_c]: O_s / l_s (fp32, or bf16 for the tiled kernel)
   void* o_hat;            // [B][n_h][d_c] output (element type)
   float* lse;             // optional [B][n_h], natural log
 };

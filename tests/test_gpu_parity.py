@@ -254,8 +254,10 @@ def test_split_count_invariance_and_page_permutation_invariance():
         return o.float().cpu().numpy(), lse.cpu().numpy()
 
     # probabilities enter the PV product rounded to bf16 relative to each partition's running
-    # max, so two split counts differ by at most ~2^-8 of the largest latent value, plus a
-    # rounding step of o_hat itself
+    # max (within 2^-9 of the largest latent value per run), and with more than one partition
+    # each partition's normalised output, a convex combination of latent values, is stored in
+    # bf16 (another 2^-9 of the largest latent value); o_hat itself is rounded to bf16.  Two
+    # split counts therefore differ by at most 2 * (2^-9 + 2^-9) * cmax + 2 * 2^-9 * |o_hat|.
     cmax = max(float(np.max(np.abs(pool.read_entries(b, L)[:, :dims.d_c]))) for b, L in enumerate(lens))
     o1, l1 = core(1)
     for sp in (2, 7, 0):
@@ -263,7 +265,7 @@ def test_split_count_invariance_and_page_permutation_invariance():
         # the normaliser sums the rounded probabilities: each within 2^-9 relative, so the two
         # log-sum-exps differ by at most 2 * 2^-9 in natural-log units
         assert np.max(np.abs(l2 - l1)) <= 2.0 ** -8, sp
-        assert np.all(np.abs(o2 - o1) <= 2.0 ** -8 * cmax + 2.0 ** -7 * np.abs(o1)), sp
+        assert np.all(np.abs(o2 - o1) <= 2.0 ** -7 * cmax + 2.0 ** -7 * np.abs(o1)), sp
         check(_decode_u(layer, pool.clone(), h, lens, sp), base, dims.dtype, f"u with {sp} splits")
     pool2 = WL.PagedPool(dims, [L + 1 for L in lens], seed=99)
     WL.build_context(layer, pool2, lens, recipe)
