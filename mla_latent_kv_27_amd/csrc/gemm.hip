@@ -61,6 +61,34 @@ __device__ __forceinline__ void out_elem(const GemmParams& p, int z, int row, in
   }
 }
 
+// Four consecutive columns col .. col+3 (col % 4 == 0) of one row through the epilogue; the
+// values are already rotated.  One 8- or 16-byte store when the four land next to each other
+// (no column group boundary inside), else element by element.
+template <typename T>
+__device__ __forceinline__ void out_quad(const GemmParams& p, int z, int row, int col, const float (&v)[4]) {
+  const bool hi = col >= p.E0;
+  const Epilogue& e = hi ? p.epi2 : p.epi;
+  const int c = hi ? col - p.E0 : col;
+  if (c % e.group + 3 < e.group && !e.c_f32 && !e.C2 && sizeof(T) == 2 &&
+      (reinterpret_cast<uintptr_t>(e.C) & 7) == 0) {
+    int64_t rbase;
+    if (e.block_table) {
+      const int sq = e.row_seq ? e.row_seq[row] : row, ps = e.row_pos[row];
+      rbase = ((int64_t)e.block_table[(int64_t)sq * e.max_blocks + ps / e.block_size] * e.block_size +
+               ps % e.block_size) * e.ldc;
+    } else {
+      rbase = (int64_t)row * e.ldc;
+    }
+    const int64_t idx = (int64_t)z * e.batch_stride + rbase + (int64_t)(c / e.group) * e.group_stride + e.group_off +
+                        c % e.group;
+    bf16x4 q = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+    *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(e.C) + idx) = q;
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) epi_store<T>(e, z, row, c + i, v[i]);
+}
+
 // Whether any column of [c0, c1) is rotated (so that partners must be exchanged).
 __device__ __forceinline__ bool cols_have_rope(const GemmParams& p, int c0, int c1) {
   const int64_t lo_end = std::min<int64_t>(c1, p.E0);
@@ -177,7 +205,7 @@ __global__ void __launch_bounds__(64 * WM * WN)
 // Sums the split-K partials [splits][batch][M][N] and runs the epilogue; a thread owns an even
 // number of consecutive columns so that RoPE pairs stay together.
 template <typename T, int V>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(128)
     splitk_reduce_kernel(GemmParams p, int splits, const float* __restrict__ partial) {
   // one thread per V consecutive columns of one row; the splits are summed in order, eight
   // partial loads in flight at a time
@@ -201,10 +229,26 @@ __global__ void __launch_bounds__(256)
       for (int i = 0; i < 8; ++i) acc += v[i];
     }
     for (; s < splits; ++s) acc += *reinterpret_cast<const vec_t*>(src + s * stride);
+    if constexpr (V == 4) {
+      float v[4];
 #pragma unroll
-    for (int i = 0; i < V; i += 2) {
-      out_elem<T>(p, z, row, col + i, acc[i], acc[i + 1]);
-      out_elem<T>(p, z, row, col + i + 1, acc[i + 1], acc[i]);
+      for (int i = 0; i < 4; i += 2) {
+        const bool hi = col + i >= p.E0;
+        const Epilogue& e = hi ? p.epi2 : p.epi;
+        const int c = hi ? col + i - p.E0 : col + i;
+        float v0 = acc[i], v1 = acc[i + 1];
+        rope_pair(e, row, c, v0, acc[i + 1]);
+        rope_pair(e, row, c + 1, v1, acc[i]);
+        v[i] = v0;
+        v[i + 1] = v1;
+      }
+      out_quad<T>(p, z, row, col, v);
+    } else {
+#pragma unroll
+      for (int i = 0; i < V; i += 2) {
+        out_elem<T>(p, z, row, col + i, acc[i], acc[i + 1]);
+        out_elem<T>(p, z, row, col + i + 1, acc[i + 1], acc[i]);
+      }
     }
   }
 }
@@ -492,14 +536,15 @@ hipError_t run_t(const GemmParams& p, const GemmPlan& plan, float* partial, hipS
     default: err = launch_cfg<T, 2>(p, plan, partial, s); break;
   }
   if (err != hipSuccess || plan.splits == 1) return err;
-  if (p.N % 4 == 0) {
+  // 128-thread blocks so that small outputs still spread over the compute units
+  if (p.N % 4 == 0 && p.E0 % 4 == 0) {
     const int64_t groups = (int64_t)p.batch * p.M * (p.N / 4);
-    const int blocks = (int)std::min<int64_t>((groups + 255) / 256, 8192);
-    hipLaunchKernelGGL((splitk_reduce_kernel<T, 4>), dim3(blocks), dim3(256), 0, s, p, plan.splits, partial);
+    const int blocks = (int)std::min<int64_t>((groups + 127) / 128, 16384);
+    hipLaunchKernelGGL((splitk_reduce_kernel<T, 4>), dim3(blocks), dim3(128), 0, s, p, plan.splits, partial);
   } else {
     const int64_t groups = (int64_t)p.batch * p.M * (p.N / 2);
-    const int blocks = (int)std::min<int64_t>((groups + 255) / 256, 8192);
-    hipLaunchKernelGGL((splitk_reduce_kernel<T, 2>), dim3(blocks), dim3(256), 0, s, p, plan.splits, partial);
+    const int blocks = (int)std::min<int64_t>((groups + 127) / 128, 16384);
+    hipLaunchKernelGGL((splitk_reduce_kernel<T, 2>), dim3(blocks), dim3(128), 0, s, p, plan.splits, partial);
   }
   return hipGetLastError();
 }
