@@ -273,6 +273,9 @@ __device__ __forceinline__ void tiled_compute(const Frag8<bf16> (&q)[18], TiledS
                                               float scale_log2, int lane, const TiledCtx& c, bool issue_next, int w) {
   using namespace tiled;
   const char* buf = kv_buf<BUF>();
+  // refill the buffer of tile t-1 (free since the barrier) with tile t+3 first, so that all
+  // waves' shares of that tile leave at about the same time
+  if (issue_next) issue_tile<(BUF + kNBuf - 1) % kNBuf>(c, t + kNBuf - 1, w, lane);
   // the lane's LDS offsets are recomputed in every step (a few integer ops) rather than kept live
   // for all four ring buffers across the loop
   asm volatile("" : "+v"(lane));
@@ -303,7 +306,6 @@ __device__ __forceinline__ void tiled_compute(const Frag8<bf16> (&q)[18], TiledS
       sc[1] = mma16(a[kc % 3][1], q[kc], sc[1]);
     }
   }
-  if (issue_next) issue_tile<(BUF + kNBuf - 1) % kNBuf>(c, t + kNBuf - 1, w, lane);
   // ---- lazy online softmax
   float lmax = -INFINITY;
   const bool full = (t + 1) * kT <= kv_len;
@@ -387,7 +389,7 @@ __device__ __forceinline__ void tiled_step(const TiledCtx& c, const Frag8<bf16> 
     MLA_TILE_BARRIER(kWaitLgkm0);
   }
   // multiply tile t; the copies of tile t+3 into the buffer of tile t-1 (free since the barrier)
-  // are issued inside, after the S^T products, which overlaps them best with the arithmetic
+  // are issued first thing inside
   tiled_compute<BUF>(q, st, t, c.kv_len, scale_log2, lane, c, t + kNBuf - 1 < t_end, w);
 }
 
