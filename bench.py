@@ -132,6 +132,69 @@ def cpu_baseline(dims, W_np, lens, recipe, budget_s):
                       f"cached tokens), un-absorbed fp64 numpy, {spent:.1f} s; cache entries precomputed untimed"}
 
 
+def prefill_flops(dims, T, B):
+    """Causal attention over key <= query, un-absorbed (d_qk = d_h + d_hr, d_v = d_h), plus every
+    weight applied once per token."""
+    attn = B * 2 * dims.n_h * (dims.d_h + dims.d_hr + dims.d_h) * T * (T + 1) // 2
+    return attn, 2 * B * T * dims.param_count()
+
+
+def prefill_bench(args, w):
+    """A step is one mla_prefill of the workload's sequences (projections, cache writer, causal
+    attention, W_O); MFMA-bound, reported against the dense bf16 peak."""
+    import numpy as np
+    import torch
+    import mla_synth as S
+    import mla_latent_kv_27_amd as M
+    from mla_latent_kv_27_amd import workload as WL
+
+    dims, B, T = w.dims, w.batch, w.tokens
+    torch.cuda.set_device(0)
+    W_np = S.make_weights(dims, std=w.weight_std)
+    layer = WL.DeviceLayer(dims, W_np)
+    pool = WL.PagedPool(dims, [T] * B, block_size=w.block_size)
+    h_np = np.stack(S.hidden_histories(dims, [T] * B, w.hidden))
+    h = WL.to_device(h_np.reshape(B, T, dims.d_model), dims)
+    u = torch.empty((B, T, dims.d_model), dtype=WL.torch_dtype(dims), device="cuda")
+    ws = WL.prefill_workspace(layer, B, T)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        M.prefill(layer.cdims, layer.cweights, pool.ccache, h, u, ws, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        M.prefill(layer.cdims, layer.cweights, pool.ccache, h, u, ws, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    attn_f, proj_f = prefill_flops(dims, T, B)
+    tflops = (attn_f + proj_f) / (ms / 1e3) / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle.mla_oracle as O
+        n = min(T, 256)
+        t0 = time.perf_counter()
+        O.mla_prefill(W_np, dims, h_np[0, :n])
+        dt = time.perf_counter() - t0
+        cpu = {"value": n / dt, "unit": "tokens/s", "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+               "sample": f"the first {n} tokens of sequence 0 (causal, un-absorbed fp64 numpy), {dt:.1f} s; "
+                         f"longer prefixes cost more per token"}
+    rec = {"metric": "MLA prefill tokens/s (causal, writes the latent cache), DeepSeek-V2 shape, 1 GPU",
+           "value": round(B * T / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": dims.dtype,
+           "data": "synthetic (seeded weights N(0,0.02), RMS-normalised N(0,1) hidden states, random page order)",
+           "config": {"workload": w.name, "batch": B, "tokens": T, "d_model": dims.d_model, "n_h": dims.n_h,
+                      "d_h": dims.d_h, "d_c": dims.d_c, "d_cq": dims.d_cq, "d_hr": dims.d_hr},
+           "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                        "kernel": "whole mla_prefill call (projections, cache writer, causal attention, W_O)",
+                        "attention_flops": attn_f, "projection_flops": proj_f},
+           "cpu_baseline": cpu}
+    print(json.dumps(rec))
+
+
 def main():
     args = parse()
     if args.only == "copy":
@@ -148,9 +211,9 @@ def main():
     from mla_latent_kv_27_amd import workload as WL
 
     w = S.WORKLOADS[args.workload]
-    if w.kind != "decode":
-        print("bench.py times the decode hot path; choose a decode workload", file=sys.stderr)
-        sys.exit(2)
+    if w.kind == "prefill":
+        prefill_bench(args, w)
+        return
     dims = w.dims
     torch.cuda.set_device(0)
     lens = S.context_lengths(w)

@@ -174,6 +174,246 @@ __global__ void __launch_bounds__(256) prefill_attn_kernel(PrefillAttnParams p) 
     }
 }
 
+// ----------------------------------------------------------------------------- pipelined kernel
+// The DeepSeek-V2 case (bf16, d_h = 128, d_hr = 64).  Same arithmetic as above, with the K and V^T
+// tiles streamed by direct global->LDS copies into a ring of three 40 KiB stages (two tiles in
+// flight while one is multiplied), one barrier per tile, and eight waves (256 queries of one head)
+// sharing every tile.  LDS rows swizzle 16-byte chunks (slot = chunk ^ (row & 7)) so that the
+// fragment reads of 32 rows spread over the banks.  Workgroups of the same head are placed on
+// the same XCD so that their tiles come from its L2.
+namespace pf2 {
+constexpr int kWaves = 8;
+constexpr int kQ = 32 * kWaves;      // queries per workgroup
+constexpr int kKV = 64;              // keys per tile
+constexpr int kDH = 128, kDR = 64, kDQ = kDH + kDR;
+constexpr int kKRow = kDQ * 2;       // 384 bytes per key row (24 chunks)
+constexpr int kKBytes = kKV * kKRow;  // 24 KiB
+constexpr int kVRow = kKV * 2;      // 128 bytes per value row (one dim, 64 keys)
+constexpr int kVBytes = kDH * kVRow;   // 16 KiB
+constexpr int kStage = kKBytes + kVBytes;
+constexpr int kNS = 3;
+constexpr int kKCopies = kKBytes / 1024 / kWaves;  // 3 per wave
+constexpr int kVCopies = kVBytes / 1024 / kWaves;  // 2 per wave
+constexpr int kCopies = kKCopies + kVCopies;
+}  // namespace pf2
+
+__shared__ __attribute__((aligned(1024))) char g_pf_s0[pf2::kStage];
+__shared__ __attribute__((aligned(1024))) char g_pf_s1[pf2::kStage];
+__shared__ __attribute__((aligned(1024))) char g_pf_s2[pf2::kStage];
+
+template <int ST>
+__device__ __forceinline__ char* pf_stage() { return ST == 0 ? g_pf_s0 : (ST == 1 ? g_pf_s1 : g_pf_s2); }
+
+struct Pf2Ctx {
+  const bf16* k;    // key rows of this (sequence, head): [T][128]
+  const bf16* kr;   // rope key rows of this sequence, ld_kr apart
+  int64_t ld_kr;
+  const bf16* vt;   // V^T rows of this (sequence, head): row d at vt + d * vrow
+  int64_t vrow;
+  int T;
+};
+
+// Tile kt into stage ST: key rows (clamped to T-1, masked later) and V^T rows (padded to whole
+// tiles, so always in bounds).
+template <int ST>
+__device__ __forceinline__ void pf2_issue(const Pf2Ctx& c, int kt, int w, int lane) {
+  using namespace pf2;
+  char* st = pf_stage<ST>();
+  const int j0 = kt * kKV;
+#pragma unroll
+  for (int i = 0; i < kKCopies; ++i) {
+    const int P = i * kWaves + w;
+    const int C = P * 64 + lane;  // chunk slot of the tile
+    const int r = C / 24, sl = C % 24;
+    const int ch = sl ^ (r & 7);
+    const int j = min(j0 + r, c.T - 1);
+    const bf16* src = ch < 16 ? c.k + (int64_t)j * kDH + ch * 8 : c.kr + (int64_t)j * c.ld_kr + (ch - 16) * 8;
+    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(st + P * 1024), 16, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < kVCopies; ++i) {
+    const int P = i * kWaves + w;
+    const int C = P * 64 + lane;
+    const int d = C / 8, sl = C % 8;
+    const int ch = sl ^ (d & 7);
+    const bf16* src = c.vt + (int64_t)d * c.vrow + j0 + ch * 8;
+    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(st + kKBytes + P * 1024), 16, 0, 0);
+  }
+}
+
+struct Pf2State {
+  floatx16 o[4];  // O^T: 4 blocks of 32 dims; lane: query l32, dims 32 d + 8 (r/4) + 4g + r%4
+  float m_run, l_run;
+};
+
+template <int ST>
+__device__ __forceinline__ void pf2_compute(const Frag8<bf16> (&q)[12], Pf2State& s, int kt, int qi, int T,
+                                            float scale_log2, int lane) {
+  using namespace pf2;
+  const char* st = pf_stage<ST>();
+  asm volatile("" : "+v"(lane));
+  const int g = lane >> 5, l32 = lane & 31, x = l32 & 7;
+  const int j0 = kt * kKV;
+  floatx16 sc[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sc[kb][r] = 0.f;
+    const char* krow = st + (kb * 32 + l32) * kKRow;
+#pragma unroll
+    for (int ks = 0; ks < 12; ++ks) {
+      Frag8<bf16> a;
+      a.v = *reinterpret_cast<const bf16x8*>(krow + (((2 * ks + g) ^ x) * 16));
+      sc[kb] = mma32(a, q[ks], sc[kb]);
+    }
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int j = j0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+      const float v = (j <= qi && j < T) ? sc[kb][r] * scale_log2 : -INFINITY;
+      sc[kb][r] = v;
+      mx = fmaxf(mx, v);
+    }
+  mx = wave_max_xor(mx, 32);
+  const float m_new = fmaxf(s.m_run, mx);
+  const float m_use = m_new == -INFINITY ? 0.f : m_new;
+  const float alpha = exp2f(s.m_run - m_use);
+  float sum = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float e = (float)(bf16)exp2f(sc[kb][r] - m_use);  // as rounded for PV
+      sc[kb][r] = e;
+      sum += e;
+    }
+  sum = wave_sum_xor(sum, 32);
+  s.l_run = s.l_run * alpha + sum;
+  s.m_run = m_new;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) s.o[d] *= alpha;
+  // O^T += V^T P^T: lane (dim 32 d + l32, group g) reads keys 16 (2kb + half) + 4g + 0..3 and
+  // + 8 + 0..3, i.e. chunk 4kb + 2half (+1) of its row, byte 8g
+  const char* vrow = st + kKBytes + l32 * kVRow + 8 * g;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      Frag8<bf16> pfr;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pfr.v[e] = (bf16)sc[kb][8 * half + e];
+      const int c0 = 4 * kb + 2 * half;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const char* vr = vrow + d * 32 * kVRow;
+        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr + ((c0 ^ x) * 16));
+        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vr + (((c0 + 1) ^ x) * 16));
+        Frag8<bf16> a;
+        a.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        s.o[d] = mma32(a, pfr, s.o[d]);
+      }
+    }
+}
+
+// Tile kt of the ring (stage ST = kt % 3): wait for it (tile kt+1 may be in flight), refill the
+// stage of tile kt-1 with tile kt+2, zero the value columns past the end of the sequence, and
+// multiply unless every query of this wave precedes the tile.
+template <int ST>
+__device__ __forceinline__ void pf2_step(const Pf2Ctx& c, const Frag8<bf16> (&q)[12], Pf2State& s, int kt,
+                                         int kt_end, int qi_last, int qi, float scale_log2, int w, int lane, int tid) {
+  using namespace pf2;
+  if (kt + 1 < kt_end) MLA_TILE_BARRIER(waitcnt_vm(kCopies));
+  else MLA_TILE_BARRIER(waitcnt_vm(0));
+  if (kt + 2 < kt_end) pf2_issue<(ST + 2) % kNS>(c, kt + 2, w, lane);
+  const int valid = c.T - kt * kKV;
+  if (valid < kKV) {  // uniform: V^T columns of keys >= T (padding, uninitialised) -> 0
+    char* v = pf_stage<ST>() + kKBytes;
+    for (int i = tid; i < kDH * (kKV - valid); i += 64 * kWaves) {
+      const int d = i / (kKV - valid), key = valid + i % (kKV - valid);
+      const int slot = (key >> 3) ^ (d & 7);
+      *reinterpret_cast<bf16*>(v + d * kVRow + slot * 16 + (key & 7) * 2) = (bf16)0.f;
+    }
+    MLA_TILE_BARRIER(kWaitLgkm0);
+  }
+  if (kt * kKV <= qi_last) pf2_compute<ST>(q, s, kt, qi, c.T, scale_log2, lane);
+}
+
+__global__ void __launch_bounds__(512)
+    prefill_attn_pipelined_kernel(PrefillAttnParams p, int nqt, int units) {
+  using namespace pf2;
+  // block id -> (unit = sequence * n_h + head, query tile): the query tiles of a unit share an
+  // XCD (ids are dealt to the 8 XCDs round robin), longest rows first
+  const int xcd = blockIdx.x % 8, r = blockIdx.x / 8;
+  const int unit = (r / nqt) * 8 + xcd;
+  if (unit >= units) return;
+  const int qt = nqt - 1 - r % nqt;
+  const int sq = unit / p.n_h, head = unit % p.n_h;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, ql = lane & 31;
+  const int qi = qt * kQ + w * 32 + ql;
+  const int qi_last = min(qt * kQ + w * 32 + 31, p.T - 1);  // this wave's last query
+  const int64_t MT = (int64_t)p.S * p.T;
+  const int Tp = (p.T + kKV - 1) / kKV * kKV;
+
+  Pf2Ctx c;
+  c.k = reinterpret_cast<const bf16*>(p.k) + ((int64_t)head * MT + (int64_t)sq * p.T) * kDH;
+  c.kr = reinterpret_cast<const bf16*>(p.kr) + (int64_t)sq * p.T * p.ld_kr + p.kr_off;
+  c.ld_kr = p.ld_kr;
+  c.vt = reinterpret_cast<const bf16*>(p.vt) + ((int64_t)head * kDH * p.S + sq) * Tp;
+  c.vrow = (int64_t)p.S * Tp;
+  c.T = p.T;
+
+  Frag8<bf16> q[12];
+  {
+    const bf16* qrow = reinterpret_cast<const bf16*>(p.q) + (((int64_t)sq * p.T + min(qi, p.T - 1)) * p.n_h + head) * kDQ;
+#pragma unroll
+    for (int ks = 0; ks < 12; ++ks) {
+      if (qi < p.T) load8(q[ks], qrow + ks * 16 + 8 * g);
+      else zero8(q[ks]);
+    }
+  }
+  Pf2State s;
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) s.o[d][rr] = 0.f;
+  s.m_run = -INFINITY;
+  s.l_run = 0.f;
+
+  const int kt_end = min((p.T + kKV - 1) / kKV, ((qt + 1) * kQ + kKV - 1) / kKV);
+  if (kt_end > 0) pf2_issue<0>(c, 0, w, lane);
+  if (kt_end > 1) pf2_issue<1>(c, 1, w, lane);
+  for (int kt = 0; kt < kt_end; kt += kNS) {
+    pf2_step<0>(c, q, s, kt, kt_end, qi_last, qi, p.scale_log2, w, lane, tid);
+    if (kt + 1 < kt_end) pf2_step<1>(c, q, s, kt + 1, kt_end, qi_last, qi, p.scale_log2, w, lane, tid);
+    if (kt + 2 < kt_end) pf2_step<2>(c, q, s, kt + 2, kt_end, qi_last, qi, p.scale_log2, w, lane, tid);
+  }
+  MLA_WAVE_WAIT(waitcnt_vm(0));
+
+  if (qi >= p.T) return;
+  const float inv = s.l_run > 0.f ? 1.f / s.l_run : 0.f;
+  const int64_t orow = (((int64_t)sq * p.T + qi) * p.n_h + head) * kDH;
+  bf16* out = reinterpret_cast<bf16*>(p.o) + orow;
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+#pragma unroll
+    for (int rr = 0; rr < 16; rr += 4) {
+      const int dim = d * 32 + 8 * (rr >> 2) + 4 * g;
+      bf16x4 v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float f = s.o[d][rr + i] * inv;
+        v[i] = (bf16)f;
+        if (p.o_f32) p.o_f32[orow + dim + i] = f;
+      }
+      *reinterpret_cast<bf16x4*>(out + dim) = v;
+    }
+}
+
 bool prefill_supported(int d_h, int d_hr) { return (d_h == 128 && d_hr == 64) || (d_h == 16 && d_hr == 8) || (d_h == 32 && d_hr == 8); }
 
 namespace {
@@ -188,6 +428,15 @@ hipError_t launch(const PrefillAttnParams& p, hipStream_t s) {
 }  // namespace
 
 hipError_t prefill_attention(DType t, const PrefillAttnParams& p, hipStream_t s) {
+  if (t == DType::BF16 && p.d_h == 128 && p.d_hr == 64) {
+    const int nqt = (p.T + pf2::kQ - 1) / pf2::kQ;
+    const int units = p.S * p.n_h;
+    const int64_t blocks = (int64_t)(units + 7) / 8 * 8 * nqt;
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(prefill_attn_pipelined_kernel, dim3((unsigned)blocks), dim3(64 * pf2::kWaves), 0, s, p, nqt,
+                       units);
+    return hipGetLastError();
+  }
   if (p.d_h == 128 && p.d_hr == 64)
     return t == DType::BF16 ? launch<bf16, 128, 64>(p, s) : launch<float, 128, 64>(p, s);
   if (p.d_h == 16 && p.d_hr == 8)
