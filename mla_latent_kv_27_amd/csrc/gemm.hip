@@ -500,6 +500,234 @@ __global__ void __launch_bounds__(256)
     }
 }
 
+// ----------------------------------------------------------------------------- large-M kernel
+// Prefill-sized bf16 "NT" products (M in the thousands).  A workgroup of eight waves computes a
+// 256 x 256 tile, each wave 128 x 64 (4 x 2 blocks of 32x32x16 MFMA).  Both operands arrive by
+// direct global->LDS copies into two 64-k stages (the next stage's copies in flight while the
+// current one is multiplied), one barrier per stage.  LDS rows are 128 bytes (eight 16-byte
+// chunks); chunk c of row r sits in slot c ^ ((r >> 1) & 7), which keeps the 16-byte fragment
+// reads free of bank conflicts.
+namespace big {
+constexpr int kTileM = 256, kTileN = 256, kStepK = 64;
+constexpr int kWaves = 8;                     // 2 (rows) x 4 (columns)
+constexpr int kFM = 4, kFN = 2;               // 32-blocks per wave
+constexpr int kRowB = kStepK * 2;             // bytes per LDS row
+constexpr int kOp = kTileM * kRowB;           // 32 KiB per operand per stage
+constexpr int kCopies = kOp / 1024 / kWaves;  // 4 copy instructions per operand per wave
+constexpr int kGroupM = 4;                    // tile rows per group of the tile order
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+}  // namespace big
+
+__shared__ __attribute__((aligned(1024))) char g_big_s0[2 * big::kOp];
+__shared__ __attribute__((aligned(1024))) char g_big_s1[2 * big::kOp];
+template <int ST>
+__device__ __forceinline__ char* big_stage() { return ST == 0 ? g_big_s0 : g_big_s1; }
+
+struct BigCtx {
+  const bf16* a[big::kCopies];  // this lane's source of A copy i at k = 0
+  const bf16* b[big::kCopies];
+  int w, lane;
+};
+
+template <int ST>
+__device__ __forceinline__ void big_issue(const BigCtx& x, int step) {
+  using namespace big;
+  char* st = big_stage<ST>();
+  const int k = step * kStepK;
+#pragma unroll
+  for (int i = 0; i < kCopies; ++i) {
+    const int P = i * kWaves + x.w;
+    __builtin_amdgcn_global_load_lds((const void*)(x.a[i] + k), (lds_void_t*)(st + P * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(x.b[i] + k), (lds_void_t*)(st + kOp + P * 1024), 16, 0, 0);
+  }
+}
+
+// Fragments of two 16-k sub-steps (2h, 2h + 1) of stage ST.  The reads and their wait are one asm
+// block: with the other stage's copies in flight the compiler would otherwise wait for all of
+// them before the first LDS read.
+struct BigHalf {
+  bf16x8 a[2][big::kFM], b[2][big::kFN];
+};
+template <int ST>
+__device__ __forceinline__ void big_read(const BigCtx& x, int h, BigHalf& f) {
+  using namespace big;
+  int lane = x.lane;
+  asm volatile("" : "+v"(lane));
+  const int g = lane >> 5, l32 = lane & 31, sw = swz(l32);
+  const int wm = x.w >> 2, wn = x.w & 3;
+  const uint32_t st = lds_addr(big_stage<ST>());
+  const uint32_t s0 = ((4 * h + g) ^ sw) * 16, s1 = ((4 * h + 2 + g) ^ sw) * 16;
+  const uint32_t pa = st + (wm * 128 + l32) * kRowB, pb = st + kOp + (wn * 64 + l32) * kRowB;
+  asm volatile(
+      "ds_read_b128 %0, %12\n\tds_read_b128 %1, %12 offset:4096\n\t"
+      "ds_read_b128 %2, %12 offset:8192\n\tds_read_b128 %3, %12 offset:12288\n\t"
+      "ds_read_b128 %4, %13\n\tds_read_b128 %5, %13 offset:4096\n\t"
+      "ds_read_b128 %6, %13 offset:8192\n\tds_read_b128 %7, %13 offset:12288\n\t"
+      "ds_read_b128 %8, %14\n\tds_read_b128 %9, %14 offset:4096\n\t"
+      "ds_read_b128 %10, %15\n\tds_read_b128 %11, %15 offset:4096\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(f.a[0][0]), "=&v"(f.a[0][1]), "=&v"(f.a[0][2]), "=&v"(f.a[0][3]), "=&v"(f.a[1][0]),
+        "=&v"(f.a[1][1]), "=&v"(f.a[1][2]), "=&v"(f.a[1][3]), "=&v"(f.b[0][0]), "=&v"(f.b[0][1]),
+        "=&v"(f.b[1][0]), "=&v"(f.b[1][1])
+      : "v"(pa + s0), "v"(pa + s1), "v"(pb + s0), "v"(pb + s1));
+}
+__device__ __forceinline__ void big_mfma(const BigHalf& f, floatx16 (&acc)[big::kFM][big::kFN]) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int fm = 0; fm < big::kFM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < big::kFN; ++fn) {
+        Frag8<bf16> a, b;
+        a.v = f.a[t][fm];
+        b.v = f.b[t][fn];
+        acc[fm][fn] = mma32(a, b, acc[fm][fn]);
+      }
+}
+
+// One 64-k stage: half the stage's fragments are read, multiplied, then the other half.
+template <int ST>
+__device__ __forceinline__ void big_step(const BigCtx& x, int s, int nsteps, floatx16 (&acc)[big::kFM][big::kFN]) {
+  MLA_TILE_BARRIER(waitcnt_vm(0));  // this stage's copies have landed, the other stage is free
+  if (s + 1 < nsteps) big_issue<1 - ST>(x, s + 1);
+  BigHalf f;
+  big_read<ST>(x, 0, f);
+  big_mfma(f, acc);
+  big_read<ST>(x, 1, f);
+  big_mfma(f, acc);
+}
+
+// Row base (element offset of the row's start) of an epilogue.
+__device__ __forceinline__ int64_t epi_row_base(const Epilogue& e, int row) {
+  if (e.block_table) {
+    const int sq = e.row_seq ? e.row_seq[row] : row, ps = e.row_pos[row];
+    return ((int64_t)e.block_table[(int64_t)sq * e.max_blocks + ps / e.block_size] * e.block_size +
+            ps % e.block_size) * e.ldc;
+  }
+  return (int64_t)row * e.ldc;
+}
+
+__global__ void __launch_bounds__(512) gemm_big_kernel(GemmParams p) {
+  using namespace big;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tiles_m = (p.M + kTileM - 1) / kTileM, tiles_n = (p.N + kTileN - 1) / kTileN;
+  // Tile order: workgroups are dealt to the 8 XCDs in turn, so block b runs on XCD b % 8.  Give
+  // each XCD a contiguous range of the tile order, and walk that order in groups of kGroupM tile
+  // rows (column by column inside a group): the workgroups resident on one XCD then share a few
+  // A and B panels in that XCD's L2.
+  int t;
+  {
+    const int T = tiles_m * tiles_n, b = blockIdx.x, xcd = b & 7, local = b >> 3;
+    const int per = T >> 3, extra = T & 7;
+    t = xcd * per + min(xcd, extra) + local;
+  }
+  int m_t, n_t;
+  {
+    const int span = kGroupM * tiles_n, grp = t / span, in = t % span;
+    const int gm = min(kGroupM, tiles_m - grp * kGroupM);
+    m_t = grp * kGroupM + in % gm;
+    n_t = in / gm;
+  }
+  const int m0 = m_t * kTileM, n0 = n_t * kTileN;
+  const int z = blockIdx.y;
+  BigCtx x;
+  x.w = w;
+  x.lane = lane;
+  {
+    const bf16* A = reinterpret_cast<const bf16*>(p.A) + (int64_t)z * p.strideA;
+#pragma unroll
+    for (int i = 0; i < kCopies; ++i) {
+      const int row = (i * kWaves + w) * 8 + (lane >> 3);  // tile row of this lane's copy
+      const int ch = (lane & 7) ^ swz(row);                 // source chunk landing in slot lane & 7
+      x.a[i] = A + (int64_t)min(m0 + row, p.M - 1) * p.lda + ch * 8;
+      x.b[i] = b_row<bf16>(p, z, min(n0 + row, p.N - 1)) + ch * 8;
+    }
+  }
+  floatx16 acc[kFM][kFN];
+#pragma unroll
+  for (int i = 0; i < kFM; ++i)
+#pragma unroll
+    for (int j = 0; j < kFN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  const int nsteps = p.K / kStepK;
+  big_issue<0>(x, 0);
+  for (int s = 0; s < nsteps; s += 2) {
+    big_step<0>(x, s, nsteps, acc);
+    if (s + 1 < nsteps) big_step<1>(x, s + 1, nsteps, acc);
+  }
+
+  // Epilogue through LDS, half a wave block (64 x 64) at a time, in the wave's own 16 KiB: the
+  // accumulators are only ever indexed by constants (a loop over them that is too long to unroll
+  // would move them to scratch memory).  On the way out each lane owns one column, so the column's
+  // part of the address is worked out once and the row's part is shared by the wave.
+  __syncthreads();  // every wave is done with the operand stages
+  const int g = lane >> 5, l32 = lane & 31;
+  const int wm = w >> 2, wn = w & 3;
+  float* ep = reinterpret_cast<float*>((w < 4 ? g_big_s0 : g_big_s1) + (w & 3) * 16384);
+  const int col = n0 + wn * 64 + lane;
+  const bool hi = col >= p.E0;
+  const int c = hi ? col - p.E0 : col;
+  // this lane's epilogue fields, picked once (the two epilogues are kernel arguments)
+  const int e_group = hi ? p.epi2.group : p.epi.group;
+  const int64_t col_off = (int64_t)z * (hi ? p.epi2.batch_stride : p.epi.batch_stride) +
+                          (int64_t)(c / e_group) * (hi ? p.epi2.group_stride : p.epi.group_stride) +
+                          (hi ? p.epi2.group_off : p.epi.group_off) + c % e_group;
+  const int e_rope0 = hi ? p.epi2.rope_col0 : p.epi.rope_col0, e_dhr = hi ? p.epi2.d_hr : p.epi.d_hr;
+  const float2* e_tab = hi ? p.epi2.rope_tab : p.epi.rope_tab;
+  const bool rot = c >= e_rope0;
+  const int rk = rot ? ((c - e_rope0) % e_dhr) >> 1 : 0;
+  void* e_C = hi ? p.epi2.C : p.epi.C;
+  float* e_C2 = hi ? p.epi2.C2 : p.epi.C2;
+  const bool e_f32 = hi ? p.epi2.c_f32 : p.epi.c_f32;
+  const bool col_ok = col < p.N;
+  // element (lr, lc) at lr*64 + (lc ^ 32*((lr >> 2) & 1)): the two row groups one write covers
+  // land in different banks
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int fn = 0; fn < kFN; ++fn)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int lr = f * 32 + 8 * (r >> 2) + 4 * g + (r & 3), lc = fn * 32 + l32;
+          ep[lr * 64 + (lc ^ (((lr >> 2) & 1) << 5))] = acc[2 * h + f][fn][r];
+        }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_wave_barrier();
+    const int row0 = m0 + wm * 128 + h * 64;
+    const int my_row = min(row0 + lane, p.M - 1);
+    const int64_t rb_lo = epi_row_base(p.epi, my_row);
+    const int64_t rb_hi = p.E0 < p.N ? epi_row_base(p.epi2, my_row) : 0;
+    const int nrows = min(64, p.M - row0);
+    for (int lr = 0; lr < nrows; ++lr) {
+      const int sw = ((lr >> 2) & 1) << 5;
+      float v = ep[lr * 64 + (lane ^ sw)];
+      const int64_t lo = (int64_t)(uint32_t)__builtin_amdgcn_readlane((int)rb_lo, lr) |
+                         ((int64_t)__builtin_amdgcn_readlane((int)(rb_lo >> 32), lr) << 32);
+      const int64_t hib = (int64_t)(uint32_t)__builtin_amdgcn_readlane((int)rb_hi, lr) |
+                          ((int64_t)__builtin_amdgcn_readlane((int)(rb_hi >> 32), lr) << 32);
+      if (rot) {
+        const float partner = ep[lr * 64 + ((lane ^ 1) ^ sw)];
+        const float2 cs = e_tab[(int64_t)(row0 + lr) * (e_dhr >> 1) + rk];
+        v = (c & 1) ? (partner * cs.y + v * cs.x) : (v * cs.x - partner * cs.y);
+      }
+      if (col_ok) {
+        const int64_t idx = (hi ? hib : lo) + col_off;
+        if (e_f32)
+          reinterpret_cast<float*>(e_C)[idx] = v;
+        else
+          reinterpret_cast<bf16*>(e_C)[idx] = from_f32<bf16>(v);
+        if (e_C2) e_C2[idx] = v;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
 // ----------------------------------------------------------------------------- host side
 namespace {
 struct Cfg {
@@ -523,6 +751,12 @@ hipError_t run_t(const GemmParams& p, const GemmPlan& plan, float* partial, hipS
   switch (plan.cfg) {
     case 0: err = launch_cfg<T, 0>(p, plan, partial, s); break;
     case 1: err = launch_cfg<T, 1>(p, plan, partial, s); break;
+    case 5: {
+      dim3 grid(((p.M + big::kTileM - 1) / big::kTileM) * ((p.N + big::kTileN - 1) / big::kTileN), p.batch);
+      hipLaunchKernelGGL(gemm_big_kernel, grid, dim3(64 * big::kWaves), 0, s, p);
+      err = hipGetLastError();
+      break;
+    }
     case 3:
     case 4: {
       dim3 grid((p.N + skinny::kBN - 1) / skinny::kBN, p.batch * plan.splits);
@@ -579,6 +813,18 @@ GemmPlan gemm_plan_skinny(int M, int N, int K, int batch, int cus) {
 
 GemmPlan gemm_plan(int M, int N, int K, int batch, int cus, bool skinny_ok) {
   if (skinny_ok && M <= 64 && K % skinny::kKS == 0 && N % 2 == 0) return gemm_plan_skinny(M, N, K, batch, cus);
+  // large products: 256 x 256 tiles, one k range (enough tiles to fill the compute units)
+  if (skinny_ok && K % big::kStepK == 0 && N % 2 == 0 &&
+      (int64_t)((M + big::kTileM - 1) / big::kTileM) * ((N + big::kTileN - 1) / big::kTileN) * batch >= cus) {
+    GemmPlan pl;
+    pl.cfg = 5;
+    pl.bm = big::kTileM;
+    pl.bn = big::kTileN;
+    pl.splits = 1;
+    pl.k_per_split = K;
+    pl.partial_bytes = 0;
+    return pl;
+  }
   GemmPlan pl;
   pl.cfg = M <= 32 ? 0 : (M <= 64 ? 1 : 2);
   pl.bm = kCfgs[pl.cfg].bm;
@@ -613,6 +859,9 @@ size_t gemm_partial_bound(int M, int N, int K, int batch, int cus, bool skinny_o
 hipError_t gemm_run(DType t, const GemmParams& p, const GemmPlan& plan, float* partial, hipStream_t s) {
   if (p.M == 0 || p.N == 0 || p.batch == 0) return hipSuccess;
   if ((plan.cfg == 3 || plan.cfg == 4) && (t != DType::BF16 || !gemm_skinny_ok(t, p))) return hipErrorInvalidValue;
+  if (plan.cfg == 5 && (t != DType::BF16 || p.nn || p.K % big::kStepK != 0 || p.lda % 8 != 0 || p.ldb % 8 != 0 ||
+                        p.strideA % 8 != 0 || p.strideB % 8 != 0))
+    return hipErrorInvalidValue;
   return t == DType::BF16 ? run_t<bf16>(p, plan, partial, s) : run_t<float>(p, plan, partial, s);
 }
 

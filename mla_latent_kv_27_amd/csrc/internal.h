@@ -64,7 +64,7 @@ struct GemmPlan {
 };
 
 // skinny_ok: the product is bf16, "NT" and 16-byte aligned, so rows M <= 64 may take the
-// weight-streaming kernel.
+// weight-streaming kernel and products with enough 256 x 256 tiles the large-tile kernel.
 GemmPlan gemm_plan(int M, int N, int K, int batch, int cus, bool skinny_ok);
 // Largest partial_bytes of gemm_plan(m, ...) over 1 <= m <= M (workspace sized for M then also
 // serves every smaller call).

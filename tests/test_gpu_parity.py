@@ -172,7 +172,10 @@ def _end_to_end(name, lens, splits, std=0.02, recipe=None):
 
 
 # ----------------------------------------------------------------------------- prefill
-@pytest.mark.parametrize("name,batch,T", [("tiny", 1, 16), ("tiny", 2, 37), ("v2lite", 1, 200), ("v2", 2, 130)])
+# ("v2", 1, 1000): enough rows that the projections take the 256 x 256-tile kernel, with ragged
+# last tiles along both M and N
+@pytest.mark.parametrize("name,batch,T", [("tiny", 1, 16), ("tiny", 2, 37), ("v2lite", 1, 200), ("v2", 2, 130),
+                                          ("v2", 1, 1000)])
 def test_prefill_matches_oracle(name, batch, T):
     dims, recipe = SMALL[name]
     W = S.make_weights(dims)
