@@ -208,7 +208,7 @@ __global__ void __launch_bounds__(64 * NW) decode_attn_kernel(DecodeAttnParams p
 //     cross-lane exchange; every lane keeps a partial sum that is combined once at the end.
 namespace tiled {
 constexpr int kT = 32;                    // tokens per tile
-constexpr int kNBuf = 4;                  // ring depth
+constexpr int kNBuf = 4;                  // ring buffers (two tile pairs)
 constexpr int kD = 576, kDC = 512;        // entry width, latent width
 constexpr int kCPR = kD * 2 / 16;         // 72 chunks per entry
 constexpr int kRow = kCPR * 16;           // 1152 bytes per entry
@@ -270,12 +270,9 @@ struct TiledState {
 
 template <int BUF>
 __device__ __forceinline__ void tiled_compute(const Frag8<bf16> (&q)[18], TiledState& st, int t, int kv_len,
-                                              float scale_log2, int lane, const TiledCtx& c, bool issue_next, int w) {
+                                              float scale_log2, int lane) {
   using namespace tiled;
   const char* buf = kv_buf<BUF>();
-  // refill the buffer of tile t-1 (free since the barrier) with tile t+3 first, so that all
-  // waves' shares of that tile leave at about the same time
-  if (issue_next) issue_tile<(BUF + kNBuf - 1) % kNBuf>(c, t + kNBuf - 1, w, lane);
   // the lane's LDS offsets are recomputed in every step (a few integer ops) rather than kept live
   // for all four ring buffers across the loop
   asm volatile("" : "+v"(lane));
@@ -365,32 +362,27 @@ __device__ __forceinline__ void tiled_compute(const Frag8<bf16> (&q)[18], TiledS
   }
 }
 
-// One pipeline step on ring buffer BUF (= t % 4): wait for tile t, publish it to the workgroup,
-// multiply tile t (refilling the buffer of tile t-1 with tile t+3 on the way).
-template <int BUF>
-__device__ __forceinline__ void tiled_step(const TiledCtx& c, const Frag8<bf16> (&q)[18], TiledState& st, int t,
+// Two tiles per barrier: tiles t and t+1 sit in ring buffers B0 and B0+1 (B0 = 0 or 2), and the
+// only copies in flight are theirs.  Once they have landed and every wave is past the previous
+// pair, the copies of tiles t+2 and t+3 go into the other two buffers, then both tiles are
+// multiplied.  Half as many workgroup barriers as one per tile, and no pipeline drain between the
+// two tiles of a pair.
+template <int B0>
+__device__ __forceinline__ void tiled_pair(const TiledCtx& c, const Frag8<bf16> (&q)[18], TiledState& st, int t,
                                            int t_end, float scale_log2, int w, int lane, int tid) {
   using namespace tiled;
-  const int ahead = min(t_end - 1 - t, kNBuf - 2);  // tiles issued after t and still in flight
-  static_assert(kNBuf == 2 || kNBuf == 4, "waits below");
-  if (kNBuf == 4 && ahead >= 2) {
-    if (w < 4) MLA_TILE_BARRIER(waitcnt_vm(10));
-    else MLA_TILE_BARRIER(waitcnt_vm(8));
-  } else if (kNBuf == 4 && ahead == 1) {
-    if (w < 4) MLA_TILE_BARRIER(waitcnt_vm(5));
-    else MLA_TILE_BARRIER(waitcnt_vm(4));
-  } else {
-    MLA_TILE_BARRIER(waitcnt_vm(0));
-  }
-  const int valid = c.kv_len - t * kT;
+  MLA_TILE_BARRIER(waitcnt_vm(0));
+  if (t + 2 < t_end) issue_tile<(B0 + 2) % kNBuf>(c, t + 2, w, lane);
+  if (t + 3 < t_end) issue_tile<(B0 + 3) % kNBuf>(c, t + 3, w, lane);
+  const int last = min(t + 1, t_end - 1);  // only the sequence's last tile can be partial
+  const int valid = c.kv_len - last * kT;
   if (valid < kT) {  // zero the rows past the end of the context (uniform branch)
-    char* buf = kv_buf<BUF>();
+    char* buf = last == t ? kv_buf<B0>() : kv_buf<B0 + 1>();
     for (int i = tid; i < (kT - valid) * kCPR; i += 64 * kWaves) st16(buf + (valid * kCPR + i) * 16, zero16());
     MLA_TILE_BARRIER(kWaitLgkm0);
   }
-  // multiply tile t; the copies of tile t+3 into the buffer of tile t-1 (free since the barrier)
-  // are issued first thing inside
-  tiled_compute<BUF>(q, st, t, c.kv_len, scale_log2, lane, c, t + kNBuf - 1 < t_end, w);
+  tiled_compute<B0>(q, st, t, c.kv_len, scale_log2, lane);
+  if (t + 1 < t_end) tiled_compute<B0 + 1>(q, st, t + 1, c.kv_len, scale_log2, lane);
 }
 
 __global__ void __launch_bounds__(512)
@@ -435,13 +427,10 @@ __global__ void __launch_bounds__(512)
   st.l_part = 0.f;
 
   if (t_begin < t_end) issue_tile<0>(c, t_begin, w, lane);
-  if (kNBuf > 2 && t_begin + 1 < t_end) issue_tile<1 % kNBuf>(c, t_begin + 1, w, lane);
-  if (kNBuf > 3 && t_begin + 2 < t_end) issue_tile<2 % kNBuf>(c, t_begin + 2, w, lane);
+  if (t_begin + 1 < t_end) issue_tile<1>(c, t_begin + 1, w, lane);
   for (int t = t_begin; t < t_end; t += kNBuf) {
-    tiled_step<0>(c, q, st, t, t_end, p.scale_log2, w, lane, tid);
-    if (t + 1 < t_end) tiled_step<1 % kNBuf>(c, q, st, t + 1, t_end, p.scale_log2, w, lane, tid);
-    if (kNBuf > 2 && t + 2 < t_end) tiled_step<2 % kNBuf>(c, q, st, t + 2, t_end, p.scale_log2, w, lane, tid);
-    if (kNBuf > 3 && t + 3 < t_end) tiled_step<3 % kNBuf>(c, q, st, t + 3, t_end, p.scale_log2, w, lane, tid);
+    tiled_pair<0>(c, q, st, t, t_end, p.scale_log2, w, lane, tid);
+    if (t + 2 < t_end) tiled_pair<2>(c, q, st, t + 2, t_end, p.scale_log2, w, lane, tid);
   }
   // the four lane groups of a head hold partial sums over different tokens
   float l_run = wave_sum_xor(st.l_part, 16);
