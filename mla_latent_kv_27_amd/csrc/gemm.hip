@@ -728,6 +728,217 @@ __global__ void __launch_bounds__(512) gemm_big_kernel(GemmParams p) {
   }
 }
 
+// ----------------------------------------------------------------------------- W_UK absorption
+// q_hat[b][h][c] = sum_k q^C[b][h][k] W_UK[h*d_h + k][c] (App. C, W_UK folded into the query):
+// per head a product whose weight operand has its output dimension contiguous, so the
+// k-contiguous fragments the MFMA takes come from an LDS copy of the weight slice read with
+// ds_read_b64_tr_b16 (16 lanes read a 4 (k) x 16 (c) block and each lane receives one column).
+// Workgroup = (128-column slice of d_c, head): its d_h x 128 weight slice is copied to LDS once
+// and serves every batch row; 4 waves of 32 columns each; the head's queries are copied to LDS
+// in blocks of 64 batch rows.
+namespace absorb {
+constexpr int kCols = 128;  // columns of d_c per workgroup
+constexpr int kDh = 128;    // d_h (both operands' LDS rows are 256 bytes = 16 chunks)
+constexpr int kRowB = 256;
+constexpr int kMB = 64;     // batch rows per block
+constexpr int kWaves = 4;
+// weight row r, chunk c at slot c ^ (2 (r & 3)): the four rows one transposed read covers fall
+// in distinct banks; query row m, chunk c at slot c ^ (m & 15): the 16 rows one fragment read
+// covers fall in distinct banks
+__device__ __forceinline__ int wslot(int r, int c) { return c ^ ((r & 3) << 1); }
+__device__ __forceinline__ int qslot(int m, int c) { return c ^ (m & 15); }
+}  // namespace absorb
+
+__global__ void __launch_bounds__(256) absorb_kernel(const bf16* __restrict__ qc, const bf16* __restrict__ w,
+                                                     bf16* __restrict__ out, int B, int n_h, int d_c,
+                                                     int64_t out_ld, int64_t out_hs) {
+  using namespace absorb;
+  __shared__ __attribute__((aligned(1024))) char lw[kDh * kRowB];
+  __shared__ __attribute__((aligned(1024))) char lq[kMB * kRowB];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c0 = blockIdx.x * kCols, h = blockIdx.y;
+  const int sub = lane >> 4, sl = lane & 15;  // copy lane: row 4P + sub, slot sl (1 KiB = 4 rows)
+  // the weight slice: 32 copies, 8 per wave
+#pragma unroll
+  for (int i = 0; i < kDh / 4 / kWaves; ++i) {
+    const int P = i * kWaves + wv, r = 4 * P + sub;
+    const bf16* src = w + ((int64_t)h * kDh + r) * d_c + c0 + 8 * wslot(r, sl);
+    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(lw + P * 1024), 16, 0, 0);
+  }
+  // one block of the head's queries: 16 copies, 4 per wave (rows past B repeat row B-1)
+  auto copy_q = [&](int m0) {
+#pragma unroll
+    for (int i = 0; i < kMB / 4 / kWaves; ++i) {
+      const int P = i * kWaves + wv, r = 4 * P + sub;
+      const int m = min(m0 + r, B - 1);
+      const bf16* src = qc + ((int64_t)m * n_h + h) * kDh + 8 * qslot(r, sl);
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(lq + P * 1024), 16, 0, 0);
+    }
+  };
+  copy_q(0);
+  const int G = lane >> 4, i16 = lane & 15;
+  MLA_TILE_BARRIER(waitcnt_vm(0));
+  // B fragments of this wave's two 16-column blocks for every 32-k step: lane (G, i) holds column
+  // i, k = 32 kk + 8G .. +7; source lane s of the two reads supplies row 32 kk + 8G + s/4 (+4),
+  // columns 4 (s % 4) .. +3
+  Frag8<bf16> bf[kDh / 32][2];
+  {
+    const int rsub = i16 >> 2, cq = i16 & 3;
+#pragma unroll
+    for (int kk = 0; kk < kDh / 32; ++kk)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int col = wv * 32 + nb * 16 + 4 * cq;  // within the slice
+        const int chunk = col >> 3, byte = (col & 7) * 2;
+        const int r_lo = 32 * kk + 8 * G + rsub, r_hi = r_lo + 4;
+        const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_shortx4_t*)(lw + r_lo * kRowB + wslot(r_lo, chunk) * 16 + byte));
+        const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_shortx4_t*)(lw + r_hi * kRowB + wslot(r_hi, chunk) * 16 + byte));
+        bf[kk][nb].v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+  }
+  for (int m0 = 0; m0 < B; m0 += kMB) {
+    if (m0 > 0) {
+      __syncthreads();  // every wave is done with the previous block
+      copy_q(m0);
+      MLA_TILE_BARRIER(waitcnt_vm(0));
+    }
+    floatx4 acc[4][2];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = floatx4{0, 0, 0, 0};
+#pragma unroll
+    for (int kk = 0; kk < kDh / 32; ++kk)
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        // A fragment: batch row m0 + 16 mb + i, k = 32 kk + 8G .. +7 (chunk 4 kk + G)
+        const int r = mb * 16 + i16;
+        Frag8<bf16> a;
+        a.v = *reinterpret_cast<const bf16x8*>(lq + r * kRowB + qslot(r, 4 * kk + G) * 16);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mma16(a, bf[kk][nb], acc[mb][nb]);
+      }
+    // C lane: column i, rows 4G + j
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int m = m0 + mb * 16 + 4 * G + j;
+        if (m < B) {
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb)
+            out[(int64_t)m * out_ld + (int64_t)h * out_hs + c0 + wv * 32 + nb * 16 + i16] = (bf16)acc[mb][nb][j];
+        }
+      }
+  }
+}
+
+bool absorb_ok(DType t, int d_h, int d_c) {
+  return t == DType::BF16 && d_h == absorb::kDh && d_c % absorb::kCols == 0;
+}
+
+hipError_t absorb_run(const void* qc, const void* w_uk, void* qhat, int B, int n_h, int d_h, int d_c,
+                      int64_t out_ld, int64_t out_hs, hipStream_t s) {
+  if (B == 0) return hipSuccess;
+  dim3 grid(d_c / absorb::kCols, n_h);
+  (void)d_h;  // == absorb::kDh (absorb_ok)
+  hipLaunchKernelGGL(absorb_kernel, grid, dim3(64 * absorb::kWaves), 0, s, reinterpret_cast<const bf16*>(qc),
+                     reinterpret_cast<const bf16*>(w_uk), reinterpret_cast<bf16*>(qhat), B, n_h, d_c, out_ld, out_hs);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------- W_UV per head
+// o[b][h][d] = sum_c W_UV[h*d_h + d][c] o_hat[b][h][c] (App. C, W_UV applied after the softmax):
+// per head a skinny product over d_c = 512 with both operands c-contiguous.  Workgroup = (64
+// columns d of one head): the head's o_hat rows (64 at a time, 1 KiB each) are copied to LDS and
+// shared by 4 waves of 16 columns, each wave holding its 16 weight rows in registers.  One pass
+// over k, no split: 2 x n_h workgroups at d_h = 128.
+namespace uvk {
+constexpr int kDc = 512;    // d_c: an LDS row of o_hat is 1 KiB (64 chunks)
+constexpr int kRowB = 2 * kDc;
+constexpr int kMB = 64;     // batch rows per block
+constexpr int kWaves = 4;
+constexpr int kCols = 16 * kWaves;
+// chunk c of o_hat row m at slot c ^ (m & 15): the 16 rows one fragment read covers fall in
+// distinct banks
+__device__ __forceinline__ int slot(int m, int c) { return c ^ (m & 15); }
+}  // namespace uvk
+
+__global__ void __launch_bounds__(256) uv_kernel(const bf16* __restrict__ ohat, const bf16* __restrict__ w,
+                                                 bf16* __restrict__ o, float* __restrict__ o32, int B, int n_h,
+                                                 int d_h) {
+  using namespace uvk;
+  __shared__ __attribute__((aligned(1024))) char la[kMB * kRowB];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = blockIdx.y, d0 = blockIdx.x * kCols + wv * 16;
+  const int G = lane >> 4, i16 = lane & 15;
+  // one copy instruction per o_hat row (rows past B repeat row B-1)
+  auto copy_a = [&](int m0) {
+#pragma unroll
+    for (int i = 0; i < kMB / kWaves; ++i) {
+      const int r = i * kWaves + wv;
+      const int m = min(m0 + r, B - 1);
+      const bf16* src = ohat + ((int64_t)m * n_h + h) * kDc + 8 * slot(r, lane);
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(la + r * kRowB), 16, 0, 0);
+    }
+  };
+  copy_a(0);
+  // B fragments: lane (G, i) holds weight row d0 + i, k = 32 kk + 8G .. +7
+  Frag8<bf16> bw[kDc / 32];
+  {
+    const bf16* wr = w + ((int64_t)h * d_h + d0 + i16) * kDc + 8 * G;
+#pragma unroll
+    for (int kk = 0; kk < kDc / 32; ++kk) load8(bw[kk], wr + 32 * kk);
+  }
+  MLA_TILE_BARRIER(waitcnt_vm(0));
+  for (int m0 = 0; m0 < B; m0 += kMB) {
+    if (m0 > 0) {
+      __syncthreads();  // every wave is done with the previous block
+      copy_a(m0);
+      MLA_TILE_BARRIER(waitcnt_vm(0));
+    }
+    floatx4 acc[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) acc[mb] = floatx4{0, 0, 0, 0};
+#pragma unroll
+    for (int kk = 0; kk < kDc / 32; ++kk)
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const int r = mb * 16 + i16;  // A fragment: row r, k = 32 kk + 8G .. +7 (chunk 4 kk + G)
+        Frag8<bf16> a;
+        a.v = *reinterpret_cast<const bf16x8*>(la + r * kRowB + slot(r, 4 * kk + G) * 16);
+        acc[mb] = mma16(a, bw[kk], acc[mb]);
+      }
+    // C lane: column d0 + i, rows 4G + j
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int m = m0 + mb * 16 + 4 * G + j;
+        if (m < B) {
+          const int64_t idx = ((int64_t)m * n_h + h) * d_h + d0 + i16;
+          o[idx] = (bf16)acc[mb][j];
+          if (o32) o32[idx] = acc[mb][j];
+        }
+      }
+  }
+}
+
+bool uv_ok(DType t, int d_h, int d_c) { return t == DType::BF16 && d_c == uvk::kDc && d_h % uvk::kCols == 0; }
+
+hipError_t uv_run(const void* ohat, const void* w_uv, void* o, float* o32, int B, int n_h, int d_h,
+                  hipStream_t s) {
+  if (B == 0) return hipSuccess;
+  dim3 grid(d_h / uvk::kCols, n_h);
+  hipLaunchKernelGGL(uv_kernel, grid, dim3(64 * uvk::kWaves), 0, s, reinterpret_cast<const bf16*>(ohat),
+                     reinterpret_cast<const bf16*>(w_uv), reinterpret_cast<bf16*>(o), o32, B, n_h, d_h);
+  return hipGetLastError();
+}
+
 // ----------------------------------------------------------------------------- host side
 namespace {
 struct Cfg {

@@ -66,6 +66,17 @@ struct GemmPlan {
 // skinny_ok: the product is bf16, "NT" and 16-byte aligned, so rows M <= 64 may take the
 // weight-streaming kernel and products with enough 256 x 256 tiles the large-tile kernel.
 GemmPlan gemm_plan(int M, int N, int K, int batch, int cus, bool skinny_ok);
+// W_UK absorption for bf16 (d_h == 128, d_c a multiple of 128):
+// qhat[b*out_ld + h*out_hs + c] = sum_k qc[(b*n_h + h)*d_h + k] * w_uk[(h*d_h + k)*d_c + c].
+bool absorb_ok(DType t, int d_h, int d_c);
+hipError_t absorb_run(const void* qc, const void* w_uk, void* qhat, int B, int n_h, int d_h, int d_c,
+                      int64_t out_ld, int64_t out_hs, hipStream_t s);
+// o = W_UV per head for bf16 (d_c == 512, d_h a multiple of 64):
+// o[(b*n_h + h)*d_h + d] = sum_c w_uv[(h*d_h + d)*512 + c] * ohat[(b*n_h + h)*512 + c]; o32 (may be
+// null) receives the same values in fp32.
+bool uv_ok(DType t, int d_h, int d_c);
+hipError_t uv_run(const void* ohat, const void* w_uv, void* o, float* o32, int B, int n_h, int d_h,
+                  hipStream_t s);
 // Largest partial_bytes of gemm_plan(m, ...) over 1 <= m <= M (workspace sized for M then also
 // serves every smaller call).
 size_t gemm_partial_bound(int M, int N, int K, int batch, int cus, bool skinny_ok);

@@ -431,7 +431,9 @@ int mla_decode(const mla_dims* d, const mla_weights* w, const mla_paged_cache* c
     g.epi2.rope_col0 = 0; g.epi2.d_hr = d->d_hr; g.epi2.rope_tab = ws.rope;
     MLA_HIP(gemm_run(t, g, ws.gm.q, ws.partial, s));
   }
-  {  // q_hat_i = W_UK_i^T q^C_i -> columns [0, d_c) of each head's row
+  if (absorb_ok(t, d->d_h, d->d_c)) {  // q_hat_i = W_UK_i^T q^C_i -> columns [0, d_c) of each head's row
+    MLA_HIP(absorb_run(ws.qc, w->W_UK, ws.qcat, B, d->n_h, d->d_h, d->d_c, (int64_t)d->n_h * E, E, s));
+  } else {
     GemmParams g;
     g.A = ws.qc; g.lda = (int64_t)d->n_h * d->d_h; g.strideA = d->d_h;
     g.B0 = w->W_UK; g.ldb = d->d_c; g.strideB = (int64_t)d->d_h * d->d_c; g.nn = true;
@@ -452,7 +454,9 @@ int mla_decode(const mla_dims* d, const mla_weights* w, const mla_paged_cache* c
     a.o_hat = ws.ohat; a.lse = nullptr;
     MLA_HIP(decode_attention(t, a, s));
   }
-  {  // o_i = W_UV_i o_hat_i
+  if (uv_ok(t, d->d_h, d->d_c)) {  // o_i = W_UV_i o_hat_i
+    MLA_HIP(uv_run(ws.ohat, w->W_UV, ws.o, o_heads, B, d->n_h, d->d_h, s));
+  } else {
     GemmParams g;
     g.A = ws.ohat; g.lda = (int64_t)d->n_h * d->d_c; g.strideA = d->d_c;
     g.B0 = w->W_UV; g.ldb = d->d_c; g.strideB = (int64_t)d->d_h * d->d_c;
