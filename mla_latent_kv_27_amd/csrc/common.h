@@ -114,6 +114,20 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4_t;
 
+// Buffer-form copies (buffer_load_dwordx4 ... lds).  Same transfer as the global form: lane i's
+// 16 bytes land at the LDS destination + 16 i.  The compiler counts the buffer form as a vector
+// memory access only, whereas it treats a global-form copy as possibly in flight on the LDS
+// counter as well and then makes every later wait for an LDS read drain all LDS reads in flight;
+// with the buffer form, fragment reads of other LDS buffers keep their partial waits.
+// The resource spans `bytes` from a wave-uniform base: offsets stay 32-bit, and a copy whose
+// offset falls outside the span reads zeros instead of faulting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dma_span(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t span, uint32_t off, lds_void_t* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(span, dst, 16, off, 0, 0, 0);
+}
+
 // s_waitcnt immediates (gfx9 encoding): vmcnt in bits [3:0] and [15:14], expcnt [6:4],
 // lgkmcnt [11:8]; the unused counters are left at their maximum.
 constexpr int waitcnt_vm(int n) { return ((n >> 4) << 14) | (0xF << 8) | (0x7 << 4) | (n & 0xF); }

@@ -238,7 +238,7 @@ struct TiledCtx {
 };
 
 // This wave's share (5 or 4) of the 36 direct-to-LDS copies of tile `tile` into buffer BUF.  block_size is a multiple
-// of 64, so a tile lies inside one block: one uniform block-table lookup, and every row copied
+// of the tile size, so a tile lies inside one block: one uniform block-table lookup, and every row copied
 // is a row of an allocated block (rows past the context are zeroed once the copies land).
 template <int BUF>
 __device__ __forceinline__ void issue_tile(const TiledCtx& c, int tile, int w, int lane) {
@@ -250,14 +250,14 @@ __device__ __forceinline__ void issue_tile(const TiledCtx& c, int tile, int w, i
   int ln = lane;
   asm volatile("" : "+v"(ln));  // recompute the lane offsets here instead of keeping them live
   const int first = dma_first(w), cnt = dma_count(w);
+  const __amdgpu_buffer_rsrc_t span = dma_span(base, kBytes);  // the tile: 32 consecutive rows
 #pragma unroll
   for (int i = 0; i < 5; ++i) {
     if (i < cnt) {
       const int P = (first + i) * 64 + ln;
       const int t = P / kCPR;
       const int ch = (P - t * kCPR) ^ (t & 7);
-      __builtin_amdgcn_global_load_lds((const void*)(base + (uint32_t)(t * kRow + ch * 16)),
-                                       (lds_void_t*)(dst + (first + i) * 1024), 16, 0, 0);
+      dma16(span, t * kRow + ch * 16, (lds_void_t*)(dst + (first + i) * 1024));
     }
   }
 }

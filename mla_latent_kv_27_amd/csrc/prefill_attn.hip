@@ -186,15 +186,23 @@ constexpr int kWaves = 8;
 constexpr int kQ = 32 * kWaves;      // queries per workgroup
 constexpr int kKV = 64;              // keys per tile
 constexpr int kDH = 128, kDR = 64, kDQ = kDH + kDR;
-constexpr int kKRow = kDQ * 2;       // 384 bytes per key row (24 chunks)
-constexpr int kKBytes = kKV * kKRow;  // 24 KiB
-constexpr int kVRow = kKV * 2;      // 128 bytes per value row (one dim, 64 keys)
-constexpr int kVBytes = kDH * kVRow;   // 16 KiB
-constexpr int kStage = kKBytes + kVBytes;
+// a stage: key content rows (64 x 256 bytes), rope key rows (64 x 128 bytes), V^T rows (128 dims
+// x 128 bytes = 64 keys); every copy instruction reads one of the three sources
+constexpr int kKRow = kDH * 2, kRRow = kDR * 2;
+constexpr int kKBytes = kKV * kKRow;    // 16 KiB
+constexpr int kRBytes = kKV * kRRow;    // 8 KiB
+constexpr int kVRow = kKV * 2;          // 128 bytes per value row (one dim, 64 keys)
+constexpr int kVBytes = kDH * kVRow;    // 16 KiB
+constexpr int kROff = kKBytes, kVOff = kKBytes + kRBytes;
+constexpr int kStage = kKBytes + kRBytes + kVBytes;
 constexpr int kNS = 3;
-constexpr int kKCopies = kKBytes / 1024 / kWaves;  // 3 per wave
-constexpr int kVCopies = kVBytes / 1024 / kWaves;  // 2 per wave
-constexpr int kCopies = kKCopies + kVCopies;
+constexpr int kKCopies = kKBytes / 1024 / kWaves;  // 2 per wave (4 rows each)
+constexpr int kRCopies = kRBytes / 1024 / kWaves;  // 1 per wave (8 rows)
+constexpr int kVCopies = kVBytes / 1024 / kWaves;  // 2 per wave (8 rows)
+constexpr int kCopies = kKCopies + kRCopies + kVCopies;
+// 16-byte chunk c of a row r sits at slot c ^ swizzle: 16 consecutive rows then cover all banks
+__device__ __forceinline__ int kslot(int r, int c) { return c ^ (r & 15); }         // 16-chunk rows
+__device__ __forceinline__ int rslot(int r, int c) { return c ^ ((r >> 1) & 7); }   // 8-chunk rows
 }  // namespace pf2
 
 __shared__ __attribute__((aligned(1024))) char g_pf_s0[pf2::kStage];
@@ -205,11 +213,10 @@ template <int ST>
 __device__ __forceinline__ char* pf_stage() { return ST == 0 ? g_pf_s0 : (ST == 1 ? g_pf_s1 : g_pf_s2); }
 
 struct Pf2Ctx {
-  const bf16* k;    // key rows of this (sequence, head): [T][128]
-  const bf16* kr;   // rope key rows of this sequence, ld_kr apart
-  int64_t ld_kr;
-  const bf16* vt;   // V^T rows of this (sequence, head): row d at vt + d * vrow
-  int64_t vrow;
+  __amdgpu_buffer_rsrc_t k;   // key rows of this (sequence, head): [T][128]
+  __amdgpu_buffer_rsrc_t kr;  // rope key rows of this sequence, ld_kr elements apart
+  __amdgpu_buffer_rsrc_t vt;  // V^T rows of this (sequence, head): row d at d * vrow elements
+  int ld_kr, vrow;
   int T;
 };
 
@@ -222,13 +229,15 @@ __device__ __forceinline__ void pf2_issue(const Pf2Ctx& c, int kt, int w, int la
   const int j0 = kt * kKV;
 #pragma unroll
   for (int i = 0; i < kKCopies; ++i) {
-    const int P = i * kWaves + w;
-    const int C = P * 64 + lane;  // chunk slot of the tile
-    const int r = C / 24, sl = C % 24;
-    const int ch = sl ^ (r & 7);
+    const int P = i * kWaves + w, r = 4 * P + (lane >> 4);
     const int j = min(j0 + r, c.T - 1);
-    const bf16* src = ch < 16 ? c.k + (int64_t)j * kDH + ch * 8 : c.kr + (int64_t)j * c.ld_kr + (ch - 16) * 8;
-    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(st + P * 1024), 16, 0, 0);
+    dma16(c.k, (uint32_t)(j * kKRow + kslot(r, lane & 15) * 16), (lds_void_t*)(st + P * 1024));
+  }
+#pragma unroll
+  for (int i = 0; i < kRCopies; ++i) {
+    const int P = i * kWaves + w, r = 8 * P + (lane >> 3);
+    const int j = min(j0 + r, c.T - 1);
+    dma16(c.kr, (uint32_t)(j * c.ld_kr * 2 + rslot(r, lane & 7) * 16), (lds_void_t*)(st + kROff + P * 1024));
   }
 #pragma unroll
   for (int i = 0; i < kVCopies; ++i) {
@@ -236,8 +245,7 @@ __device__ __forceinline__ void pf2_issue(const Pf2Ctx& c, int kt, int w, int la
     const int C = P * 64 + lane;
     const int d = C / 8, sl = C % 8;
     const int ch = sl ^ (d & 7);
-    const bf16* src = c.vt + (int64_t)d * c.vrow + j0 + ch * 8;
-    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(st + kKBytes + P * 1024), 16, 0, 0);
+    dma16(c.vt, (uint32_t)((d * c.vrow + j0 + ch * 8) * 2), (lds_void_t*)(st + kVOff + P * 1024));
   }
 }
 
@@ -259,11 +267,14 @@ __device__ __forceinline__ void pf2_compute(const Frag8<bf16> (&q)[12], Pf2State
   for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) sc[kb][r] = 0.f;
-    const char* krow = st + (kb * 32 + l32) * kKRow;
+    const int r = kb * 32 + l32;
+    const char* krow = st + r * kKRow;
+    const char* rrow = st + kROff + r * kRRow;
 #pragma unroll
     for (int ks = 0; ks < 12; ++ks) {
       Frag8<bf16> a;
-      a.v = *reinterpret_cast<const bf16x8*>(krow + (((2 * ks + g) ^ x) * 16));
+      if (ks < 8) a.v = *reinterpret_cast<const bf16x8*>(krow + kslot(r, 2 * ks + g) * 16);
+      else a.v = *reinterpret_cast<const bf16x8*>(rrow + rslot(r, 2 * (ks - 8) + g) * 16);
       sc[kb] = mma32(a, q[ks], sc[kb]);
     }
   }
@@ -297,7 +308,7 @@ __device__ __forceinline__ void pf2_compute(const Frag8<bf16> (&q)[12], Pf2State
   for (int d = 0; d < 4; ++d) s.o[d] *= alpha;
   // O^T += V^T P^T: lane (dim 32 d + l32, group g) reads keys 16 (2kb + half) + 4g + 0..3 and
   // + 8 + 0..3, i.e. chunk 4kb + 2half (+1) of its row, byte 8g
-  const char* vrow = st + kKBytes + l32 * kVRow + 8 * g;
+  const char* vrow = st + kVOff + l32 * kVRow + 8 * g;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -330,7 +341,7 @@ __device__ __forceinline__ void pf2_step(const Pf2Ctx& c, const Frag8<bf16> (&q)
   if (kt + 2 < kt_end) pf2_issue<(ST + 2) % kNS>(c, kt + 2, w, lane);
   const int valid = c.T - kt * kKV;
   if (valid < kKV) {  // uniform: V^T columns of keys >= T (padding, uninitialised) -> 0
-    char* v = pf_stage<ST>() + kKBytes;
+    char* v = pf_stage<ST>() + kVOff;
     for (int i = tid; i < kDH * (kKV - valid); i += 64 * kWaves) {
       const int d = i / (kKV - valid), key = valid + i % (kKV - valid);
       const int slot = (key >> 3) ^ (d & 7);
@@ -360,11 +371,15 @@ __global__ void __launch_bounds__(512)
   const int Tp = (p.T + kKV - 1) / kKV * kKV;
 
   Pf2Ctx c;
-  c.k = reinterpret_cast<const bf16*>(p.k) + ((int64_t)head * MT + (int64_t)sq * p.T) * kDH;
-  c.kr = reinterpret_cast<const bf16*>(p.kr) + (int64_t)sq * p.T * p.ld_kr + p.kr_off;
-  c.ld_kr = p.ld_kr;
-  c.vt = reinterpret_cast<const bf16*>(p.vt) + ((int64_t)head * kDH * p.S + sq) * Tp;
-  c.vrow = (int64_t)p.S * Tp;
+  // spans below 2 GiB (checked by the launcher): offsets within them are 32-bit
+  c.k = dma_span(reinterpret_cast<const bf16*>(p.k) + ((int64_t)head * MT + (int64_t)sq * p.T) * kDH,
+                 (uint32_t)p.T * kKRow);
+  c.kr = dma_span(reinterpret_cast<const bf16*>(p.kr) + (int64_t)sq * p.T * p.ld_kr + p.kr_off,
+                  (uint32_t)(((int64_t)(p.T - 1) * p.ld_kr + kDR) * 2));
+  c.ld_kr = (int)p.ld_kr;
+  c.vrow = p.S * Tp;
+  c.vt = dma_span(reinterpret_cast<const bf16*>(p.vt) + ((int64_t)head * kDH * p.S + sq) * Tp,
+                  (uint32_t)(((int64_t)(kDH - 1) * c.vrow + Tp) * 2));
   c.T = p.T;
 
   Frag8<bf16> q[12];
@@ -428,7 +443,12 @@ hipError_t launch(const PrefillAttnParams& p, hipStream_t s) {
 }  // namespace
 
 hipError_t prefill_attention(DType t, const PrefillAttnParams& p, hipStream_t s) {
-  if (t == DType::BF16 && p.d_h == 128 && p.d_hr == 64) {
+  // the pipelined kernel addresses each source span with 32-bit byte offsets
+  const int64_t Tp = (p.T + pf2::kKV - 1) / pf2::kKV * pf2::kKV;
+  const bool spans_fit = (int64_t)p.T * pf2::kKRow < (1LL << 31) &&
+                         ((int64_t)(p.T - 1) * p.ld_kr + pf2::kDR) * 2 < (1LL << 31) &&
+                         ((int64_t)(pf2::kDH - 1) * p.S * Tp + Tp) * 2 < (1LL << 31);
+  if (t == DType::BF16 && p.d_h == 128 && p.d_hr == 64 && spans_fit) {
     const int nqt = (p.T + pf2::kQ - 1) / pf2::kQ;
     const int units = p.S * p.n_h;
     const int64_t blocks = (int64_t)(units + 7) / 8 * 8 * nqt;
