@@ -100,7 +100,9 @@ def counters_for(kernel_file, workload):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    src = open(os.path.join(ROOT, "mla_latent_kv_27_amd", "csrc", kernel_file), "rb").read()
+    # the kernel's source and the shared header it includes (copy helpers, waits)
+    csrc = os.path.join(ROOT, "mla_latent_kv_27_amd", "csrc")
+    src = open(os.path.join(csrc, kernel_file), "rb").read() + open(os.path.join(csrc, "common.h"), "rb").read()
     if kv.get("kernel_source_sha256") != hashlib.sha256(src).hexdigest():
         return None
     try:
