@@ -67,14 +67,22 @@ def copy_only(args):
                       "GBps": round(2 * n / (ms / 1e3) / 1e9, 1)}))
 
 
-def decode_bytes(dims, lens, B):
+def entry_bytes(dims, cache="native"):
+    """Bytes of one cached entry: bf16/fp32 values, or e4m3 codes plus two fp32 scales."""
+    if cache == "fp8":
+        return dims.entry + 8
+    return dims.entry * (2 if dims.dtype == "bf16" else 4)
+
+
+def decode_bytes(dims, lens, B, cache="native"):
     """Algorithmic HBM bytes of one decode step: each cached entry once, each weight once, h in,
     u out, the new entries written."""
     es = 2 if dims.dtype == "bf16" else 4
-    cache = sum(int(L) + 1 for L in lens) * dims.entry * es
+    eb = entry_bytes(dims, cache)
+    cache_b = sum(int(L) + 1 for L in lens) * eb
     weights = dims.param_count() * es
-    io = B * 2 * dims.d_model * es + B * dims.entry * es
-    return cache, weights, io
+    io = B * 2 * dims.d_model * es + B * eb
+    return cache_b, weights, io
 
 
 def decode_flops(dims, lens, B):
@@ -83,10 +91,10 @@ def decode_flops(dims, lens, B):
     return attn, proj
 
 
-def attn_core_bytes(dims, lens, B):
+def attn_core_bytes(dims, lens, B, cache="native"):
     """Algorithmic bytes of the attention core: cached entries, the absorbed queries and o_hat."""
     es = 2 if dims.dtype == "bf16" else 4
-    return sum(int(L) + 1 for L in lens) * dims.entry * es + B * dims.n_h * (dims.entry + dims.d_c) * es
+    return sum(int(L) + 1 for L in lens) * entry_bytes(dims, cache) + B * dims.n_h * (dims.entry + dims.d_c) * es
 
 
 def counters_for(kernel_file, workload):
@@ -175,7 +183,7 @@ def prefill_bench(args, w):
     attn_f, proj_f = prefill_flops(dims, T, B)
     tflops = (attn_f + proj_f) / (ms / 1e3) / 1e12
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not fp8:  # the oracle baseline is timed on the bf16 cache only
         import oracle.mla_oracle as O
         n = min(T, 256)
         t0 = time.perf_counter()
@@ -224,8 +232,9 @@ def main():
     B = w.batch
     max_ctx = int(max(lens))
     W_np = S.make_weights(dims, std=w.weight_std)
-    layer = WL.DeviceLayer(dims, W_np)
-    pool = WL.PagedPool(dims, [int(L) + 1 for L in lens], block_size=w.block_size)
+    fp8 = w.cache == "fp8"
+    layer = WL.DeviceLayer(dims, W_np, cache_dtype="fp8" if fp8 else 0)
+    pool = WL.PagedPool(dims, [int(L) + 1 for L in lens], block_size=w.block_size, fp8=fp8)
     t0 = time.perf_counter()
     WL.build_context(layer, pool, lens, w.hidden)
     setup_s = time.perf_counter() - t0
@@ -260,7 +269,7 @@ def main():
     if args.only == "attn":
         attn_ms = timed(attn)
         print(json.dumps({"only": "attn", "workload": w.name, "num_splits": splits, "ms": round(attn_ms, 5),
-                          "algorithmic_bytes": attn_core_bytes(dims, lens, B)}))
+                          "algorithmic_bytes": attn_core_bytes(dims, lens, B, w.cache)}))
         return
 
     def step(i):
@@ -272,15 +281,15 @@ def main():
     value = B / (ms / 1e3)
     # dominant kernel: the latent attention core, timed on the same stream
     attn_ms = timed(attn)
-    core_bytes = attn_core_bytes(dims, lens, B)
+    core_bytes = attn_core_bytes(dims, lens, B, w.cache)
     achieved = core_bytes / (attn_ms / 1e3) / 1e9
     traffic = counters_for("decode_attn.hip", args.workload)
 
-    cache_b, weight_b, io_b = decode_bytes(dims, lens, B)
+    cache_b, weight_b, io_b = decode_bytes(dims, lens, B, w.cache)
     step_bytes = cache_b + weight_b + io_b
     attn_f, proj_f = decode_flops(dims, lens, B)
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not fp8:  # the oracle baseline is timed on the bf16 cache only
         cpu = cpu_baseline(dims, W_np, lens, w.hidden, args.cpu_seconds)
 
     rec = {
@@ -298,7 +307,8 @@ def main():
         "data": "synthetic (seeded weights N(0,0.02), RMS-normalised N(0,1) hidden states, random page order)",
         "config": {"workload": w.name, "batch": B, "ctx_tokens": [int(min(lens)), int(max(lens))],
                    "d_model": dims.d_model, "n_h": dims.n_h, "d_h": dims.d_h, "d_c": dims.d_c, "d_cq": dims.d_cq,
-                   "d_hr": dims.d_hr, "block_size": w.block_size, "num_splits": splits, "replicas": len(reps)},
+                   "d_hr": dims.d_hr, "block_size": w.block_size, "num_splits": splits, "replicas": len(reps),
+                   "cache": "fp8_e4m3 (per-token scales)" if fp8 else dims.dtype},
         "step_GBps": round(step_bytes / (ms / 1e3) / 1e9, 1),
         "step_hbm_frac": round(step_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
         "step_bytes": step_bytes,

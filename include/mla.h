@@ -19,8 +19,9 @@
  *
  * Conventions for every entry point
  *   - Weights are row-major [out][in] (y = W x), in dims->dtype, device memory, 16-byte aligned.
- *   - The cache pool is [num_blocks][block_size][d_c + d_hr] in dims->dtype; each token's entry is
- *     [c^KV | k^R] (d_c + d_hr = 576 values at DeepSeek-V2 sizes).  block_table[b][k] is the
+ *   - The cache pool is [num_blocks][block_size][d_c + d_hr] in dims->dtype (bytes of e4m3 codes
+ *     when dims->cache_dtype is MLA_FP8_E4M3, with per-token scales beside it); each token's
+ *     entry is [c^KV | k^R] (d_c + d_hr = 576 values at DeepSeek-V2 sizes).  block_table[b][k] is the
  *     physical block holding logical block k of sequence b (int32, device).
  *   - Every pointer argument is a device pointer unless marked "host".
  *   - The caller owns all memory (weights, cache, tables, inputs, outputs, workspace).  The
@@ -52,7 +53,7 @@ typedef enum {
   MLA_ERR_HIP = -4          /* a HIP call or kernel launch failed */
 } mla_status;
 
-typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
+typedef enum { MLA_F32 = 0, MLA_BF16 = 1, MLA_FP8_E4M3 = 2 } mla_dtype;
 
 typedef enum { MLA_OP_CACHE_APPEND = 0, MLA_OP_PREFILL = 1, MLA_OP_DECODE = 2 } mla_op;
 
@@ -67,6 +68,14 @@ typedef struct {
   float softmax_scale; /* 0 => 1/sqrt(d_h + d_hr) (App. C) */
   float rope_base;     /* RoPE frequency base (10000 for DeepSeek-V2) */
   int32_t dtype;       /* mla_dtype: storage of weights, h, cache, u */
+  int32_t cache_dtype; /* element type of the cache pool: 0 = dtype, or MLA_FP8_E4M3 (with
+                          dtype MLA_BF16, d_c 512, d_hr 64): the low-bit cache of the serving
+                          section (section 3.2.3, "about 6 bits per element"), read here as
+                          OCP e4m3 codes with one fp32 scale per token for each of the two
+                          parts [c^KV] and [k^R]: s = amax(|part|) / 448 (448 = the largest e4m3
+                          value), code = e4m3(x / s), rounded to nearest even, saturating; an
+                          all-zero part has s = 0.  The quantised entry is the bf16 entry the
+                          bf16 path would store.  Attention reads value(code) * s. */
 } mla_dims;
 
 /* Device pointers, row-major [out][in].  W_DQ is NULL iff d_cq == 0. */
@@ -88,6 +97,8 @@ typedef struct {
   int32_t block_size;         /* tokens per block (64 at DeepSeek-V2 sizes); >= 1 */
   int32_t max_blocks_per_seq; /* columns of block_table */
   const int32_t *block_table; /* [batch][max_blocks_per_seq] */
+  float *scales;              /* fp8 cache: [num_blocks][block_size][2] fp32 (s_c, s_r) per token,
+                                 written with the codes; else ignored (may be NULL) */
 } mla_paged_cache;
 
 /*
@@ -101,6 +112,16 @@ typedef struct {
  */
 int mla_workspace_size(const mla_dims *dims, int op, int32_t batch, int32_t max_tokens,
                        int32_t max_ctx_len, int32_t num_splits, size_t *bytes);
+
+/*
+ * The fp8 cache quantiser alone (the cache_dtype reading above), for tests and for callers that
+ * form entries themselves: for each of n dense bf16 entries [c^KV | k^R] (entry = d_c + d_hr
+ * values), codes[r][:] = its e4m3 codes and scales[r][0..1] = (s_c, s_r).
+ *   entries [n][entry] bf16; codes [n][entry] uint8; scales [n][2] fp32 (all device)
+ * Requires dims->cache_dtype == MLA_FP8_E4M3 (else MLA_ERR_INVALID_ARG).
+ */
+int mla_quantize_entries(const mla_dims *dims, const void *entries, int32_t n, uint8_t *codes,
+                         float *scales, void *stream);
 
 /*
  * Cache writer (section 2.1.2 compression, section 2.1.3 shared rope key, App. C cached

@@ -20,11 +20,12 @@ MLA_ERR_WORKSPACE = -3
 MLA_ERR_HIP = -4
 MLA_F32 = 0
 MLA_BF16 = 1
+MLA_FP8_E4M3 = 2
 OP_CACHE_APPEND, OP_PREFILL, OP_DECODE = 0, 1, 2
 
 EXPORTED = (
     "mla_workspace_size", "mla_cache_append", "mla_prefill", "mla_decode", "mla_decode_attention",
-    "mla_decode_auto_splits", "mla_status_string",
+    "mla_decode_auto_splits", "mla_quantize_entries", "mla_status_string",
 )
 
 
@@ -37,7 +38,8 @@ class MlaError(RuntimeError):
 class Dims(ctypes.Structure):
     _fields_ = [("d_model", ctypes.c_int32), ("n_h", ctypes.c_int32), ("d_h", ctypes.c_int32),
                 ("d_c", ctypes.c_int32), ("d_cq", ctypes.c_int32), ("d_hr", ctypes.c_int32),
-                ("softmax_scale", ctypes.c_float), ("rope_base", ctypes.c_float), ("dtype", ctypes.c_int32)]
+                ("softmax_scale", ctypes.c_float), ("rope_base", ctypes.c_float), ("dtype", ctypes.c_int32),
+                ("cache_dtype", ctypes.c_int32)]
 
 
 class Weights(ctypes.Structure):
@@ -46,7 +48,7 @@ class Weights(ctypes.Structure):
 
 class PagedCache(ctypes.Structure):
     _fields_ = [("pool", ctypes.c_void_p), ("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
-                ("max_blocks_per_seq", ctypes.c_int32), ("block_table", ctypes.c_void_p)]
+                ("max_blocks_per_seq", ctypes.c_int32), ("block_table", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
 
 
 _lib = None
@@ -68,6 +70,8 @@ def lib() -> ctypes.CDLL:
         L.mla_decode.argtypes = [D, W, C, P, I32, P, I32, I32, P, P, P, SZ, P]
         L.mla_decode_attention.argtypes = [D, C, P, I32, P, I32, I32, P, P, P, SZ, P]
         L.mla_decode_auto_splits.argtypes = [D, I32, I32]
+        L.mla_quantize_entries.argtypes = [D, P, I32, P, P, P]
+        L.mla_quantize_entries.restype = ctypes.c_int
         L.mla_decode_auto_splits.restype = I32
         L.mla_status_string.argtypes = [ctypes.c_int]
         L.mla_status_string.restype = ctypes.c_char_p
@@ -100,9 +104,11 @@ def _stream(stream) -> int | None:
     return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def make_dims(d_model, n_h, d_h, d_c, d_cq, d_hr, dtype, softmax_scale=0.0, rope_base=10000.0) -> Dims:
+def make_dims(d_model, n_h, d_h, d_c, d_cq, d_hr, dtype, softmax_scale=0.0, rope_base=10000.0,
+              cache_dtype=0) -> Dims:
     dt = {"bf16": MLA_BF16, "f32": MLA_F32, MLA_BF16: MLA_BF16, MLA_F32: MLA_F32}[dtype]
-    return Dims(d_model, n_h, d_h, d_c, d_cq, d_hr, float(softmax_scale), float(rope_base), dt)
+    cdt = {0: 0, None: 0, "fp8": MLA_FP8_E4M3, MLA_FP8_E4M3: MLA_FP8_E4M3}[cache_dtype]
+    return Dims(d_model, n_h, d_h, d_c, d_cq, d_hr, float(softmax_scale), float(rope_base), dt, cdt)
 
 
 def make_weights(W: dict) -> Weights:
@@ -110,9 +116,11 @@ def make_weights(W: dict) -> Weights:
     return Weights(*[_ptr(W.get(n)) for n, _ in Weights._fields_])
 
 
-def make_cache(pool, block_table) -> PagedCache:
-    """pool [num_blocks][block_size][d_c + d_hr], block_table [batch][max_blocks] int32."""
-    return PagedCache(_ptr(pool), pool.shape[0], pool.shape[1], block_table.shape[1], _ptr(block_table))
+def make_cache(pool, block_table, scales=None) -> PagedCache:
+    """pool [num_blocks][block_size][d_c + d_hr], block_table [batch][max_blocks] int32;
+    scales [num_blocks][block_size][2] fp32 for an fp8 cache."""
+    return PagedCache(_ptr(pool), pool.shape[0], pool.shape[1], block_table.shape[1], _ptr(block_table),
+                      _ptr(scales))
 
 
 def workspace_size(dims: Dims, op: int, batch: int = 0, max_tokens: int = 0, max_ctx_len: int = 0,
@@ -156,6 +164,12 @@ def decode_attention(dims, cache, q, kv_lens, max_kv_len, o_hat, workspace, num_
     _check(lib().mla_decode_attention(ctypes.byref(dims), ctypes.byref(cache), _ptr(q), int(q.shape[0]),
                                       _ptr(kv_lens), int(max_kv_len), int(num_splits), _ptr(o_hat), _ptr(lse),
                                       p, n, _stream(stream)), "mla_decode_attention")
+
+
+def quantize_entries(dims, entries, codes, scales, stream=None):
+    """entries [n][d_c + d_hr] bf16 -> codes [n][d_c + d_hr] uint8, scales [n][2] fp32."""
+    _check(lib().mla_quantize_entries(ctypes.byref(dims), _ptr(entries), int(entries.shape[0]), _ptr(codes),
+                                      _ptr(scales), _stream(stream)), "mla_quantize_entries")
 
 
 def auto_splits(dims, batch, max_ctx_len) -> int:

@@ -15,7 +15,7 @@ INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 LIB = os.path.join(PKG, "lib", "libmla.so")
 ARCH = os.environ.get("MLA_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["gemm.hip", "rope.hip", "decode_attn.hip", "prefill_attn.hip", "mla_api.cpp"]
+SOURCES = ["gemm.hip", "rope.hip", "decode_attn.hip", "prefill_attn.hip", "latent_fp8.hip", "mla_api.cpp"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -268,6 +268,41 @@ struct TiledState {
   float l_part;    // this lane's partial normaliser
 };
 
+// O^T += V^T P^T over the 32 tokens of the bf16 tile in buffer BUF (rows of 1152 bytes, chunk c of
+// row r at slot c ^ (r & 7)); pf holds P for the lane's head, slot s = token 16 (s/4) + 4g + s%4.
+template <int BUF>
+__device__ __forceinline__ void tiled_pv(TiledState& st, const Frag8<bf16>& pf, int lane) {
+  using namespace tiled;
+  const char* buf = kv_buf<BUF>();
+  const int g = lane >> 4, l16 = lane & 15;
+  // O^T += V^T P^T : 32 blocks of 16 latent dims over the tile's 32 tokens
+  // lane group g reads tokens 4g + s/4 (+16 for the second read); source lane s supplies dims
+  // 16 d + 4 (s % 4) .. +3 = chunk 2d + (s%4)/2, byte (s % 2) * 8
+  const int x = (4 * g + (l16 >> 2)) & 7;
+  const int clo = (l16 & 3) >> 1;
+  const char* vb[4];
+#pragma unroll
+  for (int par = 0; par < 4; ++par)
+    vb[par] = buf + (4 * g + (l16 >> 2)) * kRow + (l16 & 1) * 8 + ((2 * par + clo) ^ x) * 16;
+  shortx4 vlo[3], vhi[3];  // fragments two blocks ahead are in flight
+#pragma unroll
+  for (int d0 = 0; d0 < 2; ++d0) {
+    vlo[d0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)vb[d0]);
+    vhi[d0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)(vb[d0] + 16 * kRow));
+  }
+#pragma unroll
+  for (int d = 0; d < 32; ++d) {
+    if (d + 2 < 32) {
+      const char* pv = vb[(d + 2) & 3] + 128 * ((d + 2) >> 2);
+      vlo[(d + 2) % 3] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)pv);
+      vhi[(d + 2) % 3] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)(pv + 16 * kRow));
+    }
+    Frag8<bf16> a;
+    a.v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vlo[d % 3], vhi[d % 3], 0, 1, 2, 3, 4, 5, 6, 7));
+    st.o[d] = mma16(a, pf, st.o[d]);
+  }
+}
+
 template <int BUF>
 __device__ __forceinline__ void tiled_compute(const Frag8<bf16> (&q)[18], TiledState& st, int t, int kv_len,
                                               float scale_log2, int lane) {
@@ -334,32 +369,7 @@ __device__ __forceinline__ void tiled_compute(const Frag8<bf16> (&q)[18], TiledS
       st.l_part += (float)e;
       pf.v[tb * 4 + j] = e;
     }
-  // ---- O^T += V^T P^T : 32 blocks of 16 latent dims over the tile's 32 tokens
-  // lane group g reads tokens 4g + s/4 (+16 for the second read); source lane s supplies dims
-  // 16 d + 4 (s % 4) .. +3 = chunk 2d + (s%4)/2, byte (s % 2) * 8
-  const int x = (4 * g + (l16 >> 2)) & 7;
-  const int clo = (l16 & 3) >> 1;
-  const char* vb[4];
-#pragma unroll
-  for (int par = 0; par < 4; ++par)
-    vb[par] = buf + (4 * g + (l16 >> 2)) * kRow + (l16 & 1) * 8 + ((2 * par + clo) ^ x) * 16;
-  shortx4 vlo[3], vhi[3];  // fragments two blocks ahead are in flight
-#pragma unroll
-  for (int d0 = 0; d0 < 2; ++d0) {
-    vlo[d0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)vb[d0]);
-    vhi[d0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)(vb[d0] + 16 * kRow));
-  }
-#pragma unroll
-  for (int d = 0; d < 32; ++d) {
-    if (d + 2 < 32) {
-      const char* pv = vb[(d + 2) & 3] + 128 * ((d + 2) >> 2);
-      vlo[(d + 2) % 3] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)pv);
-      vhi[(d + 2) % 3] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)(pv + 16 * kRow));
-    }
-    Frag8<bf16> a;
-    a.v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vlo[d % 3], vhi[d % 3], 0, 1, 2, 3, 4, 5, 6, 7));
-    st.o[d] = mma16(a, pf, st.o[d]);
-  }
+  tiled_pv<BUF>(st, pf, lane);
 }
 
 // Two tiles per barrier: tiles t and t+1 sit in ring buffers B0 and B0+1 (B0 = 0 or 2), and the
@@ -521,6 +531,351 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeAttnParams p)
 }
 
 // ----------------------------------------------------------------------------- host side
+// ----------------------------------------------------------------------------- fp8 cache
+// The tiled kernel over the fp8 cache (per-token-scaled e4m3 codes, one scale per part of the
+// entry).  A tile is 32 tokens x 576 code bytes plus their 32 (s_c, s_r) pairs: half the bytes.
+//   * S^T = K Q^T runs on fp8 MFMAs straight from the codes: the query of each head is split
+//     into two e4m3 parts sharing one scale, q / s_q = hi + lo (hi the nearest code, lo the code
+//     of the remainder), which keeps about bf16 precision;
+//     s_tj = scale s_q (s_c,j (q . code_c,j) + s_r,j (q^R . code_r,j)).  The latent part uses the
+//     16x16x128 f8f6f4 MFMA (twice the rate of the 16x16x32 fp8 form), the rope part the
+//     16x16x32 fp8 one.
+//   * For O^T = V^T P^T each pair of tiles is first converted once, by the whole workgroup, into
+//     bf16 tiles holding value(code_c) s_c (the layout of the bf16 kernel's tiles); the PV product
+//     is then the bf16 kernel's.  Converting per wave instead would repeat it eight times.
+namespace tiled8 {
+constexpr int kT = 32;
+constexpr int kNBuf = 4;
+constexpr int kRow = 576;                  // code bytes per entry (36 chunks)
+constexpr int kCodes = kT * kRow;          // 18432
+constexpr int kScales = kT * 8;            // 256: (s_c, s_r) per token
+constexpr int kBuf = kCodes + kScales;
+constexpr int kWaves = 8;
+constexpr int kCopies = kCodes / 1024;     // 18: waves 0-1 issue 3, waves 2-7 issue 2
+constexpr float kLazy = 8.f;
+// chunk c of token row t sits at slot c ^ swz(t): the 16 rows of a K fragment read fall in distinct
+// banks
+__device__ __forceinline__ int swz(int t) { return ((t >> 2) & 3) ^ (((t >> 4) & 1) << 1); }
+}  // namespace tiled8
+
+__shared__ __attribute__((aligned(1024))) char g_kv8_0[tiled8::kBuf];
+__shared__ __attribute__((aligned(1024))) char g_kv8_1[tiled8::kBuf];
+__shared__ __attribute__((aligned(1024))) char g_kv8_2[tiled8::kBuf];
+__shared__ __attribute__((aligned(1024))) char g_kv8_3[tiled8::kBuf];
+template <int BUF>
+__device__ __forceinline__ char* kv8_buf() {
+  return BUF == 0 ? g_kv8_0 : (BUF == 1 ? g_kv8_1 : (BUF == 2 ? g_kv8_2 : g_kv8_3));
+}
+
+struct Tiled8Ctx {
+  const uint8_t* pool;
+  const float* scales;
+  const int32_t* bt;
+  int bs, kv_len;
+};
+
+// This wave's share of tile `tile` into buffer BUF: code copies P = w, w + 8, w + 16 (< 18) and, for
+// wave 7, the tile's 256 bytes of scales (4 bytes per lane).
+template <int BUF>
+__device__ __forceinline__ void issue_tile8(const Tiled8Ctx& c, int tile, int w, int lane) {
+  using namespace tiled8;
+  char* dst = kv8_buf<BUF>();
+  const int tok0 = tile * kT;
+  const int blk = tok0 / c.bs;
+  const int64_t slot0 = (int64_t)c.bt[blk] * c.bs + (tok0 - blk * c.bs);
+  const __amdgpu_buffer_rsrc_t codes = dma_span(c.pool + slot0 * kRow, kCodes);
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const int P = i * kWaves + w;
+    if (P < kCopies) {
+      const int byte = P * 1024 + ln * 16;
+      const int t = byte / kRow, sl = (byte - t * kRow) >> 4;
+      dma16(codes, t * kRow + ((sl ^ swz(t)) << 4), (lds_void_t*)(dst + P * 1024));
+    }
+  }
+  if (w == kWaves - 1) {
+    const __amdgpu_buffer_rsrc_t sc = dma_span(c.scales + 2 * slot0, kScales);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(sc, (lds_void_t*)(dst + kCodes), 4, ln * 4, 0, 0, 0);
+  }
+}
+
+// The latent codes of fp8 tile FB as bf16 values (exact: every e4m3 value is a bf16 value) into
+// bf16 tile VB (rows of 1152 bytes, chunk c of row r at slot c ^ (r & 7)); the token's scale s_c
+// goes into P instead.  32 rows x 64 chunks of 8 codes: thread tid takes chunk tid % 64 of rows
+// tid / 64 + 8 i.
+template <int FB, int VB>
+__device__ __forceinline__ void convert_tile8(int tid) {
+  using namespace tiled8;
+  asm volatile("" : "+v"(tid));
+  const char* src = kv8_buf<FB>();
+  char* dst = kv_buf<VB>();
+  const int t0 = tid >> 6, c = tid & 63;
+  uint2 raw[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + 8 * i;
+    raw[i] = *reinterpret_cast<const uint2*>(src + t * kRow + (((c >> 1) ^ swz(t)) << 4) + (c & 1) * 8);
+  }
+  char* out = dst + t0 * tiled::kRow + ((c ^ (t0 & 7)) << 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    bf16x8 v;
+    const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[i].x, 1.f, false);
+    const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[i].x, 1.f, true);
+    const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[i].y, 1.f, false);
+    const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[i].y, 1.f, true);
+    v[0] = p0[0];
+    v[1] = p0[1];
+    v[2] = p1[0];
+    v[3] = p1[1];
+    v[4] = p2[0];
+    v[5] = p2[1];
+    v[6] = p3[0];
+    v[7] = p3[1];
+    *reinterpret_cast<bf16x8*>(out + 8 * i * tiled::kRow) = v;
+  }
+}
+
+struct QFp8 {
+  intx8 c_hi[4], c_lo[4];  // latent part, chunk kc: codes of dims 128 kc + 32 g .. +31
+  long r_hi[2], r_lo[2];   // rope part, chunk kr: codes of rope dims 32 kr + 8 g .. +7
+  float s;                 // the head's query scale
+};
+
+template <int FB, int VB>
+__device__ __forceinline__ void tiled8_compute(const QFp8& q, TiledState& st, int t, int kv_len, float scale_log2,
+                                               int lane) {
+  using namespace tiled8;
+  const char* buf = kv8_buf<FB>();
+  asm volatile("" : "+v"(lane));
+  const int g = lane >> 4, l16 = lane & 15;
+  // ---- S^T = K Q^T per part: lane holds head l16, tokens 16 tb + 4 g + j.  The k split of a
+  // 16x16x128 MFMA only has to match between its operands: lane group g gives 32 consecutive
+  // dims of the chunk for both K (two 16-byte slots of the row) and Q.
+  floatx4 scc[2] = {floatx4{0, 0, 0, 0}, floatx4{0, 0, 0, 0}};
+  floatx4 scr[2] = {floatx4{0, 0, 0, 0}, floatx4{0, 0, 0, 0}};
+  {
+    const char* rows[2] = {buf + l16 * kRow, buf + (16 + l16) * kRow};
+    const int sw[2] = {swz(l16), swz(16 + l16)};
+    auto kfrag = [&](int kc, int tb) {
+      const int ch = 8 * kc + 2 * g;
+      const intx4 x = *reinterpret_cast<const intx4*>(rows[tb] + ((ch ^ sw[tb]) << 4));
+      const intx4 y = *reinterpret_cast<const intx4*>(rows[tb] + (((ch + 1) ^ sw[tb]) << 4));
+      return intx8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+    };
+    intx8 a[2];
+    a[0] = kfrag(0, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {  // (chunk, token block) = (i / 2, i % 2)
+      if (i + 1 < 8) a[(i + 1) & 1] = kfrag((i + 1) >> 1, (i + 1) & 1);
+      floatx4& acc = scc[i & 1];
+      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i & 1], q.c_hi[i >> 1], acc, 0, 0, 0, 127, 0, 127);
+      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i & 1], q.c_lo[i >> 1], acc, 0, 0, 0, 127, 0, 127);
+    }
+    // rope part: 8 codes of dims 32 kr + 8 g: half (g & 1) of slot 32 + 2 kr + (g >> 1)
+#pragma unroll
+    for (int kr = 0; kr < 2; ++kr)
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        const int ch = 32 + 2 * kr + (g >> 1);
+        const long k8 = *reinterpret_cast<const long*>(rows[tb] + ((ch ^ sw[tb]) << 4) + (g & 1) * 8);
+        scr[tb] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(k8, q.r_hi[kr], scr[tb], 0, 0, 0);
+        scr[tb] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(k8, q.r_lo[kr], scr[tb], 0, 0, 0);
+      }
+  }
+  // ---- per-token and per-head scales; lazy online softmax
+  float lmax = -INFINITY;
+  float sc[2][4], s_lat[2][4];
+  const bool full = (t + 1) * kT <= kv_len;
+  const float qs = q.s * scale_log2;
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb) {
+    const float4* sp = reinterpret_cast<const float4*>(buf + kCodes + (16 * tb + 4 * g) * 8);
+    const float4 u0 = sp[0], u1 = sp[1];  // (s_c, s_r) of tokens +0 .. +3
+    s_lat[tb][0] = u0.x;
+    s_lat[tb][1] = u0.z;
+    s_lat[tb][2] = u1.x;
+    s_lat[tb][3] = u1.z;
+    const float srs[4] = {u0.y, u0.w, u1.y, u1.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float v = (s_lat[tb][j] * scc[tb][j] + srs[j] * scr[tb][j]) * qs;
+      if (!full && t * kT + tb * 16 + 4 * g + j >= kv_len) v = -INFINITY;
+      sc[tb][j] = v;
+      lmax = fmaxf(lmax, v);
+    }
+  }
+  if (__builtin_amdgcn_ballot_w64(lmax > st.m_ref + kLazy) != 0) {  // rare: raise the reference
+    float hmax = wave_max_xor(lmax, 16);
+    hmax = wave_max_xor(hmax, 32);
+    const float m_new = fmaxf(st.m_ref, hmax);
+    const float alpha = __builtin_amdgcn_exp2f(st.m_ref - m_new);  // -inf -> 0
+    st.l_part *= alpha;
+#pragma unroll
+    for (int d = 0; d < 32; ++d) st.o[d] *= alpha;
+    st.m_ref = m_new;
+  }
+  Frag8<bf16> pf;  // slot s = token 16 (s/4) + 4g + s%4: the weight times the token's s_c
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float e = __builtin_amdgcn_exp2f(sc[tb][j] - st.m_ref);  // argument <= 8
+      st.l_part += e;
+      pf.v[tb * 4 + j] = (bf16)(e * s_lat[tb][j]);
+    }
+  tiled_pv<VB>(st, pf, lane);
+}
+
+// Two fp8 tiles per barrier (fp8 buffers B0, B0+1; bf16 tiles 0 and 1): wait for them, issue the
+// next pair, convert the pair's latent parts to bf16 (all waves), then multiply both tiles.
+template <int B0>
+__device__ __forceinline__ void tiled8_pair(const Tiled8Ctx& c, const QFp8& q, TiledState& st, int t, int t_end,
+                                            float scale_log2, int w, int lane, int tid) {
+  using namespace tiled8;
+  MLA_TILE_BARRIER(waitcnt_vm(0));  // the pair has landed; every wave is done with the last pair
+  if (t + 2 < t_end) issue_tile8<(B0 + 2) % kNBuf>(c, t + 2, w, lane);
+  if (t + 3 < t_end) issue_tile8<(B0 + 3) % kNBuf>(c, t + 3, w, lane);
+  const int last = min(t + 1, t_end - 1);  // only the sequence's last tile can be partial
+  const int valid = c.kv_len - last * kT;
+  if (valid < kT) {  // rows past the end of the context: zero codes and scales (uniform branch)
+    char* buf = last == t ? kv8_buf<B0>() : kv8_buf<B0 + 1>();
+    for (int i = tid; i < (kT - valid) * (kRow / 16); i += 64 * kWaves) st16(buf + valid * kRow + i * 16, zero16());
+    if (tid < (kT - valid) * 2) reinterpret_cast<float*>(buf + kCodes)[valid * 2 + tid] = 0.f;
+    MLA_TILE_BARRIER(kWaitLgkm0);
+  }
+  convert_tile8<B0, 0>(tid);
+  if (t + 1 < t_end) convert_tile8<B0 + 1, 1>(tid);
+  MLA_TILE_BARRIER(kWaitLgkm0);
+  tiled8_compute<B0, 0>(q, st, t, c.kv_len, scale_log2, lane);
+  if (t + 1 < t_end) tiled8_compute<B0 + 1, 1>(q, st, t + 1, c.kv_len, scale_log2, lane);
+}
+
+__global__ void __launch_bounds__(512)
+    decode_attn_fp8_kernel(DecodeAttnParams p, int HG, const int32_t* __restrict__ block_table) {
+  using namespace tiled8;
+  const int units = p.B * p.splits;
+  const int grp = blockIdx.x / (8 * HG), rem = blockIdx.x % (8 * HG);
+  const int hg = rem / 8, unit = grp * 8 + rem % 8;
+  if (unit >= units) return;
+  const int b = unit / p.splits, split = unit % p.splits;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4;
+  const int head = hg * (16 * kWaves) + w * 16 + (lane & 15);
+  const bool valid_head = head < p.n_h;
+
+  Tiled8Ctx c;
+  c.pool = reinterpret_cast<const uint8_t*>(p.pool);
+  c.scales = p.scales;
+  c.bt = block_table + (int64_t)b * p.max_blocks;
+  c.bs = p.block_size;
+  c.kv_len = p.lens[b] + (p.lens_plus_one ? 1 : 0);
+  const int ntiles = (c.kv_len + kT - 1) / kT;
+  const int tps = p.tokens_per_split / kT;
+  const int t_begin = split * tps;
+  const int t_end = min(ntiles, t_begin + tps);
+
+  // the head's query as hi + lo e4m3 codes with one scale: s = amax / 448 over the head's 576
+  // values (the head's four lane groups), hi = e4m3(q / s), lo = e4m3(q / s - hi)
+  QFp8 q;
+  {
+    const bf16* qrow = reinterpret_cast<const bf16*>(p.q) + ((int64_t)b * p.n_h + (valid_head ? head : 0)) * 576;
+    Frag8<bf16> qv[18];  // 0..15: latent dims 128 (i / 4) + 32 g + 8 (i % 4); 16, 17: rope dims 32 kr + 8 g
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 18; ++i) {
+      const int off = i < 16 ? 128 * (i >> 2) + 32 * g + 8 * (i & 3) : 512 + 32 * (i - 16) + 8 * g;
+      if (valid_head) load8(qv[i], qrow + off);
+      else zero8(qv[i]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)qv[i].v[e]));
+    }
+    amax = wave_max_xor(amax, 16);
+    amax = wave_max_xor(amax, 32);
+    q.s = amax / 448.f;
+    const float inv = amax > 0.f ? 448.f / amax : 0.f;
+    // 4 values -> one word of hi codes and one of lo codes
+    auto split4 = [&](const Frag8<bf16>& v, int h, uint32_t& hw, uint32_t& lw) {
+      float x[4], r[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = fminf(fmaxf((float)v.v[4 * h + e] * inv, -448.f), 448.f);
+      int pk = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+      pk = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], pk, true);
+      const floatx2 b0 = __builtin_amdgcn_cvt_pk_f32_fp8(pk, false);
+      const floatx2 b1 = __builtin_amdgcn_cvt_pk_f32_fp8(pk, true);
+      r[0] = x[0] - b0[0];
+      r[1] = x[1] - b0[1];
+      r[2] = x[2] - b1[0];
+      r[3] = x[3] - b1[1];
+      int pl = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
+      pl = __builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], pl, true);
+      hw = (uint32_t)pk;
+      lw = (uint32_t)pl;
+    };
+#pragma unroll
+    for (int i = 0; i < 18; ++i) {
+      uint32_t h0, l0, h1, l1;
+      split4(qv[i], 0, h0, l0);
+      split4(qv[i], 1, h1, l1);
+      if (i < 16) {
+        q.c_hi[i >> 2][2 * (i & 3)] = (int)h0;
+        q.c_hi[i >> 2][2 * (i & 3) + 1] = (int)h1;
+        q.c_lo[i >> 2][2 * (i & 3)] = (int)l0;
+        q.c_lo[i >> 2][2 * (i & 3) + 1] = (int)l1;
+      } else {
+        q.r_hi[i - 16] = (long)(((uint64_t)h1 << 32) | h0);
+        q.r_lo[i - 16] = (long)(((uint64_t)l1 << 32) | l0);
+      }
+    }
+  }
+  TiledState st;
+#pragma unroll
+  for (int d = 0; d < 32; ++d) st.o[d] = floatx4{0, 0, 0, 0};
+  st.m_ref = -INFINITY;
+  st.l_part = 0.f;
+
+  if (t_begin < t_end) issue_tile8<0>(c, t_begin, w, lane);
+  if (t_begin + 1 < t_end) issue_tile8<1>(c, t_begin + 1, w, lane);
+  for (int t = t_begin; t < t_end; t += kNBuf) {
+    tiled8_pair<0>(c, q, st, t, t_end, p.scale_log2, w, lane, tid);
+    if (t + 2 < t_end) tiled8_pair<2>(c, q, st, t + 2, t_end, p.scale_log2, w, lane, tid);
+  }
+  float l_run = wave_sum_xor(st.l_part, 16);
+  l_run = wave_sum_xor(l_run, 32);
+  const float m_run = st.m_ref;
+
+  if (!valid_head) return;
+  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  if (p.splits == 1) {
+    bf16* out = reinterpret_cast<bf16*>(p.o_hat) + ((int64_t)b * p.n_h + head) * 512;
+#pragma unroll
+    for (int d = 0; d < 32; ++d) {
+      bf16x4 v;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = (bf16)(st.o[d][r] * inv);
+      *reinterpret_cast<bf16x4*>(out + d * 16 + 4 * g) = v;
+    }
+    if (p.lse && g == 0) p.lse[(int64_t)b * p.n_h + head] = (m_run + log2f(l_run)) * 0.69314718055994531f;
+    return;
+  }
+  const int64_t pi = ((int64_t)b * p.splits + split) * p.n_h + head;
+  if (g == 0) {
+    p.part_m[pi] = m_run;
+    p.part_l[pi] = l_run;
+  }
+  bf16* po = reinterpret_cast<bf16*>(p.part_o) + pi * 512;
+#pragma unroll
+  for (int d = 0; d < 32; ++d) {
+    bf16x4 v;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = (bf16)(st.o[d][r] * inv);
+    *reinterpret_cast<bf16x4*>(po + d * 16 + 4 * g) = v;
+  }
+}
+
 bool decode_tiled(DType t, int d_c, int d_hr, int block_size) {
   return t == DType::BF16 && d_c == 512 && d_hr == 64 && block_size % tiled::kT == 0;
 }
@@ -552,6 +907,19 @@ hipError_t launch(const DecodeAttnParams& p, hipStream_t s) {
 }  // namespace
 
 hipError_t decode_attention(DType t, const DecodeAttnParams& p, hipStream_t s) {
+  if (p.fp8) {
+    if (t != DType::BF16 || p.d_c != 512 || p.d_hr != 64 || p.block_size % tiled8::kT != 0 || !p.scales)
+      return hipErrorInvalidValue;
+    const int HG = (p.n_h + 16 * tiled8::kWaves - 1) / (16 * tiled8::kWaves);
+    const int units = p.B * p.splits;
+    if (units == 0) return hipSuccess;
+    const int blocks = (units + 7) / 8 * 8 * HG;
+    hipLaunchKernelGGL(decode_attn_fp8_kernel, dim3(blocks), dim3(64 * tiled8::kWaves), 0, s, p, HG, p.block_table);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.splits == 1) return e;
+    hipLaunchKernelGGL((decode_combine_kernel<bf16, bf16, 512>), dim3((p.B * p.n_h + 3) / 4), dim3(256), 0, s, p);
+    return hipGetLastError();
+  }
   if (decode_tiled(t, p.d_c, p.d_hr, p.block_size)) {
     const int HG = (p.n_h + 16 * tiled::kWaves - 1) / (16 * tiled::kWaves);
     const int units = p.B * p.splits;

@@ -77,6 +77,19 @@ hipError_t absorb_run(const void* qc, const void* w_uk, void* qhat, int B, int n
 bool uv_ok(DType t, int d_h, int d_c);
 hipError_t uv_run(const void* ohat, const void* w_uv, void* o, float* o32, int B, int n_h, int d_h,
                   hipStream_t s);
+// fp8 cache quantiser (latent_fp8.hip).  Destination of entry row r: dense row r of `codes` /
+// `scales` when block_table is null, else the paged slot of (row_seq ? row_seq[r] : r, row_pos[r]).
+struct QuantDst {
+  uint8_t* codes = nullptr;  // [..][576] e4m3 codes
+  float* scales = nullptr;   // [..][2] (s_c, s_r)
+  const int32_t* block_table = nullptr;
+  int max_blocks = 0, block_size = 1;
+  const int32_t* row_seq = nullptr;
+  const int32_t* row_pos = nullptr;
+};
+bool fp8_cache_ok(int d_c, int d_hr);
+// Quantises n bf16 entries (rows src_ld elements apart) into dst.
+hipError_t quantize_entries_run(const void* src, int64_t src_ld, int n, const QuantDst& dst, hipStream_t s);
 // Largest partial_bytes of gemm_plan(m, ...) over 1 <= m <= M (workspace sized for M then also
 // serves every smaller call).
 size_t gemm_partial_bound(int M, int N, int K, int batch, int cus, bool skinny_ok);
@@ -109,6 +122,8 @@ struct DecodeAttnParams {
   void* part_o;           // [B][splits][n_h][d_c]: O_s / l_s (fp32, or bf16 for the tiled kernel)
   void* o_hat;            // [B][n_h][d_c] output (element type)
   float* lse;             // optional [B][n_h], natural log
+  bool fp8 = false;       // pool holds e4m3 codes, with per-token (s_c, s_r) in scales
+  const float* scales = nullptr;  // [num_blocks][block_size][2]
 };
 
 bool decode_supported(int d_c, int d_hr);

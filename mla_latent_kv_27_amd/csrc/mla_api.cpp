@@ -49,8 +49,14 @@ int validate_dims(const mla_dims* d) {
   const int epc = d->dtype == MLA_BF16 ? 8 : 4;
   if (d->d_model % epc || d->d_h % epc || d->d_c % epc || d->d_cq % epc || d->d_hr % 8)
     return MLA_ERR_UNSUPPORTED;
+  if (d->cache_dtype != 0 && d->cache_dtype != d->dtype) {
+    if (d->cache_dtype != MLA_FP8_E4M3 || d->dtype != MLA_BF16) return MLA_ERR_INVALID_ARG;
+    if (!fp8_cache_ok(d->d_c, d->d_hr)) return MLA_ERR_UNSUPPORTED;
+  }
   return MLA_OK;
 }
+
+bool fp8_cache(const mla_dims* d) { return d->cache_dtype == MLA_FP8_E4M3; }
 
 inline DType dt(const mla_dims* d) { return d->dtype == MLA_BF16 ? DType::BF16 : DType::F32; }
 inline int q_in(const mla_dims* d) { return d->d_cq > 0 ? d->d_cq : d->d_model; }
@@ -64,7 +70,7 @@ inline float scale_of(const mla_dims* d) {
 int validate_cache(const mla_dims* d, const mla_paged_cache* c) {
   if (!c || !c->pool || !c->block_table) return MLA_ERR_INVALID_ARG;
   if (c->num_blocks <= 0 || c->block_size <= 0 || c->max_blocks_per_seq <= 0) return MLA_ERR_INVALID_ARG;
-  (void)d;
+  if (fp8_cache(d) && !c->scales) return MLA_ERR_INVALID_ARG;
   return MLA_OK;
 }
 
@@ -86,6 +92,7 @@ int auto_splits(const mla_dims* d, int batch, int max_ctx_len, int cus) {
 struct AppendWs {
   float2* rope;
   float* partial;
+  void* staged;  // fp8 cache: the bf16 entries before quantisation [n][entry]
   GemmPlan plan;
 };
 AppendWs carve_append(Carve& cv, const mla_dims* d, int n, int cus) {
@@ -93,6 +100,7 @@ AppendWs carve_append(Carve& cv, const mla_dims* d, int n, int cus) {
   w.plan = gemm_plan(n, entry(d), d->d_model, 1, cus, sk(d));
   w.rope = cv.take<float2>((size_t)n * (d->d_hr / 2) * sizeof(float2));
   w.partial = cv.take<float>(gemm_partial_bound(n, entry(d), d->d_model, 1, cus, sk(d)));
+  w.staged = fp8_cache(d) ? cv.take<char>((size_t)n * entry(d) * 2) : nullptr;
   return w;
 }
 
@@ -158,6 +166,7 @@ AttnWs carve_attn(Carve& cv, const mla_dims* d, int B, int max_kv_len, int split
 struct DecodeWs {
   float2* rope;
   void *cq, *qc, *qcat, *ohat, *o;
+  void* staged;  // fp8 cache: the new tokens' bf16 entries before quantisation
   AttnWs attn;
   float* partial;
   DecodeGemms gm;
@@ -171,6 +180,7 @@ DecodeWs carve_decode(Carve& cv, const mla_dims* d, int B, int max_ctx_len, int 
   w.cq = cv.take<char>((size_t)B * d->d_cq * es);
   w.qc = cv.take<char>((size_t)B * d->n_h * d->d_h * es);
   w.qcat = cv.take<char>((size_t)B * d->n_h * entry(d) * es);
+  w.staged = fp8_cache(d) ? cv.take<char>((size_t)B * entry(d) * 2) : nullptr;
   w.ohat = cv.take<char>((size_t)B * d->n_h * d->d_c * es);
   w.o = cv.take<char>((size_t)B * d->n_h * d->d_h * es);
   w.attn = carve_attn(cv, d, B, max_ctx_len + 1, splits, cus);
@@ -249,9 +259,31 @@ Epilogue cache_epilogue(const mla_dims* d, const mla_paged_cache* c, const float
   return e;
 }
 
+// fp8 cache: dense bf16 rows [c^KV | RoPE'd k^R] for the quantiser.
+Epilogue staged_epilogue(const mla_dims* d, void* staged, const float2* rope) {
+  Epilogue e;
+  e.C = staged;
+  e.ldc = entry(d);
+  e.rope_col0 = d->d_c;
+  e.d_hr = d->d_hr;
+  e.rope_tab = rope;
+  return e;
+}
+QuantDst quant_dst(const mla_paged_cache* c, const int32_t* seq, const int32_t* pos) {
+  QuantDst q;
+  q.codes = reinterpret_cast<uint8_t*>(c->pool);
+  q.scales = c->scales;
+  q.block_table = c->block_table;
+  q.max_blocks = c->max_blocks_per_seq;
+  q.block_size = c->block_size;
+  q.row_seq = seq;
+  q.row_pos = pos;
+  return q;
+}
+
 int run_cache_writer(const mla_dims* d, const mla_weights* w, const mla_paged_cache* c, const void* h, int n,
                      const int32_t* seq, const int32_t* pos, const float2* rope, const GemmPlan& plan,
-                     float* partial, hipStream_t s) {
+                     float* partial, void* staged, hipStream_t s) {
   GemmParams g;
   g.A = h;
   g.lda = d->d_model;
@@ -262,6 +294,12 @@ int run_cache_writer(const mla_dims* d, const mla_weights* w, const mla_paged_ca
   g.M = n;
   g.N = entry(d);
   g.K = d->d_model;
+  if (fp8_cache(d)) {  // bf16 entries to the staging rows, then quantised into their slots
+    g.epi = staged_epilogue(d, staged, rope);
+    MLA_HIP(gemm_run(dt(d), g, plan, partial, s));
+    MLA_HIP(quantize_entries_run(staged, entry(d), n, quant_dst(c, seq, pos), s));
+    return MLA_OK;
+  }
   g.epi = cache_epilogue(d, c, rope, seq, pos);
   MLA_HIP(gemm_run(dt(d), g, plan, partial, s));
   return MLA_OK;
@@ -330,7 +368,21 @@ int mla_cache_append(const mla_dims* d, const mla_weights* w, const mla_paged_ca
   AppendWs ws = carve_append(cv, d, n, cus);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   MLA_HIP(rope_table(pos, n, d->d_hr, d->rope_base, ws.rope, s));
-  return run_cache_writer(d, w, c, h, n, seq_idx, pos, ws.rope, ws.plan, ws.partial, s);
+  return run_cache_writer(d, w, c, h, n, seq_idx, pos, ws.rope, ws.plan, ws.partial, ws.staged, s);
+}
+
+int mla_quantize_entries(const mla_dims* d, const void* entries, int32_t n, uint8_t* codes, float* scales,
+                         void* stream) {
+  int st = validate_dims(d);
+  if (st != MLA_OK) return st;
+  if (!fp8_cache(d) || n < 0) return MLA_ERR_INVALID_ARG;
+  if (n == 0) return MLA_OK;
+  if (!entries || !codes || !scales) return MLA_ERR_INVALID_ARG;
+  QuantDst q;
+  q.codes = codes;
+  q.scales = scales;
+  MLA_HIP(quantize_entries_run(entries, entry(d), n, q, reinterpret_cast<hipStream_t>(stream)));
+  return MLA_OK;
 }
 
 int mla_decode_attention(const mla_dims* d, const mla_paged_cache* c, const void* q, int32_t batch,
@@ -351,6 +403,8 @@ int mla_decode_attention(const mla_dims* d, const mla_paged_cache* c, const void
   DecodeAttnParams a{};
   a.q = q;
   a.pool = c->pool;
+  a.fp8 = fp8_cache(d);
+  a.scales = c->scales;
   a.block_table = c->block_table;
   a.max_blocks = c->max_blocks_per_seq;
   a.block_size = c->block_size;
@@ -408,14 +462,15 @@ int mla_decode(const mla_dims* d, const mla_weights* w, const mla_paged_cache* c
       g.B2 = w->W_KR;
       g.epi = dense(ws.cq, d->d_cq);
       g.E0 = d->d_cq;
-      g.epi2 = cache_epilogue(d, c, ws.rope, nullptr, ctx_lens);
+      g.epi2 = fp8_cache(d) ? staged_epilogue(d, ws.staged, ws.rope) : cache_epilogue(d, c, ws.rope, nullptr, ctx_lens);
       qin = ws.cq;
     } else {
       g.B0 = w->W_DKV; g.N0 = d->d_c;
       g.B1 = w->W_KR;
-      g.epi = cache_epilogue(d, c, ws.rope, nullptr, ctx_lens);
+      g.epi = fp8_cache(d) ? staged_epilogue(d, ws.staged, ws.rope) : cache_epilogue(d, c, ws.rope, nullptr, ctx_lens);
     }
     MLA_HIP(gemm_run(t, g, ws.gm.kvq, ws.partial, s));
+    if (fp8_cache(d)) MLA_HIP(quantize_entries_run(ws.staged, E, B, quant_dst(c, nullptr, ctx_lens), s));
   }
   {  // [q^C | q^R] = [W_UQ; W_QR] c^q: q^C to the workspace, RoPE'd q^R into columns
      // [d_c, d_c + d_hr) of each head's absorbed query row
@@ -445,6 +500,7 @@ int mla_decode(const mla_dims* d, const mla_weights* w, const mla_paged_cache* c
   {  // latent attention over ctx_lens[b] + 1 entries
     DecodeAttnParams a{};
     a.q = ws.qcat; a.pool = c->pool; a.block_table = c->block_table;
+    a.fp8 = fp8_cache(d); a.scales = c->scales;
     a.max_blocks = c->max_blocks_per_seq; a.block_size = c->block_size;
     a.lens = ctx_lens; a.lens_plus_one = true;
     a.B = B; a.n_h = d->n_h; a.d_c = d->d_c; a.d_hr = d->d_hr;
@@ -533,8 +589,11 @@ int mla_prefill(const mla_dims* d, const mla_weights* w, const mla_paged_cache* 
     g.epi = dense(ws.kvd, E);
     g.epi.rope_col0 = d->d_c; g.epi.d_hr = d->d_hr; g.epi.rope_tab = ws.rope;
     MLA_HIP(gemm_run(t, g, ws.kv_p, ws.partial, s));
-    MLA_HIP(scatter_rows(t, ws.kvd, M, E, c->pool, ws.seq, ws.pos, c->block_table, c->max_blocks_per_seq,
-                         c->block_size, s));
+    if (fp8_cache(d))
+      MLA_HIP(quantize_entries_run(ws.kvd, E, M, quant_dst(c, ws.seq, ws.pos), s));
+    else
+      MLA_HIP(scatter_rows(t, ws.kvd, M, E, c->pool, ws.seq, ws.pos, c->block_table, c->max_blocks_per_seq,
+                           c->block_size, s));
   }
   {  // k^C_i = W_UK_i c^KV, stored head-major [n_h][M][d_h]
     GemmParams g;

@@ -26,12 +26,13 @@ def to_device(x: np.ndarray, dims: S.Dims, device="cuda") -> torch.Tensor:
 class DeviceLayer:
     """One MLA layer's weights on the device plus the C structs describing them."""
 
-    def __init__(self, dims: S.Dims, W_np: dict, device="cuda"):
+    def __init__(self, dims: S.Dims, W_np: dict, device="cuda", cache_dtype=0):
+        """cache_dtype: 0 (the layer's dtype) or "fp8" (per-token-scaled e4m3 cache)."""
         self.dims = dims
         self.device = device
         self.W = {k: to_device(v, dims, device) for k, v in W_np.items()}
         self.cdims = make_dims(dims.d_model, dims.n_h, dims.d_h, dims.d_c, dims.d_cq, dims.d_hr, dims.dtype,
-                               dims.softmax_scale, dims.rope_base)
+                               dims.softmax_scale, dims.rope_base, cache_dtype)
         self.cweights = make_weights(self.W)
 
     def clone(self) -> "DeviceLayer":
@@ -47,22 +48,48 @@ class PagedPool:
     sequence b may hold.  Unused slots are filled with `fill` (NaN by default, so that a read of
     a slot outside a context shows up in the outputs)."""
 
-    def __init__(self, dims: S.Dims, capacity, block_size=64, device="cuda", fill=float("nan"), seed=S.SEED_PAGES):
+    def __init__(self, dims: S.Dims, capacity, block_size=64, device="cuda", fill=float("nan"), seed=S.SEED_PAGES,
+                 fp8=False):
+        """fp8: the pool holds e4m3 codes (unused slots 0x7F, a NaN code) with per-token scales."""
         table, nblk = S.block_table(capacity, block_size, seed)
         self.dims = dims
         self.block_size = block_size
-        self.pool = torch.full((nblk, block_size, dims.entry), fill, dtype=torch_dtype(dims), device=device)
+        self.fp8 = fp8
+        if fp8:
+            self.pool = torch.full((nblk, block_size, dims.entry), 0x7F, dtype=torch.uint8, device=device)
+            self.scales = torch.full((nblk, block_size, 2), fill, dtype=torch.float32, device=device)
+        else:
+            self.pool = torch.full((nblk, block_size, dims.entry), fill, dtype=torch_dtype(dims), device=device)
+            self.scales = None
         self.table_np = table
         self.block_table = torch.from_numpy(table).to(device)
-        self.ccache = make_cache(self.pool, self.block_table)
+        self.ccache = make_cache(self.pool, self.block_table, self.scales)
 
     def clone(self) -> "PagedPool":
         c = PagedPool.__new__(PagedPool)
-        c.dims, c.block_size, c.table_np = self.dims, self.block_size, self.table_np
+        c.dims, c.block_size, c.table_np, c.fp8 = self.dims, self.block_size, self.table_np, self.fp8
         c.pool = self.pool.clone()
+        c.scales = None if self.scales is None else self.scales.clone()
         c.block_table = self.block_table.clone()
-        c.ccache = make_cache(c.pool, c.block_table)
+        c.ccache = make_cache(c.pool, c.block_table, c.scales)
         return c
+
+    def _slots(self, b: int, n: int):
+        pos = np.arange(n)
+        blk = torch.from_numpy(self.table_np[b, pos // self.block_size].astype(np.int64)).to(self.pool.device)
+        off = torch.from_numpy((pos % self.block_size).astype(np.int64)).to(self.pool.device)
+        return blk, off
+
+    def read_codes(self, b: int, n: int):
+        """fp8 pool: codes [n, entry] uint8 and scales [n, 2] fp32 of positions 0..n-1 of sequence b."""
+        blk, off = self._slots(b, n)
+        return self.pool[blk, off].cpu().numpy(), self.scales[blk, off].cpu().numpy()
+
+    def write_codes(self, b: int, codes: torch.Tensor, scales: torch.Tensor) -> None:
+        """fp8 pool: stores device codes [n, entry] and scales [n, 2] at positions 0..n-1 of sequence b."""
+        blk, off = self._slots(b, codes.shape[0])
+        self.pool[blk, off] = codes
+        self.scales[blk, off] = scales
 
     def read_entries(self, b: int, n: int) -> np.ndarray:
         """Entries of positions 0..n-1 of sequence b, as fp32 numpy [n, d_c + d_hr]."""

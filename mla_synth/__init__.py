@@ -87,6 +87,7 @@ class Workload:
     block_size: int = 64
     hidden: str = "rmsnorm"  # "rmsnorm" (N(0,1) then RMS-normalised) | "normal002"
     weight_std: float = 0.02
+    cache: str = "native"  # "native" (the dims' dtype) | "fp8" (per-token-scaled e4m3 codes)
 
 
 TINY = Dims(d_model=64, n_h=4, d_h=16, d_c=32, d_cq=48, d_hr=8, dtype=F32)
@@ -99,6 +100,8 @@ WORKLOADS = {
     "v2lite_decode_b8_ctx4096": Workload("v2lite_decode_b8_ctx4096", V2_LITE, "decode", batch=8,
                                          ctx=4096),
     "v2_decode_b64_ctx8192": Workload("v2_decode_b64_ctx8192", V2, "decode", batch=64, ctx=8192),
+    "v2_decode_b64_ctx8192_fp8": Workload("v2_decode_b64_ctx8192_fp8", V2, "decode", batch=64, ctx=8192,
+                                          cache="fp8"),
     "v2_prefill_16384": Workload("v2_prefill_16384", V2, "prefill", batch=1, tokens=16384),
     "v2_long_decode_b4": Workload("v2_long_decode_b4", V2, "decode", batch=4, ctx_lo=32768,
                                   ctx_hi=131072),
@@ -209,3 +212,45 @@ def block_table(lens_plus_new, block_size: int, seed: int = SEED_PAGES):
         table[b, :k] = perm[o:o + k]
         o += k
     return table, max(total, 1)
+
+
+# ----------------------------------------------------------------------------- fp8 cache inputs
+SEED_FP8 = 5
+
+
+def fp8_codes(n: int, entry: int, seed: int = SEED_FP8) -> np.ndarray:
+    """Random e4m3 codes [n, entry] (uint8): random sign, exponent field 3..13, random mantissa,
+    about 2% zero codes; never the NaN codes."""
+    rng = np.random.default_rng(seed)
+    sign = rng.integers(0, 2, (n, entry)) << 7
+    e = rng.integers(3, 14, (n, entry)) << 3
+    m = rng.integers(0, 8, (n, entry))
+    codes = (sign | e | m).astype(np.uint8)
+    codes[rng.random((n, entry)) < 0.02] = 0
+    return codes
+
+
+def fp8_scales(n: int, seed: int = SEED_FP8 + 1) -> np.ndarray:
+    """Per-token (s_c, s_r) [n, 2] fp32: log-uniform in [2^-9, 2^-5], a few zero (all-zero parts)."""
+    rng = np.random.default_rng(seed)
+    s = np.exp2(rng.uniform(-9.0, -5.0, (n, 2))).astype(np.float32)
+    s[rng.random((n, 2)) < 0.01] = 0.0
+    return s
+
+
+def quantizer_rows(n: int, entry: int, d_c: int, seed: int = SEED_FP8 + 2) -> np.ndarray:
+    """bf16-exact rows [n, entry] for the fp8 quantiser: normal values at a per-row magnitude
+    10^U(-4, 2), with some all-zero parts, single outliers, and values spread down into the
+    subnormal range of the codes."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((n, entry)) * np.power(10.0, rng.uniform(-4, 2, (n, 1)))
+    x[0] = 0.0
+    if n > 1:
+        x[1, :d_c] = 0.0
+    if n > 2:
+        x[2, d_c:] = 0.0
+    for r in range(3, n, 7):
+        x[r, rng.integers(0, entry)] *= 1e3          # one outlier: everything else small
+    for r in range(5, n, 11):
+        x[r] *= np.exp2(rng.uniform(-14, 0, entry))  # wide dynamic range within the row
+    return round_bf16(x.astype(np.float32))

@@ -1,0 +1,131 @@
+"""GPU parity of the fp8 latent cache (per-token-scaled e4m3, see oracle/latent_fp8.py) through the
+C ABI: the quantiser bit-exact against the oracle, the attention core on synthetic fp8 caches
+(the oracle dequantises the same codes), the cache writer, and whole decode steps against the
+oracle's fp8 decode (which quantises its own entries)."""
+import numpy as np
+import pytest
+
+import mla_synth as S
+import oracle.latent_fp8 as F
+import oracle.mla_oracle as O
+from tests.gpu_util import check, have_gpu, torch
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not have_gpu(), reason="needs a GPU")]
+
+import mla_latent_kv_27_amd as M  # noqa: E402
+from mla_latent_kv_27_amd import workload as WL  # noqa: E402
+
+DIMS = {"v2": S.V2, "v2lite": S.V2_LITE}
+
+
+@pytest.mark.parametrize("n", [1, 37, 500])
+def test_quantizer_bit_exact(n):
+    dims = S.V2
+    cd = M.make_dims(dims.d_model, dims.n_h, dims.d_h, dims.d_c, dims.d_cq, dims.d_hr, dims.dtype,
+                     dims.softmax_scale, dims.rope_base, "fp8")
+    rows = S.quantizer_rows(n, dims.entry, dims.d_c, seed=100 + n)
+    x = torch.from_numpy(rows).to("cuda", torch.bfloat16)
+    codes = torch.empty((n, dims.entry), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((n, 2), dtype=torch.float32, device="cuda")
+    M.quantize_entries(cd, x, codes, scales)
+    torch.cuda.synchronize()
+    ref_codes, ref_scales = F.quantize_entries(rows, dims.d_c)
+    got_codes, got_scales = codes.cpu().numpy(), scales.cpu().numpy()
+    bad = np.argwhere(got_codes != ref_codes)
+    assert bad.size == 0, f"{len(bad)} codes differ, first at {bad[:3].tolist()}: " \
+        f"{got_codes[tuple(bad[0])]:#x} vs {ref_codes[tuple(bad[0])]:#x}"
+    assert np.array_equal(got_scales.view(np.uint32), ref_scales.view(np.uint32))
+
+
+def _fp8_attention_case(name, lens, splits, block=64, q_std=0.5):
+    dims = DIMS[name]
+    cd = M.make_dims(dims.d_model, dims.n_h, dims.d_h, dims.d_c, dims.d_cq, dims.d_hr, dims.dtype,
+                     dims.softmax_scale, dims.rope_base, "fp8")
+    B = len(lens)
+    pool = WL.PagedPool(dims, list(lens), block_size=block, fp8=True)
+    deq = []
+    for b, L in enumerate(lens):
+        codes = S.fp8_codes(L, dims.entry, seed=300 + b)
+        scales = S.fp8_scales(L, seed=400 + b)
+        pool.write_codes(b, torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda())
+        deq.append(F.dequantize(codes, scales, dims.d_c))
+    rng = np.random.default_rng(7)
+    q = S.to_dtype((rng.standard_normal((B, dims.n_h, dims.entry)) * q_std).astype(np.float32), dims.dtype)
+    kv = torch.tensor(np.asarray(lens, np.int32), device="cuda")
+    mx = int(max(lens))
+    ws = WL.ws_tensor(M.workspace_size(cd, M.OP_DECODE, batch=B, max_ctx_len=mx - 1, num_splits=splits))
+    oh = torch.empty((B, dims.n_h, dims.d_c), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, dims.n_h), dtype=torch.float32, device="cuda")
+    M.decode_attention(cd, pool.ccache, WL.to_device(q, dims), kv, mx, oh, ws, num_splits=splits, lse=lse)
+    torch.cuda.synchronize()
+    scale = O.softmax_scale(dims)
+    for b, L in enumerate(lens):
+        ref_o, ref_lse = O.latent_attention(q[b:b + 1], deq[b], np.array([L]), scale, dims.d_c)
+        check(oh[b].float().cpu().numpy(), ref_o[0], dims.dtype, f"{name} fp8 o_hat b={b} L={L}")
+        assert np.max(np.abs(lse[b].cpu().numpy() - ref_lse[0])) < 2e-2, f"{name} fp8 lse b={b}"
+
+
+@pytest.mark.parametrize("name,lens,splits", [("v2", [1, 31, 33, 64], 1), ("v2", [300, 1000], 0),
+                                              ("v2", [500, 777], 3), ("v2lite", [129, 2049], 4)])
+def test_fp8_attention_core_matches_oracle(name, lens, splits):
+    _fp8_attention_case(name, lens, splits)
+
+
+def test_fp8_attention_core_block_32():
+    _fp8_attention_case("v2", [95, 160], 2, block=32)
+
+
+def _append_context(layer, pool, lens, recipe):
+    WL.build_context(layer, pool, lens, recipe)
+
+
+@pytest.mark.parametrize("name", ["v2lite", "v2"])
+def test_fp8_cache_writer_codes(name):
+    dims = DIMS[name]
+    W = S.make_weights(dims)
+    layer = WL.DeviceLayer(dims, W, cache_dtype="fp8")
+    lens = [70, 131]
+    pool = WL.PagedPool(dims, lens, fp8=True)
+    _append_context(layer, pool, lens, "rmsnorm")
+    torch.cuda.synchronize()
+    for b, L in enumerate(lens):
+        h = S.hidden_history(dims, b, L, "rmsnorm")
+        ref_codes, ref_scales = F.quantize_entries(F.bf16_round(O.latent_entries(W, dims, h, np.arange(L))), dims.d_c)
+        got_codes, got_scales = pool.read_codes(b, L)
+        same = float(np.mean(got_codes == ref_codes))
+        # the entries themselves come from fp32 (device) vs fp64 (oracle) products: a bf16 entry
+        # may differ by one ulp, and then its code may move by one step
+        assert same >= 0.995, f"{name} b={b}: {same:.5f} of the codes equal"
+        d = np.abs(F.dequantize(got_codes, got_scales, dims.d_c) - F.dequantize(ref_codes, ref_scales, dims.d_c))
+        step = np.maximum(np.abs(F.dequantize(ref_codes, ref_scales, dims.d_c)) * 2.0 ** -3,
+                          np.repeat(ref_scales, [dims.d_c, dims.d_hr], axis=1) * 2.0 ** -9)
+        assert np.all(d <= 1.01 * step + 1e-30), f"{name} b={b}: a code off by more than one step"
+        assert np.allclose(got_scales, ref_scales, rtol=2e-2), f"{name} b={b}: scales"
+
+
+@pytest.mark.parametrize("name,lens", [("v2lite", [40, 333]), ("v2", [300, 1000])])
+def test_fp8_decode_end_to_end(name, lens):
+    dims = DIMS[name]
+    W = S.make_weights(dims)
+    layer = WL.DeviceLayer(dims, W, cache_dtype="fp8")
+    B = len(lens)
+    pool = WL.PagedPool(dims, [L + 1 for L in lens], fp8=True)
+    _append_context(layer, pool, lens, "rmsnorm")
+    h = S.hidden_step(dims, B, "rmsnorm")
+    ctx = torch.tensor(np.asarray(lens, np.int32), device="cuda")
+    ws = WL.decode_workspace(layer, B, max(lens))
+    u = torch.empty((B, dims.d_model), dtype=torch.bfloat16, device="cuda")
+    oh = torch.empty((B, dims.n_h, dims.d_h), dtype=torch.float32, device="cuda")
+    M.decode(layer.cdims, layer.cweights, pool.ccache, WL.to_device(h, dims), ctx, max(lens), u, ws, o_heads=oh)
+    torch.cuda.synchronize()
+    codes, scales = [], []
+    for b, L in enumerate(lens):
+        hh = S.hidden_history(dims, b, L, "rmsnorm")
+        c, s = F.quantize_entries(F.bf16_round(O.latent_entries(W, dims, hh, np.arange(L))), dims.d_c)
+        codes.append(c)
+        scales.append(s)
+    ref = F.mla_decode_fp8(W, dims, h, codes, scales)
+    check(oh.cpu().numpy(), ref["o"], dims.dtype, f"{name} fp8 decode o")
+    check(u.float().cpu().numpy(), ref["u"], dims.dtype, f"{name} fp8 decode u")
+    new_codes = np.stack([pool.read_codes(b, L + 1)[0][L] for b, L in enumerate(lens)])
+    assert np.mean(new_codes == ref["codes"]) >= 0.99, f"{name}: new entries' codes"
