@@ -45,6 +45,13 @@ class Dims:
     dtype: str = BF16
     rope_base: float = 10000.0
     softmax_scale: float = 0.0  # 0: the layer's default scale
+    # YaRN context extension (off unless rope_scale > 1): scale s, original context length L,
+    # ramp bounds alpha, beta, and the coefficient c of sqrt(t) = c ln s + 1
+    rope_scale: float = 1.0
+    rope_orig_ctx: int = 0
+    yarn_alpha: float = 1.0
+    yarn_beta: float = 32.0
+    yarn_mscale: float = 0.0707
 
     @property
     def entry(self) -> int:
@@ -93,6 +100,9 @@ class Workload:
 TINY = Dims(d_model=64, n_h=4, d_h=16, d_c=32, d_cq=48, d_hr=8, dtype=F32)
 V2_LITE = Dims(d_model=2048, n_h=16, d_h=128, d_c=512, d_cq=0, d_hr=64, dtype=BF16)
 V2 = Dims(d_model=5120, n_h=128, d_h=128, d_c=512, d_cq=1536, d_hr=64, dtype=BF16)
+# V2 with the long-context extension of section 3.1.4: s = 40 over a 4096-token original context
+V2_YARN = dataclasses.replace(V2, rope_scale=40.0, rope_orig_ctx=4096)
+TINY_YARN = dataclasses.replace(TINY, rope_scale=4.0, rope_orig_ctx=64)
 
 WORKLOADS = {
     "tiny_fp32": Workload("tiny_fp32", TINY, "prefill", batch=1, tokens=16, decode_steps=4,

@@ -29,6 +29,16 @@ notes):
     entry is laid out [c_KV | k_R].
   * "No query compression" (App. B.1, V2-Lite) means c^q := h.
   * Softmax over j in [1, t], inclusive of the token itself.
+  * YaRN (section 3.1.4: s = 40, alpha = 1, beta = 32, sqrt(t) = 0.0707 ln s + 1; the page
+    cites the YaRN paper for the rest), when the layer sets rope_scale s > 1: the "NTK-by-parts"
+    frequencies of that paper, measured against the original context length L.  For the pair
+    k with frequency theta_k, wavelength lambda_k = 2 pi / theta_k and r_k = L / lambda_k
+    rotations over L; gamma_k = 0 for r_k < alpha, 1 for r_k > beta, linear in between; the
+    pair rotates by (1 - gamma_k) theta_k / s + gamma_k theta_k.  Short wavelengths keep their
+    frequency, long ones are interpolated by s.  The logits are multiplied by
+    t = (0.0707 ln s + 1)^2 (the page names only sqrt(t) and says it adjusts the attention
+    entropy; applying it to the logit scale is the plain reading).  Both rope parts (q^R and the
+    shared k^R) use the same frequencies.
 
 Parity pins: every function here is checked by tests that do not reuse this
 code (a scalar brute-force layer on tiny inputs, reduction to textbook MHA, a
@@ -42,20 +52,41 @@ import numpy as np
 
 
 # ----------------------------------------------------------------------------- RoPE
-def rope_angles(pos, d_hr: int, base: float) -> np.ndarray:
-    """Angles m * theta_k, theta_k = base^(-2k/d_hr), k = 0..d_hr/2-1, in fp64.
+def yarn_frequencies(theta, s: float, orig_ctx: int, alpha: float, beta: float) -> np.ndarray:
+    """YaRN frequencies (NTK-by-parts) of the plain RoPE frequencies theta (fp64), scale s,
+    original context length orig_ctx, ramp bounds alpha < beta (see the module notes)."""
+    theta = np.asarray(theta, dtype=np.float64)
+    wavelength = 2.0 * np.pi / theta
+    rotations = np.float64(orig_ctx) / wavelength
+    gamma = np.clip((rotations - alpha) / (beta - alpha), 0.0, 1.0)
+    return (1.0 - gamma) * theta / s + gamma * theta
+
+
+def yarn_of(dims):
+    """The layer's YaRN parameters (s, L, alpha, beta), or None for plain RoPE."""
+    s = float(getattr(dims, "rope_scale", 1.0))
+    if s <= 1.0:
+        return None
+    return s, int(dims.rope_orig_ctx), float(dims.yarn_alpha), float(dims.yarn_beta)
+
+
+def rope_angles(pos, d_hr: int, base: float, yarn=None) -> np.ndarray:
+    """Angles m * theta_k, theta_k = base^(-2k/d_hr), k = 0..d_hr/2-1, in fp64 (with yarn =
+    (s, L, alpha, beta): the YaRN frequencies of those).
     pos: int or int array [...]; returns [..., d_hr/2]."""
     k = np.arange(d_hr // 2, dtype=np.float64)
     theta = np.power(np.float64(base), -2.0 * k / d_hr)
+    if yarn is not None:
+        theta = yarn_frequencies(theta, *yarn)
     return np.asarray(pos, dtype=np.float64)[..., None] * theta
 
 
-def apply_rope(x: np.ndarray, pos, base: float) -> np.ndarray:
+def apply_rope(x: np.ndarray, pos, base: float, yarn=None) -> np.ndarray:
     """Rotate interleaved pairs of the last axis of x by the angles of position(s) pos.
     x: [..., d_hr]; pos broadcastable to x.shape[:-1]."""
     x = np.asarray(x, dtype=np.float64)
     d = x.shape[-1]
-    ang = rope_angles(pos, d, base)
+    ang = rope_angles(pos, d, base, yarn)
     c, s = np.cos(ang), np.sin(ang)
     xe, xo = x[..., 0::2], x[..., 1::2]
     out = np.empty(np.broadcast_shapes(x.shape, ang.shape[:-1] + (d,)), dtype=np.float64)
@@ -77,7 +108,7 @@ def query(W: dict, dims, h: np.ndarray, pos) -> tuple:
     cq = h @ _w(W, "W_DQ").T if dims.d_cq > 0 else h
     qc = (cq @ _w(W, "W_UQ").T).reshape(h.shape[0], dims.n_h, dims.d_h)
     qr = (cq @ _w(W, "W_QR").T).reshape(h.shape[0], dims.n_h, dims.d_hr)
-    qr = apply_rope(qr, np.asarray(pos)[:, None], dims.rope_base)
+    qr = apply_rope(qr, np.asarray(pos)[:, None], dims.rope_base, yarn_of(dims))
     return qc, qr
 
 
@@ -85,7 +116,7 @@ def latent_entries(W: dict, dims, h: np.ndarray, pos) -> np.ndarray:
     """App. C cached vectors: [c^kv_t | RoPE(W_KR h_t)] per token, [n, d_c + d_hr]."""
     h = np.asarray(h, dtype=np.float64)
     ckv = h @ _w(W, "W_DKV").T
-    kr = apply_rope(h @ _w(W, "W_KR").T, np.asarray(pos), dims.rope_base)
+    kr = apply_rope(h @ _w(W, "W_KR").T, np.asarray(pos), dims.rope_base, yarn_of(dims))
     return np.concatenate([ckv, kr], axis=1)
 
 
@@ -98,10 +129,23 @@ def softmax_rows(s: np.ndarray):
 
 
 # ----------------------------------------------------------------------------- attention
+def yarn_logit_factor(dims) -> float:
+    """YaRN's attention-entropy factor t = (c ln s + 1)^2 (section 3.1.4: c = 0.0707), 1 without YaRN."""
+    if yarn_of(dims) is None:
+        return 1.0
+    root_t = np.float64(dims.yarn_mscale) * np.log(np.float64(dims.rope_scale)) + 1.0
+    return float(root_t * root_t)
+
+
 def softmax_scale(dims) -> float:
-    """The logit scale of App. C, 1/sqrt(d_h + d_e), unless the layer fixes another value."""
+    """The logit scale of App. C, 1/sqrt(d_h + d_e) (times YaRN's t), unless the layer fixes
+    another value."""
     if dims.softmax_scale > 0:
         return float(dims.softmax_scale)
+    return yarn_logit_factor(dims) * _app_c_scale(dims)
+
+
+def _app_c_scale(dims) -> float:
     return 1.0 / np.sqrt(np.float64(dims.d_h + dims.d_hr))
 
 

@@ -22,8 +22,8 @@ MUTATIONS = {
         "qc = (cq @ _w(W, \"W_UQ\").T).reshape(h.shape[0], dims.d_h, dims.n_h).transpose(0, 2, 1)"),
     "causal_off_by_one": ("o, lse = attend(W, dims, qc, qr, cache, idx + 1)",
                           "o, lse = attend(W, dims, qc, qr, cache, np.maximum(idx, 1))"),
-    "rope_on_wrong_position": ("kr = apply_rope(h @ _w(W, \"W_KR\").T, np.asarray(pos), dims.rope_base)",
-                               "kr = apply_rope(h @ _w(W, \"W_KR\").T, np.asarray(pos) + 1, dims.rope_base)"),
+    "rope_on_wrong_position": ("kr = apply_rope(h @ _w(W, \"W_KR\").T, np.asarray(pos), dims.rope_base, yarn_of(dims))",
+                               "kr = apply_rope(h @ _w(W, \"W_KR\").T, np.asarray(pos) + 1, dims.rope_base, yarn_of(dims))"),
     "wrong_scale": ("return 1.0 / np.sqrt(np.float64(dims.d_h + dims.d_hr))",
                     "return 1.0 / np.sqrt(np.float64(dims.d_h))"),
     "no_max_subtraction": ("    e = np.exp(s - m)\n", "    e = np.exp(s - m * 0.0)\n    e = e * np.exp(-m)\n"),
