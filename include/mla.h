@@ -13,9 +13,14 @@
  *   o_{t,i} = sum_{j<=t} softmax_j(scale * ([q^C;q^R]_{t,i} . [k^C_{j,i};k^R_j])) v_{j,i}
  *   u_t    = W_O [o_{t,1}; ...; o_{t,n_h}]
  *
- * RoPE rotates interleaved pairs (x_2k, x_2k+1) by angle pos * rope_base^(-2k/d_hr), pos = the
- * token's 0-based index in its sequence.  The page only names "the RoPE matrix"; this is the
- * RoFormer rotation it cites.
+ * RoPE rotates interleaved pairs (x_2k, x_2k+1) by angle pos * theta_k, theta_k =
+ * rope_base^(-2k/d_hr), pos = the token's 0-based index in its sequence.  The page only names
+ * "the RoPE matrix"; this is the RoFormer rotation it cites.  With YaRN (section 3.1.4, a layer
+ * with rope_scale s > 1) each pair rotates by (1 - g_k) theta_k / s + g_k theta_k instead, where
+ * g_k ramps linearly from 0 to 1 as the pair's number of turns over the original context,
+ * r_k = rope_orig_ctx * theta_k / (2 pi), goes from yarn_alpha to yarn_beta (the YaRN paper's
+ * "NTK-by-parts" frequencies, which the page cites), and the default scale is multiplied by
+ * t = (yarn_mscale ln s + 1)^2 (the page gives sqrt(t) = 0.0707 ln s + 1).
  *
  * Conventions for every entry point
  *   - Weights are row-major [out][in] (y = W x), in dims->dtype, device memory, 16-byte aligned.
@@ -65,7 +70,7 @@ typedef struct {
   int32_t d_c;         /* KV compression dimension (latent width) */
   int32_t d_cq;        /* query compression dimension d'_q; 0 = no query compression */
   int32_t d_hr;        /* per-head decoupled rope dimension d_e (d_h^R); even */
-  float softmax_scale; /* 0 => 1/sqrt(d_h + d_hr) (App. C) */
+  float softmax_scale; /* 0 => 1/sqrt(d_h + d_hr) (App. C), times YaRN's t when it is on */
   float rope_base;     /* RoPE frequency base (10000 for DeepSeek-V2) */
   int32_t dtype;       /* mla_dtype: storage of weights, h, cache, u */
   int32_t cache_dtype; /* element type of the cache pool: 0 = dtype, or MLA_FP8_E4M3 (with
@@ -76,6 +81,13 @@ typedef struct {
                           value), code = e4m3(x / s), rounded to nearest even, saturating; an
                           all-zero part has s = 0.  The quantised entry is the bf16 entry the
                           bf16 path would store.  Attention reads value(code) * s. */
+  /* YaRN context extension (section 3.1.4; off when rope_scale <= 1, e.g. all zero): */
+  float rope_scale;      /* s (40 for DeepSeek-V2); finite, >= 0 */
+  int32_t rope_orig_ctx; /* original context length the turns are counted over (4096); > 0 when on */
+  float yarn_alpha;      /* ramp start in turns (1); >= 0 when on */
+  float yarn_beta;       /* ramp end in turns (32); > yarn_alpha when on */
+  float yarn_mscale;     /* c in sqrt(t) = c ln s + 1 (0.0707); finite, >= 0 when on; applies to the
+                            default scale only (softmax_scale == 0) */
 } mla_dims;
 
 /* Device pointers, row-major [out][in].  W_DQ is NULL iff d_cq == 0. */

@@ -39,7 +39,8 @@ class Dims(ctypes.Structure):
     _fields_ = [("d_model", ctypes.c_int32), ("n_h", ctypes.c_int32), ("d_h", ctypes.c_int32),
                 ("d_c", ctypes.c_int32), ("d_cq", ctypes.c_int32), ("d_hr", ctypes.c_int32),
                 ("softmax_scale", ctypes.c_float), ("rope_base", ctypes.c_float), ("dtype", ctypes.c_int32),
-                ("cache_dtype", ctypes.c_int32)]
+                ("cache_dtype", ctypes.c_int32), ("rope_scale", ctypes.c_float), ("rope_orig_ctx", ctypes.c_int32),
+                ("yarn_alpha", ctypes.c_float), ("yarn_beta", ctypes.c_float), ("yarn_mscale", ctypes.c_float)]
 
 
 class Weights(ctypes.Structure):
@@ -105,10 +106,13 @@ def _stream(stream) -> int | None:
 
 
 def make_dims(d_model, n_h, d_h, d_c, d_cq, d_hr, dtype, softmax_scale=0.0, rope_base=10000.0,
-              cache_dtype=0) -> Dims:
+              cache_dtype=0, rope_scale=1.0, rope_orig_ctx=0, yarn_alpha=1.0, yarn_beta=32.0,
+              yarn_mscale=0.0707) -> Dims:
+    """YaRN is on when rope_scale > 1 (then rope_orig_ctx > 0 is required)."""
     dt = {"bf16": MLA_BF16, "f32": MLA_F32, MLA_BF16: MLA_BF16, MLA_F32: MLA_F32}[dtype]
     cdt = {0: 0, None: 0, "fp8": MLA_FP8_E4M3, MLA_FP8_E4M3: MLA_FP8_E4M3}[cache_dtype]
-    return Dims(d_model, n_h, d_h, d_c, d_cq, d_hr, float(softmax_scale), float(rope_base), dt, cdt)
+    return Dims(d_model, n_h, d_h, d_c, d_cq, d_hr, float(softmax_scale), float(rope_base), dt, cdt,
+                float(rope_scale), int(rope_orig_ctx), float(yarn_alpha), float(yarn_beta), float(yarn_mscale))
 
 
 def make_weights(W: dict) -> Weights:

@@ -97,8 +97,15 @@ size_t gemm_partial_bound(int M, int N, int K, int batch, int cus, bool skinny_o
 hipError_t gemm_run(DType t, const GemmParams& p, const GemmPlan& plan, float* partial,
                     hipStream_t s);
 
-// rope_tab[r][k] = (cos, sin)(pos[r] * base^(-2k/d_hr)), r < n; angles formed in fp64.
-hipError_t rope_table(const int32_t* pos, int n, int d_hr, float base, float2* tab, hipStream_t s);
+// RoPE frequencies: theta_k = base^(-2k/d_hr), or their YaRN form when scale > 1 (turns counted
+// over orig_ctx positions, ramp from alpha to beta turns).
+struct RopeFreq {
+  double base = 10000.0;
+  double scale = 1.0;
+  double orig_ctx = 0.0, alpha = 1.0, beta = 32.0;
+};
+// rope_tab[r][k] = (cos, sin)(pos[r] * theta_k), r < n; angles formed in fp64.
+hipError_t rope_table(const int32_t* pos, int n, int d_hr, const RopeFreq& f, float2* tab, hipStream_t s);
 // pos[r] = r % T, seq[r] = r / T for r < n.
 hipError_t prefill_rows(int n, int T, int32_t* seq, int32_t* pos, hipStream_t s);
 // Copies dense rows src[r][0..width) into paged cache slots (row_seq/row_pos/block_table).

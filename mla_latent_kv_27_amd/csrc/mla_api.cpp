@@ -45,6 +45,12 @@ int validate_dims(const mla_dims* d) {
   if (d->dtype != MLA_F32 && d->dtype != MLA_BF16) return MLA_ERR_INVALID_ARG;
   if (!(d->softmax_scale >= 0.f) || !std::isfinite(d->softmax_scale)) return MLA_ERR_INVALID_ARG;
   if (!(d->rope_base > 0.f) || !std::isfinite(d->rope_base)) return MLA_ERR_INVALID_ARG;
+  if (!(d->rope_scale >= 0.f) || !std::isfinite(d->rope_scale)) return MLA_ERR_INVALID_ARG;
+  if (d->rope_scale > 1.f) {
+    if (d->rope_orig_ctx <= 0 || !(d->yarn_alpha >= 0.f) || !std::isfinite(d->yarn_beta) ||
+        !(d->yarn_beta > d->yarn_alpha) || !(d->yarn_mscale >= 0.f) || !std::isfinite(d->yarn_mscale))
+      return MLA_ERR_INVALID_ARG;
+  }
   // every contraction and row is moved in 16-byte chunks
   const int epc = d->dtype == MLA_BF16 ? 8 : 4;
   if (d->d_model % epc || d->d_h % epc || d->d_c % epc || d->d_cq % epc || d->d_hr % 8)
@@ -63,8 +69,27 @@ inline int q_in(const mla_dims* d) { return d->d_cq > 0 ? d->d_cq : d->d_model; 
 inline int entry(const mla_dims* d) { return d->d_c + d->d_hr; }
 // bf16 "NT" products may take the weight-streaming kernel for small row counts
 inline bool sk(const mla_dims* d) { return d->dtype == MLA_BF16; }
+inline bool yarn_on(const mla_dims* d) { return d->rope_scale > 1.f; }
+// The logit scale: the layer's own, else 1/sqrt(d_h + d_hr) times YaRN's t = (c ln s + 1)^2.
 inline float scale_of(const mla_dims* d) {
-  return d->softmax_scale > 0.f ? d->softmax_scale : 1.0f / std::sqrt((float)(d->d_h + d->d_hr));
+  if (d->softmax_scale > 0.f) return d->softmax_scale;
+  double sc = 1.0 / std::sqrt((double)(d->d_h + d->d_hr));
+  if (yarn_on(d)) {
+    const double root_t = (double)d->yarn_mscale * std::log((double)d->rope_scale) + 1.0;
+    sc *= root_t * root_t;
+  }
+  return (float)sc;
+}
+inline RopeFreq freq_of(const mla_dims* d) {
+  RopeFreq f;
+  f.base = d->rope_base;
+  if (yarn_on(d)) {
+    f.scale = d->rope_scale;
+    f.orig_ctx = d->rope_orig_ctx;
+    f.alpha = d->yarn_alpha;
+    f.beta = d->yarn_beta;
+  }
+  return f;
 }
 
 int validate_cache(const mla_dims* d, const mla_paged_cache* c) {
@@ -367,7 +392,7 @@ int mla_cache_append(const mla_dims* d, const mla_weights* w, const mla_paged_ca
   Carve cv(workspace);
   AppendWs ws = carve_append(cv, d, n, cus);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  MLA_HIP(rope_table(pos, n, d->d_hr, d->rope_base, ws.rope, s));
+  MLA_HIP(rope_table(pos, n, d->d_hr, freq_of(d), ws.rope, s));
   return run_cache_writer(d, w, c, h, n, seq_idx, pos, ws.rope, ws.plan, ws.partial, ws.staged, s);
 }
 
@@ -449,7 +474,7 @@ int mla_decode(const mla_dims* d, const mla_weights* w, const mla_paged_cache* c
   const int B = batch, E = entry(d), qw = q_in(d);
 
   // positions of the new tokens are ctx_lens[b]; rows are sequences 0..B-1
-  MLA_HIP(rope_table(ctx_lens, B, d->d_hr, d->rope_base, ws.rope, s));
+  MLA_HIP(rope_table(ctx_lens, B, d->d_hr, freq_of(d), ws.rope, s));
   const void* qin = h;
   {  // [c^q | c^KV | k^R] = [W_DQ; W_DKV; W_KR] h: c^q to the workspace, the new token's cache
      // entry to position ctx_lens[b] of its sequence
@@ -555,7 +580,7 @@ int mla_prefill(const mla_dims* d, const mla_weights* w, const mla_paged_cache* 
   const int M = batch * T, E = entry(d), qw = q_in(d), QD = d->d_h + d->d_hr;
 
   MLA_HIP(prefill_rows(M, T, ws.seq, ws.pos, s));
-  MLA_HIP(rope_table(ws.pos, M, d->d_hr, d->rope_base, ws.rope, s));
+  MLA_HIP(rope_table(ws.pos, M, d->d_hr, freq_of(d), ws.rope, s));
   const void* qin = h;
   if (d->d_cq > 0) {
     GemmParams g;

@@ -1,34 +1,42 @@
 // Small helper kernels: RoPE angle tables, prefill row bookkeeping, paged row scatter.
 //
 // RoPE follows the reading of the DeepSeek-V2 summary page's App. C ("RoPE(.)", the RoFormer
-// rotation it cites): interleaved pairs (x_2k, x_2k+1) rotate by pos * base^(-2k/d_hr).  The
-// angle is formed and reduced modulo 2*pi in fp64 so that positions near 1.3e5 keep full fp32
-// accuracy in cos/sin.
+// rotation it cites): interleaved pairs (x_2k, x_2k+1) rotate by pos * theta_k, theta_k =
+// base^(-2k/d_hr).  With YaRN (section 3.1.4; the YaRN paper's NTK-by-parts form, which the page
+// cites) a pair that turns r_k = L theta_k / (2 pi) times over the original context L keeps
+// theta_k above beta turns, is slowed to theta_k / s below alpha turns, and is blended linearly
+// in r_k between.  The angle is formed and reduced modulo 2*pi in fp64 so that positions near
+// 1.3e5 keep full fp32 accuracy in cos/sin.
 #include "common.h"
 #include "internal.h"
 
 namespace mla {
 
 __global__ void __launch_bounds__(256)
-    rope_table_kernel(const int32_t* __restrict__ pos, int n, int half, double log_base, float2* tab) {
+    rope_table_kernel(const int32_t* __restrict__ pos, int n, int half, RopeFreq f, float2* tab) {
   const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (i >= (int64_t)n * half) return;
   const int r = (int)(i / half), k = (int)(i % half);
-  const double theta = exp(-(2.0 * k / (2.0 * half)) * log_base);
-  double a = (double)pos[r] * theta;
   const double two_pi = 6.283185307179586476925286766559;
+  double theta = exp(-(2.0 * k / (2.0 * half)) * log(f.base));
+  if (f.scale > 1.0) {
+    const double turns = f.orig_ctx * theta / two_pi;
+    const double g = fmin(fmax((turns - f.alpha) / (f.beta - f.alpha), 0.0), 1.0);
+    theta = g * theta + (1.0 - g) * (theta / f.scale);
+  }
+  double a = (double)pos[r] * theta;
   a = a - floor(a / two_pi) * two_pi;
   double sn, cs;
   sincos(a, &sn, &cs);
   tab[i] = make_float2((float)cs, (float)sn);
 }
 
-hipError_t rope_table(const int32_t* pos, int n, int d_hr, float base, float2* tab, hipStream_t s) {
+hipError_t rope_table(const int32_t* pos, int n, int d_hr, const RopeFreq& f, float2* tab, hipStream_t s) {
   const int half = d_hr / 2;
   const int64_t total = (int64_t)n * half;
   if (total == 0) return hipSuccess;
   hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, pos, n,
-                     half, log((double)base), tab);
+                     half, f, tab);
   return hipGetLastError();
 }
 

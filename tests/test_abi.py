@@ -39,11 +39,25 @@ def _dims(**kw):
 
 
 @pytest.mark.parametrize("bad", [dict(d_model=0), dict(n_h=-1), dict(d_hr=7), dict(d_c=0), dict(d_cq=-4),
-                                 dict(rope_base=0.0), dict(softmax_scale=-1.0)])
+                                 dict(rope_base=0.0), dict(softmax_scale=-1.0),
+                                 dict(rope_scale=-1.0), dict(rope_scale=float("nan")),
+                                 dict(rope_scale=40.0, rope_orig_ctx=0),
+                                 dict(rope_scale=40.0, rope_orig_ctx=4096, yarn_alpha=32.0, yarn_beta=32.0),
+                                 dict(rope_scale=40.0, rope_orig_ctx=4096, yarn_alpha=-1.0),
+                                 dict(rope_scale=40.0, rope_orig_ctx=4096, yarn_mscale=-0.1)])
 def test_invalid_dims_rejected(bad):
     out = ctypes.c_size_t(0)
     st = M.lib().mla_workspace_size(ctypes.byref(_dims(**bad)), M.OP_DECODE, 1, 0, 4, 0, ctypes.byref(out))
     assert st == M.MLA_ERR_INVALID_ARG
+
+
+def test_yarn_off_values_accepted():
+    # a scale of at most 1 turns YaRN off whatever the other fields hold
+    out = ctypes.c_size_t(0)
+    for kw in (dict(rope_scale=0.0), dict(rope_scale=1.0, rope_orig_ctx=-5, yarn_beta=-1.0),
+               dict(rope_scale=40.0, rope_orig_ctx=4096)):
+        st = M.lib().mla_workspace_size(ctypes.byref(_dims(**kw)), M.OP_DECODE, 1, 0, 4, 0, ctypes.byref(out))
+        assert st == M.MLA_OK, kw
 
 
 def test_unaligned_dims_unsupported():
