@@ -30,6 +30,7 @@ SEED_HISTORY = 1
 SEED_PAGES = 2
 SEED_LENGTHS = 3
 SEED_STEP = 4
+SEED_GAINS = 6
 
 
 @dataclasses.dataclass(frozen=True)
@@ -52,6 +53,9 @@ class Dims:
     yarn_alpha: float = 1.0
     yarn_beta: float = 32.0
     yarn_mscale: float = 0.0707
+    # RMSNorm after the compressed latents c^q and c^KV (with learned gains), epsilon
+    latent_norm: bool = False
+    rms_eps: float = 1e-6
 
     @property
     def entry(self) -> int:
@@ -103,6 +107,10 @@ V2 = Dims(d_model=5120, n_h=128, d_h=128, d_c=512, d_cq=1536, d_hr=64, dtype=BF1
 # V2 with the long-context extension of section 3.1.4: s = 40 over a 4096-token original context
 V2_YARN = dataclasses.replace(V2, rope_scale=40.0, rope_orig_ctx=4096)
 TINY_YARN = dataclasses.replace(TINY, rope_scale=4.0, rope_orig_ctx=64)
+# the layers with RMSNorm on the latents (section 3.1.2)
+V2_NORM = dataclasses.replace(V2, latent_norm=True)
+V2_LITE_NORM = dataclasses.replace(V2_LITE, latent_norm=True)
+TINY_NORM = dataclasses.replace(TINY, latent_norm=True)
 
 WORKLOADS = {
     "tiny_fp32": Workload("tiny_fp32", TINY, "prefill", batch=1, tokens=16, decode_steps=4,
@@ -157,6 +165,11 @@ def make_weights(dims: Dims, std: float = 0.02, seed: int = SEED_WEIGHTS) -> dic
             continue
         w = rng.standard_normal(shapes[name]) * std
         out[name] = to_dtype(w.astype(np.float32), dims.dtype)
+    if dims.latent_norm:  # norm gains 1 + N(0, 0.1), from their own generator
+        g = np.random.default_rng(SEED_GAINS)
+        if dims.d_cq > 0:
+            out["g_cq"] = to_dtype((1.0 + 0.1 * g.standard_normal(dims.d_cq)).astype(np.float32), dims.dtype)
+        out["g_ckv"] = to_dtype((1.0 + 0.1 * g.standard_normal(dims.d_c)).astype(np.float32), dims.dtype)
     return out
 
 

@@ -39,6 +39,12 @@ notes):
     t = (0.0707 ln s + 1)^2 (the page names only sqrt(t) and says it adjusts the attention
     entropy; applying it to the logit scale is the plain reading).  Both rope parts (q^R and the
     shared k^R) use the same frequencies.
+  * RMSNorm after the compressed latents (section 3.1.2), when the weights carry the gains
+    g_cq / g_ckv: c^q <- g_cq * c^q / sqrt(mean(c^q^2) + eps) before W_UQ and W_QR, and
+    c^KV <- g_ckv * c^KV / sqrt(mean(c^KV^2) + eps) before it is cached (so W_UK and W_UV see
+    the normalised latent); the rope key is not normalised.  The page also multiplies
+    "additional scaling factors" at the width bottlenecks without giving them; a constant factor
+    folds into the gains, so none is modelled apart from them.
 
 Parity pins: every function here is checked by tests that do not reuse this
 code (a scalar brute-force layer on tiny inputs, reduction to textbook MHA, a
@@ -100,12 +106,21 @@ def _w(W: dict, name: str) -> np.ndarray:
     return np.asarray(W[name], dtype=np.float64)
 
 
+def rms_norm(x: np.ndarray, gain, eps: float) -> np.ndarray:
+    """RMSNorm over the last axis: gain * x / sqrt(mean(x^2) + eps), fp64."""
+    x = np.asarray(x, dtype=np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * np.asarray(gain, dtype=np.float64)
+
+
 def query(W: dict, dims, h: np.ndarray, pos) -> tuple:
     """App. C query side.  h [n, d] -> (q^C [n, n_h, d_h], rotated q^R [n, n_h, d_hr]).
     c^q = W_DQ h (or h itself without query compression); q^C = W_UQ c^q;
     q^R = RoPE(W_QR c^q), head i = rows [i*d_hr, (i+1)*d_hr)."""
     h = np.asarray(h, dtype=np.float64)
     cq = h @ _w(W, "W_DQ").T if dims.d_cq > 0 else h
+    if dims.d_cq > 0 and "g_cq" in W:
+        cq = rms_norm(cq, _w(W, "g_cq"), dims.rms_eps)
     qc = (cq @ _w(W, "W_UQ").T).reshape(h.shape[0], dims.n_h, dims.d_h)
     qr = (cq @ _w(W, "W_QR").T).reshape(h.shape[0], dims.n_h, dims.d_hr)
     qr = apply_rope(qr, np.asarray(pos)[:, None], dims.rope_base, yarn_of(dims))
@@ -116,6 +131,8 @@ def latent_entries(W: dict, dims, h: np.ndarray, pos) -> np.ndarray:
     """App. C cached vectors: [c^kv_t | RoPE(W_KR h_t)] per token, [n, d_c + d_hr]."""
     h = np.asarray(h, dtype=np.float64)
     ckv = h @ _w(W, "W_DKV").T
+    if "g_ckv" in W:
+        ckv = rms_norm(ckv, _w(W, "g_ckv"), dims.rms_eps)
     kr = apply_rope(h @ _w(W, "W_KR").T, np.asarray(pos), dims.rope_base, yarn_of(dims))
     return np.concatenate([ckv, kr], axis=1)
 
