@@ -308,7 +308,9 @@ def main():
         "config": {"workload": w.name, "batch": B, "ctx_tokens": [int(min(lens)), int(max(lens))],
                    "d_model": dims.d_model, "n_h": dims.n_h, "d_h": dims.d_h, "d_c": dims.d_c, "d_cq": dims.d_cq,
                    "d_hr": dims.d_hr, "block_size": w.block_size, "num_splits": splits, "replicas": len(reps),
-                   "cache": "fp8_e4m3 (per-token scales)" if fp8 else dims.dtype},
+                   "cache": "fp8_e4m3 (per-token scales)" if fp8 else dims.dtype,
+                   "latent_rmsnorm": bool(dims.latent_norm),
+                   "yarn_scale": float(dims.rope_scale) if dims.rope_scale > 1 else None},
         "step_GBps": round(step_bytes / (ms / 1e3) / 1e9, 1),
         "step_hbm_frac": round(step_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
         "step_bytes": step_bytes,

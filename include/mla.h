@@ -88,6 +88,7 @@ typedef struct {
   float yarn_beta;       /* ramp end in turns (32); > yarn_alpha when on */
   float yarn_mscale;     /* c in sqrt(t) = c ln s + 1 (0.0707); finite, >= 0 when on; applies to the
                             default scale only (softmax_scale == 0) */
+  float rms_eps;         /* epsilon of the latent RMSNorms (see mla_weights); 0 => 1e-6 */
 } mla_dims;
 
 /* Device pointers, row-major [out][in].  W_DQ is NULL iff d_cq == 0. */
@@ -100,6 +101,12 @@ typedef struct {
   const void *W_UK;  /* [n_h*d_h][d_c] */
   const void *W_UV;  /* [n_h*d_h][d_c] */
   const void *W_O;   /* [d_model][n_h*d_h] */
+  /* RMSNorm after the compressed latents (section 3.1.2), each optional (NULL = no norm):
+   * x <- g * x / sqrt(mean(x^2) + rms_eps) over the d_cq values of c^q (before W_UQ and W_QR;
+   * requires d_cq > 0) and over the d_c values of c^KV (before it is cached; the rope key is not
+   * normalised).  The page's unspecified bottleneck scaling factors fold into the gains. */
+  const void *g_cq;  /* [d_cq] */
+  const void *g_ckv; /* [d_c] */
 } mla_weights;
 
 /* Paged latent cache (the App. C cached vectors, in pages of block_size tokens). */

@@ -40,11 +40,13 @@ class Dims(ctypes.Structure):
                 ("d_c", ctypes.c_int32), ("d_cq", ctypes.c_int32), ("d_hr", ctypes.c_int32),
                 ("softmax_scale", ctypes.c_float), ("rope_base", ctypes.c_float), ("dtype", ctypes.c_int32),
                 ("cache_dtype", ctypes.c_int32), ("rope_scale", ctypes.c_float), ("rope_orig_ctx", ctypes.c_int32),
-                ("yarn_alpha", ctypes.c_float), ("yarn_beta", ctypes.c_float), ("yarn_mscale", ctypes.c_float)]
+                ("yarn_alpha", ctypes.c_float), ("yarn_beta", ctypes.c_float), ("yarn_mscale", ctypes.c_float),
+                ("rms_eps", ctypes.c_float)]
 
 
 class Weights(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("W_DQ", "W_UQ", "W_QR", "W_DKV", "W_KR", "W_UK", "W_UV", "W_O")]
+    _fields_ = [(n, ctypes.c_void_p) for n in ("W_DQ", "W_UQ", "W_QR", "W_DKV", "W_KR", "W_UK", "W_UV", "W_O",
+                                                "g_cq", "g_ckv")]
 
 
 class PagedCache(ctypes.Structure):
@@ -107,16 +109,18 @@ def _stream(stream) -> int | None:
 
 def make_dims(d_model, n_h, d_h, d_c, d_cq, d_hr, dtype, softmax_scale=0.0, rope_base=10000.0,
               cache_dtype=0, rope_scale=1.0, rope_orig_ctx=0, yarn_alpha=1.0, yarn_beta=32.0,
-              yarn_mscale=0.0707) -> Dims:
-    """YaRN is on when rope_scale > 1 (then rope_orig_ctx > 0 is required)."""
+              yarn_mscale=0.0707, rms_eps=0.0) -> Dims:
+    """YaRN is on when rope_scale > 1 (then rope_orig_ctx > 0 is required); rms_eps 0 = 1e-6."""
     dt = {"bf16": MLA_BF16, "f32": MLA_F32, MLA_BF16: MLA_BF16, MLA_F32: MLA_F32}[dtype]
     cdt = {0: 0, None: 0, "fp8": MLA_FP8_E4M3, MLA_FP8_E4M3: MLA_FP8_E4M3}[cache_dtype]
     return Dims(d_model, n_h, d_h, d_c, d_cq, d_hr, float(softmax_scale), float(rope_base), dt, cdt,
-                float(rope_scale), int(rope_orig_ctx), float(yarn_alpha), float(yarn_beta), float(yarn_mscale))
+                float(rope_scale), int(rope_orig_ctx), float(yarn_alpha), float(yarn_beta), float(yarn_mscale),
+                float(rms_eps))
 
 
 def make_weights(W: dict) -> Weights:
-    """W maps the names W_DQ .. W_O to device tensors (W_DQ may be absent)."""
+    """W maps the names W_DQ .. W_O (and the optional norm gains g_cq, g_ckv) to device tensors
+    (W_DQ and the gains may be absent)."""
     return Weights(*[_ptr(W.get(n)) for n, _ in Weights._fields_])
 
 

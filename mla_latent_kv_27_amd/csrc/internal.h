@@ -106,9 +106,13 @@ struct RopeFreq {
 };
 // rope_tab[r][k] = (cos, sin)(pos[r] * theta_k), r < n; angles formed in fp64.
 hipError_t rope_table(const int32_t* pos, int n, int d_hr, const RopeFreq& f, float2* tab, hipStream_t s);
+// x[r][0..W) <- gain * x / sqrt(mean(x^2) + eps) for rows r < n, ld elements apart, in place
+// (the RMSNorm of the compressed latents).
+hipError_t rmsnorm_rows(DType t, void* x, int n, int W, int64_t ld, const void* gain, float eps, hipStream_t s);
 // pos[r] = r % T, seq[r] = r / T for r < n.
 hipError_t prefill_rows(int n, int T, int32_t* seq, int32_t* pos, hipStream_t s);
-// Copies dense rows src[r][0..width) into paged cache slots (row_seq/row_pos/block_table).
+// Copies dense rows src[r][0..width) into paged cache slots (row_seq/row_pos/block_table;
+// row_seq == nullptr: row r belongs to sequence r).
 hipError_t scatter_rows(DType t, const void* src, int n, int width, void* pool,
                         const int32_t* row_seq, const int32_t* row_pos, const int32_t* block_table,
                         int max_blocks, int block_size, hipStream_t s);

@@ -46,6 +46,7 @@ int validate_dims(const mla_dims* d) {
   if (!(d->softmax_scale >= 0.f) || !std::isfinite(d->softmax_scale)) return MLA_ERR_INVALID_ARG;
   if (!(d->rope_base > 0.f) || !std::isfinite(d->rope_base)) return MLA_ERR_INVALID_ARG;
   if (!(d->rope_scale >= 0.f) || !std::isfinite(d->rope_scale)) return MLA_ERR_INVALID_ARG;
+  if (!(d->rms_eps >= 0.f) || !std::isfinite(d->rms_eps)) return MLA_ERR_INVALID_ARG;
   if (d->rope_scale > 1.f) {
     if (d->rope_orig_ctx <= 0 || !(d->yarn_alpha >= 0.f) || !std::isfinite(d->yarn_beta) ||
         !(d->yarn_beta > d->yarn_alpha) || !(d->yarn_mscale >= 0.f) || !std::isfinite(d->yarn_mscale))
@@ -70,6 +71,9 @@ inline int entry(const mla_dims* d) { return d->d_c + d->d_hr; }
 // bf16 "NT" products may take the weight-streaming kernel for small row counts
 inline bool sk(const mla_dims* d) { return d->dtype == MLA_BF16; }
 inline bool yarn_on(const mla_dims* d) { return d->rope_scale > 1.f; }
+inline float eps_of(const mla_dims* d) { return d->rms_eps > 0.f ? d->rms_eps : 1e-6f; }
+// The gain of the c^q norm exists only with query compression.
+inline bool weights_norm_ok(const mla_dims* d, const mla_weights* w) { return !w->g_cq || d->d_cq > 0; }
 // The logit scale: the layer's own, else 1/sqrt(d_h + d_hr) times YaRN's t = (c ln s + 1)^2.
 inline float scale_of(const mla_dims* d) {
   if (d->softmax_scale > 0.f) return d->softmax_scale;
@@ -117,7 +121,7 @@ int auto_splits(const mla_dims* d, int batch, int max_ctx_len, int cus) {
 struct AppendWs {
   float2* rope;
   float* partial;
-  void* staged;  // fp8 cache: the bf16 entries before quantisation [n][entry]
+  void* staged;  // entries before their latent norm and/or quantisation [n][entry]
   GemmPlan plan;
 };
 AppendWs carve_append(Carve& cv, const mla_dims* d, int n, int cus) {
@@ -125,7 +129,8 @@ AppendWs carve_append(Carve& cv, const mla_dims* d, int n, int cus) {
   w.plan = gemm_plan(n, entry(d), d->d_model, 1, cus, sk(d));
   w.rope = cv.take<float2>((size_t)n * (d->d_hr / 2) * sizeof(float2));
   w.partial = cv.take<float>(gemm_partial_bound(n, entry(d), d->d_model, 1, cus, sk(d)));
-  w.staged = fp8_cache(d) ? cv.take<char>((size_t)n * entry(d) * 2) : nullptr;
+  // the workspace size does not know whether the weights carry a c^KV norm: always room to stage
+  w.staged = cv.take<char>((size_t)n * entry(d) * dsize(dt(d)));
   return w;
 }
 
@@ -191,7 +196,7 @@ AttnWs carve_attn(Carve& cv, const mla_dims* d, int B, int max_kv_len, int split
 struct DecodeWs {
   float2* rope;
   void *cq, *qc, *qcat, *ohat, *o;
-  void* staged;  // fp8 cache: the new tokens' bf16 entries before quantisation
+  void* staged;  // the new tokens' entries before their latent norm and/or quantisation
   AttnWs attn;
   float* partial;
   DecodeGemms gm;
@@ -205,7 +210,7 @@ DecodeWs carve_decode(Carve& cv, const mla_dims* d, int B, int max_ctx_len, int 
   w.cq = cv.take<char>((size_t)B * d->d_cq * es);
   w.qc = cv.take<char>((size_t)B * d->n_h * d->d_h * es);
   w.qcat = cv.take<char>((size_t)B * d->n_h * entry(d) * es);
-  w.staged = fp8_cache(d) ? cv.take<char>((size_t)B * entry(d) * 2) : nullptr;
+  w.staged = cv.take<char>((size_t)B * entry(d) * es);
   w.ohat = cv.take<char>((size_t)B * d->n_h * d->d_c * es);
   w.o = cv.take<char>((size_t)B * d->n_h * d->d_h * es);
   w.attn = carve_attn(cv, d, B, max_ctx_len + 1, splits, cus);
@@ -284,7 +289,7 @@ Epilogue cache_epilogue(const mla_dims* d, const mla_paged_cache* c, const float
   return e;
 }
 
-// fp8 cache: dense bf16 rows [c^KV | RoPE'd k^R] for the quantiser.
+// Dense rows [c^KV | RoPE'd k^R] for the latent norm and/or the fp8 quantiser.
 Epilogue staged_epilogue(const mla_dims* d, void* staged, const float2* rope) {
   Epilogue e;
   e.C = staged;
@@ -306,6 +311,23 @@ QuantDst quant_dst(const mla_paged_cache* c, const int32_t* seq, const int32_t* 
   return q;
 }
 
+// Entries are staged (dense rows) when they need a pass after the projection: the c^KV norm and/or
+// the fp8 quantiser.
+inline bool staged_entries(const mla_dims* d, const mla_weights* w) { return fp8_cache(d) || w->g_ckv; }
+
+// Staged rows -> their cache slots: the c^KV norm in place, then quantised (fp8) or copied.
+// seq == nullptr: row r belongs to sequence r.
+int finish_entries(const mla_dims* d, const mla_weights* w, const mla_paged_cache* c, void* staged, int n,
+                   const int32_t* seq, const int32_t* pos, hipStream_t s) {
+  if (w->g_ckv) MLA_HIP(rmsnorm_rows(dt(d), staged, n, d->d_c, entry(d), w->g_ckv, eps_of(d), s));
+  if (fp8_cache(d))
+    MLA_HIP(quantize_entries_run(staged, entry(d), n, quant_dst(c, seq, pos), s));
+  else
+    MLA_HIP(scatter_rows(dt(d), staged, n, entry(d), c->pool, seq, pos, c->block_table, c->max_blocks_per_seq,
+                         c->block_size, s));
+  return MLA_OK;
+}
+
 int run_cache_writer(const mla_dims* d, const mla_weights* w, const mla_paged_cache* c, const void* h, int n,
                      const int32_t* seq, const int32_t* pos, const float2* rope, const GemmPlan& plan,
                      float* partial, void* staged, hipStream_t s) {
@@ -319,11 +341,10 @@ int run_cache_writer(const mla_dims* d, const mla_weights* w, const mla_paged_ca
   g.M = n;
   g.N = entry(d);
   g.K = d->d_model;
-  if (fp8_cache(d)) {  // bf16 entries to the staging rows, then quantised into their slots
+  if (staged_entries(d, w)) {  // entries to the staging rows, then normalised / quantised into their slots
     g.epi = staged_epilogue(d, staged, rope);
     MLA_HIP(gemm_run(dt(d), g, plan, partial, s));
-    MLA_HIP(quantize_entries_run(staged, entry(d), n, quant_dst(c, seq, pos), s));
-    return MLA_OK;
+    return finish_entries(d, w, c, staged, n, seq, pos, s);
   }
   g.epi = cache_epilogue(d, c, rope, seq, pos);
   MLA_HIP(gemm_run(dt(d), g, plan, partial, s));
@@ -382,7 +403,7 @@ int mla_cache_append(const mla_dims* d, const mla_weights* w, const mla_paged_ca
   int st = validate_dims(d);
   if (st != MLA_OK) return st;
   if ((st = validate_cache(d, c)) != MLA_OK) return st;
-  if (!w || !w->W_DKV || !w->W_KR || n < 0) return MLA_ERR_INVALID_ARG;
+  if (!w || !w->W_DKV || !w->W_KR || n < 0 || !weights_norm_ok(d, w)) return MLA_ERR_INVALID_ARG;
   if (n == 0) return MLA_OK;
   if (!h || !seq_idx || !pos) return MLA_ERR_INVALID_ARG;
   const int cus = device_cus();
@@ -459,7 +480,7 @@ int mla_decode(const mla_dims* d, const mla_weights* w, const mla_paged_cache* c
   if ((st = validate_cache(d, c)) != MLA_OK) return st;
   if (!w || !w->W_UQ || !w->W_QR || !w->W_DKV || !w->W_KR || !w->W_UK || !w->W_UV || !w->W_O)
     return MLA_ERR_INVALID_ARG;
-  if ((d->d_cq > 0) != (w->W_DQ != nullptr)) return MLA_ERR_INVALID_ARG;
+  if ((d->d_cq > 0) != (w->W_DQ != nullptr) || !weights_norm_ok(d, w)) return MLA_ERR_INVALID_ARG;
   if (!h || !ctx_lens || !u || batch <= 0 || max_ctx_len < 0 || num_splits < 0) return MLA_ERR_INVALID_ARG;
   if ((int64_t)max_ctx_len + 1 > (int64_t)c->max_blocks_per_seq * c->block_size) return MLA_ERR_INVALID_ARG;
   if (!decode_supported(d->d_c, d->d_hr)) return MLA_ERR_UNSUPPORTED;
@@ -487,15 +508,21 @@ int mla_decode(const mla_dims* d, const mla_weights* w, const mla_paged_cache* c
       g.B2 = w->W_KR;
       g.epi = dense(ws.cq, d->d_cq);
       g.E0 = d->d_cq;
-      g.epi2 = fp8_cache(d) ? staged_epilogue(d, ws.staged, ws.rope) : cache_epilogue(d, c, ws.rope, nullptr, ctx_lens);
+      g.epi2 = staged_entries(d, w) ? staged_epilogue(d, ws.staged, ws.rope)
+                                    : cache_epilogue(d, c, ws.rope, nullptr, ctx_lens);
       qin = ws.cq;
     } else {
       g.B0 = w->W_DKV; g.N0 = d->d_c;
       g.B1 = w->W_KR;
-      g.epi = fp8_cache(d) ? staged_epilogue(d, ws.staged, ws.rope) : cache_epilogue(d, c, ws.rope, nullptr, ctx_lens);
+      g.epi = staged_entries(d, w) ? staged_epilogue(d, ws.staged, ws.rope)
+                                   : cache_epilogue(d, c, ws.rope, nullptr, ctx_lens);
     }
     MLA_HIP(gemm_run(t, g, ws.gm.kvq, ws.partial, s));
-    if (fp8_cache(d)) MLA_HIP(quantize_entries_run(ws.staged, E, B, quant_dst(c, nullptr, ctx_lens), s));
+    if (w->g_cq) MLA_HIP(rmsnorm_rows(t, ws.cq, B, d->d_cq, d->d_cq, w->g_cq, eps_of(d), s));
+    if (staged_entries(d, w)) {
+      const int rc = finish_entries(d, w, c, ws.staged, B, nullptr, ctx_lens, s);
+      if (rc != MLA_OK) return rc;
+    }
   }
   {  // [q^C | q^R] = [W_UQ; W_QR] c^q: q^C to the workspace, RoPE'd q^R into columns
      // [d_c, d_c + d_hr) of each head's absorbed query row
@@ -564,7 +591,7 @@ int mla_prefill(const mla_dims* d, const mla_weights* w, const mla_paged_cache* 
   if ((st = validate_cache(d, c)) != MLA_OK) return st;
   if (!w || !w->W_UQ || !w->W_QR || !w->W_DKV || !w->W_KR || !w->W_UK || !w->W_UV || !w->W_O)
     return MLA_ERR_INVALID_ARG;
-  if ((d->d_cq > 0) != (w->W_DQ != nullptr)) return MLA_ERR_INVALID_ARG;
+  if ((d->d_cq > 0) != (w->W_DQ != nullptr) || !weights_norm_ok(d, w)) return MLA_ERR_INVALID_ARG;
   if (!h || !u || batch <= 0 || T <= 0) return MLA_ERR_INVALID_ARG;
   if ((int64_t)T > (int64_t)c->max_blocks_per_seq * c->block_size) return MLA_ERR_INVALID_ARG;
   if ((int64_t)batch * T > (1LL << 30)) return MLA_ERR_UNSUPPORTED;
@@ -588,6 +615,7 @@ int mla_prefill(const mla_dims* d, const mla_weights* w, const mla_paged_cache* 
     g.M = M; g.N = d->d_cq; g.K = d->d_model;
     g.epi = dense(ws.cq, d->d_cq);
     MLA_HIP(gemm_run(t, g, ws.cq_p, ws.partial, s));
+    if (w->g_cq) MLA_HIP(rmsnorm_rows(t, ws.cq, M, d->d_cq, d->d_cq, w->g_cq, eps_of(d), s));
     qin = ws.cq;
   }
   {  // q^C -> columns [0, d_h) of each head's [q^C | q^R] row
@@ -614,6 +642,7 @@ int mla_prefill(const mla_dims* d, const mla_weights* w, const mla_paged_cache* 
     g.epi = dense(ws.kvd, E);
     g.epi.rope_col0 = d->d_c; g.epi.d_hr = d->d_hr; g.epi.rope_tab = ws.rope;
     MLA_HIP(gemm_run(t, g, ws.kv_p, ws.partial, s));
+    if (w->g_ckv) MLA_HIP(rmsnorm_rows(t, ws.kvd, M, d->d_c, E, w->g_ckv, eps_of(d), s));
     if (fp8_cache(d))
       MLA_HIP(quantize_entries_run(ws.kvd, E, M, quant_dst(c, ws.seq, ws.pos), s));
     else

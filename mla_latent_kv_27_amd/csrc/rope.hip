@@ -1,4 +1,5 @@
-// Small helper kernels: RoPE angle tables, prefill row bookkeeping, paged row scatter.
+// Small helper kernels: RoPE angle tables, the latent RMSNorm, prefill row bookkeeping, paged
+// row scatter.
 //
 // RoPE follows the reading of the DeepSeek-V2 summary page's App. C ("RoPE(.)", the RoFormer
 // rotation it cites): interleaved pairs (x_2k, x_2k+1) rotate by pos * theta_k, theta_k =
@@ -40,6 +41,38 @@ hipError_t rope_table(const int32_t* pos, int n, int d_hr, const RopeFreq& f, fl
   return hipGetLastError();
 }
 
+// RMSNorm after the compressed latents (section 3.1.2 of the DeepSeek-V2 summary page): one wave
+// per row; the mean square is accumulated in fp32 from the stored values.
+template <typename T>
+__global__ void __launch_bounds__(256)
+    rmsnorm_rows_kernel(T* __restrict__ x, int n, int W, int64_t ld, const T* __restrict__ g, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= n) return;
+  T* r = x + row * ld;
+  float ss = 0.f;
+  for (int i = lane; i < W; i += 64) {
+    const float v = to_f32(r[i]);
+    ss += v * v;
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) ss = wave_sum_xor(ss, m);
+  const float inv = 1.0f / sqrtf(ss / (float)W + eps);
+  for (int i = lane; i < W; i += 64) r[i] = from_f32<T>(to_f32(r[i]) * inv * to_f32(g[i]));
+}
+
+hipError_t rmsnorm_rows(DType t, void* x, int n, int W, int64_t ld, const void* gain, float eps, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const dim3 grid((n + 3) / 4), block(256);
+  if (t == DType::BF16)
+    hipLaunchKernelGGL(rmsnorm_rows_kernel<bf16>, grid, block, 0, s, reinterpret_cast<bf16*>(x), n, W, ld,
+                       reinterpret_cast<const bf16*>(gain), eps);
+  else
+    hipLaunchKernelGGL(rmsnorm_rows_kernel<float>, grid, block, 0, s, reinterpret_cast<float*>(x), n, W, ld,
+                       reinterpret_cast<const float*>(gain), eps);
+  return hipGetLastError();
+}
+
 __global__ void __launch_bounds__(256) prefill_rows_kernel(int n, int T, int32_t* seq, int32_t* pos) {
   const int r = blockIdx.x * blockDim.x + threadIdx.x;
   if (r < n) {
@@ -63,7 +96,7 @@ __global__ void __launch_bounds__(256)
   const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (i >= (int64_t)n * cpr) return;
   const int r = (int)(i / cpr), c = (int)(i % cpr);
-  const int sq = row_seq[r], ps = row_pos[r];
+  const int sq = row_seq ? row_seq[r] : r, ps = row_pos[r];
   const int64_t slot = (int64_t)bt[(int64_t)sq * max_blocks + ps / block_size] * block_size + ps % block_size;
   st16(pool + slot * row_bytes + c * 16, ld16(src + (int64_t)r * row_bytes + c * 16));
 }

@@ -34,7 +34,7 @@ class DeviceLayer:
         self.cdims = make_dims(dims.d_model, dims.n_h, dims.d_h, dims.d_c, dims.d_cq, dims.d_hr, dims.dtype,
                                dims.softmax_scale, dims.rope_base, cache_dtype, rope_scale=dims.rope_scale,
                                rope_orig_ctx=dims.rope_orig_ctx, yarn_alpha=dims.yarn_alpha,
-                               yarn_beta=dims.yarn_beta, yarn_mscale=dims.yarn_mscale)
+                               yarn_beta=dims.yarn_beta, yarn_mscale=dims.yarn_mscale, rms_eps=dims.rms_eps)
         self.cweights = make_weights(self.W)
 
     def clone(self) -> "DeviceLayer":

@@ -120,6 +120,10 @@ WORKLOADS = {
     "v2_decode_b64_ctx8192": Workload("v2_decode_b64_ctx8192", V2, "decode", batch=64, ctx=8192),
     "v2_decode_b64_ctx8192_fp8": Workload("v2_decode_b64_ctx8192_fp8", V2, "decode", batch=64, ctx=8192,
                                           cache="fp8"),
+    # the same step with the latent RMSNorms (section 3.1.2) and YaRN (section 3.1.4) on
+    "v2_decode_b64_ctx8192_norm_yarn": Workload("v2_decode_b64_ctx8192_norm_yarn",
+                                                dataclasses.replace(V2_YARN, latent_norm=True), "decode",
+                                                batch=64, ctx=8192),
     "v2_prefill_16384": Workload("v2_prefill_16384", V2, "prefill", batch=1, tokens=16384),
     "v2_long_decode_b4": Workload("v2_long_decode_b4", V2, "decode", batch=4, ctx_lo=32768,
                                   ctx_hi=131072),

@@ -44,7 +44,8 @@ def _dims(**kw):
                                  dict(rope_scale=40.0, rope_orig_ctx=0),
                                  dict(rope_scale=40.0, rope_orig_ctx=4096, yarn_alpha=32.0, yarn_beta=32.0),
                                  dict(rope_scale=40.0, rope_orig_ctx=4096, yarn_alpha=-1.0),
-                                 dict(rope_scale=40.0, rope_orig_ctx=4096, yarn_mscale=-0.1)])
+                                 dict(rope_scale=40.0, rope_orig_ctx=4096, yarn_mscale=-0.1),
+                                 dict(rms_eps=-1e-6), dict(rms_eps=float("inf"))])
 def test_invalid_dims_rejected(bad):
     out = ctypes.c_size_t(0)
     st = M.lib().mla_workspace_size(ctypes.byref(_dims(**bad)), M.OP_DECODE, 1, 0, 4, 0, ctypes.byref(out))
@@ -70,8 +71,8 @@ def _fake(n):
     return ctypes.c_void_p(0x1000 * n)
 
 
-def _weights(dq=True):
-    return M.Weights(*( [_fake(1) if dq else None] + [_fake(i) for i in range(2, 9)] ))
+def _weights(dq=True, g_cq=None, g_ckv=None):
+    return M.Weights(*([_fake(1) if dq else None] + [_fake(i) for i in range(2, 9)] + [g_cq, g_ckv]))
 
 
 def _cache(num_blocks=4, block=64, maxb=2):
@@ -96,6 +97,10 @@ def test_decode_host_validation():
     # W_DQ must be present iff d_cq > 0
     assert _decode(w=_weights(dq=False)) == M.MLA_ERR_INVALID_ARG
     assert _decode(dims=_dims(d_cq=0)) == M.MLA_ERR_INVALID_ARG
+    # the c^q norm needs query compression; the c^KV norm does not
+    assert _decode(dims=_dims(d_cq=0), w=_weights(dq=False, g_cq=_fake(50))) == M.MLA_ERR_INVALID_ARG
+    assert _decode(dims=_dims(d_cq=0), w=_weights(dq=False, g_ckv=_fake(51)), max_ctx=127) == M.MLA_ERR_WORKSPACE
+    assert _decode(w=_weights(g_cq=_fake(50), g_ckv=_fake(51)), max_ctx=127) == M.MLA_ERR_WORKSPACE
     # ctx_len + 1 must fit in max_blocks_per_seq * block_size (2 * 64)
     assert _decode(max_ctx=128) == M.MLA_ERR_INVALID_ARG
     # no cache pool

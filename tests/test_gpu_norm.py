@@ -1,0 +1,122 @@
+"""GPU parity of the latent RMSNorm (section 3.1.2 of the DeepSeek-V2 summary page; the oracle's
+reading is pinned in test_rmsnorm_oracle.py) through the C ABI: the cache writer, decode and
+prefill with the c^q and c^KV norms, on V2, V2-Lite (no query compression: the c^KV norm only)
+and the fp32 tiny layer, plus the fp8 cache, whose quantiser takes the normalised entries."""
+import numpy as np
+import pytest
+
+import mla_synth as S
+import oracle.latent_fp8 as F
+import oracle.mla_oracle as O
+from tests.gpu_util import check, have_gpu, torch
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not have_gpu(), reason="needs a GPU")]
+
+import mla_latent_kv_27_amd as M  # noqa: E402
+from mla_latent_kv_27_amd import workload as WL  # noqa: E402
+
+CASES = {"tiny": (S.TINY_NORM, "normal002", 4), "v2lite": (S.V2_LITE_NORM, "rmsnorm", 64),
+         "v2": (S.V2_NORM, "rmsnorm", 64)}
+
+
+@pytest.mark.parametrize("name", ["tiny", "v2"])
+def test_cache_append_normalises_the_latent(name):
+    dims, recipe, block = CASES[name]
+    W = S.make_weights(dims)
+    layer = WL.DeviceLayer(dims, W)
+    lens = [37, 5]
+    pool = WL.PagedPool(dims, lens, block_size=block)
+    rows = [(b, p) for p in range(max(lens)) for b in range(2) if p < lens[b]]
+    h = S.hidden_step(dims, len(rows), recipe, step=5)
+    seq = torch.tensor([r[0] for r in rows], dtype=torch.int32, device="cuda")
+    pos = torch.tensor([r[1] for r in rows], dtype=torch.int32, device="cuda")
+    ws = WL.ws_tensor(M.workspace_size(layer.cdims, M.OP_CACHE_APPEND, max_tokens=len(rows)))
+    M.cache_append(layer.cdims, layer.cweights, pool.ccache, WL.to_device(h, dims), seq, pos, ws)
+    torch.cuda.synchronize()
+    ref = O.latent_entries(W, dims, h, np.array([r[1] for r in rows]))
+    got = np.zeros_like(ref)
+    for b in range(2):
+        e = pool.read_entries(b, lens[b])
+        idx = [i for i, r in enumerate(rows) if r[0] == b]
+        got[idx] = e[[rows[i][1] for i in idx]]
+    check(got, ref, dims.dtype, f"{name} normalised entries")
+    if name == "v2":  # latents far above eps: unit mean square before the gain
+        ms = np.mean(np.square(got[:, :dims.d_c] / np.asarray(W["g_ckv"], np.float64)), axis=1)
+        assert np.allclose(ms, 1.0, rtol=2e-2)
+
+
+@pytest.mark.parametrize("name,lens,splits", [("tiny", [16, 3, 0, 40], 0), ("v2lite", [0, 100, 64, 257], 0),
+                                              ("v2", [0, 63, 200], 0), ("v2", [300, 77], 3)])
+def test_decode_end_to_end(name, lens, splits):
+    dims, recipe, block = CASES[name]
+    W = S.make_weights(dims)
+    layer = WL.DeviceLayer(dims, W)
+    B = len(lens)
+    pool = WL.PagedPool(dims, [L + 1 for L in lens], block_size=block)
+    WL.build_context(layer, pool, lens, recipe)
+    h = S.hidden_step(dims, B, recipe)
+    u = torch.empty((B, dims.d_model), dtype=WL.torch_dtype(dims), device="cuda")
+    oh = torch.empty((B, dims.n_h, dims.d_h), dtype=torch.float32, device="cuda")
+    ctx = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    M.decode(layer.cdims, layer.cweights, pool.ccache, WL.to_device(h, dims), ctx, max(lens), u,
+             WL.decode_workspace(layer, B, max(lens), splits), num_splits=splits, o_heads=oh)
+    torch.cuda.synchronize()
+    caches = [O.latent_entries(W, dims, S.hidden_history(dims, b, L, recipe), np.arange(L))
+              for b, L in enumerate(lens)]
+    ref = O.mla_decode(W, dims, h, caches)
+    check(oh.cpu().numpy(), ref["o"], dims.dtype, f"{name} norm decode o")
+    check(u.float().cpu().numpy(), ref["u"], dims.dtype, f"{name} norm decode u")
+    new = np.stack([pool.read_entries(b, L + 1)[L] for b, L in enumerate(lens)])
+    check(new, ref["entry"], dims.dtype, f"{name} norm decode new entries")
+
+
+@pytest.mark.parametrize("name,batch,T", [("tiny", 1, 37), ("v2lite", 1, 200), ("v2", 2, 130)])
+def test_prefill(name, batch, T):
+    dims, recipe, block = CASES[name]
+    W = S.make_weights(dims)
+    layer = WL.DeviceLayer(dims, W)
+    pool = WL.PagedPool(dims, [T] * batch, block_size=8 if name == "tiny" else 64)
+    hs = [S.hidden_history(dims, b, T, recipe) for b in range(batch)]
+    u = torch.empty((batch, T, dims.d_model), dtype=WL.torch_dtype(dims), device="cuda")
+    oh = torch.empty((batch, T, dims.n_h, dims.d_h), dtype=torch.float32, device="cuda")
+    M.prefill(layer.cdims, layer.cweights, pool.ccache, WL.to_device(np.stack(hs), dims), u,
+              WL.prefill_workspace(layer, batch, T), o_heads=oh)
+    torch.cuda.synchronize()
+    for b in range(batch):
+        ref = O.mla_prefill(W, dims, hs[b])
+        check(pool.read_entries(b, T), ref["cache"], dims.dtype, f"{name} norm prefill cache b={b}")
+        check(oh[b].cpu().numpy(), ref["o"], dims.dtype, f"{name} norm prefill o b={b}")
+        check(u[b].float().cpu().numpy(), ref["u"], dims.dtype, f"{name} norm prefill u b={b}")
+
+
+def test_fp8_cache_quantises_the_normalised_entries():
+    dims = S.V2_NORM
+    W = S.make_weights(dims)
+    layer = WL.DeviceLayer(dims, W, cache_dtype="fp8")
+    lens = [40, 333]
+    B = len(lens)
+    pool = WL.PagedPool(dims, [L + 1 for L in lens], fp8=True)
+    WL.build_context(layer, pool, lens, "rmsnorm")
+    h = S.hidden_step(dims, B, "rmsnorm")
+    u = torch.empty((B, dims.d_model), dtype=torch.bfloat16, device="cuda")
+    oh = torch.empty((B, dims.n_h, dims.d_h), dtype=torch.float32, device="cuda")
+    ctx = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    M.decode(layer.cdims, layer.cweights, pool.ccache, WL.to_device(h, dims), ctx, max(lens), u,
+             WL.decode_workspace(layer, B, max(lens)), o_heads=oh)
+    torch.cuda.synchronize()
+    # attention over the codes the writer stored (an e4m3 code is a coarse function of its input:
+    # the device's normalised bf16 entry may sit one bf16 step from the oracle's and move a code by
+    # one e4m3 step, so the codes themselves are compared below with that allowance)
+    hist = [pool.read_codes(b, L) for b, L in enumerate(lens)]
+    ref = F.mla_decode_fp8(W, dims, h, [c for c, _ in hist], [s for _, s in hist])
+    check(oh.cpu().numpy(), ref["o"], dims.dtype, "norm fp8 decode o")
+    check(u.float().cpu().numpy(), ref["u"], dims.dtype, "norm fp8 decode u")
+    for b, L in enumerate(lens):
+        hh = S.hidden_history(dims, b, L, "rmsnorm")
+        ref_codes, ref_scales = F.quantize_entries(F.bf16_round(O.latent_entries(W, dims, hh, np.arange(L))), dims.d_c)
+        got_codes, got_scales = hist[b]
+        assert np.mean(got_codes == ref_codes) >= 0.95, b
+        d = np.abs(F.dequantize(got_codes, got_scales, dims.d_c) - F.dequantize(ref_codes, ref_scales, dims.d_c))
+        step = np.maximum(np.abs(F.dequantize(ref_codes, ref_scales, dims.d_c)) * 2.0 ** -3,
+                          np.repeat(ref_scales, [dims.d_c, dims.d_hr], axis=1) * 2.0 ** -9)
+        assert np.all(d <= 1.05 * step + 1e-30), b
