@@ -60,7 +60,7 @@ typedef enum {
 
 typedef enum { MLA_F32 = 0, MLA_BF16 = 1, MLA_FP8_E4M3 = 2 } mla_dtype;
 
-typedef enum { MLA_OP_CACHE_APPEND = 0, MLA_OP_PREFILL = 1, MLA_OP_DECODE = 2 } mla_op;
+typedef enum { MLA_OP_CACHE_APPEND = 0, MLA_OP_PREFILL = 1, MLA_OP_DECODE = 2, MLA_OP_PREFILL_CHUNK = 3 } mla_op;
 
 /* Layer sizes, in the pages' notation (section 3.1.2; App. B.1). */
 typedef struct {
@@ -126,6 +126,8 @@ typedef struct {
  *   MLA_OP_PREFILL:      batch sequences of max_tokens tokens each.
  *   MLA_OP_DECODE:       batch sequences, max_ctx_len = largest ctx_lens[b] the call may see,
  *                        num_splits = the value that will be passed to mla_decode (0 = auto).
+ *   MLA_OP_PREFILL_CHUNK: batch sequences, chunks of max_tokens tokens, max_ctx_len = the
+ *                        largest start position (tokens already cached) a call may see.
  * The size is an upper bound for every call whose sizes (batch, tokens, context) do not exceed
  * these, with the same num_splits.  Returns MLA_OK or MLA_ERR_INVALID_ARG/UNSUPPORTED.
  */
@@ -165,6 +167,26 @@ int mla_cache_append(const mla_dims *dims, const mla_weights *w, const mla_paged
 int mla_prefill(const mla_dims *dims, const mla_weights *w, const mla_paged_cache *cache,
                 const void *h, int32_t batch, int32_t T, void *u, float *o_heads,
                 void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Chunked prefill: the next T tokens of each of `batch` sequences whose first start_pos[b]
+ * tokens are already in the cache (App. C's causal sum over j = 1..t with t = start_pos[b] + i:
+ * every new token attends to the whole cached prefix and to the new tokens up to itself).
+ * mla_prefill is the case start_pos == 0.  Writes the new tokens' cache entries at positions
+ * start_pos[b] .. start_pos[b] + T - 1 (sequence b = block_table row b) and u.  Attention uses
+ * the un-absorbed form over the prefix read back from the cache (dequantised to bf16 for the fp8
+ * cache) and the chunk's own entries as computed (as mla_prefill does), with per-head keys and
+ * values built in the workspace.
+ *   h  [batch][T][d_model], u [batch][T][d_model] (dims->dtype)
+ *   start_pos [batch] int32 (device): tokens already cached in each sequence.
+ *   max_start (host) >= every start_pos[b]; sizes the key buffers.  Requires
+ *             max_start + T <= max_blocks_per_seq * block_size.
+ *   o_heads: NULL, or fp32 [batch][T][n_h][d_h].
+ * The workspace is MLA_OP_PREFILL_CHUNK's for (batch, T, max_start).
+ */
+int mla_prefill_chunk(const mla_dims *dims, const mla_weights *w, const mla_paged_cache *cache,
+                      const void *h, int32_t batch, int32_t T, const int32_t *start_pos, int32_t max_start,
+                      void *u, float *o_heads, void *workspace, size_t ws_bytes, void *stream);
 
 /*
  * One decode step for `batch` sequences (App. C with the absorption that the page derives

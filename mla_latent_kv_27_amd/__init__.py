@@ -21,10 +21,10 @@ MLA_ERR_HIP = -4
 MLA_F32 = 0
 MLA_BF16 = 1
 MLA_FP8_E4M3 = 2
-OP_CACHE_APPEND, OP_PREFILL, OP_DECODE = 0, 1, 2
+OP_CACHE_APPEND, OP_PREFILL, OP_DECODE, OP_PREFILL_CHUNK = 0, 1, 2, 3
 
 EXPORTED = (
-    "mla_workspace_size", "mla_cache_append", "mla_prefill", "mla_decode", "mla_decode_attention",
+    "mla_workspace_size", "mla_cache_append", "mla_prefill", "mla_prefill_chunk", "mla_decode", "mla_decode_attention",
     "mla_decode_auto_splits", "mla_quantize_entries", "mla_status_string",
 )
 
@@ -70,6 +70,7 @@ def lib() -> ctypes.CDLL:
         L.mla_workspace_size.argtypes = [D, ctypes.c_int, I32, I32, I32, I32, ctypes.POINTER(SZ)]
         L.mla_cache_append.argtypes = [D, W, C, P, I32, P, P, P, SZ, P]
         L.mla_prefill.argtypes = [D, W, C, P, I32, I32, P, P, P, SZ, P]
+        L.mla_prefill_chunk.argtypes = [D, W, C, P, I32, I32, P, I32, P, P, P, SZ, P]
         L.mla_decode.argtypes = [D, W, C, P, I32, P, I32, I32, P, P, P, SZ, P]
         L.mla_decode_attention.argtypes = [D, C, P, I32, P, I32, I32, P, P, P, SZ, P]
         L.mla_decode_auto_splits.argtypes = [D, I32, I32]
@@ -78,7 +79,8 @@ def lib() -> ctypes.CDLL:
         L.mla_decode_auto_splits.restype = I32
         L.mla_status_string.argtypes = [ctypes.c_int]
         L.mla_status_string.restype = ctypes.c_char_p
-        for n in ("mla_workspace_size", "mla_cache_append", "mla_prefill", "mla_decode", "mla_decode_attention"):
+        for n in ("mla_workspace_size", "mla_cache_append", "mla_prefill", "mla_prefill_chunk", "mla_decode",
+                  "mla_decode_attention"):
             getattr(L, n).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -156,6 +158,14 @@ def prefill(dims, weights, cache, h, u, workspace, o_heads=None, stream=None):
     _check(lib().mla_prefill(ctypes.byref(dims), ctypes.byref(weights), ctypes.byref(cache), _ptr(h),
                              int(h.shape[0]), int(h.shape[1]), _ptr(u), _ptr(o_heads), p, n, _stream(stream)),
            "mla_prefill")
+
+
+def prefill_chunk(dims, weights, cache, h, start_pos, max_start, u, workspace, o_heads=None, stream=None):
+    """h, u: [batch][T][d_model]; start_pos: int32 device tensor [batch] of tokens already cached."""
+    p, n = _ws(workspace)
+    _check(lib().mla_prefill_chunk(ctypes.byref(dims), ctypes.byref(weights), ctypes.byref(cache), _ptr(h),
+                                   int(h.shape[0]), int(h.shape[1]), _ptr(start_pos), int(max_start), _ptr(u),
+                                   _ptr(o_heads), p, n, _stream(stream)), "mla_prefill_chunk")
 
 
 def decode(dims, weights, cache, h, ctx_lens, max_ctx_len, u, workspace, num_splits=0, o_heads=None,

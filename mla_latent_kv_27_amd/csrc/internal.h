@@ -109,8 +109,15 @@ hipError_t rope_table(const int32_t* pos, int n, int d_hr, const RopeFreq& f, fl
 // x[r][0..W) <- gain * x / sqrt(mean(x^2) + eps) for rows r < n, ld elements apart, in place
 // (the RMSNorm of the compressed latents).
 hipError_t rmsnorm_rows(DType t, void* x, int n, int W, int64_t ld, const void* gain, float eps, hipStream_t s);
-// pos[r] = r % T, seq[r] = r / T for r < n.
-hipError_t prefill_rows(int n, int T, int32_t* seq, int32_t* pos, hipStream_t s);
+// seq[r] = r / T, pos[r] = r % T (+ start[seq[r]] when start != nullptr) for r < n.
+hipError_t prefill_rows(int n, int T, int32_t* seq, int32_t* pos, hipStream_t s, const int32_t* start = nullptr);
+// Dense key rows of a chunked prefill, out[b][j] for sequences b < S and j < Tk (entries of E
+// values): the cached prefix j < start[b] from the pages (an fp8 pool, scales != nullptr, is
+// dequantised, value(code) * s, to bf16), then the chunk's own rows fresh[b][0..T) as computed,
+// then zeros.
+hipError_t gather_entries(DType t, const void* pool, const float* scales, const int32_t* block_table, int max_blocks,
+                          int block_size, const int32_t* start, const void* fresh, int T, int S, int Tk, int E, int d_c,
+                          void* out, hipStream_t s);
 // Copies dense rows src[r][0..width) into paged cache slots (row_seq/row_pos/block_table;
 // row_seq == nullptr: row r belongs to sequence r).
 hipError_t scatter_rows(DType t, const void* src, int n, int width, void* pool,
@@ -140,16 +147,21 @@ struct DecodeAttnParams {
 bool decode_supported(int d_c, int d_hr);
 hipError_t decode_attention(DType t, const DecodeAttnParams& p, hipStream_t s);
 
+// T queries per sequence at positions q_off[s] .. q_off[s] + T - 1 (q_off == nullptr: 0), each
+// attending to keys 0 .. its position; a sequence's keys sit in a slot of Tk >= max q_off + T rows,
+// of which the first q_off[s] + T are valid.
 struct PrefillAttnParams {
   const void* q;      // [S*T][n_h][d_h + d_hr]   ([q^C | q^R])
-  const void* k;      // [n_h][S*T][d_h]          (W_UK_i c^KV)
-  const void* kr;     // [S*T] rows of ld_kr elements; k^R at column kr_off
+  const void* k;      // [n_h][S*Tk][d_h]         (W_UK_i c^KV)
+  const void* kr;     // [S*Tk] rows of ld_kr elements; k^R at column kr_off
   int64_t ld_kr;
   int kr_off;
-  const void* vt;     // [n_h][d_h][S*T]          (W_UV_i c^KV, token-contiguous)
+  const void* vt;     // [n_h][d_h][S][Tkp]       (W_UV_i c^KV, token-contiguous; Tkp = Tk rounded up to 64)
   void* o;            // [S*T][n_h][d_h]
   float* o_f32;       // optional fp32 copy
   int S, T, n_h, d_h, d_hr;
+  int Tk = 0;                     // 0: T
+  const int32_t* q_off = nullptr;
   float scale_log2;
 };
 bool prefill_supported(int d_h, int d_hr);

@@ -221,23 +221,27 @@ DecodeWs carve_decode(Carve& cv, const mla_dims* d, int B, int max_ctx_len, int 
 struct PrefillWs {
   int32_t *seq, *pos;
   float2* rope;
-  void *cq, *qp, *kvd, *kp, *vt, *o;
+  void *cq, *qp, *kvd, *kva, *kp, *vt, *o;  // kva: chunked prefill's gathered keys (else kvd)
   float* partial;
   GemmPlan cq_p, qc_p, qr_p, kv_p, k_p, v_p, out_p;
-  int Tp;
+  int Tk, Tp;  // key rows per sequence (T, or max_start + T when chunked), rounded up to 64
 };
-PrefillWs carve_prefill(Carve& cv, const mla_dims* d, int S, int T, int cus) {
+// chunked: keys are the cached prefix plus the new rows, max_start + T per sequence
+PrefillWs carve_prefill(Carve& cv, const mla_dims* d, int S, int T, int cus, bool chunked = false,
+                        int max_start = 0) {
   PrefillWs w;
   const size_t es = dsize(dt(d));
   const int M = S * T;
-  w.Tp = (T + 63) / 64 * 64;
+  w.Tk = chunked ? max_start + T : T;
+  const int Mk = S * w.Tk;
+  w.Tp = (w.Tk + 63) / 64 * 64;
   const int qw = d->n_h * (d->d_h + d->d_hr);
   w.cq_p = d->d_cq > 0 ? gemm_plan(M, d->d_cq, d->d_model, 1, cus, sk(d)) : GemmPlan{};
   w.qc_p = gemm_plan(M, d->n_h * d->d_h, q_in(d), 1, cus, sk(d));
   w.qr_p = gemm_plan(M, d->n_h * d->d_hr, q_in(d), 1, cus, sk(d));
   w.kv_p = gemm_plan(M, entry(d), d->d_model, 1, cus, sk(d));
-  w.k_p = gemm_plan(M, d->n_h * d->d_h, d->d_c, 1, cus, sk(d));
-  w.v_p = gemm_plan(d->n_h * d->d_h, M, d->d_c, 1, cus, sk(d));
+  w.k_p = gemm_plan(Mk, d->n_h * d->d_h, d->d_c, 1, cus, sk(d));
+  w.v_p = gemm_plan(d->n_h * d->d_h, Mk, d->d_c, 1, cus, sk(d));
   w.out_p = gemm_plan(M, d->d_model, d->n_h * d->d_h, 1, cus, sk(d));
   w.seq = cv.take<int32_t>((size_t)M * 4);
   w.pos = cv.take<int32_t>((size_t)M * 4);
@@ -245,14 +249,15 @@ PrefillWs carve_prefill(Carve& cv, const mla_dims* d, int S, int T, int cus) {
   w.cq = cv.take<char>((size_t)M * d->d_cq * es);
   w.qp = cv.take<char>((size_t)M * qw * es);
   w.kvd = cv.take<char>((size_t)M * entry(d) * es);
-  w.kp = cv.take<char>((size_t)M * d->n_h * d->d_h * es);
+  w.kva = chunked ? cv.take<char>((size_t)Mk * entry(d) * es) : w.kvd;
+  w.kp = cv.take<char>((size_t)Mk * d->n_h * d->d_h * es);
   w.vt = cv.take<char>((size_t)d->n_h * d->d_h * S * w.Tp * es);
   w.o = cv.take<char>((size_t)M * d->n_h * d->d_h * es);
   size_t mp = std::max({gemm_partial_bound(M, d->n_h * d->d_h, q_in(d), 1, cus, sk(d)),
                         gemm_partial_bound(M, d->n_h * d->d_hr, q_in(d), 1, cus, sk(d)),
                         gemm_partial_bound(M, entry(d), d->d_model, 1, cus, sk(d)),
-                        gemm_partial_bound(M, d->n_h * d->d_h, d->d_c, 1, cus, sk(d)),
-                        gemm_partial_bound(d->n_h * d->d_h, M, d->d_c, 1, cus, sk(d)),
+                        gemm_partial_bound(Mk, d->n_h * d->d_h, d->d_c, 1, cus, sk(d)),
+                        gemm_partial_bound(d->n_h * d->d_h, Mk, d->d_c, 1, cus, sk(d)),
                         gemm_partial_bound(M, d->d_model, d->n_h * d->d_h, 1, cus, sk(d))});
   if (d->d_cq > 0) mp = std::max(mp, gemm_partial_bound(M, d->d_cq, d->d_model, 1, cus, sk(d)));
   w.partial = cv.take<float>(mp);
@@ -351,6 +356,114 @@ int run_cache_writer(const mla_dims* d, const mla_weights* w, const mla_paged_ca
   return MLA_OK;
 }
 
+// mla_prefill (start == nullptr) and mla_prefill_chunk (the new rows start at start[b]; the keys
+// are the cached prefix gathered back from the pages plus the new rows).
+int prefill_impl(const mla_dims* d, const mla_weights* w, const mla_paged_cache* c, const void* h, int32_t batch,
+                 int32_t T, const int32_t* start, int32_t max_start, void* u, float* o_heads, void* workspace,
+                 size_t ws_bytes, void* stream) {
+  int st = validate_dims(d);
+  if (st != MLA_OK) return st;
+  if ((st = validate_cache(d, c)) != MLA_OK) return st;
+  if (!w || !w->W_UQ || !w->W_QR || !w->W_DKV || !w->W_KR || !w->W_UK || !w->W_UV || !w->W_O)
+    return MLA_ERR_INVALID_ARG;
+  if ((d->d_cq > 0) != (w->W_DQ != nullptr) || !weights_norm_ok(d, w)) return MLA_ERR_INVALID_ARG;
+  if (!h || !u || batch <= 0 || T <= 0) return MLA_ERR_INVALID_ARG;
+  const bool chunked = start != nullptr;
+  if ((int64_t)max_start + T > (int64_t)c->max_blocks_per_seq * c->block_size) return MLA_ERR_INVALID_ARG;
+  if ((int64_t)batch * (max_start + T) > (1LL << 30)) return MLA_ERR_UNSUPPORTED;
+  if (!prefill_supported(d->d_h, d->d_hr)) return MLA_ERR_UNSUPPORTED;
+  const int cus = device_cus();
+  Carve sz(nullptr);
+  carve_prefill(sz, d, batch, T, cus, chunked, max_start);
+  if (!workspace || ws_bytes < sz.off) return MLA_ERR_WORKSPACE;
+  Carve cv(workspace);
+  PrefillWs ws = carve_prefill(cv, d, batch, T, cus, chunked, max_start);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const DType t = dt(d);
+  const int M = batch * T, E = entry(d), qw = q_in(d), QD = d->d_h + d->d_hr;
+  const int Mk = batch * ws.Tk;  // key rows
+
+  MLA_HIP(prefill_rows(M, T, ws.seq, ws.pos, s, start));
+  MLA_HIP(rope_table(ws.pos, M, d->d_hr, freq_of(d), ws.rope, s));
+  const void* qin = h;
+  if (d->d_cq > 0) {
+    GemmParams g;
+    g.A = h; g.lda = d->d_model; g.B0 = w->W_DQ; g.ldb = d->d_model;
+    g.M = M; g.N = d->d_cq; g.K = d->d_model;
+    g.epi = dense(ws.cq, d->d_cq);
+    MLA_HIP(gemm_run(t, g, ws.cq_p, ws.partial, s));
+    if (w->g_cq) MLA_HIP(rmsnorm_rows(t, ws.cq, M, d->d_cq, d->d_cq, w->g_cq, eps_of(d), s));
+    qin = ws.cq;
+  }
+  {  // q^C -> columns [0, d_h) of each head's [q^C | q^R] row
+    GemmParams g;
+    g.A = qin; g.lda = qw; g.B0 = w->W_UQ; g.ldb = qw;
+    g.M = M; g.N = d->n_h * d->d_h; g.K = qw;
+    g.epi = dense(ws.qp, (int64_t)d->n_h * QD);
+    g.epi.group = d->d_h; g.epi.group_stride = QD; g.epi.group_off = 0;
+    MLA_HIP(gemm_run(t, g, ws.qc_p, ws.partial, s));
+  }
+  {  // RoPE(q^R) -> columns [d_h, d_h + d_hr)
+    GemmParams g;
+    g.A = qin; g.lda = qw; g.B0 = w->W_QR; g.ldb = qw;
+    g.M = M; g.N = d->n_h * d->d_hr; g.K = qw;
+    g.epi = dense(ws.qp, (int64_t)d->n_h * QD);
+    g.epi.group = d->d_hr; g.epi.group_stride = QD; g.epi.group_off = d->d_h;
+    g.epi.rope_col0 = 0; g.epi.d_hr = d->d_hr; g.epi.rope_tab = ws.rope;
+    MLA_HIP(gemm_run(t, g, ws.qr_p, ws.partial, s));
+  }
+  {  // dense [c^KV | RoPE(k^R)] rows, then copied into the paged cache
+    GemmParams g;
+    g.A = h; g.lda = d->d_model; g.B0 = w->W_DKV; g.B1 = w->W_KR; g.N0 = d->d_c; g.ldb = d->d_model;
+    g.M = M; g.N = E; g.K = d->d_model;
+    g.epi = dense(ws.kvd, E);
+    g.epi.rope_col0 = d->d_c; g.epi.d_hr = d->d_hr; g.epi.rope_tab = ws.rope;
+    MLA_HIP(gemm_run(t, g, ws.kv_p, ws.partial, s));
+    if (w->g_ckv) MLA_HIP(rmsnorm_rows(t, ws.kvd, M, d->d_c, E, w->g_ckv, eps_of(d), s));
+    if (fp8_cache(d))
+      MLA_HIP(quantize_entries_run(ws.kvd, E, M, quant_dst(c, ws.seq, ws.pos), s));
+    else
+      MLA_HIP(scatter_rows(t, ws.kvd, M, E, c->pool, ws.seq, ws.pos, c->block_table, c->max_blocks_per_seq,
+                           c->block_size, s));
+    if (chunked)  // key rows: the cached prefix read back from the pages, then the chunk's rows
+      MLA_HIP(gather_entries(t, c->pool, fp8_cache(d) ? c->scales : nullptr, c->block_table, c->max_blocks_per_seq,
+                             c->block_size, start, ws.kvd, T, batch, ws.Tk, E, d->d_c, ws.kva, s));
+  }
+  {  // k^C_i = W_UK_i c^KV, stored head-major [n_h][M][d_h]
+    GemmParams g;
+    g.A = ws.kva; g.lda = E; g.B0 = w->W_UK; g.ldb = d->d_c;
+    g.M = Mk; g.N = d->n_h * d->d_h; g.K = d->d_c;
+    g.epi = dense(ws.kp, d->d_h);
+    g.epi.group = d->d_h; g.epi.group_stride = (int64_t)Mk * d->d_h;
+    MLA_HIP(gemm_run(t, g, ws.k_p, ws.partial, s));
+  }
+  {  // v^T: rows (head, dim) of W_UV times c^KV^T, token-contiguous [n_h][d_h][S][Tp]
+    GemmParams g;
+    g.A = w->W_UV; g.lda = d->d_c; g.B0 = ws.kva; g.ldb = E;
+    g.M = d->n_h * d->d_h; g.N = Mk; g.K = d->d_c;
+    g.epi = dense(ws.vt, (int64_t)batch * ws.Tp);
+    g.epi.group = ws.Tk; g.epi.group_stride = ws.Tp;
+    MLA_HIP(gemm_run(t, g, ws.v_p, ws.partial, s));
+  }
+  {
+    PrefillAttnParams a{};
+    a.q = ws.qp; a.k = ws.kp; a.kr = ws.kva; a.ld_kr = E; a.kr_off = d->d_c; a.vt = ws.vt;
+    a.o = ws.o; a.o_f32 = o_heads;
+    a.S = batch; a.T = T; a.n_h = d->n_h; a.d_h = d->d_h; a.d_hr = d->d_hr;
+    a.Tk = ws.Tk; a.q_off = start;
+    a.scale_log2 = scale_of(d) * 1.4426950408889634f;
+    MLA_HIP(prefill_attention(t, a, s));
+  }
+  {
+    GemmParams g;
+    g.A = ws.o; g.lda = (int64_t)d->n_h * d->d_h; g.B0 = w->W_O; g.ldb = (int64_t)d->n_h * d->d_h;
+    g.M = M; g.N = d->d_model; g.K = d->n_h * d->d_h;
+    g.epi = dense(u, d->d_model);
+    MLA_HIP(gemm_run(t, g, ws.out_p, ws.partial, s));
+  }
+  return MLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -392,6 +505,10 @@ int mla_workspace_size(const mla_dims* d, int op, int32_t batch, int32_t max_tok
       carve_decode(cv, d, batch, max_ctx_len, num_splits, cus);
       break;
     }
+    case MLA_OP_PREFILL_CHUNK:
+      if (batch <= 0 || max_tokens <= 0 || max_ctx_len < 0) return MLA_ERR_INVALID_ARG;
+      carve_prefill(cv, d, batch, max_tokens, cus, true, max_ctx_len);
+      break;
     default: return MLA_ERR_INVALID_ARG;
   }
   *bytes = cv.off;
@@ -586,101 +703,14 @@ int mla_decode(const mla_dims* d, const mla_weights* w, const mla_paged_cache* c
 
 int mla_prefill(const mla_dims* d, const mla_weights* w, const mla_paged_cache* c, const void* h, int32_t batch,
                 int32_t T, void* u, float* o_heads, void* workspace, size_t ws_bytes, void* stream) {
-  int st = validate_dims(d);
-  if (st != MLA_OK) return st;
-  if ((st = validate_cache(d, c)) != MLA_OK) return st;
-  if (!w || !w->W_UQ || !w->W_QR || !w->W_DKV || !w->W_KR || !w->W_UK || !w->W_UV || !w->W_O)
-    return MLA_ERR_INVALID_ARG;
-  if ((d->d_cq > 0) != (w->W_DQ != nullptr) || !weights_norm_ok(d, w)) return MLA_ERR_INVALID_ARG;
-  if (!h || !u || batch <= 0 || T <= 0) return MLA_ERR_INVALID_ARG;
-  if ((int64_t)T > (int64_t)c->max_blocks_per_seq * c->block_size) return MLA_ERR_INVALID_ARG;
-  if ((int64_t)batch * T > (1LL << 30)) return MLA_ERR_UNSUPPORTED;
-  if (!prefill_supported(d->d_h, d->d_hr)) return MLA_ERR_UNSUPPORTED;
-  const int cus = device_cus();
-  Carve sz(nullptr);
-  carve_prefill(sz, d, batch, T, cus);
-  if (!workspace || ws_bytes < sz.off) return MLA_ERR_WORKSPACE;
-  Carve cv(workspace);
-  PrefillWs ws = carve_prefill(cv, d, batch, T, cus);
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const DType t = dt(d);
-  const int M = batch * T, E = entry(d), qw = q_in(d), QD = d->d_h + d->d_hr;
+  return prefill_impl(d, w, c, h, batch, T, nullptr, 0, u, o_heads, workspace, ws_bytes, stream);
+}
 
-  MLA_HIP(prefill_rows(M, T, ws.seq, ws.pos, s));
-  MLA_HIP(rope_table(ws.pos, M, d->d_hr, freq_of(d), ws.rope, s));
-  const void* qin = h;
-  if (d->d_cq > 0) {
-    GemmParams g;
-    g.A = h; g.lda = d->d_model; g.B0 = w->W_DQ; g.ldb = d->d_model;
-    g.M = M; g.N = d->d_cq; g.K = d->d_model;
-    g.epi = dense(ws.cq, d->d_cq);
-    MLA_HIP(gemm_run(t, g, ws.cq_p, ws.partial, s));
-    if (w->g_cq) MLA_HIP(rmsnorm_rows(t, ws.cq, M, d->d_cq, d->d_cq, w->g_cq, eps_of(d), s));
-    qin = ws.cq;
-  }
-  {  // q^C -> columns [0, d_h) of each head's [q^C | q^R] row
-    GemmParams g;
-    g.A = qin; g.lda = qw; g.B0 = w->W_UQ; g.ldb = qw;
-    g.M = M; g.N = d->n_h * d->d_h; g.K = qw;
-    g.epi = dense(ws.qp, (int64_t)d->n_h * QD);
-    g.epi.group = d->d_h; g.epi.group_stride = QD; g.epi.group_off = 0;
-    MLA_HIP(gemm_run(t, g, ws.qc_p, ws.partial, s));
-  }
-  {  // RoPE(q^R) -> columns [d_h, d_h + d_hr)
-    GemmParams g;
-    g.A = qin; g.lda = qw; g.B0 = w->W_QR; g.ldb = qw;
-    g.M = M; g.N = d->n_h * d->d_hr; g.K = qw;
-    g.epi = dense(ws.qp, (int64_t)d->n_h * QD);
-    g.epi.group = d->d_hr; g.epi.group_stride = QD; g.epi.group_off = d->d_h;
-    g.epi.rope_col0 = 0; g.epi.d_hr = d->d_hr; g.epi.rope_tab = ws.rope;
-    MLA_HIP(gemm_run(t, g, ws.qr_p, ws.partial, s));
-  }
-  {  // dense [c^KV | RoPE(k^R)] rows, then copied into the paged cache
-    GemmParams g;
-    g.A = h; g.lda = d->d_model; g.B0 = w->W_DKV; g.B1 = w->W_KR; g.N0 = d->d_c; g.ldb = d->d_model;
-    g.M = M; g.N = E; g.K = d->d_model;
-    g.epi = dense(ws.kvd, E);
-    g.epi.rope_col0 = d->d_c; g.epi.d_hr = d->d_hr; g.epi.rope_tab = ws.rope;
-    MLA_HIP(gemm_run(t, g, ws.kv_p, ws.partial, s));
-    if (w->g_ckv) MLA_HIP(rmsnorm_rows(t, ws.kvd, M, d->d_c, E, w->g_ckv, eps_of(d), s));
-    if (fp8_cache(d))
-      MLA_HIP(quantize_entries_run(ws.kvd, E, M, quant_dst(c, ws.seq, ws.pos), s));
-    else
-      MLA_HIP(scatter_rows(t, ws.kvd, M, E, c->pool, ws.seq, ws.pos, c->block_table, c->max_blocks_per_seq,
-                           c->block_size, s));
-  }
-  {  // k^C_i = W_UK_i c^KV, stored head-major [n_h][M][d_h]
-    GemmParams g;
-    g.A = ws.kvd; g.lda = E; g.B0 = w->W_UK; g.ldb = d->d_c;
-    g.M = M; g.N = d->n_h * d->d_h; g.K = d->d_c;
-    g.epi = dense(ws.kp, d->d_h);
-    g.epi.group = d->d_h; g.epi.group_stride = (int64_t)M * d->d_h;
-    MLA_HIP(gemm_run(t, g, ws.k_p, ws.partial, s));
-  }
-  {  // v^T: rows (head, dim) of W_UV times c^KV^T, token-contiguous [n_h][d_h][S][Tp]
-    GemmParams g;
-    g.A = w->W_UV; g.lda = d->d_c; g.B0 = ws.kvd; g.ldb = E;
-    g.M = d->n_h * d->d_h; g.N = M; g.K = d->d_c;
-    g.epi = dense(ws.vt, (int64_t)batch * ws.Tp);
-    g.epi.group = T; g.epi.group_stride = ws.Tp;
-    MLA_HIP(gemm_run(t, g, ws.v_p, ws.partial, s));
-  }
-  {
-    PrefillAttnParams a{};
-    a.q = ws.qp; a.k = ws.kp; a.kr = ws.kvd; a.ld_kr = E; a.kr_off = d->d_c; a.vt = ws.vt;
-    a.o = ws.o; a.o_f32 = o_heads;
-    a.S = batch; a.T = T; a.n_h = d->n_h; a.d_h = d->d_h; a.d_hr = d->d_hr;
-    a.scale_log2 = scale_of(d) * 1.4426950408889634f;
-    MLA_HIP(prefill_attention(t, a, s));
-  }
-  {
-    GemmParams g;
-    g.A = ws.o; g.lda = (int64_t)d->n_h * d->d_h; g.B0 = w->W_O; g.ldb = (int64_t)d->n_h * d->d_h;
-    g.M = M; g.N = d->d_model; g.K = d->n_h * d->d_h;
-    g.epi = dense(u, d->d_model);
-    MLA_HIP(gemm_run(t, g, ws.out_p, ws.partial, s));
-  }
-  return MLA_OK;
+int mla_prefill_chunk(const mla_dims* d, const mla_weights* w, const mla_paged_cache* c, const void* h,
+                      int32_t batch, int32_t T, const int32_t* start_pos, int32_t max_start, void* u, float* o_heads,
+                      void* workspace, size_t ws_bytes, void* stream) {
+  if (!start_pos || max_start < 0) return MLA_ERR_INVALID_ARG;
+  return prefill_impl(d, w, c, h, batch, T, start_pos, max_start, u, o_heads, workspace, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -41,9 +41,13 @@ __global__ void __launch_bounds__(256) prefill_attn_kernel(PrefillAttnParams p) 
   const int s = (x % (p.n_h * p.S)) / p.n_h;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, ql = lane & 31;
-  const int qi = qt * kBQ + w * 32 + ql;  // query index within the sequence
-  const int64_t MT = (int64_t)p.S * p.T;
-  const int Tp = (p.T + kBKV - 1) / kBKV * kBKV;
+  const int qi = qt * kBQ + w * 32 + ql;  // query index within the chunk
+  const int off = p.q_off ? p.q_off[s] : 0;  // position of the chunk's first query
+  const int qpos = off + qi;
+  const int nk = off + p.T;                  // valid keys of this sequence
+  const int Tk = p.Tk > 0 ? p.Tk : p.T;
+  const int64_t MT = (int64_t)p.S * Tk;
+  const int Tp = (Tk + kBKV - 1) / kBKV * kBKV;
 
   Frag8<T> q[KS];
   {
@@ -72,12 +76,12 @@ __global__ void __launch_bounds__(256) prefill_attn_kernel(PrefillAttnParams p) 
     for (int r = 0; r < 16; ++r) o[d][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  const T* kbase = reinterpret_cast<const T*>(p.k) + ((int64_t)head * MT + (int64_t)s * p.T) * DH;
-  const T* krbase = reinterpret_cast<const T*>(p.kr) + (int64_t)s * p.T * p.ld_kr + p.kr_off;
+  const T* kbase = reinterpret_cast<const T*>(p.k) + ((int64_t)head * MT + (int64_t)s * Tk) * DH;
+  const T* krbase = reinterpret_cast<const T*>(p.kr) + (int64_t)s * Tk * p.ld_kr + p.kr_off;
   const T* vbase = reinterpret_cast<const T*>(p.vt) + ((int64_t)head * DH * p.S + s) * Tp;  // row d at + d*S*Tp
   const int64_t vrow = (int64_t)p.S * Tp;
 
-  const int kt_end = min((p.T + kBKV - 1) / kBKV, ((qt + 1) * kBQ + kBKV - 1) / kBKV);
+  const int kt_end = min((nk + kBKV - 1) / kBKV, (off + (qt + 1) * kBQ + kBKV - 1) / kBKV);
   for (int kt = 0; kt < kt_end; ++kt) {
     const int j0 = kt * kBKV;
     __syncthreads();
@@ -85,16 +89,16 @@ __global__ void __launch_bounds__(256) prefill_attn_kernel(PrefillAttnParams p) 
       const int r = c / (DQ / EPC), cc = (c % (DQ / EPC)) * EPC;
       const int j = j0 + r;
       Chunk16 v = zero16();
-      if (j < p.T) v = cc < DH ? ld16(kbase + (int64_t)j * DH + cc) : ld16(krbase + (int64_t)j * p.ld_kr + (cc - DH));
+      if (j < nk) v = cc < DH ? ld16(kbase + (int64_t)j * DH + cc) : ld16(krbase + (int64_t)j * p.ld_kr + (cc - DH));
       st16(&Ks[r * LDK + cc], v);
     }
     for (int c = tid; c < DH * (kBKV / EPC); c += 256) {
       const int d = c / (kBKV / EPC), cc = (c % (kBKV / EPC)) * EPC;
       Chunk16 v = ld16(vbase + d * vrow + j0 + cc);  // padded rows: always in bounds
-      if (j0 + cc + EPC > p.T) {
+      if (j0 + cc + EPC > nk) {
         T* e = reinterpret_cast<T*>(&v);
         for (int xx = 0; xx < EPC; ++xx)
-          if (j0 + cc + xx >= p.T) e[xx] = from_f32<T>(0.f);
+          if (j0 + cc + xx >= nk) e[xx] = from_f32<T>(0.f);
       }
       st16(&Vt[d * LDV + cc], v);
     }
@@ -118,7 +122,7 @@ __global__ void __launch_bounds__(256) prefill_attn_kernel(PrefillAttnParams p) 
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int j = j0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-        const float v = (j <= qi && j < p.T) ? sc[kb][r] * p.scale_log2 : -INFINITY;
+        const float v = (j <= qpos && j < nk) ? sc[kb][r] * p.scale_log2 : -INFINITY;
         sc[kb][r] = v;
         mx = fmaxf(mx, v);
       }
@@ -217,11 +221,11 @@ struct Pf2Ctx {
   __amdgpu_buffer_rsrc_t kr;  // rope key rows of this sequence, ld_kr elements apart
   __amdgpu_buffer_rsrc_t vt;  // V^T rows of this (sequence, head): row d at d * vrow elements
   int ld_kr, vrow;
-  int T;
+  int T;  // valid keys of this sequence
 };
 
-// Tile kt into stage ST: key rows (clamped to T-1, masked later) and V^T rows (padded to whole
-// tiles, so always in bounds).
+// Tile kt into stage ST: key rows (clamped to the last valid key, masked later) and V^T rows
+// (padded to whole tiles, so always in bounds).
 template <int ST>
 __device__ __forceinline__ void pf2_issue(const Pf2Ctx& c, int kt, int w, int lane) {
   using namespace pf2;
@@ -255,7 +259,7 @@ struct Pf2State {
 };
 
 template <int ST>
-__device__ __forceinline__ void pf2_compute(const Frag8<bf16> (&q)[12], Pf2State& s, int kt, int qi, int T,
+__device__ __forceinline__ void pf2_compute(const Frag8<bf16> (&q)[12], Pf2State& s, int kt, int qpos, int nk,
                                             float scale_log2, int lane) {
   using namespace pf2;
   const char* st = pf_stage<ST>();
@@ -284,7 +288,7 @@ __device__ __forceinline__ void pf2_compute(const Frag8<bf16> (&q)[12], Pf2State
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int j = j0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-      const float v = (j <= qi && j < T) ? sc[kb][r] * scale_log2 : -INFINITY;
+      const float v = (j <= qpos && j < nk) ? sc[kb][r] * scale_log2 : -INFINITY;
       sc[kb][r] = v;
       mx = fmaxf(mx, v);
     }
@@ -334,7 +338,8 @@ __device__ __forceinline__ void pf2_compute(const Frag8<bf16> (&q)[12], Pf2State
 // multiply unless every query of this wave precedes the tile.
 template <int ST>
 __device__ __forceinline__ void pf2_step(const Pf2Ctx& c, const Frag8<bf16> (&q)[12], Pf2State& s, int kt,
-                                         int kt_end, int qi_last, int qi, float scale_log2, int w, int lane, int tid) {
+                                         int kt_end, int qpos_last, int qpos, float scale_log2, int w, int lane,
+                                         int tid) {
   using namespace pf2;
   if (kt + 1 < kt_end) MLA_TILE_BARRIER(waitcnt_vm(kCopies));
   else MLA_TILE_BARRIER(waitcnt_vm(0));
@@ -349,7 +354,7 @@ __device__ __forceinline__ void pf2_step(const Pf2Ctx& c, const Frag8<bf16> (&q)
     }
     MLA_TILE_BARRIER(kWaitLgkm0);
   }
-  if (kt * kKV <= qi_last) pf2_compute<ST>(q, s, kt, qi, c.T, scale_log2, lane);
+  if (kt * kKV <= qpos_last) pf2_compute<ST>(q, s, kt, qpos, c.T, scale_log2, lane);
 }
 
 __global__ void __launch_bounds__(512)
@@ -366,21 +371,24 @@ __global__ void __launch_bounds__(512)
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, ql = lane & 31;
   const int qi = qt * kQ + w * 32 + ql;
-  const int qi_last = min(qt * kQ + w * 32 + 31, p.T - 1);  // this wave's last query
-  const int64_t MT = (int64_t)p.S * p.T;
-  const int Tp = (p.T + kKV - 1) / kKV * kKV;
+  const int off = p.q_off ? p.q_off[sq] : 0;  // position of the chunk's first query
+  const int nk = off + p.T;                   // valid keys of this sequence
+  const int qpos_last = off + min(qt * kQ + w * 32 + 31, p.T - 1);  // this wave's last query
+  const int Tk = p.Tk > 0 ? p.Tk : p.T;
+  const int64_t MT = (int64_t)p.S * Tk;
+  const int Tp = (Tk + kKV - 1) / kKV * kKV;
 
   Pf2Ctx c;
   // spans below 2 GiB (checked by the launcher): offsets within them are 32-bit
-  c.k = dma_span(reinterpret_cast<const bf16*>(p.k) + ((int64_t)head * MT + (int64_t)sq * p.T) * kDH,
-                 (uint32_t)p.T * kKRow);
-  c.kr = dma_span(reinterpret_cast<const bf16*>(p.kr) + (int64_t)sq * p.T * p.ld_kr + p.kr_off,
-                  (uint32_t)(((int64_t)(p.T - 1) * p.ld_kr + kDR) * 2));
+  c.k = dma_span(reinterpret_cast<const bf16*>(p.k) + ((int64_t)head * MT + (int64_t)sq * Tk) * kDH,
+                 (uint32_t)nk * kKRow);
+  c.kr = dma_span(reinterpret_cast<const bf16*>(p.kr) + (int64_t)sq * Tk * p.ld_kr + p.kr_off,
+                  (uint32_t)(((int64_t)(nk - 1) * p.ld_kr + kDR) * 2));
   c.ld_kr = (int)p.ld_kr;
   c.vrow = p.S * Tp;
   c.vt = dma_span(reinterpret_cast<const bf16*>(p.vt) + ((int64_t)head * kDH * p.S + sq) * Tp,
                   (uint32_t)(((int64_t)(kDH - 1) * c.vrow + Tp) * 2));
-  c.T = p.T;
+  c.T = nk;
 
   Frag8<bf16> q[12];
   {
@@ -399,13 +407,14 @@ __global__ void __launch_bounds__(512)
   s.m_run = -INFINITY;
   s.l_run = 0.f;
 
-  const int kt_end = min((p.T + kKV - 1) / kKV, ((qt + 1) * kQ + kKV - 1) / kKV);
+  const int kt_end = min((nk + kKV - 1) / kKV, (off + (qt + 1) * kQ + kKV - 1) / kKV);
+  const int qpos = off + qi;
   if (kt_end > 0) pf2_issue<0>(c, 0, w, lane);
   if (kt_end > 1) pf2_issue<1>(c, 1, w, lane);
   for (int kt = 0; kt < kt_end; kt += kNS) {
-    pf2_step<0>(c, q, s, kt, kt_end, qi_last, qi, p.scale_log2, w, lane, tid);
-    if (kt + 1 < kt_end) pf2_step<1>(c, q, s, kt + 1, kt_end, qi_last, qi, p.scale_log2, w, lane, tid);
-    if (kt + 2 < kt_end) pf2_step<2>(c, q, s, kt + 2, kt_end, qi_last, qi, p.scale_log2, w, lane, tid);
+    pf2_step<0>(c, q, s, kt, kt_end, qpos_last, qpos, p.scale_log2, w, lane, tid);
+    if (kt + 1 < kt_end) pf2_step<1>(c, q, s, kt + 1, kt_end, qpos_last, qpos, p.scale_log2, w, lane, tid);
+    if (kt + 2 < kt_end) pf2_step<2>(c, q, s, kt + 2, kt_end, qpos_last, qpos, p.scale_log2, w, lane, tid);
   }
   MLA_WAVE_WAIT(waitcnt_vm(0));
 
@@ -444,9 +453,10 @@ hipError_t launch(const PrefillAttnParams& p, hipStream_t s) {
 
 hipError_t prefill_attention(DType t, const PrefillAttnParams& p, hipStream_t s) {
   // the pipelined kernel addresses each source span with 32-bit byte offsets
-  const int64_t Tp = (p.T + pf2::kKV - 1) / pf2::kKV * pf2::kKV;
-  const bool spans_fit = (int64_t)p.T * pf2::kKRow < (1LL << 31) &&
-                         ((int64_t)(p.T - 1) * p.ld_kr + pf2::kDR) * 2 < (1LL << 31) &&
+  const int64_t Tk = p.Tk > 0 ? p.Tk : p.T;
+  const int64_t Tp = (Tk + pf2::kKV - 1) / pf2::kKV * pf2::kKV;
+  const bool spans_fit = Tk * pf2::kKRow < (1LL << 31) &&
+                         ((Tk - 1) * p.ld_kr + pf2::kDR) * 2 < (1LL << 31) &&
                          ((int64_t)(pf2::kDH - 1) * p.S * Tp + Tp) * 2 < (1LL << 31);
   if (t == DType::BF16 && p.d_h == 128 && p.d_hr == 64 && spans_fit) {
     const int nqt = (p.T + pf2::kQ - 1) / pf2::kQ;

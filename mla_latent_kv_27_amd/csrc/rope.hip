@@ -73,17 +73,80 @@ hipError_t rmsnorm_rows(DType t, void* x, int n, int W, int64_t ld, const void* 
   return hipGetLastError();
 }
 
-__global__ void __launch_bounds__(256) prefill_rows_kernel(int n, int T, int32_t* seq, int32_t* pos) {
+__global__ void __launch_bounds__(256)
+    prefill_rows_kernel(int n, int T, int32_t* seq, int32_t* pos, const int32_t* __restrict__ start) {
   const int r = blockIdx.x * blockDim.x + threadIdx.x;
   if (r < n) {
     seq[r] = r / T;
-    pos[r] = r % T;
+    pos[r] = r % T + (start ? start[r / T] : 0);
   }
 }
 
-hipError_t prefill_rows(int n, int T, int32_t* seq, int32_t* pos, hipStream_t s) {
+hipError_t prefill_rows(int n, int T, int32_t* seq, int32_t* pos, hipStream_t s, const int32_t* start) {
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(prefill_rows_kernel, dim3((n + 255) / 256), dim3(256), 0, s, n, T, seq, pos);
+  hipLaunchKernelGGL(prefill_rows_kernel, dim3((n + 255) / 256), dim3(256), 0, s, n, T, seq, pos, start);
+  return hipGetLastError();
+}
+
+// One thread per 16-byte chunk of an output row.  fp8: the chunk's 8 values come from 8 code
+// bytes and the part's scale (the latent part's for columns < d_c, else the rope key's).
+template <bool FP8>
+__global__ void __launch_bounds__(256)
+    gather_entries_kernel(const char* __restrict__ pool, const float* __restrict__ scales,
+                          const int32_t* __restrict__ bt, int max_blocks, int block_size,
+                          const int32_t* __restrict__ start, const char* __restrict__ fresh, int T, int S, int Tk,
+                          int row_bytes, int d_c, char* __restrict__ out) {
+  const int cpr = row_bytes / 16;
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= (int64_t)S * Tk * cpr) return;
+  const int64_t row = i / cpr;
+  const int c = (int)(i % cpr);
+  const int b = (int)(row / Tk), j = (int)(row % Tk);
+  const int s0 = start[b];
+  Chunk16 v = zero16();
+  if (j >= s0 && j < s0 + T) {  // a row of the chunk itself, as computed
+    v = ld16(fresh + ((int64_t)b * T + (j - s0)) * row_bytes + c * 16);
+  } else if (j < s0) {  // the cached prefix
+    const int64_t slot = (int64_t)bt[(int64_t)b * max_blocks + j / block_size] * block_size + j % block_size;
+    if (FP8) {
+      const int E = row_bytes / 2;  // bf16 values per entry = code bytes per entry
+      const uint2 raw = *reinterpret_cast<const uint2*>(pool + slot * E + 8 * c);
+      const float sc = scales[2 * slot + (8 * c < d_c ? 0 : 1)];
+      const floatx2 f0 = __builtin_amdgcn_cvt_pk_f32_fp8(raw.x, false), f1 = __builtin_amdgcn_cvt_pk_f32_fp8(raw.x, true);
+      const floatx2 f2 = __builtin_amdgcn_cvt_pk_f32_fp8(raw.y, false), f3 = __builtin_amdgcn_cvt_pk_f32_fp8(raw.y, true);
+      bf16x8 o;
+      o[0] = (bf16)(f0[0] * sc);
+      o[1] = (bf16)(f0[1] * sc);
+      o[2] = (bf16)(f1[0] * sc);
+      o[3] = (bf16)(f1[1] * sc);
+      o[4] = (bf16)(f2[0] * sc);
+      o[5] = (bf16)(f2[1] * sc);
+      o[6] = (bf16)(f3[0] * sc);
+      o[7] = (bf16)(f3[1] * sc);
+      v = __builtin_bit_cast(Chunk16, o);
+    } else {
+      v = ld16(pool + slot * row_bytes + c * 16);
+    }
+  }
+  st16(out + row * row_bytes + c * 16, v);
+}
+
+hipError_t gather_entries(DType t, const void* pool, const float* scales, const int32_t* block_table, int max_blocks,
+                          int block_size, const int32_t* start, const void* fresh, int T, int S, int Tk, int E, int d_c,
+                          void* out, hipStream_t s) {
+  const int es = scales ? 2 : (int)dsize(t);  // output element size (bf16 for the fp8 cache)
+  const int row_bytes = E * es;
+  const int64_t total = (int64_t)S * Tk * (row_bytes / 16);
+  if (total == 0) return hipSuccess;
+  const dim3 grid((unsigned)((total + 255) / 256)), block(256);
+  if (scales)
+    hipLaunchKernelGGL(gather_entries_kernel<true>, grid, block, 0, s, reinterpret_cast<const char*>(pool), scales,
+                       block_table, max_blocks, block_size, start, reinterpret_cast<const char*>(fresh), T, S, Tk, row_bytes, d_c,
+                       reinterpret_cast<char*>(out));
+  else
+    hipLaunchKernelGGL(gather_entries_kernel<false>, grid, block, 0, s, reinterpret_cast<const char*>(pool), scales,
+                       block_table, max_blocks, block_size, start, reinterpret_cast<const char*>(fresh), T, S, Tk, row_bytes, d_c,
+                       reinterpret_cast<char*>(out));
   return hipGetLastError();
 }
 

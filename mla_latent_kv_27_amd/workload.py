@@ -9,7 +9,7 @@ import torch
 
 import mla_synth as S
 
-from . import (OP_CACHE_APPEND, OP_DECODE, OP_PREFILL, cache_append, make_cache, make_dims, make_weights,
+from . import (OP_CACHE_APPEND, OP_DECODE, OP_PREFILL, OP_PREFILL_CHUNK, cache_append, make_cache, make_dims, make_weights,
                workspace_size)
 
 
@@ -144,3 +144,8 @@ def decode_workspace(layer: DeviceLayer, batch: int, max_ctx_len: int, num_split
 
 def prefill_workspace(layer: DeviceLayer, batch: int, T: int) -> torch.Tensor:
     return ws_tensor(workspace_size(layer.cdims, OP_PREFILL, batch=batch, max_tokens=T), layer.device)
+
+
+def chunk_workspace(layer: DeviceLayer, batch: int, T: int, max_start: int) -> torch.Tensor:
+    return ws_tensor(workspace_size(layer.cdims, OP_PREFILL_CHUNK, batch=batch, max_tokens=T, max_ctx_len=max_start),
+                     layer.device)

@@ -129,6 +129,27 @@ def test_prefill_and_append_host_validation():
                                   None) == M.MLA_ERR_INVALID_ARG
 
 
+def test_prefill_chunk_host_validation():
+    L = M.lib()
+    d, w, c = _dims(), _weights(), _cache()  # capacity 2 blocks x 64 tokens
+    P = ctypes.byref
+
+    def chunk(start=_fake(5), max_start=10, T=16, ws=None, ws_bytes=0):
+        return L.mla_prefill_chunk(P(d), P(w), P(c), _fake(1), 1, T, start, max_start, _fake(2), None, ws, ws_bytes,
+                                   None)
+    assert chunk(start=None) == M.MLA_ERR_INVALID_ARG
+    assert chunk(max_start=-1) == M.MLA_ERR_INVALID_ARG
+    assert chunk(max_start=113) == M.MLA_ERR_INVALID_ARG  # 113 + 16 > 128
+    assert chunk(max_start=112) == M.MLA_ERR_WORKSPACE
+    out = ctypes.c_size_t(0)
+    assert L.mla_workspace_size(P(d), M.OP_PREFILL_CHUNK, 1, 16, -1, 0, P(out)) == M.MLA_ERR_INVALID_ARG
+    sizes = []
+    for ms in (0, 100, 1000):
+        assert L.mla_workspace_size(P(d), M.OP_PREFILL_CHUNK, 2, 16, ms, 0, P(out)) == M.MLA_OK
+        sizes.append(out.value)
+    assert sizes[0] < sizes[1] < sizes[2]
+
+
 def test_workspace_sizes_grow_with_work():
     d = _dims()
     a = M.workspace_size(d, M.OP_DECODE, batch=2, max_ctx_len=100)
