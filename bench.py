@@ -183,7 +183,7 @@ def prefill_bench(args, w):
     attn_f, proj_f = prefill_flops(dims, T, B)
     tflops = (attn_f + proj_f) / (ms / 1e3) / 1e12
     cpu = None
-    if not args.no_cpu_baseline and not fp8:  # the oracle baseline is timed on the bf16 cache only
+    if not args.no_cpu_baseline:
         import oracle.mla_oracle as O
         n = min(T, 256)
         t0 = time.perf_counter()
@@ -207,6 +207,76 @@ def prefill_bench(args, w):
     print(json.dumps(rec))
 
 
+def chunk_flops(dims, P, T, B):
+    """Chunked prefill of T tokens after P cached ones: causal attention of the chunk over P + i + 1
+    keys (d_qk = d_h + d_hr, d_v = d_h), the per-head keys and values rebuilt from all P + T
+    latents, and the other weights applied once per new token."""
+    attn = B * 2 * dims.n_h * (dims.d_h + dims.d_hr + dims.d_h) * (T * P + T * (T + 1) // 2)
+    rebuild = B * 2 * 2 * (P + T) * dims.d_c * dims.n_h * dims.d_h
+    per_token = dims.param_count() - 2 * dims.n_h * dims.d_h * dims.d_c  # all but W_UK, W_UV
+    return attn, rebuild + 2 * B * T * per_token
+
+
+def chunk_bench(args, w):
+    """A step is one mla_prefill_chunk: the next w.tokens tokens of each sequence after w.ctx
+    cached ones (the same chunk slots are rewritten every step); MFMA-bound."""
+    import numpy as np
+    import torch
+    import mla_synth as S
+    import mla_latent_kv_27_amd as M
+    from mla_latent_kv_27_amd import workload as WL
+
+    dims, B, T, P = w.dims, w.batch, w.tokens, w.ctx
+    torch.cuda.set_device(0)
+    W_np = S.make_weights(dims, std=w.weight_std)
+    layer = WL.DeviceLayer(dims, W_np)
+    pool = WL.PagedPool(dims, [P + T] * B, block_size=w.block_size)
+    WL.build_context(layer, pool, [P] * B, w.hidden)
+    h_np = np.stack([S.hidden_history(dims, b, P + T, w.hidden)[P:] for b in range(B)])
+    h = WL.to_device(h_np, dims)
+    u = torch.empty((B, T, dims.d_model), dtype=WL.torch_dtype(dims), device="cuda")
+    start = torch.full((B,), P, dtype=torch.int32, device="cuda")
+    ws = WL.chunk_workspace(layer, B, T, P)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        M.prefill_chunk(layer.cdims, layer.cweights, pool.ccache, h, start, P, u, ws, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        M.prefill_chunk(layer.cdims, layer.cweights, pool.ccache, h, start, P, u, ws, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    attn_f, other_f = chunk_flops(dims, P, T, B)
+    tflops = (attn_f + other_f) / (ms / 1e3) / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle.mla_oracle as O
+        n = min(T, 32)
+        prefix = O.latent_entries(W_np, dims, S.hidden_history(dims, 0, P, w.hidden), np.arange(P))
+        t0 = time.perf_counter()
+        O.mla_prefill(W_np, dims, h_np[0, :n], start_pos=P, prefix_cache=prefix)
+        dt = time.perf_counter() - t0
+        cpu = {"value": n / dt, "unit": "tokens/s", "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+               "sample": f"the first {n} chunk tokens of sequence 0 after its {P} cached ones (un-absorbed fp64 "
+                         f"numpy), {dt:.1f} s; prefix entries precomputed untimed"}
+    rec = {"metric": "MLA chunked prefill tokens/s (chunk after a cached prefix), DeepSeek-V2 shape, 1 GPU",
+           "value": round(B * T / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": dims.dtype,
+           "data": "synthetic (seeded weights N(0,0.02), RMS-normalised N(0,1) hidden states, random page order)",
+           "config": {"workload": w.name, "batch": B, "prefix_tokens": P, "chunk_tokens": T, "d_model": dims.d_model,
+                      "n_h": dims.n_h, "d_h": dims.d_h, "d_c": dims.d_c, "d_cq": dims.d_cq, "d_hr": dims.d_hr},
+           "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                        "kernel": "whole mla_prefill_chunk call (projections, writer, prefix gather, key/value "
+                                  "rebuild, causal attention, W_O)",
+                        "attention_flops": attn_f, "other_flops": other_f},
+           "cpu_baseline": cpu}
+    print(json.dumps(rec))
+
+
 def main():
     args = parse()
     if args.only == "copy":
@@ -225,6 +295,9 @@ def main():
     w = S.WORKLOADS[args.workload]
     if w.kind == "prefill":
         prefill_bench(args, w)
+        return
+    if w.kind == "chunk":
+        chunk_bench(args, w)
         return
     dims = w.dims
     torch.cuda.set_device(0)

@@ -88,8 +88,10 @@ struct QuantDst {
   const int32_t* row_pos = nullptr;
 };
 bool fp8_cache_ok(int d_c, int d_hr);
-// Quantises n bf16 entries (rows src_ld elements apart) into dst.
-hipError_t quantize_entries_run(const void* src, int64_t src_ld, int n, const QuantDst& dst, hipStream_t s);
+// Quantises n bf16 entries (rows src_ld elements apart) into dst; with gain, their latent part is
+// RMS-normalised first (and written back into src when writeback).
+hipError_t quantize_entries_run(const void* src, int64_t src_ld, int n, const QuantDst& dst, hipStream_t s,
+                                const void* gain = nullptr, float eps = 0.f, bool writeback = false);
 // Largest partial_bytes of gemm_plan(m, ...) over 1 <= m <= M (workspace sized for M then also
 // serves every smaller call).
 size_t gemm_partial_bound(int M, int N, int K, int batch, int cus, bool skinny_ok);
@@ -109,6 +111,25 @@ hipError_t rope_table(const int32_t* pos, int n, int d_hr, const RopeFreq& f, fl
 // x[r][0..W) <- gain * x / sqrt(mean(x^2) + eps) for rows r < n, ld elements apart, in place
 // (the RMSNorm of the compressed latents).
 hipError_t rmsnorm_rows(DType t, void* x, int n, int W, int64_t ld, const void* gain, float eps, hipStream_t s);
+// One launch for the latent norms of new tokens: entries[r] (r < n_e, E values, rows E apart) get
+// their first d_c values normalised with g_ckv (if not null), in place, and are copied to their
+// cache pages (slot of (seq[r] or r, pos[r])); cq[r] (r < n_q, d_cq values) is normalised in place
+// with g_cq.
+struct LatentFinish {
+  void* entries = nullptr;
+  int n_e = 0, E = 0, d_c = 0;
+  const void* g_ckv = nullptr;
+  void* pool = nullptr;
+  const int32_t* block_table = nullptr;
+  int max_blocks = 0, block_size = 1;
+  const int32_t* seq = nullptr;
+  const int32_t* pos = nullptr;
+  void* cq = nullptr;
+  int n_q = 0, d_cq = 0;
+  const void* g_cq = nullptr;
+  float eps = 1e-6f;
+};
+hipError_t latent_finish(DType t, const LatentFinish& f, hipStream_t s);
 // seq[r] = r / T, pos[r] = r % T (+ start[seq[r]] when start != nullptr) for r < n.
 hipError_t prefill_rows(int n, int T, int32_t* seq, int32_t* pos, hipStream_t s, const int32_t* start = nullptr);
 // Dense key rows of a chunked prefill, out[b][j] for sequences b < S and j < Tk (entries of E

@@ -42,14 +42,30 @@ __device__ __forceinline__ uint32_t e4m3_code(float y) {
 
 constexpr int kDc = 512, kDr = 64, kEntry = kDc + kDr;
 
-__global__ void __launch_bounds__(256) quantize_entries_kernel(const bf16* __restrict__ src, int64_t src_ld, int n,
-                                                               QuantDst dst) {
+// gain != nullptr: the latent part is first RMS-normalised (x * g / sqrt(mean(x^2) + eps), the
+// latent norm of section 3.1.2) and rounded to bf16, as the bf16 cache would store it; with
+// writeback the normalised bf16 values also replace the source row.
+__global__ void __launch_bounds__(256) quantize_entries_kernel(bf16* __restrict__ src, int64_t src_ld, int n,
+                                                               QuantDst dst, const bf16* __restrict__ gain, float eps,
+                                                               bool writeback) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= n) return;
-  const bf16* e = src + (int64_t)row * src_ld;
+  bf16* e = src + (int64_t)row * src_ld;
   bf16x8 cv = *reinterpret_cast<const bf16x8*>(e + 8 * lane);
   const float rv = (float)e[kDc + lane];
+  if (gain) {
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss += (float)cv[i] * (float)cv[i];
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) ss = wave_sum_xor(ss, m);
+    const float inv = 1.0f / sqrtf(ss / (float)kDc + eps);
+    const bf16x8 gv = *reinterpret_cast<const bf16x8*>(gain + 8 * lane);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) cv[i] = (bf16)((float)cv[i] * inv * (float)gv[i]);
+    if (writeback) *reinterpret_cast<bf16x8*>(e + 8 * lane) = cv;
+  }
   float c[8];
   float amax_c = 0.f;
 #pragma unroll
@@ -88,10 +104,12 @@ __global__ void __launch_bounds__(256) quantize_entries_kernel(const bf16* __res
 
 bool fp8_cache_ok(int d_c, int d_hr) { return d_c == kDc && d_hr == kDr; }
 
-hipError_t quantize_entries_run(const void* src, int64_t src_ld, int n, const QuantDst& dst, hipStream_t s) {
+hipError_t quantize_entries_run(const void* src, int64_t src_ld, int n, const QuantDst& dst, hipStream_t s,
+                                const void* gain, float eps, bool writeback) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(quantize_entries_kernel, dim3((n + 3) / 4), dim3(256), 0, s, reinterpret_cast<const bf16*>(src),
-                     src_ld, n, dst);
+  hipLaunchKernelGGL(quantize_entries_kernel, dim3((n + 3) / 4), dim3(256), 0, s,
+                     reinterpret_cast<bf16*>(const_cast<void*>(src)), src_ld, n, dst,
+                     reinterpret_cast<const bf16*>(gain), eps, writeback);
   return hipGetLastError();
 }
 

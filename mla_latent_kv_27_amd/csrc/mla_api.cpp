@@ -320,16 +320,29 @@ QuantDst quant_dst(const mla_paged_cache* c, const int32_t* seq, const int32_t* 
 // the fp8 quantiser.
 inline bool staged_entries(const mla_dims* d, const mla_weights* w) { return fp8_cache(d) || w->g_ckv; }
 
-// Staged rows -> their cache slots: the c^KV norm in place, then quantised (fp8) or copied.
-// seq == nullptr: row r belongs to sequence r.
+// Staged rows -> their cache slots (seq == nullptr: row r belongs to sequence r): the c^KV norm
+// in place, then quantised (fp8) or copied into the pages.  cq (n_q rows), when given, gets the
+// c^q norm in the same launch on the bf16/fp32 path.
 int finish_entries(const mla_dims* d, const mla_weights* w, const mla_paged_cache* c, void* staged, int n,
-                   const int32_t* seq, const int32_t* pos, hipStream_t s) {
-  if (w->g_ckv) MLA_HIP(rmsnorm_rows(dt(d), staged, n, d->d_c, entry(d), w->g_ckv, eps_of(d), s));
-  if (fp8_cache(d))
-    MLA_HIP(quantize_entries_run(staged, entry(d), n, quant_dst(c, seq, pos), s));
-  else
+                   const int32_t* seq, const int32_t* pos, hipStream_t s, void* cq = nullptr, int n_q = 0) {
+  const bool q_norm = cq && w->g_cq;
+  if (fp8_cache(d)) {
+    MLA_HIP(quantize_entries_run(staged, entry(d), n, quant_dst(c, seq, pos), s, w->g_ckv, eps_of(d), true));
+    if (q_norm) MLA_HIP(rmsnorm_rows(dt(d), cq, n_q, d->d_cq, d->d_cq, w->g_cq, eps_of(d), s));
+    return MLA_OK;
+  }
+  if (!w->g_ckv && !q_norm) {
     MLA_HIP(scatter_rows(dt(d), staged, n, entry(d), c->pool, seq, pos, c->block_table, c->max_blocks_per_seq,
                          c->block_size, s));
+    return MLA_OK;
+  }
+  LatentFinish f;
+  f.entries = staged; f.n_e = n; f.E = entry(d); f.d_c = d->d_c; f.g_ckv = w->g_ckv;
+  f.pool = c->pool; f.block_table = c->block_table; f.max_blocks = c->max_blocks_per_seq;
+  f.block_size = c->block_size; f.seq = seq; f.pos = pos;
+  if (q_norm) { f.cq = cq; f.n_q = n_q; f.d_cq = d->d_cq; f.g_cq = w->g_cq; }
+  f.eps = eps_of(d);
+  MLA_HIP(latent_finish(dt(d), f, s));
   return MLA_OK;
 }
 
@@ -419,12 +432,10 @@ int prefill_impl(const mla_dims* d, const mla_weights* w, const mla_paged_cache*
     g.epi = dense(ws.kvd, E);
     g.epi.rope_col0 = d->d_c; g.epi.d_hr = d->d_hr; g.epi.rope_tab = ws.rope;
     MLA_HIP(gemm_run(t, g, ws.kv_p, ws.partial, s));
-    if (w->g_ckv) MLA_HIP(rmsnorm_rows(t, ws.kvd, M, d->d_c, E, w->g_ckv, eps_of(d), s));
-    if (fp8_cache(d))
-      MLA_HIP(quantize_entries_run(ws.kvd, E, M, quant_dst(c, ws.seq, ws.pos), s));
-    else
-      MLA_HIP(scatter_rows(t, ws.kvd, M, E, c->pool, ws.seq, ws.pos, c->block_table, c->max_blocks_per_seq,
-                           c->block_size, s));
+    {  // c^KV norm in place (the K/V products below read it), then into the pages
+      const int rc = finish_entries(d, w, c, ws.kvd, M, ws.seq, ws.pos, s);
+      if (rc != MLA_OK) return rc;
+    }
     if (chunked)  // key rows: the cached prefix read back from the pages, then the chunk's rows
       MLA_HIP(gather_entries(t, c->pool, fp8_cache(d) ? c->scales : nullptr, c->block_table, c->max_blocks_per_seq,
                              c->block_size, start, ws.kvd, T, batch, ws.Tk, E, d->d_c, ws.kva, s));
@@ -635,10 +646,11 @@ int mla_decode(const mla_dims* d, const mla_weights* w, const mla_paged_cache* c
                                    : cache_epilogue(d, c, ws.rope, nullptr, ctx_lens);
     }
     MLA_HIP(gemm_run(t, g, ws.gm.kvq, ws.partial, s));
-    if (w->g_cq) MLA_HIP(rmsnorm_rows(t, ws.cq, B, d->d_cq, d->d_cq, w->g_cq, eps_of(d), s));
-    if (staged_entries(d, w)) {
-      const int rc = finish_entries(d, w, c, ws.staged, B, nullptr, ctx_lens, s);
+    if (staged_entries(d, w)) {  // entries to their pages; the c^q norm rides along
+      const int rc = finish_entries(d, w, c, ws.staged, B, nullptr, ctx_lens, s, d->d_cq > 0 ? ws.cq : nullptr, B);
       if (rc != MLA_OK) return rc;
+    } else if (w->g_cq) {
+      MLA_HIP(rmsnorm_rows(t, ws.cq, B, d->d_cq, d->d_cq, w->g_cq, eps_of(d), s));
     }
   }
   {  // [q^C | q^R] = [W_UQ; W_QR] c^q: q^C to the workspace, RoPE'd q^R into columns

@@ -73,6 +73,48 @@ hipError_t rmsnorm_rows(DType t, void* x, int n, int W, int64_t ld, const void* 
   return hipGetLastError();
 }
 
+// One wave per row: rows < n_e are new cache entries (normalise the latent part, store in place
+// and into the page), the next n_q rows are c^q rows (normalise in place).
+template <typename T>
+__global__ void __launch_bounds__(256) latent_finish_kernel(LatentFinish f) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= f.n_e + f.n_q) return;
+  const bool entry = row < f.n_e;
+  T* x = entry ? reinterpret_cast<T*>(f.entries) + (int64_t)row * f.E
+               : reinterpret_cast<T*>(f.cq) + (int64_t)(row - f.n_e) * f.d_cq;
+  const int W = entry ? f.d_c : f.d_cq;
+  const T* g = reinterpret_cast<const T*>(entry ? f.g_ckv : f.g_cq);
+  if (g) {
+    float ss = 0.f;
+    for (int i = lane; i < W; i += 64) {
+      const float v = to_f32(x[i]);
+      ss += v * v;
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) ss = wave_sum_xor(ss, m);
+    const float inv = 1.0f / sqrtf(ss / (float)W + f.eps);
+    for (int i = lane; i < W; i += 64) x[i] = from_f32<T>(to_f32(x[i]) * inv * to_f32(g[i]));
+  }
+  if (!entry) return;
+  const int sq = f.seq ? f.seq[row] : row, ps = f.pos[row];
+  const int64_t slot = (int64_t)f.block_table[(int64_t)sq * f.max_blocks + ps / f.block_size] * f.block_size +
+                       ps % f.block_size;
+  T* dst = reinterpret_cast<T*>(f.pool) + slot * f.E;
+  for (int i = lane; i < f.E; i += 64) dst[i] = x[i];  // this lane's own writes above: no barrier needed
+}
+
+hipError_t latent_finish(DType t, const LatentFinish& f, hipStream_t s) {
+  const int rows = f.n_e + f.n_q;
+  if (rows <= 0) return hipSuccess;
+  const dim3 grid((rows + 3) / 4), block(256);
+  if (t == DType::BF16)
+    hipLaunchKernelGGL(latent_finish_kernel<bf16>, grid, block, 0, s, f);
+  else
+    hipLaunchKernelGGL(latent_finish_kernel<float>, grid, block, 0, s, f);
+  return hipGetLastError();
+}
+
 __global__ void __launch_bounds__(256)
     prefill_rows_kernel(int n, int T, int32_t* seq, int32_t* pos, const int32_t* __restrict__ start) {
   const int r = blockIdx.x * blockDim.x + threadIdx.x;

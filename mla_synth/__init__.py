@@ -88,7 +88,7 @@ class Dims:
 class Workload:
     name: str
     dims: Dims
-    kind: str  # "decode" | "prefill"
+    kind: str  # "decode" | "prefill" | "chunk" (ctx cached tokens, then a chunk of `tokens`)
     batch: int
     ctx: int = 0  # decode: tokens cached before the step (uniform contexts)
     ctx_lo: int = 0  # decode, ragged: lengths uniform in [ctx_lo, ctx_hi]
@@ -125,6 +125,9 @@ WORKLOADS = {
                                                 dataclasses.replace(V2_YARN, latent_norm=True), "decode",
                                                 batch=64, ctx=8192),
     "v2_prefill_16384": Workload("v2_prefill_16384", V2, "prefill", batch=1, tokens=16384),
+    # chunked prefill: the last 512 tokens of a 16384-token prompt after 15872 cached ones
+    "v2_chunk_512_after_15872": Workload("v2_chunk_512_after_15872", V2, "chunk", batch=1, ctx=15872,
+                                         tokens=512),
     "v2_long_decode_b4": Workload("v2_long_decode_b4", V2, "decode", batch=4, ctx_lo=32768,
                                   ctx_hi=131072),
 }
