@@ -254,13 +254,18 @@ __device__ __forceinline__ void pf2_issue(const Pf2Ctx& c, int kt, int w, int la
 }
 
 struct Pf2State {
-  floatx16 o[4];  // O^T: 4 blocks of 32 dims; lane: query l32, dims 32 d + 8 (r/4) + 4g + r%4
-  float m_run, l_run;
+  floatx16 o[4];   // O^T: 4 blocks of 32 dims; lane: query l32, dims 32 d + 8 (r/4) + 4g + r%4
+  float m_ref;     // the query's reference max, raw score units (shared by its two lanes)
+  float l_part;    // this lane's partial normaliser (the two lanes of a query combine at the end)
 };
+
+// Lazy softmax: the reference max only moves (and O is rescaled) when a score exceeds it by more
+// than kLazy / scale in log2 units, so the common tile needs no cross-lane exchange and no rescale.
+constexpr float kPfLazy = 8.f;
 
 template <int ST>
 __device__ __forceinline__ void pf2_compute(const Frag8<bf16> (&q)[12], Pf2State& s, int kt, int qpos, int nk,
-                                            float scale_log2, int lane) {
+                                            bool masked, float scale_log2, int lane) {
   using namespace pf2;
   const char* st = pf_stage<ST>();
   asm volatile("" : "+v"(lane));
@@ -282,34 +287,40 @@ __device__ __forceinline__ void pf2_compute(const Frag8<bf16> (&q)[12], Pf2State
       sc[kb] = mma32(a, q[ks], sc[kb]);
     }
   }
+  // raw scores; keys past the query or past the sequence only on the diagonal / last tile
   float mx = -INFINITY;
+  if (masked) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = j0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+        if (!(j <= qpos && j < nk)) sc[kb][r] = -INFINITY;
+      }
+  }
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+  if (__builtin_amdgcn_ballot_w64((mx - s.m_ref) * scale_log2 > kPfLazy) != 0) {  // rare: raise the reference
+    const float qmax = wave_max_xor(mx, 32);
+    const float m_new = fmaxf(s.m_ref, qmax);
+    const float alpha = m_new == -INFINITY ? 1.f : exp2f((s.m_ref - m_new) * scale_log2);  // first key: 0
+    s.l_part *= alpha;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) s.o[d] *= alpha;
+    s.m_ref = m_new;
+  }
+  // p = 2^((s - m) scale) (argument <= kPfLazy); a query with no visible key yet keeps m = -inf
+  const float mb = s.m_ref == -INFINITY ? 0.f : -s.m_ref * scale_log2;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int j = j0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-      const float v = (j <= qpos && j < nk) ? sc[kb][r] * scale_log2 : -INFINITY;
-      sc[kb][r] = v;
-      mx = fmaxf(mx, v);
-    }
-  mx = wave_max_xor(mx, 32);
-  const float m_new = fmaxf(s.m_run, mx);
-  const float m_use = m_new == -INFINITY ? 0.f : m_new;
-  const float alpha = exp2f(s.m_run - m_use);
-  float sum = 0.f;
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float e = (float)(bf16)exp2f(sc[kb][r] - m_use);  // as rounded for PV
+      const float e = __builtin_amdgcn_exp2f(fmaf(sc[kb][r], scale_log2, mb));
+      s.l_part += e;
       sc[kb][r] = e;
-      sum += e;
     }
-  sum = wave_sum_xor(sum, 32);
-  s.l_run = s.l_run * alpha + sum;
-  s.m_run = m_new;
-#pragma unroll
-  for (int d = 0; d < 4; ++d) s.o[d] *= alpha;
   // O^T += V^T P^T: lane (dim 32 d + l32, group g) reads keys 16 (2kb + half) + 4g + 0..3 and
   // + 8 + 0..3, i.e. chunk 4kb + 2half (+1) of its row, byte 8g
   const char* vrow = st + kVOff + l32 * kVRow + 8 * g;
@@ -338,8 +349,8 @@ __device__ __forceinline__ void pf2_compute(const Frag8<bf16> (&q)[12], Pf2State
 // multiply unless every query of this wave precedes the tile.
 template <int ST>
 __device__ __forceinline__ void pf2_step(const Pf2Ctx& c, const Frag8<bf16> (&q)[12], Pf2State& s, int kt,
-                                         int kt_end, int qpos_last, int qpos, float scale_log2, int w, int lane,
-                                         int tid) {
+                                         int kt_end, int qpos_first, int qpos_last, int qpos, float scale_log2,
+                                         int w, int lane, int tid) {
   using namespace pf2;
   if (kt + 1 < kt_end) MLA_TILE_BARRIER(waitcnt_vm(kCopies));
   else MLA_TILE_BARRIER(waitcnt_vm(0));
@@ -354,7 +365,9 @@ __device__ __forceinline__ void pf2_step(const Pf2Ctx& c, const Frag8<bf16> (&q)
     }
     MLA_TILE_BARRIER(kWaitLgkm0);
   }
-  if (kt * kKV <= qpos_last) pf2_compute<ST>(q, s, kt, qpos, c.T, scale_log2, lane);
+  // the mask is needed only where the tile reaches past the wave's first query or the sequence
+  const bool masked = kt * kKV + kKV - 1 > qpos_first || (kt + 1) * kKV > c.T;
+  if (kt * kKV <= qpos_last) pf2_compute<ST>(q, s, kt, qpos, c.T, masked, scale_log2, lane);
 }
 
 __global__ void __launch_bounds__(512)
@@ -374,6 +387,7 @@ __global__ void __launch_bounds__(512)
   const int off = p.q_off ? p.q_off[sq] : 0;  // position of the chunk's first query
   const int nk = off + p.T;                   // valid keys of this sequence
   const int qpos_last = off + min(qt * kQ + w * 32 + 31, p.T - 1);  // this wave's last query
+  const int qpos_first = off + qt * kQ + w * 32;                     // and its first
   const int Tk = p.Tk > 0 ? p.Tk : p.T;
   const int64_t MT = (int64_t)p.S * Tk;
   const int Tp = (Tk + kKV - 1) / kKV * kKV;
@@ -404,22 +418,25 @@ __global__ void __launch_bounds__(512)
   for (int d = 0; d < 4; ++d)
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) s.o[d][rr] = 0.f;
-  s.m_run = -INFINITY;
-  s.l_run = 0.f;
+  s.m_ref = -INFINITY;
+  s.l_part = 0.f;
 
   const int kt_end = min((nk + kKV - 1) / kKV, (off + (qt + 1) * kQ + kKV - 1) / kKV);
   const int qpos = off + qi;
   if (kt_end > 0) pf2_issue<0>(c, 0, w, lane);
   if (kt_end > 1) pf2_issue<1>(c, 1, w, lane);
   for (int kt = 0; kt < kt_end; kt += kNS) {
-    pf2_step<0>(c, q, s, kt, kt_end, qpos_last, qpos, p.scale_log2, w, lane, tid);
-    if (kt + 1 < kt_end) pf2_step<1>(c, q, s, kt + 1, kt_end, qpos_last, qpos, p.scale_log2, w, lane, tid);
-    if (kt + 2 < kt_end) pf2_step<2>(c, q, s, kt + 2, kt_end, qpos_last, qpos, p.scale_log2, w, lane, tid);
+    pf2_step<0>(c, q, s, kt, kt_end, qpos_first, qpos_last, qpos, p.scale_log2, w, lane, tid);
+    if (kt + 1 < kt_end)
+      pf2_step<1>(c, q, s, kt + 1, kt_end, qpos_first, qpos_last, qpos, p.scale_log2, w, lane, tid);
+    if (kt + 2 < kt_end)
+      pf2_step<2>(c, q, s, kt + 2, kt_end, qpos_first, qpos_last, qpos, p.scale_log2, w, lane, tid);
   }
   MLA_WAVE_WAIT(waitcnt_vm(0));
 
+  const float l_run = wave_sum_xor(s.l_part, 32);  // the query's two lanes
   if (qi >= p.T) return;
-  const float inv = s.l_run > 0.f ? 1.f / s.l_run : 0.f;
+  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
   const int64_t orow = (((int64_t)sq * p.T + qi) * p.n_h + head) * kDH;
   bf16* out = reinterpret_cast<bf16*>(p.o) + orow;
 #pragma unroll
