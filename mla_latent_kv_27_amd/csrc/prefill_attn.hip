@@ -182,7 +182,7 @@ __global__ void __launch_bounds__(256) prefill_attn_kernel(PrefillAttnParams p) 
 // The DeepSeek-V2 case (bf16, d_h = 128, d_hr = 64).  Same arithmetic as above, with the K and V^T
 // tiles streamed by direct global->LDS copies into a ring of three 40 KiB stages (two tiles in
 // flight while one is multiplied), one barrier per tile, and eight waves (256 queries of one head)
-// sharing every tile.  LDS rows swizzle 16-byte chunks (slot = chunk ^ (row & 7)) so that the
+// sharing every tile.  LDS rows swizzle 16-byte chunks (slot = chunk ^ f(row)) so that the
 // fragment reads of 32 rows spread over the banks.  Workgroups of the same head are placed on
 // the same XCD so that their tiles come from its L2.
 namespace pf2 {
@@ -207,6 +207,10 @@ constexpr int kCopies = kKCopies + kRCopies + kVCopies;
 // 16-byte chunk c of a row r sits at slot c ^ swizzle: 16 consecutive rows then cover all banks
 __device__ __forceinline__ int kslot(int r, int c) { return c ^ (r & 15); }         // 16-chunk rows
 __device__ __forceinline__ int rslot(int r, int c) { return c ^ ((r >> 1) & 7); }   // 8-chunk rows
+// V^T rows (128 bytes: 8 chunks): the 32 rows of a fragment read share parity in pairs of bank
+// halves, so the chunk is XORed with (row >> 1) & 7: each slot of a half serves two rows, the
+// least a 32-lane 8-byte read of 32 rows can do (row & 7 would give four)
+__device__ __forceinline__ int vswz(int d) { return (d >> 1) & 7; }
 }  // namespace pf2
 
 __shared__ __attribute__((aligned(1024))) char g_pf_s0[pf2::kStage];
@@ -248,7 +252,7 @@ __device__ __forceinline__ void pf2_issue(const Pf2Ctx& c, int kt, int w, int la
     const int P = i * kWaves + w;
     const int C = P * 64 + lane;
     const int d = C / 8, sl = C % 8;
-    const int ch = sl ^ (d & 7);
+    const int ch = sl ^ vswz(d);
     dma16(c.vt, (uint32_t)((d * c.vrow + j0 + ch * 8) * 2), (lds_void_t*)(st + kVOff + P * 1024));
   }
 }
@@ -269,7 +273,7 @@ __device__ __forceinline__ void pf2_compute(const Frag8<bf16> (&q)[12], Pf2State
   using namespace pf2;
   const char* st = pf_stage<ST>();
   asm volatile("" : "+v"(lane));
-  const int g = lane >> 5, l32 = lane & 31, x = l32 & 7;
+  const int g = lane >> 5, l32 = lane & 31, x = vswz(l32);
   const int j0 = kt * kKV;
   floatx16 sc[2];
 #pragma unroll
@@ -360,7 +364,7 @@ __device__ __forceinline__ void pf2_step(const Pf2Ctx& c, const Frag8<bf16> (&q)
     char* v = pf_stage<ST>() + kVOff;
     for (int i = tid; i < kDH * (kKV - valid); i += 64 * kWaves) {
       const int d = i / (kKV - valid), key = valid + i % (kKV - valid);
-      const int slot = (key >> 3) ^ (d & 7);
+      const int slot = (key >> 3) ^ vswz(d);
       *reinterpret_cast<bf16*>(v + d * kVRow + slot * 16 + (key & 7) * 2) = (bf16)0.f;
     }
     MLA_TILE_BARRIER(kWaitLgkm0);
