@@ -906,7 +906,12 @@ hipError_t launch(const DecodeAttnParams& p, hipStream_t s) {
 }
 }  // namespace
 
+bool decode_bf16_partials(DType t, const DecodeAttnParams& p) {
+  return p.fp8 || decode_tiled(t, p.d_c, p.d_hr, p.block_size);
+}
+
 hipError_t decode_attention(DType t, const DecodeAttnParams& p, hipStream_t s) {
+  if (p.leave_partials && !decode_bf16_partials(t, p)) return hipErrorInvalidValue;
   if (p.fp8) {
     if (t != DType::BF16 || p.d_c != 512 || p.d_hr != 64 || p.block_size % tiled8::kT != 0 || !p.scales)
       return hipErrorInvalidValue;
@@ -916,7 +921,7 @@ hipError_t decode_attention(DType t, const DecodeAttnParams& p, hipStream_t s) {
     const int blocks = (units + 7) / 8 * 8 * HG;
     hipLaunchKernelGGL(decode_attn_fp8_kernel, dim3(blocks), dim3(64 * tiled8::kWaves), 0, s, p, HG, p.block_table);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || p.splits == 1) return e;
+    if (e != hipSuccess || p.splits == 1 || p.leave_partials) return e;
     hipLaunchKernelGGL((decode_combine_kernel<bf16, bf16, 512>), dim3((p.B * p.n_h + 3) / 4), dim3(256), 0, s, p);
     return hipGetLastError();
   }
@@ -928,7 +933,7 @@ hipError_t decode_attention(DType t, const DecodeAttnParams& p, hipStream_t s) {
     hipLaunchKernelGGL(decode_attn_tiled_kernel, dim3(blocks), dim3(64 * tiled::kWaves), 0, s, p, HG,
                        p.block_table);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || p.splits == 1) return e;
+    if (e != hipSuccess || p.splits == 1 || p.leave_partials) return e;
     hipLaunchKernelGGL((decode_combine_kernel<bf16, bf16, 512>), dim3((p.B * p.n_h + 3) / 4), dim3(256), 0, s, p);
     return hipGetLastError();
   }

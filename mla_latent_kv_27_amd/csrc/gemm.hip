@@ -434,6 +434,13 @@ __global__ void __launch_bounds__(256)
     gemm_skinny_kernel(GemmParams p, int splits, int k_per_split, float* __restrict__ partial) {
   using namespace skinny;
   const int tid = threadIdx.x, lane = tid & 63;
+  if (p.side_rope.tab && blockIdx.x == gridDim.x - 1) {  // the extra column: the RoPE table
+    const RopeJob& r = p.side_rope;
+    for (int64_t i = blockIdx.y * (int64_t)blockDim.x + tid; i < (int64_t)r.n * r.half;
+         i += (int64_t)gridDim.y * blockDim.x)
+      r.tab[i] = rope_table_entry(r.pos, r.half, r.f, i);
+    return;
+  }
   const int w = tid >> 6;
   const int n0 = blockIdx.x * kBN;
   const int z = blockIdx.y / splits, sp = blockIdx.y % splits;
@@ -852,41 +859,117 @@ hipError_t absorb_run(const void* qc, const void* w_uk, void* qhat, int B, int n
 
 // ----------------------------------------------------------------------------- W_UV per head
 // o[b][h][d] = sum_c W_UV[h*d_h + d][c] o_hat[b][h][c] (App. C, W_UV applied after the softmax):
-// per head a skinny product over d_c = 512 with both operands c-contiguous.  Workgroup = (64
-// columns d of one head): the head's o_hat rows (64 at a time, 1 KiB each) are copied to LDS and
-// shared by 4 waves of 16 columns, each wave holding its 16 weight rows in registers.  One pass
-// over k, no split: 2 x n_h workgroups at d_h = 128.
+// per head a skinny product over d_c = 512 with both operands c-contiguous.  Workgroup = (16 NW
+// columns d of one head): the head's o_hat rows (64 at a time, 1 KiB each) are staged in LDS and
+// shared by NW waves of 16 columns, each wave holding its 16 weight rows in registers.  One pass
+// over k, no split.
+//
+// With the KV partitions' outputs given (split-KV decode), the rows are not read from o_hat but
+// combined on the way into LDS: o_hat = sum_s w_s o_s / sum_s w_s with w_s = 2^(m_s - M) l_s and
+// M = max_s m_s (the log-sum-exp rule), o_s = O_s / l_s in bf16.  Then one workgroup takes a
+// whole head (NW = d_h / 16) so that every partition row is read once.
 namespace uvk {
 constexpr int kDc = 512;    // d_c: an LDS row of o_hat is 1 KiB (64 chunks)
 constexpr int kRowB = 2 * kDc;
 constexpr int kMB = 64;     // batch rows per block
-constexpr int kWaves = 4;
+constexpr int kWaves = 4;   // plain o_hat input
+constexpr int kWavesParts = 8;  // partition input: d_h = 128
 constexpr int kCols = 16 * kWaves;
+constexpr int kMBParts = 32;  // rows per workgroup with partition input
+constexpr int kRowsInFlight = kMBParts / kWavesParts;  // rows a wave combines at once (loads in flight)
 // chunk c of o_hat row m at slot c ^ (m & 15): the 16 rows one fragment read covers fall in
 // distinct banks
 __device__ __forceinline__ int slot(int m, int c) { return c ^ (m & 15); }
 }  // namespace uvk
 
-__global__ void __launch_bounds__(256) uv_kernel(const bf16* __restrict__ ohat, const bf16* __restrict__ w,
-                                                 bf16* __restrict__ o, float* __restrict__ o32, int B, int n_h,
-                                                 int d_h) {
+template <int NW, bool PARTS>
+__global__ void __launch_bounds__(64 * NW) uv_kernel(const bf16* __restrict__ ohat, UvPartials parts,
+                                                     const bf16* __restrict__ w, bf16* __restrict__ o,
+                                                     float* __restrict__ o32, int B, int n_h, int d_h) {
   using namespace uvk;
-  __shared__ __attribute__((aligned(1024))) char la[kMB * kRowB];
+  constexpr int MB = PARTS ? kMBParts : kMB;  // rows per LDS block
+  __shared__ __attribute__((aligned(1024))) char la[MB * kRowB];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = blockIdx.y, d0 = blockIdx.x * kCols + wv * 16;
+  int h, c0, m_begin, m_stop;
+  if constexpr (PARTS) {  // block id -> (head, chunk of MB rows); a head's chunks 8 ids apart
+    const int RB = (B + MB - 1) / MB, r = blockIdx.x / 8;
+    h = (r / RB) * 8 + blockIdx.x % 8;
+    if (h >= n_h) return;
+    c0 = 0;
+    m_begin = (r % RB) * MB;
+    m_stop = m_begin + 1;
+  } else {
+    h = blockIdx.y;
+    c0 = blockIdx.x * 16 * NW;
+    m_begin = 0;
+    m_stop = B;
+  }
+  const int d0 = c0 + wv * 16;
   const int G = lane >> 4, i16 = lane & 15;
   // one copy instruction per o_hat row (rows past B repeat row B-1)
   auto copy_a = [&](int m0) {
 #pragma unroll
-    for (int i = 0; i < kMB / kWaves; ++i) {
-      const int r = i * kWaves + wv;
+    for (int i = 0; i < MB / NW; ++i) {
+      const int r = i * NW + wv;
       const int m = min(m0 + r, B - 1);
       const bf16* src = ohat + ((int64_t)m * n_h + h) * kDc + 8 * slot(r, lane);
       __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(la + r * kRowB), 16, 0, 0);
     }
   };
-  copy_a(0);
+  // rows r = i NW + wv of the block, kRowsInFlight at a time: lane holds dims 8 lane .. +7; the
+  // partitions go four at a time, all their loads issued before any is used
+  auto combine_a = [&](int m0) {
+    for (int i0 = 0; i0 < MB / NW; i0 += kRowsInFlight) {
+      float M[kRowsInFlight], L[kRowsInFlight], acc[kRowsInFlight][8];
+      int64_t base[kRowsInFlight];
+#pragma unroll
+      for (int k = 0; k < kRowsInFlight; ++k) {
+        const int m = min(m0 + (i0 + k) * NW + wv, B - 1);
+        base[k] = (int64_t)m * parts.splits * n_h + h;  // partition s at base + s n_h
+        M[k] = -INFINITY;
+        for (int sp = 0; sp < parts.splits; ++sp) M[k] = fmaxf(M[k], parts.m[base[k] + (int64_t)sp * n_h]);
+        L[k] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[k][e] = 0.f;
+      }
+      for (int s0 = 0; s0 < parts.splits; s0 += 4) {
+        float ms[kRowsInFlight][4], ls[kRowsInFlight][4];
+        bf16x8 v[kRowsInFlight][4];
+#pragma unroll
+        for (int k = 0; k < kRowsInFlight; ++k)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            ms[k][u] = -INFINITY;
+            if (s0 + u < parts.splits) {
+              const int64_t pi = base[k] + (int64_t)(s0 + u) * n_h;
+              ms[k][u] = parts.m[pi];
+              ls[k][u] = parts.l[pi];
+              v[k][u] = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(parts.o) + pi * kDc + 8 * lane);
+            }
+          }
+#pragma unroll
+        for (int k = 0; k < kRowsInFlight; ++k)
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (ms[k][u] > -INFINITY) {
+              const float ws = exp2f(ms[k][u] - M[k]) * ls[k][u];
+              L[k] += ws;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) acc[k][e] += ws * (float)v[k][u][e];
+            }
+      }
+#pragma unroll
+      for (int k = 0; k < kRowsInFlight; ++k) {
+        const int r = (i0 + k) * NW + wv;
+        const float inv = L[k] > 0.f ? 1.f / L[k] : 0.f;
+        bf16x8 out;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) out[e] = (bf16)(acc[k][e] * inv);
+        *reinterpret_cast<bf16x8*>(la + r * kRowB + slot(r, lane) * 16) = out;
+      }
+    }
+  };
   // B fragments: lane (G, i) holds weight row d0 + i, k = 32 kk + 8G .. +7
   Frag8<bf16> bw[kDc / 32];
   {
@@ -894,20 +977,31 @@ __global__ void __launch_bounds__(256) uv_kernel(const bf16* __restrict__ ohat, 
 #pragma unroll
     for (int kk = 0; kk < kDc / 32; ++kk) load8(bw[kk], wr + 32 * kk);
   }
-  MLA_TILE_BARRIER(waitcnt_vm(0));
-  for (int m0 = 0; m0 < B; m0 += kMB) {
-    if (m0 > 0) {
+  if constexpr (PARTS) {
+    combine_a(m_begin);
+    MLA_TILE_BARRIER(kWaitLgkm0);
+  } else {
+    copy_a(0);
+    MLA_TILE_BARRIER(waitcnt_vm(0));
+  }
+  for (int m0 = m_begin; m0 < m_stop; m0 += MB) {
+    if (m0 > m_begin) {
       __syncthreads();  // every wave is done with the previous block
-      copy_a(m0);
-      MLA_TILE_BARRIER(waitcnt_vm(0));
+      if constexpr (PARTS) {
+        combine_a(m0);
+        MLA_TILE_BARRIER(kWaitLgkm0);
+      } else {
+        copy_a(m0);
+        MLA_TILE_BARRIER(waitcnt_vm(0));
+      }
     }
-    floatx4 acc[4];
+    floatx4 acc[MB / 16];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) acc[mb] = floatx4{0, 0, 0, 0};
+    for (int mb = 0; mb < MB / 16; ++mb) acc[mb] = floatx4{0, 0, 0, 0};
 #pragma unroll
     for (int kk = 0; kk < kDc / 32; ++kk)
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
+      for (int mb = 0; mb < MB / 16; ++mb) {
         const int r = mb * 16 + i16;  // A fragment: row r, k = 32 kk + 8G .. +7 (chunk 4 kk + G)
         Frag8<bf16> a;
         a.v = *reinterpret_cast<const bf16x8*>(la + r * kRowB + slot(r, 4 * kk + G) * 16);
@@ -915,7 +1009,7 @@ __global__ void __launch_bounds__(256) uv_kernel(const bf16* __restrict__ ohat, 
       }
     // C lane: column d0 + i, rows 4G + j
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < MB / 16; ++mb)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int m = m0 + mb * 16 + 4 * G + j;
@@ -929,13 +1023,23 @@ __global__ void __launch_bounds__(256) uv_kernel(const bf16* __restrict__ ohat, 
 }
 
 bool uv_ok(DType t, int d_h, int d_c) { return t == DType::BF16 && d_c == uvk::kDc && d_h % uvk::kCols == 0; }
+bool uv_parts_ok(DType t, int d_h, int d_c) { return uv_ok(t, d_h, d_c) && d_h == 16 * uvk::kWavesParts; }
 
 hipError_t uv_run(const void* ohat, const void* w_uv, void* o, float* o32, int B, int n_h, int d_h,
-                  hipStream_t s) {
+                  hipStream_t s, const UvPartials* parts) {
   if (B == 0) return hipSuccess;
+  if (parts) {
+    if (d_h != 16 * uvk::kWavesParts || parts->splits < 1) return hipErrorInvalidValue;
+    const int blocks = (n_h + 7) / 8 * 8 * ((B + uvk::kMBParts - 1) / uvk::kMBParts);
+    hipLaunchKernelGGL((uv_kernel<uvk::kWavesParts, true>), dim3(blocks), dim3(64 * uvk::kWavesParts), 0, s,
+                       nullptr, *parts, reinterpret_cast<const bf16*>(w_uv), reinterpret_cast<bf16*>(o), o32, B,
+                       n_h, d_h);
+    return hipGetLastError();
+  }
   dim3 grid(d_h / uvk::kCols, n_h);
-  hipLaunchKernelGGL(uv_kernel, grid, dim3(64 * uvk::kWaves), 0, s, reinterpret_cast<const bf16*>(ohat),
-                     reinterpret_cast<const bf16*>(w_uv), reinterpret_cast<bf16*>(o), o32, B, n_h, d_h);
+  hipLaunchKernelGGL((uv_kernel<uvk::kWaves, false>), grid, dim3(64 * uvk::kWaves), 0, s,
+                     reinterpret_cast<const bf16*>(ohat), UvPartials{}, reinterpret_cast<const bf16*>(w_uv),
+                     reinterpret_cast<bf16*>(o), o32, B, n_h, d_h);
   return hipGetLastError();
 }
 
@@ -957,8 +1061,18 @@ hipError_t launch_cfg(const GemmParams& p, const GemmPlan& plan, float* partial,
 }
 
 template <typename T>
-hipError_t run_t(const GemmParams& p, const GemmPlan& plan, float* partial, hipStream_t s) {
+hipError_t run_t(const GemmParams& p_in, const GemmPlan& plan, float* partial, hipStream_t s) {
   hipError_t err;
+  // the RoPE table rides along in the skinny kernel when a reduce pass (which runs the epilogue)
+  // follows it; otherwise it is filled by its own launch first
+  const bool side = p_in.side_rope.tab && (plan.cfg == 3 || plan.cfg == 4) && plan.splits > 1;
+  GemmParams p = p_in;
+  if (p.side_rope.tab && !side) {
+    const RopeJob& r = p.side_rope;
+    err = rope_table(r.pos, r.n, 2 * r.half, r.f, r.tab, s);
+    if (err != hipSuccess) return err;
+    p.side_rope = RopeJob{};
+  }
   switch (plan.cfg) {
     case 0: err = launch_cfg<T, 0>(p, plan, partial, s); break;
     case 1: err = launch_cfg<T, 1>(p, plan, partial, s); break;
@@ -970,7 +1084,7 @@ hipError_t run_t(const GemmParams& p, const GemmPlan& plan, float* partial, hipS
     }
     case 3:
     case 4: {
-      dim3 grid((p.N + skinny::kBN - 1) / skinny::kBN, p.batch * plan.splits);
+      dim3 grid((p.N + skinny::kBN - 1) / skinny::kBN + (side ? 1 : 0), p.batch * plan.splits);
       if (plan.cfg == 3)
         hipLaunchKernelGGL(gemm_skinny_kernel<1>, grid, dim3(256), 0, s, p, plan.splits, plan.k_per_split, partial);
       else

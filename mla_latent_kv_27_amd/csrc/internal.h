@@ -11,6 +11,40 @@ enum class DType { F32 = 0, BF16 = 1 };
 
 inline size_t dsize(DType t) { return t == DType::BF16 ? 2 : 4; }
 
+// RoPE frequencies: theta_k = base^(-2k/d_hr), or their YaRN form when scale > 1 (turns counted
+// over orig_ctx positions, ramp from alpha to beta turns).
+struct RopeFreq {
+  double base = 10000.0;
+  double scale = 1.0;
+  double orig_ctx = 0.0, alpha = 1.0, beta = 32.0;
+};
+// Entry i = r * half + k of the RoPE table: (cos, sin)(pos[r] * theta_k), the angle formed and
+// reduced in fp64 (positions up to 1.3e5 keep full fp32 accuracy in cos/sin).
+__device__ inline float2 rope_table_entry(const int32_t* pos, int half, const RopeFreq& f, int64_t i) {
+  const int r = (int)(i / half), k = (int)(i % half);
+  const double two_pi = 6.283185307179586476925286766559;
+  double theta = exp(-(2.0 * k / (2.0 * half)) * log(f.base));
+  if (f.scale > 1.0) {
+    const double turns = f.orig_ctx * theta / two_pi;
+    const double g = fmin(fmax((turns - f.alpha) / (f.beta - f.alpha), 0.0), 1.0);
+    theta = g * theta + (1.0 - g) * (theta / f.scale);
+  }
+  double a = (double)pos[r] * theta;
+  a = a - floor(a / two_pi) * two_pi;
+  double sn, cs;
+  sincos(a, &sn, &cs);
+  return make_float2((float)cs, (float)sn);
+}
+
+// A RoPE table for n positions that a GEMM fills on the side (in extra workgroups of its first
+// kernel) when its epilogue runs in a later split-K pass; otherwise gemm_run fills it first.
+struct RopeJob {
+  const int32_t* pos = nullptr;
+  int n = 0, half = 0;
+  RopeFreq f;
+  float2* tab = nullptr;  // null: no job
+};
+
 // Where a GEMM result element (row, col) of batch z is stored, and what happens on the way.
 //   address = z*batch_stride + rowbase(row) + (col/group)*group_stride + group_off + col%group
 //   rowbase = row*ldc, or, when block_table is set, slot(row)*ldc with
@@ -53,6 +87,7 @@ struct GemmParams {
   Epilogue epi;
   Epilogue epi2;
   int E0 = 1 << 30;
+  RopeJob side_rope;  // the table the epilogues read, filled before they run
 };
 
 struct GemmPlan {
@@ -74,9 +109,18 @@ hipError_t absorb_run(const void* qc, const void* w_uk, void* qhat, int B, int n
 // o = W_UV per head for bf16 (d_c == 512, d_h a multiple of 64):
 // o[(b*n_h + h)*d_h + d] = sum_c w_uv[(h*d_h + d)*512 + c] * ohat[(b*n_h + h)*512 + c]; o32 (may be
 // null) receives the same values in fp32.
+// With `parts` (split-KV decode's per-partition outputs, bf16 O_s / l_s, uv_parts_ok: d_h == 128)
+// o_hat is not read: its rows are combined from the partitions by the log-sum-exp rule on the way.
+struct UvPartials {
+  const float* m = nullptr;  // [B][splits][n_h] partition max (log2 domain)
+  const float* l = nullptr;  // [B][splits][n_h] partition normaliser
+  const void* o = nullptr;   // [B][splits][n_h][512] bf16 O_s / l_s
+  int splits = 0;
+};
 bool uv_ok(DType t, int d_h, int d_c);
+bool uv_parts_ok(DType t, int d_h, int d_c);
 hipError_t uv_run(const void* ohat, const void* w_uv, void* o, float* o32, int B, int n_h, int d_h,
-                  hipStream_t s);
+                  hipStream_t s, const UvPartials* parts = nullptr);
 // fp8 cache quantiser (latent_fp8.hip).  Destination of entry row r: dense row r of `codes` /
 // `scales` when block_table is null, else the paged slot of (row_seq ? row_seq[r] : r, row_pos[r]).
 struct QuantDst {
@@ -99,13 +143,6 @@ size_t gemm_partial_bound(int M, int N, int K, int batch, int cus, bool skinny_o
 hipError_t gemm_run(DType t, const GemmParams& p, const GemmPlan& plan, float* partial,
                     hipStream_t s);
 
-// RoPE frequencies: theta_k = base^(-2k/d_hr), or their YaRN form when scale > 1 (turns counted
-// over orig_ctx positions, ramp from alpha to beta turns).
-struct RopeFreq {
-  double base = 10000.0;
-  double scale = 1.0;
-  double orig_ctx = 0.0, alpha = 1.0, beta = 32.0;
-};
 // rope_tab[r][k] = (cos, sin)(pos[r] * theta_k), r < n; angles formed in fp64.
 hipError_t rope_table(const int32_t* pos, int n, int d_hr, const RopeFreq& f, float2* tab, hipStream_t s);
 // x[r][0..W) <- gain * x / sqrt(mean(x^2) + eps) for rows r < n, ld elements apart, in place
@@ -163,7 +200,12 @@ struct DecodeAttnParams {
   float* lse;             // optional [B][n_h], natural log
   bool fp8 = false;       // pool holds e4m3 codes, with per-token (s_c, s_r) in scales
   const float* scales = nullptr;  // [num_blocks][block_size][2]
+  bool leave_partials = false;    // splits > 1: skip the combine (the consumer combines; needs
+                                  // decode_bf16_partials), o_hat and lse are not written
 };
+
+// true when the kernel decode_attention picks writes bf16 partition outputs
+bool decode_bf16_partials(DType t, const DecodeAttnParams& p);
 
 bool decode_supported(int d_c, int d_hr);
 hipError_t decode_attention(DType t, const DecodeAttnParams& p, hipStream_t s);

@@ -622,13 +622,15 @@ int mla_decode(const mla_dims* d, const mla_weights* w, const mla_paged_cache* c
   const DType t = dt(d);
   const int B = batch, E = entry(d), qw = q_in(d);
 
-  // positions of the new tokens are ctx_lens[b]; rows are sequences 0..B-1
-  MLA_HIP(rope_table(ctx_lens, B, d->d_hr, freq_of(d), ws.rope, s));
   const void* qin = h;
   {  // [c^q | c^KV | k^R] = [W_DQ; W_DKV; W_KR] h: c^q to the workspace, the new token's cache
      // entry to position ctx_lens[b] of its sequence
     GemmParams g;
     g.A = h; g.lda = d->d_model; g.ldb = d->d_model;
+    // the RoPE table of the new tokens' positions ctx_lens[b] (rows are sequences 0..B-1), read
+    // by this product's epilogue and the next one's
+    g.side_rope.pos = ctx_lens; g.side_rope.n = B; g.side_rope.half = d->d_hr / 2;
+    g.side_rope.f = freq_of(d); g.side_rope.tab = ws.rope;
     g.M = B; g.N = kvq_cols(d); g.K = d->d_model;
     if (d->d_cq > 0) {
       g.B0 = w->W_DQ; g.N0 = d->d_cq;
@@ -678,6 +680,7 @@ int mla_decode(const mla_dims* d, const mla_weights* w, const mla_paged_cache* c
     g.epi.batch_stride = E;
     MLA_HIP(gemm_run(t, g, ws.gm.absorb, ws.partial, s));
   }
+  UvPartials parts;
   {  // latent attention over ctx_lens[b] + 1 entries
     DecodeAttnParams a{};
     a.q = ws.qcat; a.pool = c->pool; a.block_table = c->block_table;
@@ -689,9 +692,15 @@ int mla_decode(const mla_dims* d, const mla_weights* w, const mla_paged_cache* c
     a.splits = ws.attn.splits; a.tokens_per_split = ws.attn.tps;
     a.part_m = ws.attn.pm; a.part_l = ws.attn.pl; a.part_o = ws.attn.po;
     a.o_hat = ws.ohat; a.lse = nullptr;
+    // with several partitions and the W_UV kernel that combines them, the combine pass is skipped
+    a.leave_partials = a.splits > 1 && uv_parts_ok(t, d->d_h, d->d_c) && decode_bf16_partials(t, a);
     MLA_HIP(decode_attention(t, a, s));
+    parts.m = a.part_m; parts.l = a.part_l; parts.o = a.part_o;
+    parts.splits = a.leave_partials ? a.splits : 0;
   }
-  if (uv_ok(t, d->d_h, d->d_c)) {  // o_i = W_UV_i o_hat_i
+  if (parts.splits > 0) {  // o_i = W_UV_i o_hat_i, o_hat_i combined from the partitions
+    MLA_HIP(uv_run(nullptr, w->W_UV, ws.o, o_heads, B, d->n_h, d->d_h, s, &parts));
+  } else if (uv_ok(t, d->d_h, d->d_c)) {  // o_i = W_UV_i o_hat_i
     MLA_HIP(uv_run(ws.ohat, w->W_UV, ws.o, o_heads, B, d->n_h, d->d_h, s));
   } else {
     GemmParams g;

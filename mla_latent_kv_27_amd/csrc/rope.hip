@@ -17,19 +17,7 @@ __global__ void __launch_bounds__(256)
     rope_table_kernel(const int32_t* __restrict__ pos, int n, int half, RopeFreq f, float2* tab) {
   const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (i >= (int64_t)n * half) return;
-  const int r = (int)(i / half), k = (int)(i % half);
-  const double two_pi = 6.283185307179586476925286766559;
-  double theta = exp(-(2.0 * k / (2.0 * half)) * log(f.base));
-  if (f.scale > 1.0) {
-    const double turns = f.orig_ctx * theta / two_pi;
-    const double g = fmin(fmax((turns - f.alpha) / (f.beta - f.alpha), 0.0), 1.0);
-    theta = g * theta + (1.0 - g) * (theta / f.scale);
-  }
-  double a = (double)pos[r] * theta;
-  a = a - floor(a / two_pi) * two_pi;
-  double sn, cs;
-  sincos(a, &sn, &cs);
-  tab[i] = make_float2((float)cs, (float)sn);
+  tab[i] = rope_table_entry(pos, half, f, i);
 }
 
 hipError_t rope_table(const int32_t* pos, int n, int d_hr, const RopeFreq& f, float2* tab, hipStream_t s) {
