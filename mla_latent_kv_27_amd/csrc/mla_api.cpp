@@ -223,7 +223,7 @@ struct PrefillWs {
   float2* rope;
   void *cq, *qp, *kvd, *kva, *kp, *vt, *o;  // kva: chunked prefill's gathered keys (else kvd)
   float* partial;
-  GemmPlan cq_p, qc_p, qr_p, kv_p, k_p, v_p, out_p;
+  GemmPlan kvq_p, q_p, kv_p, k_p, v_p, out_p;  // kvq_p: [W_DQ; W_DKV; W_KR] (d_cq > 0), else kv_p
   int Tk, Tp;  // key rows per sequence (T, or max_start + T when chunked), rounded up to 64
 };
 // chunked: keys are the cached prefix plus the new rows, max_start + T per sequence
@@ -236,10 +236,9 @@ PrefillWs carve_prefill(Carve& cv, const mla_dims* d, int S, int T, int cus, boo
   const int Mk = S * w.Tk;
   w.Tp = (w.Tk + 63) / 64 * 64;
   const int qw = d->n_h * (d->d_h + d->d_hr);
-  w.cq_p = d->d_cq > 0 ? gemm_plan(M, d->d_cq, d->d_model, 1, cus, sk(d)) : GemmPlan{};
-  w.qc_p = gemm_plan(M, d->n_h * d->d_h, q_in(d), 1, cus, sk(d));
-  w.qr_p = gemm_plan(M, d->n_h * d->d_hr, q_in(d), 1, cus, sk(d));
-  w.kv_p = gemm_plan(M, entry(d), d->d_model, 1, cus, sk(d));
+  w.kvq_p = d->d_cq > 0 ? gemm_plan(M, d->d_cq + entry(d), d->d_model, 1, cus, sk(d)) : GemmPlan{};
+  w.q_p = gemm_plan(M, qw, q_in(d), 1, cus, sk(d));
+  w.kv_p = d->d_cq > 0 ? GemmPlan{} : gemm_plan(M, entry(d), d->d_model, 1, cus, sk(d));
   w.k_p = gemm_plan(Mk, d->n_h * d->d_h, d->d_c, 1, cus, sk(d));
   w.v_p = gemm_plan(d->n_h * d->d_h, Mk, d->d_c, 1, cus, sk(d));
   w.out_p = gemm_plan(M, d->d_model, d->n_h * d->d_h, 1, cus, sk(d));
@@ -253,13 +252,12 @@ PrefillWs carve_prefill(Carve& cv, const mla_dims* d, int S, int T, int cus, boo
   w.kp = cv.take<char>((size_t)Mk * d->n_h * d->d_h * es);
   w.vt = cv.take<char>((size_t)d->n_h * d->d_h * S * w.Tp * es);
   w.o = cv.take<char>((size_t)M * d->n_h * d->d_h * es);
-  size_t mp = std::max({gemm_partial_bound(M, d->n_h * d->d_h, q_in(d), 1, cus, sk(d)),
-                        gemm_partial_bound(M, d->n_h * d->d_hr, q_in(d), 1, cus, sk(d)),
+  size_t mp = std::max({gemm_partial_bound(M, qw, q_in(d), 1, cus, sk(d)),
                         gemm_partial_bound(M, entry(d), d->d_model, 1, cus, sk(d)),
                         gemm_partial_bound(Mk, d->n_h * d->d_h, d->d_c, 1, cus, sk(d)),
                         gemm_partial_bound(d->n_h * d->d_h, Mk, d->d_c, 1, cus, sk(d)),
                         gemm_partial_bound(M, d->d_model, d->n_h * d->d_h, 1, cus, sk(d))});
-  if (d->d_cq > 0) mp = std::max(mp, gemm_partial_bound(M, d->d_cq, d->d_model, 1, cus, sk(d)));
+  if (d->d_cq > 0) mp = std::max(mp, gemm_partial_bound(M, d->d_cq + entry(d), d->d_model, 1, cus, sk(d)));
   w.partial = cv.take<float>(mp);
   return w;
 }
@@ -399,39 +397,43 @@ int prefill_impl(const mla_dims* d, const mla_weights* w, const mla_paged_cache*
   MLA_HIP(prefill_rows(M, T, ws.seq, ws.pos, s, start));
   MLA_HIP(rope_table(ws.pos, M, d->d_hr, freq_of(d), ws.rope, s));
   const void* qin = h;
+  // dense [c^KV | RoPE(k^R)] rows (then normalised and copied into the paged cache), and c^q
+  // when the query is compressed: one product [W_DQ; W_DKV; W_KR] h
+  Epilogue kv_epi = dense(ws.kvd, E);
+  kv_epi.rope_col0 = d->d_c; kv_epi.d_hr = d->d_hr; kv_epi.rope_tab = ws.rope;
   if (d->d_cq > 0) {
     GemmParams g;
-    g.A = h; g.lda = d->d_model; g.B0 = w->W_DQ; g.ldb = d->d_model;
-    g.M = M; g.N = d->d_cq; g.K = d->d_model;
+    g.A = h; g.lda = d->d_model; g.ldb = d->d_model;
+    g.B0 = w->W_DQ; g.N0 = d->d_cq; g.B1 = w->W_DKV; g.N1 = d->d_cq + d->d_c; g.B2 = w->W_KR;
+    g.M = M; g.N = d->d_cq + E; g.K = d->d_model;
     g.epi = dense(ws.cq, d->d_cq);
-    MLA_HIP(gemm_run(t, g, ws.cq_p, ws.partial, s));
+    g.E0 = d->d_cq;
+    g.epi2 = kv_epi;
+    MLA_HIP(gemm_run(t, g, ws.kvq_p, ws.partial, s));
     if (w->g_cq) MLA_HIP(rmsnorm_rows(t, ws.cq, M, d->d_cq, d->d_cq, w->g_cq, eps_of(d), s));
     qin = ws.cq;
-  }
-  {  // q^C -> columns [0, d_h) of each head's [q^C | q^R] row
-    GemmParams g;
-    g.A = qin; g.lda = qw; g.B0 = w->W_UQ; g.ldb = qw;
-    g.M = M; g.N = d->n_h * d->d_h; g.K = qw;
-    g.epi = dense(ws.qp, (int64_t)d->n_h * QD);
-    g.epi.group = d->d_h; g.epi.group_stride = QD; g.epi.group_off = 0;
-    MLA_HIP(gemm_run(t, g, ws.qc_p, ws.partial, s));
-  }
-  {  // RoPE(q^R) -> columns [d_h, d_h + d_hr)
-    GemmParams g;
-    g.A = qin; g.lda = qw; g.B0 = w->W_QR; g.ldb = qw;
-    g.M = M; g.N = d->n_h * d->d_hr; g.K = qw;
-    g.epi = dense(ws.qp, (int64_t)d->n_h * QD);
-    g.epi.group = d->d_hr; g.epi.group_stride = QD; g.epi.group_off = d->d_h;
-    g.epi.rope_col0 = 0; g.epi.d_hr = d->d_hr; g.epi.rope_tab = ws.rope;
-    MLA_HIP(gemm_run(t, g, ws.qr_p, ws.partial, s));
-  }
-  {  // dense [c^KV | RoPE(k^R)] rows, then copied into the paged cache
+  } else {
     GemmParams g;
     g.A = h; g.lda = d->d_model; g.B0 = w->W_DKV; g.B1 = w->W_KR; g.N0 = d->d_c; g.ldb = d->d_model;
     g.M = M; g.N = E; g.K = d->d_model;
-    g.epi = dense(ws.kvd, E);
-    g.epi.rope_col0 = d->d_c; g.epi.d_hr = d->d_hr; g.epi.rope_tab = ws.rope;
+    g.epi = kv_epi;
     MLA_HIP(gemm_run(t, g, ws.kv_p, ws.partial, s));
+  }
+  {  // [q^C | RoPE(q^R)] = [W_UQ; W_QR] c^q: q^C to columns [0, d_h) and q^R to [d_h, d_h + d_hr)
+     // of each head's row
+    GemmParams g;
+    g.A = qin; g.lda = qw; g.ldb = qw;
+    g.B0 = w->W_UQ; g.N0 = d->n_h * d->d_h; g.B1 = w->W_QR;
+    g.M = M; g.N = d->n_h * QD; g.K = qw;
+    g.epi = dense(ws.qp, (int64_t)d->n_h * QD);
+    g.epi.group = d->d_h; g.epi.group_stride = QD; g.epi.group_off = 0;
+    g.E0 = d->n_h * d->d_h;
+    g.epi2 = dense(ws.qp, (int64_t)d->n_h * QD);
+    g.epi2.group = d->d_hr; g.epi2.group_stride = QD; g.epi2.group_off = d->d_h;
+    g.epi2.rope_col0 = 0; g.epi2.d_hr = d->d_hr; g.epi2.rope_tab = ws.rope;
+    MLA_HIP(gemm_run(t, g, ws.q_p, ws.partial, s));
+  }
+  {
     {  // c^KV norm in place (the K/V products below read it), then into the pages
       const int rc = finish_entries(d, w, c, ws.kvd, M, ws.seq, ws.pos, s);
       if (rc != MLA_OK) return rc;
