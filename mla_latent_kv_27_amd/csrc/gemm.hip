@@ -689,6 +689,30 @@ __global__ void __launch_bounds__(512) gemm_big_kernel(GemmParams p) {
   float* e_C2 = hi ? p.epi2.C2 : p.epi.C2;
   const bool e_f32 = hi ? p.epi2.c_f32 : p.epi.c_f32;
   const bool col_ok = col < p.N;
+  // The vector path: every group of four columns lies in one epilogue's range and one of its
+  // column groups, its RoPE pairs start at even columns, and rows of 4 elements are aligned.
+  const bool vec4 = p.N % 4 == 0 && (p.E0 >= p.N || p.E0 % 4 == 0) && p.epi.group % 4 == 0 &&
+                    p.epi2.group % 4 == 0 && p.epi.ldc % 4 == 0 && p.epi2.ldc % 4 == 0 &&
+                    p.epi.group_stride % 4 == 0 && p.epi2.group_stride % 4 == 0 &&
+                    p.epi.group_off % 4 == 0 && p.epi2.group_off % 4 == 0 && p.epi.batch_stride % 4 == 0 &&
+                    p.epi2.batch_stride % 4 == 0 && (p.epi.rope_tab == nullptr || p.epi.rope_col0 % 4 == 0) &&
+                    (p.epi2.rope_tab == nullptr || p.epi2.rope_col0 % 4 == 0) &&
+                    p.epi.d_hr % 4 == 0 && p.epi2.d_hr % 4 == 0;
+  // this lane's fields for the vector path: columns v_col .. v_col + 3
+  const int v_col = n0 + wn * 64 + 4 * (lane & 15);
+  const bool v_hi = v_col >= p.E0;
+  const int v_c = v_hi ? v_col - p.E0 : v_col;
+  const Epilogue& ve = v_hi ? p.epi2 : p.epi;
+  const int64_t v_off = (int64_t)z * ve.batch_stride + (int64_t)(v_c / ve.group) * ve.group_stride +
+                        ve.group_off + v_c % ve.group;
+  const bool v_rot = ve.rope_tab != nullptr && v_c >= ve.rope_col0;
+  const int v_dhr = ve.d_hr;
+  const int v_rk = v_rot ? ((v_c - ve.rope_col0) % v_dhr) >> 1 : 0;
+  const float2* v_tab = ve.rope_tab;
+  void* v_C = ve.C;
+  float* v_C2 = ve.C2;
+  const bool v_f32 = ve.c_f32;
+  const bool v_ok = v_col < p.N;
   // element (lr, lc) at lr*64 + (lc ^ 32*((lr >> 2) & 1)): the two row groups one write covers
   // land in different banks
 #pragma unroll
@@ -705,10 +729,41 @@ __global__ void __launch_bounds__(512) gemm_big_kernel(GemmParams p) {
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     __builtin_amdgcn_wave_barrier();
     const int row0 = m0 + wm * 128 + h * 64;
+    const int nrows = min(64, p.M - row0);
+    if (vec4) {
+      // four consecutive columns and one of four rows per lane: 8- (or 16-) byte stores, RoPE
+      // pairs inside the lane
+      const int rq = lane >> 4, cq = 4 * (lane & 15);
+      for (int lr = rq; lr < nrows; lr += 4) {
+        const int sw = ((lr >> 2) & 1) << 5;
+        floatx4 v = *reinterpret_cast<const floatx4*>(&ep[lr * 64 + (cq ^ sw)]);
+        const int row = row0 + lr;
+        if (v_rot) {
+          const float4 cs = *reinterpret_cast<const float4*>(&v_tab[(int64_t)row * (v_dhr >> 1) + v_rk]);
+          const float a0 = v[0] * cs.x - v[1] * cs.y, a1 = v[1] * cs.x + v[0] * cs.y;
+          const float b0 = v[2] * cs.z - v[3] * cs.w, b1 = v[3] * cs.z + v[2] * cs.w;
+          v = floatx4{a0, a1, b0, b1};
+        }
+        if (v_ok) {
+          const int64_t idx = epi_row_base(v_hi ? p.epi2 : p.epi, row) + v_off;
+          if (v_f32) {
+            *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(v_C) + idx) = v;
+          } else {
+            bf16x4 o;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = from_f32<bf16>(v[i]);
+            *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(v_C) + idx) = o;
+          }
+          if (v_C2) *reinterpret_cast<floatx4*>(v_C2 + idx) = v;
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      __builtin_amdgcn_wave_barrier();
+      continue;
+    }
     const int my_row = min(row0 + lane, p.M - 1);
     const int64_t rb_lo = epi_row_base(p.epi, my_row);
     const int64_t rb_hi = p.E0 < p.N ? epi_row_base(p.epi2, my_row) : 0;
-    const int nrows = min(64, p.M - row0);
     for (int lr = 0; lr < nrows; ++lr) {
       const int sw = ((lr >> 2) & 1) << 5;
       float v = ep[lr * 64 + (lane ^ sw)];
