@@ -15,7 +15,7 @@ INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 LIB = os.path.join(PKG, "lib", "libmla.so")
 ARCH = os.environ.get("MLA_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["gemm.hip", "rope.hip", "decode_attn.hip", "prefill_attn.hip", "latent_fp8.hip", "mla_api.cpp"]
+SOURCES = ["gemm.hip", "rope.hip", "decode_attn.hip", "prefill_attn.hip", "latent_fp8.hip", "blas.cpp", "mla_api.cpp"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
@@ -48,7 +48,7 @@ def build(verbose: bool = False) -> str:
     with ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
+    cmd = [_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-lhipblaslt", "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")

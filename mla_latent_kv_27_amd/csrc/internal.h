@@ -117,6 +117,12 @@ struct UvPartials {
   const void* o = nullptr;   // [B][splits][n_h][512] bf16 O_s / l_s
   int splits = 0;
 };
+// Plain product D[M][N] = A[M][K] B[N][K]^T (row-major, leading dimensions in elements, bf16,
+// fp32 accumulation) through hipBLASLt, with up to ws_bytes of workspace.  hipErrorNotSupported
+// when the library has no algorithm for it (the caller then uses gemm_run).
+constexpr size_t kBlasWs = size_t(32) << 20;
+hipError_t blas_gemm_nt(const void* A, int64_t lda, const void* B, int64_t ldb, void* D, int64_t ldd, int M, int N,
+                        int K, void* ws, size_t ws_bytes, hipStream_t s);
 bool uv_ok(DType t, int d_h, int d_c);
 bool uv_parts_ok(DType t, int d_h, int d_c);
 hipError_t uv_run(const void* ohat, const void* w_uv, void* o, float* o32, int B, int n_h, int d_h,

@@ -223,6 +223,7 @@ struct PrefillWs {
   float2* rope;
   void *cq, *qp, *kvd, *kva, *kp, *vt, *o;  // kva: chunked prefill's gathered keys (else kvd)
   float* partial;
+  void* blas;  // hipBLASLt workspace (bf16 layers), kBlasWs bytes
   GemmPlan kvq_p, q_p, kv_p, k_p, v_p, out_p;  // kvq_p: [W_DQ; W_DKV; W_KR] (d_cq > 0), else kv_p
   int Tk, Tp;  // key rows per sequence (T, or max_start + T when chunked), rounded up to 64
 };
@@ -259,6 +260,7 @@ PrefillWs carve_prefill(Carve& cv, const mla_dims* d, int S, int T, int cus, boo
                         gemm_partial_bound(M, d->d_model, d->n_h * d->d_h, 1, cus, sk(d))});
   if (d->d_cq > 0) mp = std::max(mp, gemm_partial_bound(M, d->d_cq + entry(d), d->d_model, 1, cus, sk(d)));
   w.partial = cv.take<float>(mp);
+  w.blas = cv.take<char>(dt(d) == DType::BF16 ? kBlasWs : 0);
   return w;
 }
 
@@ -467,12 +469,19 @@ int prefill_impl(const mla_dims* d, const mla_weights* w, const mla_paged_cache*
     a.scale_log2 = scale_of(d) * 1.4426950408889634f;
     MLA_HIP(prefill_attention(t, a, s));
   }
-  {
-    GemmParams g;
-    g.A = ws.o; g.lda = (int64_t)d->n_h * d->d_h; g.B0 = w->W_O; g.ldb = (int64_t)d->n_h * d->d_h;
-    g.M = M; g.N = d->d_model; g.K = d->n_h * d->d_h;
-    g.epi = dense(u, d->d_model);
-    MLA_HIP(gemm_run(t, g, ws.out_p, ws.partial, s));
+  {  // u = W_O [o_1; ...; o_n_h]: a plain product (hipBLASLt for bf16)
+    const int64_t K = (int64_t)d->n_h * d->d_h;
+    hipError_t e = t == DType::BF16 ? blas_gemm_nt(ws.o, K, w->W_O, K, u, d->d_model, M, d->d_model, (int)K, ws.blas,
+                                                   kBlasWs, s)
+                                    : hipErrorNotSupported;
+    if (e == hipErrorNotSupported) {
+      GemmParams g;
+      g.A = ws.o; g.lda = K; g.B0 = w->W_O; g.ldb = K;
+      g.M = M; g.N = d->d_model; g.K = (int)K;
+      g.epi = dense(u, d->d_model);
+      e = gemm_run(t, g, ws.out_p, ws.partial, s);
+    }
+    MLA_HIP(e);
   }
   return MLA_OK;
 }
@@ -714,7 +723,7 @@ int mla_decode(const mla_dims* d, const mla_weights* w, const mla_paged_cache* c
     g.epi.C2 = o_heads;
     MLA_HIP(gemm_run(t, g, ws.gm.uv, ws.partial, s));
   }
-  {  // u = W_O [o_1; ...; o_n_h]
+  {  // u = W_O [o_1; ...; o_n_h] (the weight-streaming kernel: faster than hipBLASLt at M <= 64)
     GemmParams g;
     g.A = ws.o; g.lda = (int64_t)d->n_h * d->d_h; g.B0 = w->W_O; g.ldb = (int64_t)d->n_h * d->d_h;
     g.M = B; g.N = d->d_model; g.K = d->n_h * d->d_h;
