@@ -117,12 +117,13 @@ struct UvPartials {
   const void* o = nullptr;   // [B][splits][n_h][512] bf16 O_s / l_s
   int splits = 0;
 };
-// Plain product D[M][N] = A[M][K] B[N][K]^T (row-major, leading dimensions in elements, bf16,
-// fp32 accumulation) through hipBLASLt, with up to ws_bytes of workspace.  hipErrorNotSupported
-// when the library has no algorithm for it (the caller then uses gemm_run).
+// Plain product D[M][N] = A[M][K] B[N][K]^T (row-major, leading dimensions in elements, bf16
+// operands, fp32 accumulation, D bf16 or fp32) through hipBLASLt, with up to ws_bytes of
+// workspace.  hipErrorNotSupported when the library has no algorithm for it (the caller then
+// uses gemm_run).
 constexpr size_t kBlasWs = size_t(32) << 20;
 hipError_t blas_gemm_nt(const void* A, int64_t lda, const void* B, int64_t ldb, void* D, int64_t ldd, int M, int N,
-                        int K, void* ws, size_t ws_bytes, hipStream_t s);
+                        int K, void* ws, size_t ws_bytes, hipStream_t s, bool d_f32 = false);
 bool uv_ok(DType t, int d_h, int d_c);
 bool uv_parts_ok(DType t, int d_h, int d_c);
 hipError_t uv_run(const void* ohat, const void* w_uv, void* o, float* o32, int B, int n_h, int d_h,
@@ -232,8 +233,16 @@ struct PrefillAttnParams {
   int Tk = 0;                     // 0: T
   const int32_t* q_off = nullptr;
   float scale_log2;
+  // Token-major operands, read by the pipelined kernel only (prefill_pipelined):
+  const void* qc = nullptr;       // set: [S*T][n_h*d_h] q^C instead of q's [q^C | q^R] rows
+  const float* qr = nullptr;      //      [S*T][n_h*d_hr] un-rotated q^R (fp32), rotated on load
+  const float2* rope = nullptr;   //      [S*T][d_hr/2] (cos, sin) of the query rows
+  int64_t k_ld = 0;               // > 0: k is [S*Tk][k_ld] with head h at columns h*d_h (else head-major)
 };
 bool prefill_supported(int d_h, int d_hr);
+// Whether prefill_attention takes the pipelined kernel for these shapes (bf16, d_h = 128,
+// d_hr = 64, every source span under 2 GiB with k token-major, k_ld = n_h * d_h).
+bool prefill_pipelined(DType t, int S, int Tk, int n_h, int d_h, int d_hr, int64_t ld_kr);
 hipError_t prefill_attention(DType t, const PrefillAttnParams& p, hipStream_t s);
 
 }  // namespace mla

@@ -226,6 +226,9 @@ struct PrefillWs {
   void* blas;  // hipBLASLt workspace (bf16 layers), kBlasWs bytes
   GemmPlan kvq_p, q_p, kv_p, k_p, v_p, out_p;  // kvq_p: [W_DQ; W_DKV; W_KR] (d_cq > 0), else kv_p
   int Tk, Tp;  // key rows per sequence (T, or max_start + T when chunked), rounded up to 64
+  bool tm;     // the pipelined attention kernel runs: q^C, q^R (fp32) and k token-major
+  void *qc2;   // tm: [M][n_h*d_h] q^C, in qp's region
+  float* qr2;  // tm: [M][n_h*d_hr] un-rotated q^R, in qp's region after qc2
 };
 // chunked: keys are the cached prefix plus the new rows, max_start + T per sequence
 PrefillWs carve_prefill(Carve& cv, const mla_dims* d, int S, int T, int cus, bool chunked = false,
@@ -247,7 +250,11 @@ PrefillWs carve_prefill(Carve& cv, const mla_dims* d, int S, int T, int cus, boo
   w.pos = cv.take<int32_t>((size_t)M * 4);
   w.rope = cv.take<float2>((size_t)M * (d->d_hr / 2) * sizeof(float2));
   w.cq = cv.take<char>((size_t)M * d->d_cq * es);
-  w.qp = cv.take<char>((size_t)M * qw * es);
+  w.tm = prefill_pipelined(dt(d), S, w.Tk, d->n_h, d->d_h, d->d_hr, entry(d));
+  const size_t tm_bytes = w.tm ? (size_t)M * d->n_h * (d->d_h * es + d->d_hr * sizeof(float)) : 0;
+  w.qp = cv.take<char>(std::max((size_t)M * qw * es, tm_bytes));
+  w.qc2 = w.qp;
+  w.qr2 = w.qp ? reinterpret_cast<float*>(reinterpret_cast<char*>(w.qp) + (size_t)M * d->n_h * d->d_h * es) : nullptr;
   w.kvd = cv.take<char>((size_t)M * entry(d) * es);
   w.kva = chunked ? cv.take<char>((size_t)Mk * entry(d) * es) : w.kvd;
   w.kp = cv.take<char>((size_t)Mk * d->n_h * d->d_h * es);
@@ -421,8 +428,20 @@ int prefill_impl(const mla_dims* d, const mla_weights* w, const mla_paged_cache*
     g.epi = kv_epi;
     MLA_HIP(gemm_run(t, g, ws.kv_p, ws.partial, s));
   }
-  {  // [q^C | RoPE(q^R)] = [W_UQ; W_QR] c^q: q^C to columns [0, d_h) and q^R to [d_h, d_h + d_hr)
-     // of each head's row
+  // With the pipelined attention kernel, q^C and the un-rotated q^R are plain products
+  // (hipBLASLt), token-major; the kernel rotates q^R as it loads it.
+  bool q_tm = false, k_tm = false;
+  if (ws.tm) {
+    hipError_t e = blas_gemm_nt(qin, qw, w->W_UQ, qw, ws.qc2, (int64_t)d->n_h * d->d_h, M, d->n_h * d->d_h, qw,
+                                ws.blas, kBlasWs, s);
+    if (e == hipSuccess)
+      e = blas_gemm_nt(qin, qw, w->W_QR, qw, ws.qr2, (int64_t)d->n_h * d->d_hr, M, d->n_h * d->d_hr, qw, ws.blas,
+                       kBlasWs, s, true);
+    if (e != hipSuccess && e != hipErrorNotSupported) return MLA_ERR_HIP;
+    q_tm = e == hipSuccess;
+  }
+  if (!q_tm) {  // [q^C | RoPE(q^R)] = [W_UQ; W_QR] c^q: q^C to columns [0, d_h) and q^R to
+                // [d_h, d_h + d_hr) of each head's row
     GemmParams g;
     g.A = qin; g.lda = qw; g.ldb = qw;
     g.B0 = w->W_UQ; g.N0 = d->n_h * d->d_h; g.B1 = w->W_QR;
@@ -444,7 +463,13 @@ int prefill_impl(const mla_dims* d, const mla_weights* w, const mla_paged_cache*
       MLA_HIP(gather_entries(t, c->pool, fp8_cache(d) ? c->scales : nullptr, c->block_table, c->max_blocks_per_seq,
                              c->block_size, start, ws.kvd, T, batch, ws.Tk, E, d->d_c, ws.kva, s));
   }
-  {  // k^C_i = W_UK_i c^KV, stored head-major [n_h][M][d_h]
+  if (ws.tm) {  // k^C = [W_UK_1; ...] c^KV token-major [Mk][n_h*d_h], a plain product
+    const hipError_t e = blas_gemm_nt(ws.kva, E, w->W_UK, d->d_c, ws.kp, (int64_t)d->n_h * d->d_h, Mk,
+                                      d->n_h * d->d_h, d->d_c, ws.blas, kBlasWs, s);
+    if (e != hipSuccess && e != hipErrorNotSupported) return MLA_ERR_HIP;
+    k_tm = e == hipSuccess;
+  }
+  if (!k_tm) {  // k^C_i = W_UK_i c^KV, stored head-major [n_h][M][d_h]
     GemmParams g;
     g.A = ws.kva; g.lda = E; g.B0 = w->W_UK; g.ldb = d->d_c;
     g.M = Mk; g.N = d->n_h * d->d_h; g.K = d->d_c;
@@ -452,7 +477,14 @@ int prefill_impl(const mla_dims* d, const mla_weights* w, const mla_paged_cache*
     g.epi.group = d->d_h; g.epi.group_stride = (int64_t)Mk * d->d_h;
     MLA_HIP(gemm_run(t, g, ws.k_p, ws.partial, s));
   }
-  {  // v^T: rows (head, dim) of W_UV times c^KV^T, token-contiguous [n_h][d_h][S][Tp]
+  bool v_done = false;
+  if (t == DType::BF16 && ws.Tp == ws.Tk) {  // no padding columns: v^T is a plain product
+    const hipError_t e = blas_gemm_nt(w->W_UV, d->d_c, ws.kva, E, ws.vt, (int64_t)batch * ws.Tp, d->n_h * d->d_h,
+                                      Mk, d->d_c, ws.blas, kBlasWs, s);
+    if (e != hipSuccess && e != hipErrorNotSupported) return MLA_ERR_HIP;
+    v_done = e == hipSuccess;
+  }
+  if (!v_done) {  // v^T: rows (head, dim) of W_UV times c^KV^T, token-contiguous [n_h][d_h][S][Tp]
     GemmParams g;
     g.A = w->W_UV; g.lda = d->d_c; g.B0 = ws.kva; g.ldb = E;
     g.M = d->n_h * d->d_h; g.N = Mk; g.K = d->d_c;
@@ -466,6 +498,10 @@ int prefill_impl(const mla_dims* d, const mla_weights* w, const mla_paged_cache*
     a.o = ws.o; a.o_f32 = o_heads;
     a.S = batch; a.T = T; a.n_h = d->n_h; a.d_h = d->d_h; a.d_hr = d->d_hr;
     a.Tk = ws.Tk; a.q_off = start;
+    if (q_tm) {
+      a.qc = ws.qc2; a.qr = ws.qr2; a.rope = ws.rope;
+    }
+    if (k_tm) a.k_ld = (int64_t)d->n_h * d->d_h;
     a.scale_log2 = scale_of(d) * 1.4426950408889634f;
     MLA_HIP(prefill_attention(t, a, s));
   }

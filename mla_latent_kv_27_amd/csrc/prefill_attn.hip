@@ -221,11 +221,12 @@ template <int ST>
 __device__ __forceinline__ char* pf_stage() { return ST == 0 ? g_pf_s0 : (ST == 1 ? g_pf_s1 : g_pf_s2); }
 
 struct Pf2Ctx {
-  __amdgpu_buffer_rsrc_t k;   // key rows of this (sequence, head): [T][128]
+  __amdgpu_buffer_rsrc_t k;   // key rows of this (sequence, head), krow bytes apart
   __amdgpu_buffer_rsrc_t kr;  // rope key rows of this sequence, ld_kr elements apart
   __amdgpu_buffer_rsrc_t vt;  // V^T rows of this (sequence, head): row d at d * vrow elements
   int ld_kr, vrow;
-  int T;  // valid keys of this sequence
+  int krow;  // bytes from one key row to the next (256 head-major, 2 n_h d_h token-major)
+  int T;     // valid keys of this sequence
 };
 
 // Tile kt into stage ST: key rows (clamped to the last valid key, masked later) and V^T rows
@@ -239,7 +240,7 @@ __device__ __forceinline__ void pf2_issue(const Pf2Ctx& c, int kt, int w, int la
   for (int i = 0; i < kKCopies; ++i) {
     const int P = i * kWaves + w, r = 4 * P + (lane >> 4);
     const int j = min(j0 + r, c.T - 1);
-    dma16(c.k, (uint32_t)(j * kKRow + kslot(r, lane & 15) * 16), (lds_void_t*)(st + P * 1024));
+    dma16(c.k, (uint32_t)(j * c.krow + kslot(r, lane & 15) * 16), (lds_void_t*)(st + P * 1024));
   }
 #pragma unroll
   for (int i = 0; i < kRCopies; ++i) {
@@ -398,8 +399,15 @@ __global__ void __launch_bounds__(512)
 
   Pf2Ctx c;
   // spans below 2 GiB (checked by the launcher): offsets within them are 32-bit
-  c.k = dma_span(reinterpret_cast<const bf16*>(p.k) + ((int64_t)head * MT + (int64_t)sq * Tk) * kDH,
-                 (uint32_t)nk * kKRow);
+  if (p.k_ld > 0) {  // token-major keys: row j of head h at j * k_ld + h * d_h
+    c.k = dma_span(reinterpret_cast<const bf16*>(p.k) + (int64_t)sq * Tk * p.k_ld + (int64_t)head * kDH,
+                   (uint32_t)(((int64_t)(nk - 1) * p.k_ld + kDH) * 2));
+    c.krow = (int)(p.k_ld * 2);
+  } else {
+    c.k = dma_span(reinterpret_cast<const bf16*>(p.k) + ((int64_t)head * MT + (int64_t)sq * Tk) * kDH,
+                   (uint32_t)nk * kKRow);
+    c.krow = kKRow;
+  }
   c.kr = dma_span(reinterpret_cast<const bf16*>(p.kr) + (int64_t)sq * Tk * p.ld_kr + p.kr_off,
                   (uint32_t)(((int64_t)(nk - 1) * p.ld_kr + kDR) * 2));
   c.ld_kr = (int)p.ld_kr;
@@ -409,7 +417,30 @@ __global__ void __launch_bounds__(512)
   c.T = nk;
 
   Frag8<bf16> q[12];
-  {
+  if (p.qc) {  // token-major q^C, and q^R rotated here: dims 16 (ks - 8) + 8g .. +7 are 4 pairs
+    const int64_t row = (int64_t)sq * p.T + min(qi, p.T - 1);
+    const bf16* qrow = reinterpret_cast<const bf16*>(p.qc) + row * p.n_h * kDH + (int64_t)head * kDH;
+    const float* rrow = p.qr + row * p.n_h * kDR + (int64_t)head * kDR;
+    const float2* tab = p.rope + row * (kDR / 2);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) load8(q[ks], qrow + ks * 16 + 8 * g);
+#pragma unroll
+    for (int ks = 8; ks < 12; ++ks) {
+      const int d0 = (ks - 8) * 16 + 8 * g;
+      const floatx4 x0 = *reinterpret_cast<const floatx4*>(rrow + d0);
+      const floatx4 x1 = *reinterpret_cast<const floatx4*>(rrow + d0 + 4);
+      const float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float2 cs = tab[d0 / 2 + i];
+        q[ks].v[2 * i] = (bf16)(x[2 * i] * cs.x - x[2 * i + 1] * cs.y);
+        q[ks].v[2 * i + 1] = (bf16)(x[2 * i + 1] * cs.x + x[2 * i] * cs.y);
+      }
+    }
+    if (qi >= p.T)
+#pragma unroll
+      for (int ks = 0; ks < 12; ++ks) zero8(q[ks]);
+  } else {
     const bf16* qrow = reinterpret_cast<const bf16*>(p.q) + (((int64_t)sq * p.T + min(qi, p.T - 1)) * p.n_h + head) * kDQ;
 #pragma unroll
     for (int ks = 0; ks < 12; ++ks) {
@@ -472,14 +503,23 @@ hipError_t launch(const PrefillAttnParams& p, hipStream_t s) {
 }
 }  // namespace
 
-hipError_t prefill_attention(DType t, const PrefillAttnParams& p, hipStream_t s) {
-  // the pipelined kernel addresses each source span with 32-bit byte offsets
-  const int64_t Tk = p.Tk > 0 ? p.Tk : p.T;
+// the pipelined kernel addresses each source span with 32-bit byte offsets
+static bool pf2_spans_fit(int64_t S, int64_t Tk, int64_t ld_kr, int64_t k_ld) {
   const int64_t Tp = (Tk + pf2::kKV - 1) / pf2::kKV * pf2::kKV;
-  const bool spans_fit = Tk * pf2::kKRow < (1LL << 31) &&
-                         ((Tk - 1) * p.ld_kr + pf2::kDR) * 2 < (1LL << 31) &&
-                         ((int64_t)(pf2::kDH - 1) * p.S * Tp + Tp) * 2 < (1LL << 31);
-  if (t == DType::BF16 && p.d_h == 128 && p.d_hr == 64 && spans_fit) {
+  const int64_t k_span = k_ld > 0 ? ((Tk - 1) * k_ld + pf2::kDH) * 2 : Tk * pf2::kKRow;
+  return k_span < (1LL << 31) && ((Tk - 1) * ld_kr + pf2::kDR) * 2 < (1LL << 31) &&
+         ((int64_t)(pf2::kDH - 1) * S * Tp + Tp) * 2 < (1LL << 31);
+}
+
+bool prefill_pipelined(DType t, int S, int Tk, int n_h, int d_h, int d_hr, int64_t ld_kr) {
+  return t == DType::BF16 && d_h == 128 && d_hr == 64 && pf2_spans_fit(S, Tk, ld_kr, (int64_t)n_h * d_h);
+}
+
+hipError_t prefill_attention(DType t, const PrefillAttnParams& p, hipStream_t s) {
+  const int64_t Tk = p.Tk > 0 ? p.Tk : p.T;
+  const bool pipelined = t == DType::BF16 && p.d_h == 128 && p.d_hr == 64 && pf2_spans_fit(p.S, Tk, p.ld_kr, p.k_ld);
+  if ((p.qc || p.k_ld > 0) && !pipelined) return hipErrorInvalidValue;  // token-major: pipelined kernel only
+  if (pipelined) {
     const int nqt = (p.T + pf2::kQ - 1) / pf2::kQ;
     const int units = p.S * p.n_h;
     const int64_t blocks = (int64_t)(units + 7) / 8 * 8 * nqt;
