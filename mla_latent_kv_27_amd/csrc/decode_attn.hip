@@ -482,7 +482,7 @@ __global__ void __launch_bounds__(512)
 // Log-sum-exp combination of the partitions: M = max_s m_s, w_s = 2^(m_s - M) l_s,
 // o_hat = sum_s w_s o_s / sum_s w_s with o_s = O_s / l_s the partition's normalised output (PT:
 // fp32 or bf16).  A 256-thread workgroup combines four (sequence, head) rows; each thread owns
-// DC/64 consecutive latent dims, and the partitions' loads are issued four at a time before any
+// DC/64 consecutive latent dims, and the partitions' loads are issued eight at a time before any
 // of them is used.
 template <typename T, typename PT, int DC>
 __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeAttnParams p) {
@@ -498,11 +498,12 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeAttnParams p)
   float acc[V];
 #pragma unroll
   for (int i = 0; i < V; ++i) acc[i] = 0.f;
-  for (int s0 = 0; s0 < p.splits; s0 += 4) {
-    float ms[4], ls[4];
-    PT v[4][V];
+  constexpr int kG = 8;  // partitions whose loads are in flight together
+  for (int s0 = 0; s0 < p.splits; s0 += kG) {
+    float ms[kG], ls[kG];
+    PT v[kG][V];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kG; ++u) {
       ms[u] = -INFINITY;
       if (s0 + u < p.splits) {
         const int64_t pi = base + (int64_t)(s0 + u) * p.n_h;
@@ -514,7 +515,7 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeAttnParams p)
       }
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kG; ++u) {
       if (ms[u] > -INFINITY) {
         const float ws = exp2f(ms[u] - M) * ls[u];
         L += ws;

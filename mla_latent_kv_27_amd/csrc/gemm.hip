@@ -978,41 +978,67 @@ __global__ void __launch_bounds__(64 * NW) uv_kernel(const bf16* __restrict__ oh
     for (int i0 = 0; i0 < MB / NW; i0 += kRowsInFlight) {
       float M[kRowsInFlight], L[kRowsInFlight], acc[kRowsInFlight][8];
       int64_t base[kRowsInFlight];
+      bool live[kRowsInFlight];  // rows past B are not read (their products are never stored)
 #pragma unroll
       for (int k = 0; k < kRowsInFlight; ++k) {
-        const int m = min(m0 + (i0 + k) * NW + wv, B - 1);
-        base[k] = (int64_t)m * parts.splits * n_h + h;  // partition s at base + s n_h
+        const int m = m0 + (i0 + k) * NW + wv;
+        live[k] = m < B;
+        base[k] = (int64_t)min(m, B - 1) * parts.splits * n_h + h;  // partition s at base + s n_h
         M[k] = -INFINITY;
-        for (int sp = 0; sp < parts.splits; ++sp) M[k] = fmaxf(M[k], parts.m[base[k] + (int64_t)sp * n_h]);
+        if (live[k])
+          for (int sp = 0; sp < parts.splits; ++sp) M[k] = fmaxf(M[k], parts.m[base[k] + (int64_t)sp * n_h]);
         L[k] = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[k][e] = 0.f;
       }
-      for (int s0 = 0; s0 < parts.splits; s0 += 4) {
-        float ms[kRowsInFlight][4], ls[kRowsInFlight][4];
-        bf16x8 v[kRowsInFlight][4];
+      // the loads of a group are all issued before any is used: four partitions of every row,
+      // or, with many partitions (long contexts, few rows), sixteen partitions of one row
+      auto part = [&](int k, int sp, float& ms, float& ls, bf16x8& v) {
+        const int64_t pi = base[k] + (int64_t)sp * n_h;
+        ms = parts.m[pi];
+        ls = parts.l[pi];
+        v = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(parts.o) + pi * kDc + 8 * lane);
+      };
+      auto add = [&](int k, float ms, float ls, const bf16x8& v) {
+        if (ms > -INFINITY) {
+          const float ws = exp2f(ms - M[k]) * ls;
+          L[k] += ws;
 #pragma unroll
-        for (int k = 0; k < kRowsInFlight; ++k)
+          for (int e = 0; e < 8; ++e) acc[k][e] += ws * (float)v[e];
+        }
+      };
+      if (parts.splits >= 16) {
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            ms[k][u] = -INFINITY;
-            if (s0 + u < parts.splits) {
-              const int64_t pi = base[k] + (int64_t)(s0 + u) * n_h;
-              ms[k][u] = parts.m[pi];
-              ls[k][u] = parts.l[pi];
-              v[k][u] = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(parts.o) + pi * kDc + 8 * lane);
+        for (int k = 0; k < kRowsInFlight; ++k) {
+          if (!live[k]) continue;
+          for (int s0 = 0; s0 < parts.splits; s0 += 16) {
+            float ms[16], ls[16];
+            bf16x8 v[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+              ms[u] = -INFINITY;
+              if (s0 + u < parts.splits) part(k, s0 + u, ms[u], ls[u], v[u]);
             }
+#pragma unroll
+            for (int u = 0; u < 16; ++u) add(k, ms[u], ls[u], v[u]);
           }
+        }
+      } else {
+        for (int s0 = 0; s0 < parts.splits; s0 += 4) {
+          float ms[kRowsInFlight][4], ls[kRowsInFlight][4];
+          bf16x8 v[kRowsInFlight][4];
 #pragma unroll
-        for (int k = 0; k < kRowsInFlight; ++k)
+          for (int k = 0; k < kRowsInFlight; ++k)
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
-            if (ms[k][u] > -INFINITY) {
-              const float ws = exp2f(ms[k][u] - M[k]) * ls[k][u];
-              L[k] += ws;
-#pragma unroll
-              for (int e = 0; e < 8; ++e) acc[k][e] += ws * (float)v[k][u][e];
+            for (int u = 0; u < 4; ++u) {
+              ms[k][u] = -INFINITY;
+              if (live[k] && s0 + u < parts.splits) part(k, s0 + u, ms[k][u], ls[k][u], v[k][u]);
             }
+#pragma unroll
+          for (int k = 0; k < kRowsInFlight; ++k)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) add(k, ms[k][u], ls[k][u], v[k][u]);
+        }
       }
 #pragma unroll
       for (int k = 0; k < kRowsInFlight; ++k) {
