@@ -187,6 +187,85 @@ __global__ void __launch_bounds__(64 * NW) decode_attn_kernel(DecodeAttnParams p
   for (int d = 0; d < Sh::DB; ++d) *reinterpret_cast<floatx4*>(po + d * 16 + 4 * g) = o[d] * inv;
 }
 
+// ----------------------------------------------------------------------------- balanced units
+// Work units of the tiled kernels for small batches, where contexts of different lengths would
+// leave most fixed-length partitions of the short sequences empty.  Each sequence has p.splits
+// partition slots; sequence b takes n_b = ceil(tiles_b / tps) of them.  tps starts at the
+// shortest length that fits the longest sequence in its slots and is raised while that lowers
+// the finish time, counted in rounds of p.cus units (one per compute unit) times tps.  The table
+// lists the partitions in sequence order, then the slots no partition uses (p >= n_b: they get
+// an empty partial, max -inf and no output rows), then B idle units: (b, p, first tile, end
+// tile), b = -1 when idle.  One workgroup builds it from the lengths in device memory (B <= 64),
+// so the host needs only B and splits.
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(v, d, 64);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum_int(int v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+  return v;
+}
+
+__global__ void __launch_bounds__(256) decode_units_kernel(DecodeAttnParams p) {
+  const int lane = threadIdx.x & 63;
+  const int plus = p.lens_plus_one ? 1 : 0, S = p.splits, T = kTile;
+  const int C = max(1, p.cus);
+  // one lane per sequence (B <= 64)
+  const int my_tiles = lane < p.B ? (p.lens[lane] + plus + T - 1) / T : 0;
+  const int tot = wave_sum_int(my_tiles);
+  int mx = my_tiles;
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) mx = max(mx, __shfl_xor(mx, d, 64));
+  // partition length: the shortest one that fits every sequence in its S slots, or a longer one
+  // when that finishes sooner; the finish time counts rounds of C units (one per compute unit)
+  const int tmin = max(1, (mx + S - 1) / S);
+  int tps = tmin;
+  long best = -1;
+  for (int k = 0; k <= 9; ++k) {
+    const int cand = k < 9 ? tmin + tmin * k / 8 : max(tmin, (tot + C - 1) / C);
+    const int used = wave_sum_int((my_tiles + cand - 1) / cand);
+    const long cost = (long)((used + C - 1) / C) * cand;
+    if (best < 0 || cost < best) {
+      best = cost;
+      tps = cand;
+    }
+  }
+  // per-sequence partition counts and their prefix sums (B <= 64 here), then every thread fills
+  // table entries
+  __shared__ int s_tiles[64], s_pend[64], s_fend[64];  // tiles, partitions / free slots up to b
+  if (threadIdx.x < 64) {
+    const int tiles = my_tiles;
+    const int n = lane < p.B ? (tiles + tps - 1) / tps : 0;
+    s_tiles[lane] = tiles;
+    s_pend[lane] = wave_incl_scan(n, lane);
+    s_fend[lane] = wave_incl_scan(lane < p.B ? S - n : 0, lane);
+  }
+  __syncthreads();
+  const int np = s_pend[p.B - 1];
+  for (int j = threadIdx.x; j < p.B * S + p.B; j += blockDim.x) {
+    int4 e = make_int4(-1, 0, 0, 0);
+    if (j < np) {
+      int i = 0;
+      while (s_pend[i] <= j) ++i;
+      const int k = j - (i ? s_pend[i - 1] : 0);
+      e = make_int4(i, k, k * tps, min(s_tiles[i], (k + 1) * tps));
+    } else if (j < p.B * S) {
+      const int f = j - np;
+      int i = 0;
+      while (s_fend[i] <= f) ++i;
+      const int n_i = s_pend[i] - (i ? s_pend[i - 1] : 0);
+      e = make_int4(i, n_i + f - (i ? s_fend[i - 1] : 0), 0, 0);
+    }
+    p.units[j] = e;
+  }
+}
+
 // ----------------------------------------------------------------------------- tiled kernel
 // The DeepSeek-V2-sized bf16 case (d_c = 512, d_hr = 64).  A workgroup is eight waves of 16 heads
 // (two waves per SIMD hide each other's LDS and copy latency); with more than 128 heads the other
@@ -400,11 +479,21 @@ __global__ void __launch_bounds__(512)
   using namespace tiled;
   // block id -> (unit = (sequence, partition), head group): the HG head groups of a unit sit 8
   // ids apart, i.e. on the same XCD (ids are dealt to the 8 XCDs round robin)
-  const int units = p.B * p.splits;
+  const int units = p.B * p.splits + (p.units ? p.B : 0);
   const int grp = blockIdx.x / (8 * HG), rem = blockIdx.x % (8 * HG);
   const int hg = rem / 8, unit = grp * 8 + rem % 8;
   if (unit >= units) return;
-  const int b = unit / p.splits, split = unit % p.splits;
+  int b, split, t_begin, t_end;
+  if (p.units) {  // the balanced table: (sequence, partition slot, first tile, end tile)
+    const int4 ue = p.units[unit];
+    if (ue.x < 0) return;
+    b = ue.x, split = ue.y, t_begin = ue.z, t_end = ue.w;
+  } else {  // fixed partitions of tokens_per_split
+    b = unit / p.splits, split = unit % p.splits;
+    const int ntiles = (p.lens[b] + (p.lens_plus_one ? 1 : 0) + kT - 1) / kT;
+    t_begin = split * (p.tokens_per_split / kT);
+    t_end = min(ntiles, t_begin + p.tokens_per_split / kT);
+  }
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4;
@@ -416,10 +505,6 @@ __global__ void __launch_bounds__(512)
   c.bt = block_table + (int64_t)b * p.max_blocks;  // read-only: block ids load as scalars
   c.bs = p.block_size;
   c.kv_len = p.lens[b] + (p.lens_plus_one ? 1 : 0);
-  const int ntiles = (c.kv_len + kT - 1) / kT;
-  const int tps = p.tokens_per_split / kT;
-  const int t_begin = split * tps;
-  const int t_end = min(ntiles, t_begin + tps);
 
   Frag8<bf16> q[18];
   {
@@ -466,6 +551,7 @@ __global__ void __launch_bounds__(512)
     p.part_m[pi] = m_run;
     p.part_l[pi] = l_run;
   }
+  if (t_begin >= t_end) return;  // an empty partition: the combines skip it by its max (-inf)
   // the partition's normalised output O_s / l_s (a convex combination of latent values) in bf16:
   // half the partial traffic of fp32 for one more rounding of 2^-9 relative
   const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
@@ -487,13 +573,19 @@ __global__ void __launch_bounds__(512)
 template <typename T, typename PT, int DC>
 __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeAttnParams p) {
   constexpr int V = DC >= 64 ? DC / 64 : 1;  // dims per thread
-  const int bh = blockIdx.x * 4 + (threadIdx.x >> 6);  // b * n_h + head
-  if (bh >= p.B * p.n_h || V * (threadIdx.x & 63) >= DC) return;
+  const int bh = blockIdx.x * 4 + (threadIdx.x >> 6);  // b * n_h + head: one wave per row
+  if (bh >= p.B * p.n_h) return;
+  const int lane = threadIdx.x & 63;
+  const bool has_dims = V * lane < DC;
   const int b = bh / p.n_h, head = bh % p.n_h;
   const int64_t base = (int64_t)b * p.splits * p.n_h + head;  // partition s at base + s * n_h
-  const int d = V * (threadIdx.x & 63);
+  const int d = V * lane;
+  // M: the partitions' maxima one per lane, then a wave reduction
   float M = -INFINITY;
-  for (int s = 0; s < p.splits; ++s) M = fmaxf(M, p.part_m[base + (int64_t)s * p.n_h]);
+  for (int c = 0; c < p.splits; c += 64)
+    if (c + lane < p.splits) M = fmaxf(M, p.part_m[base + (int64_t)(c + lane) * p.n_h]);
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
   float L = 0.f;
   float acc[V];
 #pragma unroll
@@ -508,10 +600,12 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeAttnParams p)
       if (s0 + u < p.splits) {
         const int64_t pi = base + (int64_t)(s0 + u) * p.n_h;
         ms[u] = p.part_m[pi];
-        ls[u] = p.part_l[pi];
-        const PT* src = reinterpret_cast<const PT*>(p.part_o) + pi * DC + d;
+        if (ms[u] > -INFINITY) {  // empty partitions write no output row
+          ls[u] = p.part_l[pi];
+          const PT* src = reinterpret_cast<const PT*>(p.part_o) + pi * DC + d;
 #pragma unroll
-        for (int i = 0; i < V; ++i) v[u][i] = src[i];
+          for (int i = 0; i < V; ++i) v[u][i] = has_dims ? src[i] : PT(0.f);
+        }
       }
     }
 #pragma unroll
@@ -524,6 +618,7 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeAttnParams p)
       }
     }
   }
+  if (!has_dims) return;
   const float inv = L > 0.f ? 1.f / L : 0.f;
   T* out = reinterpret_cast<T*>(p.o_hat) + (int64_t)bh * DC + d;
 #pragma unroll
@@ -757,11 +852,21 @@ __device__ __forceinline__ void tiled8_pair(const Tiled8Ctx& c, const QFp8& q, T
 __global__ void __launch_bounds__(512)
     decode_attn_fp8_kernel(DecodeAttnParams p, int HG, const int32_t* __restrict__ block_table) {
   using namespace tiled8;
-  const int units = p.B * p.splits;
+  const int units = p.B * p.splits + (p.units ? p.B : 0);
   const int grp = blockIdx.x / (8 * HG), rem = blockIdx.x % (8 * HG);
   const int hg = rem / 8, unit = grp * 8 + rem % 8;
   if (unit >= units) return;
-  const int b = unit / p.splits, split = unit % p.splits;
+  int b, split, t_begin, t_end;
+  if (p.units) {  // the balanced table: (sequence, partition slot, first tile, end tile)
+    const int4 ue = p.units[unit];
+    if (ue.x < 0) return;
+    b = ue.x, split = ue.y, t_begin = ue.z, t_end = ue.w;
+  } else {  // fixed partitions of tokens_per_split
+    b = unit / p.splits, split = unit % p.splits;
+    const int ntiles = (p.lens[b] + (p.lens_plus_one ? 1 : 0) + kT - 1) / kT;
+    t_begin = split * (p.tokens_per_split / kT);
+    t_end = min(ntiles, t_begin + p.tokens_per_split / kT);
+  }
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4;
@@ -774,10 +879,6 @@ __global__ void __launch_bounds__(512)
   c.bt = block_table + (int64_t)b * p.max_blocks;
   c.bs = p.block_size;
   c.kv_len = p.lens[b] + (p.lens_plus_one ? 1 : 0);
-  const int ntiles = (c.kv_len + kT - 1) / kT;
-  const int tps = p.tokens_per_split / kT;
-  const int t_begin = split * tps;
-  const int t_end = min(ntiles, t_begin + tps);
 
   // the head's query as hi + lo e4m3 codes with one scale: s = amax / 448 over the head's 576
   // values (the head's four lane groups), hi = e4m3(q / s), lo = e4m3(q / s - hi)
@@ -867,6 +968,7 @@ __global__ void __launch_bounds__(512)
     p.part_m[pi] = m_run;
     p.part_l[pi] = l_run;
   }
+  if (t_begin >= t_end) return;  // an empty partition: the combines skip it by its max (-inf)
   bf16* po = reinterpret_cast<bf16*>(p.part_o) + pi * 512;
 #pragma unroll
   for (int d = 0; d < 32; ++d) {
@@ -917,8 +1019,10 @@ hipError_t decode_attention(DType t, const DecodeAttnParams& p, hipStream_t s) {
     if (t != DType::BF16 || p.d_c != 512 || p.d_hr != 64 || p.block_size % tiled8::kT != 0 || !p.scales)
       return hipErrorInvalidValue;
     const int HG = (p.n_h + 16 * tiled8::kWaves - 1) / (16 * tiled8::kWaves);
-    const int units = p.B * p.splits;
-    if (units == 0) return hipSuccess;
+    if (p.B == 0) return hipSuccess;
+    if (p.units && p.B > 64) return hipErrorInvalidValue;  // the table builder takes B <= 64
+    if (p.units) hipLaunchKernelGGL(decode_units_kernel, dim3(1), dim3(256), 0, s, p);
+    const int units = p.B * p.splits + (p.units ? p.B : 0);  // with a table: + B idle entries
     const int blocks = (units + 7) / 8 * 8 * HG;
     hipLaunchKernelGGL(decode_attn_fp8_kernel, dim3(blocks), dim3(64 * tiled8::kWaves), 0, s, p, HG, p.block_table);
     hipError_t e = hipGetLastError();
@@ -928,8 +1032,10 @@ hipError_t decode_attention(DType t, const DecodeAttnParams& p, hipStream_t s) {
   }
   if (decode_tiled(t, p.d_c, p.d_hr, p.block_size)) {
     const int HG = (p.n_h + 16 * tiled::kWaves - 1) / (16 * tiled::kWaves);
-    const int units = p.B * p.splits;
-    if (units == 0) return hipSuccess;
+    if (p.B == 0) return hipSuccess;
+    if (p.units && p.B > 64) return hipErrorInvalidValue;  // the table builder takes B <= 64
+    if (p.units) hipLaunchKernelGGL(decode_units_kernel, dim3(1), dim3(256), 0, s, p);
+    const int units = p.B * p.splits + (p.units ? p.B : 0);  // with a table: + B idle entries
     const int blocks = (units + 7) / 8 * 8 * HG;
     hipLaunchKernelGGL(decode_attn_tiled_kernel, dim3(blocks), dim3(64 * tiled::kWaves), 0, s, p, HG,
                        p.block_table);

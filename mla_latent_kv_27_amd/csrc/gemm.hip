@@ -972,9 +972,13 @@ __global__ void __launch_bounds__(64 * NW) uv_kernel(const bf16* __restrict__ oh
       __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(la + r * kRowB), 16, 0, 0);
     }
   };
-  // rows r = i NW + wv of the block, kRowsInFlight at a time: lane holds dims 8 lane .. +7; the
-  // partitions go four at a time, all their loads issued before any is used
+  // rows r = i NW + wv of the block, kRowsInFlight at a time: lane holds dims 8 lane .. +7.  The
+  // partitions' maxima are read one per lane (M by a wave reduction), and a partition's output
+  // row is loaded only when its max is finite (empty partitions write none).  The loads of a
+  // group are all issued before any is used: four partitions of every row, or, with many
+  // partitions (long contexts, few rows), sixteen partitions of one row.
   auto combine_a = [&](int m0) {
+    const int S = parts.splits;
     for (int i0 = 0; i0 < MB / NW; i0 += kRowsInFlight) {
       float M[kRowsInFlight], L[kRowsInFlight], acc[kRowsInFlight][8];
       int64_t base[kRowsInFlight];
@@ -983,21 +987,24 @@ __global__ void __launch_bounds__(64 * NW) uv_kernel(const bf16* __restrict__ oh
       for (int k = 0; k < kRowsInFlight; ++k) {
         const int m = m0 + (i0 + k) * NW + wv;
         live[k] = m < B;
-        base[k] = (int64_t)min(m, B - 1) * parts.splits * n_h + h;  // partition s at base + s n_h
-        M[k] = -INFINITY;
+        base[k] = (int64_t)min(m, B - 1) * S * n_h + h;  // partition s at base + s n_h
+        float mx = -INFINITY;
         if (live[k])
-          for (int sp = 0; sp < parts.splits; ++sp) M[k] = fmaxf(M[k], parts.m[base[k] + (int64_t)sp * n_h]);
+          for (int c = 0; c < S; c += 64)
+            if (c + lane < S) mx = fmaxf(mx, parts.m[base[k] + (int64_t)(c + lane) * n_h]);
+        M[k] = wave_max_xor(wave_max_xor(wave_max_xor(mx, 1), 2), 4);
+        M[k] = wave_max_xor(wave_max_xor(wave_max_xor(M[k], 8), 16), 32);
         L[k] = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[k][e] = 0.f;
       }
-      // the loads of a group are all issued before any is used: four partitions of every row,
-      // or, with many partitions (long contexts, few rows), sixteen partitions of one row
       auto part = [&](int k, int sp, float& ms, float& ls, bf16x8& v) {
         const int64_t pi = base[k] + (int64_t)sp * n_h;
         ms = parts.m[pi];
-        ls = parts.l[pi];
-        v = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(parts.o) + pi * kDc + 8 * lane);
+        if (ms > -INFINITY) {  // uniform
+          ls = parts.l[pi];
+          v = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(parts.o) + pi * kDc + 8 * lane);
+        }
       };
       auto add = [&](int k, float ms, float ls, const bf16x8& v) {
         if (ms > -INFINITY) {
@@ -1007,24 +1014,36 @@ __global__ void __launch_bounds__(64 * NW) uv_kernel(const bf16* __restrict__ oh
           for (int e = 0; e < 8; ++e) acc[k][e] += ws * (float)v[e];
         }
       };
-      if (parts.splits >= 16) {
+      if (S >= 16) {
+        // the maxima and normalisers of 64 partitions at a time sit one per lane; a group of
+        // sixteen is skipped when all are empty, else its output rows are loaded together
 #pragma unroll
         for (int k = 0; k < kRowsInFlight; ++k) {
           if (!live[k]) continue;
-          for (int s0 = 0; s0 < parts.splits; s0 += 16) {
-            float ms[16], ls[16];
-            bf16x8 v[16];
+          for (int c0 = 0; c0 < S; c0 += 64) {
+            const int64_t pl = base[k] + (int64_t)(c0 + lane) * n_h;
+            const float m_l = c0 + lane < S ? parts.m[pl] : -INFINITY;
+            const float l_l = c0 + lane < S ? parts.l[pl] : 0.f;
+            const uint64_t used = __builtin_amdgcn_ballot_w64(m_l > -INFINITY);
+            for (int s0 = c0; s0 < min(S, c0 + 64); s0 += 16) {
+              if (((used >> (s0 - c0)) & 0xffffull) == 0) continue;
+              float ms[16], ls[16];
+              bf16x8 v[16];
 #pragma unroll
-            for (int u = 0; u < 16; ++u) {
-              ms[u] = -INFINITY;
-              if (s0 + u < parts.splits) part(k, s0 + u, ms[u], ls[u], v[u]);
+              for (int u = 0; u < 16; ++u) {
+                ms[u] = __shfl(m_l, s0 - c0 + u, 64);
+                ls[u] = __shfl(l_l, s0 - c0 + u, 64);
+                if (ms[u] > -INFINITY)
+                  v[u] = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(parts.o) +
+                                                          (base[k] + (int64_t)(s0 + u) * n_h) * kDc + 8 * lane);
+              }
+#pragma unroll
+              for (int u = 0; u < 16; ++u) add(k, ms[u], ls[u], v[u]);
             }
-#pragma unroll
-            for (int u = 0; u < 16; ++u) add(k, ms[u], ls[u], v[u]);
           }
         }
       } else {
-        for (int s0 = 0; s0 < parts.splits; s0 += 4) {
+        for (int s0 = 0; s0 < S; s0 += 4) {
           float ms[kRowsInFlight][4], ls[kRowsInFlight][4];
           bf16x8 v[kRowsInFlight][4];
 #pragma unroll
@@ -1032,7 +1051,7 @@ __global__ void __launch_bounds__(64 * NW) uv_kernel(const bf16* __restrict__ oh
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
               ms[k][u] = -INFINITY;
-              if (live[k] && s0 + u < parts.splits) part(k, s0 + u, ms[k][u], ls[k][u], v[k][u]);
+              if (live[k] && s0 + u < S) part(k, s0 + u, ms[k][u], ls[k][u], v[k][u]);
             }
 #pragma unroll
           for (int k = 0; k < kRowsInFlight; ++k)

@@ -209,6 +209,10 @@ struct DecodeAttnParams {
   const float* scales = nullptr;  // [num_blocks][block_size][2]
   bool leave_partials = false;    // splits > 1: skip the combine (the consumer combines; needs
                                   // decode_bf16_partials), o_hat and lse are not written
+  int4* units = nullptr;          // set: balanced work units for the tiled kernels (scratch of
+                                  // B * (splits + 1) entries, filled by decode_attention); null:
+                                  // fixed partitions of tokens_per_split
+  int cus = 256;                  // compute units, for the balanced units' finish time
 };
 
 // true when the kernel decode_attention picks writes bf16 partition outputs

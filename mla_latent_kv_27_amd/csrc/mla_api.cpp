@@ -117,6 +117,15 @@ int auto_splits(const mla_dims* d, int batch, int max_ctx_len, int cus) {
   return std::max(1, std::min(s, 64));
 }
 
+// Small batches (fewer than 16 workgroups per partition slot) take the balanced work units of
+// the tiled kernels, with twice the automatic slots so that long sequences can spread over more
+// compute units than short ones.
+bool balanced_units(const mla_dims* d, int batch) { return batch * ((d->n_h + 127) / 128) < 16; }
+int auto_request(const mla_dims* d, int batch, int max_ctx_len, int cus) {
+  const int s = auto_splits(d, batch, max_ctx_len, cus);
+  return balanced_units(d, batch) ? std::min(128, 2 * s) : s;
+}
+
 // ----------------------------------------------------------------------------- workspace plans
 struct AppendWs {
   float2* rope;
@@ -162,6 +171,8 @@ DecodeGemms decode_gemms(const mla_dims* d, int B, int cus) {
 
 struct AttnWs {
   float *pm, *pl, *po;
+  int4* units;    // the tiled kernels' work-unit table
+  bool balanced;  // automatic splits for a small batch: use the table
   int splits, tps;
 };
 // Partition count for a request of `splits`; *tps = tokens per partition.
@@ -177,19 +188,22 @@ int split_count(int max_kv_len, int splits, int* tps) {
 size_t attn_rows_bound(const mla_dims* d, int B, int max_kv_len, int splits_raw, int cus) {
   size_t best = 0;
   for (int b = 1; b <= B; ++b) {
-    const int req = splits_raw > 0 ? splits_raw : auto_splits(d, b, max_kv_len - 1, cus);
+    const int req = splits_raw > 0 ? splits_raw : auto_request(d, b, max_kv_len - 1, cus);
     if (req > 1) best = std::max(best, (size_t)b * req * d->n_h);
   }
   return best;
 }
 AttnWs carve_attn(Carve& cv, const mla_dims* d, int B, int max_kv_len, int splits_raw, int cus) {
   AttnWs a;
-  const int req = splits_raw > 0 ? splits_raw : auto_splits(d, B, max_kv_len - 1, cus);
+  const int req = splits_raw > 0 ? splits_raw : auto_request(d, B, max_kv_len - 1, cus);
   a.splits = split_count(max_kv_len, req, &a.tps);
+  a.balanced = splits_raw == 0 && balanced_units(d, B);
   const size_t n = attn_rows_bound(d, B, max_kv_len, splits_raw, cus);
   a.pm = cv.take<float>(n * sizeof(float));
   a.pl = cv.take<float>(n * sizeof(float));
   a.po = cv.take<float>(n * d->d_c * sizeof(float));
+  // B * (splits + 1) entries: n bounds b * splits * n_h over every call when splits > 1
+  a.units = cv.take<int4>((std::max<size_t>(n / std::max(1, d->n_h), B) + B) * sizeof(int4));
   return a;
 }
 
@@ -641,6 +655,8 @@ int mla_decode_attention(const mla_dims* d, const mla_paged_cache* c, const void
   a.part_m = ws.attn.pm;
   a.part_l = ws.attn.pl;
   a.part_o = ws.attn.po;
+  a.units = ws.attn.balanced ? ws.attn.units : nullptr;
+  a.cus = cus;
   a.o_hat = o_hat;
   a.lse = lse;
   MLA_HIP(decode_attention(dt(d), a, reinterpret_cast<hipStream_t>(stream)));
@@ -738,6 +754,7 @@ int mla_decode(const mla_dims* d, const mla_weights* w, const mla_paged_cache* c
     a.scale_log2 = scale_of(d) * 1.4426950408889634f;
     a.splits = ws.attn.splits; a.tokens_per_split = ws.attn.tps;
     a.part_m = ws.attn.pm; a.part_l = ws.attn.pl; a.part_o = ws.attn.po;
+    a.units = ws.attn.balanced ? ws.attn.units : nullptr; a.cus = cus;
     a.o_hat = ws.ohat; a.lse = nullptr;
     // with several partitions and the W_UV kernel that combines them, the combine pass is skipped
     a.leave_partials = a.splits > 1 && uv_parts_ok(t, d->d_h, d->d_c) && decode_bf16_partials(t, a);
