@@ -975,8 +975,7 @@ __global__ void __launch_bounds__(64 * NW) uv_kernel(const bf16* __restrict__ oh
   // rows r = i NW + wv of the block, kRowsInFlight at a time: lane holds dims 8 lane .. +7.  The
   // partitions' maxima are read one per lane (M by a wave reduction), and a partition's output
   // row is loaded only when its max is finite (empty partitions write none).  The loads of a
-  // group are all issued before any is used: four partitions of every row, or, with many
-  // partitions (long contexts, few rows), sixteen partitions of one row.
+  // group, four partitions of every row, are all issued before any is used.
   auto combine_a = [&](int m0) {
     const int S = parts.splits;
     for (int i0 = 0; i0 < MB / NW; i0 += kRowsInFlight) {
@@ -1014,50 +1013,20 @@ __global__ void __launch_bounds__(64 * NW) uv_kernel(const bf16* __restrict__ oh
           for (int e = 0; e < 8; ++e) acc[k][e] += ws * (float)v[e];
         }
       };
-      if (S >= 16) {
-        // the maxima and normalisers of 64 partitions at a time sit one per lane; a group of
-        // sixteen is skipped when all are empty, else its output rows are loaded together
+      for (int s0 = 0; s0 < S; s0 += 4) {
+        float ms[kRowsInFlight][4], ls[kRowsInFlight][4];
+        bf16x8 v[kRowsInFlight][4];
 #pragma unroll
-        for (int k = 0; k < kRowsInFlight; ++k) {
-          if (!live[k]) continue;
-          for (int c0 = 0; c0 < S; c0 += 64) {
-            const int64_t pl = base[k] + (int64_t)(c0 + lane) * n_h;
-            const float m_l = c0 + lane < S ? parts.m[pl] : -INFINITY;
-            const float l_l = c0 + lane < S ? parts.l[pl] : 0.f;
-            const uint64_t used = __builtin_amdgcn_ballot_w64(m_l > -INFINITY);
-            for (int s0 = c0; s0 < min(S, c0 + 64); s0 += 16) {
-              if (((used >> (s0 - c0)) & 0xffffull) == 0) continue;
-              float ms[16], ls[16];
-              bf16x8 v[16];
+        for (int k = 0; k < kRowsInFlight; ++k)
 #pragma unroll
-              for (int u = 0; u < 16; ++u) {
-                ms[u] = __shfl(m_l, s0 - c0 + u, 64);
-                ls[u] = __shfl(l_l, s0 - c0 + u, 64);
-                if (ms[u] > -INFINITY)
-                  v[u] = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(parts.o) +
-                                                          (base[k] + (int64_t)(s0 + u) * n_h) * kDc + 8 * lane);
-              }
-#pragma unroll
-              for (int u = 0; u < 16; ++u) add(k, ms[u], ls[u], v[u]);
-            }
+          for (int u = 0; u < 4; ++u) {
+            ms[k][u] = -INFINITY;
+            if (live[k] && s0 + u < S) part(k, s0 + u, ms[k][u], ls[k][u], v[k][u]);
           }
-        }
-      } else {
-        for (int s0 = 0; s0 < S; s0 += 4) {
-          float ms[kRowsInFlight][4], ls[kRowsInFlight][4];
-          bf16x8 v[kRowsInFlight][4];
 #pragma unroll
-          for (int k = 0; k < kRowsInFlight; ++k)
+        for (int k = 0; k < kRowsInFlight; ++k)
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              ms[k][u] = -INFINITY;
-              if (live[k] && s0 + u < S) part(k, s0 + u, ms[k][u], ls[k][u], v[k][u]);
-            }
-#pragma unroll
-          for (int k = 0; k < kRowsInFlight; ++k)
-#pragma unroll
-            for (int u = 0; u < 4; ++u) add(k, ms[k][u], ls[k][u], v[k][u]);
-        }
+          for (int u = 0; u < 4; ++u) add(k, ms[k][u], ls[k][u], v[k][u]);
       }
 #pragma unroll
       for (int k = 0; k < kRowsInFlight; ++k) {
@@ -1070,6 +1039,69 @@ __global__ void __launch_bounds__(64 * NW) uv_kernel(const bf16* __restrict__ oh
       }
     }
   };
+  // With many partitions (16 or more: long contexts, small batches) every wave takes part in
+  // every row: wave w walks the row's groups w, w + NW, ... of eight partitions, and the waves'
+  // partial sums meet in LDS, where the row's owner normalises them into the A block.
+  auto combine_coop = [&](int m0, float* red) {
+    constexpr int kCoopG = 8;  // partitions per wave and pass (their loads in flight together)
+    const int S = parts.splits;
+    for (int r = 0; r < MB && m0 + r < B; ++r) {
+      const int64_t base = (int64_t)(m0 + r) * S * n_h + h;
+      float M = -INFINITY;
+      for (int c = 0; c < S; c += 64)
+        if (c + lane < S) M = fmaxf(M, parts.m[base + (int64_t)(c + lane) * n_h]);
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) M = fmaxf(M, __shfl_xor(M, d, 64));
+      float L = 0.f, acc[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+      for (int s0 = kCoopG * wv; s0 < S; s0 += kCoopG * NW) {
+        const int64_t pl = base + (int64_t)(s0 + (lane % kCoopG)) * n_h;
+        const bool in = s0 + (lane % kCoopG) < S;
+        const float m_l = in ? parts.m[pl] : -INFINITY;
+        const float l_l = in ? parts.l[pl] : 0.f;
+        if (__builtin_amdgcn_ballot_w64(m_l > -INFINITY) == 0) continue;
+        float ms[kCoopG], ls[kCoopG];
+        bf16x8 v[kCoopG];
+#pragma unroll
+        for (int u = 0; u < kCoopG; ++u) {
+          ms[u] = __shfl(m_l, u, 64);
+          ls[u] = __shfl(l_l, u, 64);
+          if (ms[u] > -INFINITY)
+            v[u] = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(parts.o) +
+                                                    (base + (int64_t)(s0 + u) * n_h) * kDc + 8 * lane);
+        }
+#pragma unroll
+        for (int u = 0; u < kCoopG; ++u)
+          if (ms[u] > -INFINITY) {
+            const float ws = exp2f(ms[u] - M) * ls[u];
+            L += ws;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] += ws * (float)v[u][e];
+          }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) red[(wv * 9 + e) * 64 + lane] = acc[e];
+      red[(wv * 9 + 8) * 64 + lane] = L;
+      __syncthreads();
+      if (wv == r % NW) {
+        float Lt = 0.f, A[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) A[e] = 0.f;
+        for (int w2 = 0; w2 < NW; ++w2) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) A[e] += red[(w2 * 9 + e) * 64 + lane];
+          Lt += red[(w2 * 9 + 8) * 64 + lane];
+        }
+        const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
+        bf16x8 out;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) out[e] = (bf16)(A[e] * inv);
+        *reinterpret_cast<bf16x8*>(la + r * kRowB + slot(r, lane) * 16) = out;
+      }
+      __syncthreads();  // the partial sums are read before the next row overwrites them
+    }
+  };
   // B fragments: lane (G, i) holds weight row d0 + i, k = 32 kk + 8G .. +7
   Frag8<bf16> bw[kDc / 32];
   {
@@ -1077,8 +1109,17 @@ __global__ void __launch_bounds__(64 * NW) uv_kernel(const bf16* __restrict__ oh
 #pragma unroll
     for (int kk = 0; kk < kDc / 32; ++kk) load8(bw[kk], wr + 32 * kk);
   }
+  float* red = nullptr;  // the waves' partial sums of one row (cooperative combine)
   if constexpr (PARTS) {
-    combine_a(m_begin);
+    __shared__ float red_s[NW * 9 * 64];
+    red = red_s;
+  }
+  auto combine = [&](int m0) {
+    if (parts.splits >= 16) combine_coop(m0, red);
+    else combine_a(m0);
+  };
+  if constexpr (PARTS) {
+    combine(m_begin);
     MLA_TILE_BARRIER(kWaitLgkm0);
   } else {
     copy_a(0);
@@ -1088,7 +1129,7 @@ __global__ void __launch_bounds__(64 * NW) uv_kernel(const bf16* __restrict__ oh
     if (m0 > m_begin) {
       __syncthreads();  // every wave is done with the previous block
       if constexpr (PARTS) {
-        combine_a(m0);
+        combine(m0);
         MLA_TILE_BARRIER(kWaitLgkm0);
       } else {
         copy_a(m0);
