@@ -313,7 +313,8 @@ def main():
     setup_s = time.perf_counter() - t0
     h = WL.to_device(S.hidden_step(dims, B, w.hidden), dims)
     ctx = torch.tensor(np.asarray(lens, dtype=np.int32), device="cuda")
-    splits = args.splits if args.splits > 0 else M.auto_splits(layer.cdims, B, max_ctx)
+    # 0: the library's automatic choice (fixed partitions, or balanced units for small batches)
+    splits = args.splits if args.splits > 0 else 0
     reps = [(layer, pool)] + [(layer.clone(), pool.clone()) for _ in range(max(0, args.replicas - 1))]
     outs = [torch.empty((B, dims.d_model), dtype=WL.torch_dtype(dims), device="cuda") for _ in reps]
     wss = [WL.decode_workspace(layer, B, max_ctx, splits) for _ in reps]
@@ -322,6 +323,11 @@ def main():
                                 .astype(np.float32), dims.dtype), dims)
     kv = ctx + 1
     ohat = torch.empty((B, dims.n_h, dims.d_c), dtype=WL.torch_dtype(dims), device="cuda")
+
+    def auto_label(n):  # the library's rule: balanced units below 16 (sequence, head-group) units
+        if B * ((dims.n_h + 127) // 128) < 16:
+            return f"auto (balanced units, up to {min(128, 2 * n)} partitions per sequence)"
+        return f"auto ({n} partitions per sequence)"
 
     def attn(i):
         M.decode_attention(layer.cdims, reps[i % len(reps)][1].ccache, q, kv, max_ctx + 1, ohat, wss[0],
@@ -380,7 +386,9 @@ def main():
         "data": "synthetic (seeded weights N(0,0.02), RMS-normalised N(0,1) hidden states, random page order)",
         "config": {"workload": w.name, "batch": B, "ctx_tokens": [int(min(lens)), int(max(lens))],
                    "d_model": dims.d_model, "n_h": dims.n_h, "d_h": dims.d_h, "d_c": dims.d_c, "d_cq": dims.d_cq,
-                   "d_hr": dims.d_hr, "block_size": w.block_size, "num_splits": splits, "replicas": len(reps),
+                   "d_hr": dims.d_hr, "block_size": w.block_size,
+                   "num_splits": splits if splits > 0 else auto_label(M.auto_splits(layer.cdims, B, max_ctx)),
+                   "replicas": len(reps),
                    "cache": "fp8_e4m3 (per-token scales)" if fp8 else dims.dtype,
                    "latent_rmsnorm": bool(dims.latent_norm),
                    "yarn_scale": float(dims.rope_scale) if dims.rope_scale > 1 else None},

@@ -567,9 +567,8 @@ __global__ void __launch_bounds__(512)
 
 // Log-sum-exp combination of the partitions: M = max_s m_s, w_s = 2^(m_s - M) l_s,
 // o_hat = sum_s w_s o_s / sum_s w_s with o_s = O_s / l_s the partition's normalised output (PT:
-// fp32 or bf16).  A 256-thread workgroup combines four (sequence, head) rows; each thread owns
-// DC/64 consecutive latent dims, and the partitions' loads are issued eight at a time before any
-// of them is used.
+// fp32 or bf16).  A 256-thread workgroup combines four (sequence, head) rows, one wave each;
+// each lane owns DC/64 consecutive latent dims.  Empty partitions (max -inf) are skipped.
 template <typename T, typename PT, int DC>
 __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeAttnParams p) {
   constexpr int V = DC >= 64 ? DC / 64 : 1;  // dims per thread
@@ -590,31 +589,36 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeAttnParams p)
   float acc[V];
 #pragma unroll
   for (int i = 0; i < V; ++i) acc[i] = 0.f;
-  constexpr int kG = 8;  // partitions whose loads are in flight together
-  for (int s0 = 0; s0 < p.splits; s0 += kG) {
-    float ms[kG], ls[kG];
-    PT v[kG][V];
+  // 64 partitions' (max, normaliser) at a time sit one per lane; a group of kG is skipped when
+  // all are empty, else the output rows of its non-empty partitions are loaded together
+  constexpr int kG = 16;
+  for (int c0 = 0; c0 < p.splits; c0 += 64) {
+    const int64_t pl = base + (int64_t)(c0 + lane) * p.n_h;
+    const float m_l = c0 + lane < p.splits ? p.part_m[pl] : -INFINITY;
+    const float l_l = c0 + lane < p.splits ? p.part_l[pl] : 0.f;
+    const uint64_t used = __builtin_amdgcn_ballot_w64(m_l > -INFINITY);
+    for (int s0 = c0; s0 < min(p.splits, c0 + 64); s0 += kG) {
+      if (((used >> (s0 - c0)) & ((1ull << kG) - 1)) == 0) continue;
+      float ms[kG], ls[kG];
+      PT v[kG][V];
 #pragma unroll
-    for (int u = 0; u < kG; ++u) {
-      ms[u] = -INFINITY;
-      if (s0 + u < p.splits) {
-        const int64_t pi = base + (int64_t)(s0 + u) * p.n_h;
-        ms[u] = p.part_m[pi];
-        if (ms[u] > -INFINITY) {  // empty partitions write no output row
-          ls[u] = p.part_l[pi];
-          const PT* src = reinterpret_cast<const PT*>(p.part_o) + pi * DC + d;
+      for (int u = 0; u < kG; ++u) {
+        ms[u] = __shfl(m_l, s0 - c0 + u, 64);
+        ls[u] = __shfl(l_l, s0 - c0 + u, 64);
+        if (ms[u] > -INFINITY) {  // (-inf past the last partition too)
+          const PT* src = reinterpret_cast<const PT*>(p.part_o) + (base + (int64_t)(s0 + u) * p.n_h) * DC + d;
 #pragma unroll
           for (int i = 0; i < V; ++i) v[u][i] = has_dims ? src[i] : PT(0.f);
         }
       }
-    }
 #pragma unroll
-    for (int u = 0; u < kG; ++u) {
-      if (ms[u] > -INFINITY) {
-        const float ws = exp2f(ms[u] - M) * ls[u];
-        L += ws;
+      for (int u = 0; u < kG; ++u) {
+        if (ms[u] > -INFINITY) {
+          const float ws = exp2f(ms[u] - M) * ls[u];
+          L += ws;
 #pragma unroll
-        for (int i = 0; i < V; ++i) acc[i] += ws * to_f32(v[u][i]);
+          for (int i = 0; i < V; ++i) acc[i] += ws * to_f32(v[u][i]);
+        }
       }
     }
   }
