@@ -569,10 +569,13 @@ __global__ void __launch_bounds__(512)
 // o_hat = sum_s w_s o_s / sum_s w_s with o_s = O_s / l_s the partition's normalised output (PT:
 // fp32 or bf16).  A 256-thread workgroup combines four (sequence, head) rows, one wave each;
 // each lane owns DC/64 consecutive latent dims.  Empty partitions (max -inf) are skipped.
-template <typename T, typename PT, int DC>
+template <typename T, typename PT, int DC, bool COOP>
 __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeAttnParams p) {
   constexpr int V = DC >= 64 ? DC / 64 : 1;  // dims per thread
-  const int bh = blockIdx.x * 4 + (threadIdx.x >> 6);  // b * n_h + head: one wave per row
+  const int wv = threadIdx.x >> 6;
+  // b * n_h + head: one wave per row, or (COOP, many partitions) one workgroup per row, its four
+  // waves taking every fourth chunk of 64 partitions and adding up in LDS
+  const int bh = COOP ? blockIdx.x : blockIdx.x * 4 + wv;
   if (bh >= p.B * p.n_h) return;
   const int lane = threadIdx.x & 63;
   const bool has_dims = V * lane < DC;
@@ -592,7 +595,7 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeAttnParams p)
   // 64 partitions' (max, normaliser) at a time sit one per lane; a group of kG is skipped when
   // all are empty, else the output rows of its non-empty partitions are loaded together
   constexpr int kG = 16;
-  for (int c0 = 0; c0 < p.splits; c0 += 64) {
+  for (int c0 = COOP ? 64 * wv : 0; c0 < p.splits; c0 += COOP ? 256 : 64) {
     const int64_t pl = base + (int64_t)(c0 + lane) * p.n_h;
     const float m_l = c0 + lane < p.splits ? p.part_m[pl] : -INFINITY;
     const float l_l = c0 + lane < p.splits ? p.part_l[pl] : 0.f;
@@ -620,6 +623,22 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeAttnParams p)
           for (int i = 0; i < V; ++i) acc[i] += ws * to_f32(v[u][i]);
         }
       }
+    }
+  }
+  if constexpr (COOP) {
+    __shared__ float red[4][V + 1][64];
+#pragma unroll
+    for (int i = 0; i < V; ++i) red[wv][i][lane] = acc[i];
+    red[wv][V][lane] = L;
+    __syncthreads();
+    if (wv != 0) return;
+    L = 0.f;
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] = 0.f;
+    for (int w2 = 0; w2 < 4; ++w2) {
+#pragma unroll
+      for (int i = 0; i < V; ++i) acc[i] += red[w2][i][lane];
+      L += red[w2][V][lane];
     }
   }
   if (!has_dims) return;
@@ -1008,7 +1027,10 @@ hipError_t launch(const DecodeAttnParams& p, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<T, float, DC>), dim3((p.B * p.n_h + 3) / 4), dim3(256), 0, s, p);
+  if (p.splits >= 16)
+    hipLaunchKernelGGL((decode_combine_kernel<T, float, DC, true>), dim3(p.B * p.n_h), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((decode_combine_kernel<T, float, DC, false>), dim3((p.B * p.n_h + 3) / 4), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 }  // namespace
@@ -1031,7 +1053,11 @@ hipError_t decode_attention(DType t, const DecodeAttnParams& p, hipStream_t s) {
     hipLaunchKernelGGL(decode_attn_fp8_kernel, dim3(blocks), dim3(64 * tiled8::kWaves), 0, s, p, HG, p.block_table);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1 || p.leave_partials) return e;
-    hipLaunchKernelGGL((decode_combine_kernel<bf16, bf16, 512>), dim3((p.B * p.n_h + 3) / 4), dim3(256), 0, s, p);
+    if (p.splits >= 16)
+      hipLaunchKernelGGL((decode_combine_kernel<bf16, bf16, 512, true>), dim3(p.B * p.n_h), dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL((decode_combine_kernel<bf16, bf16, 512, false>), dim3((p.B * p.n_h + 3) / 4), dim3(256), 0,
+                         s, p);
     return hipGetLastError();
   }
   if (decode_tiled(t, p.d_c, p.d_hr, p.block_size)) {
@@ -1045,7 +1071,11 @@ hipError_t decode_attention(DType t, const DecodeAttnParams& p, hipStream_t s) {
                        p.block_table);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1 || p.leave_partials) return e;
-    hipLaunchKernelGGL((decode_combine_kernel<bf16, bf16, 512>), dim3((p.B * p.n_h + 3) / 4), dim3(256), 0, s, p);
+    if (p.splits >= 16)
+      hipLaunchKernelGGL((decode_combine_kernel<bf16, bf16, 512, true>), dim3(p.B * p.n_h), dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL((decode_combine_kernel<bf16, bf16, 512, false>), dim3((p.B * p.n_h + 3) / 4), dim3(256), 0,
+                         s, p);
     return hipGetLastError();
   }
   if (p.d_c == 512 && p.d_hr == 64)

@@ -61,11 +61,15 @@ def test_cache_append_matches_oracle(name):
 @pytest.mark.parametrize("name,lens,splits,block", [("tiny", [1, 17, 64, 100], 0, 16), ("v2lite", [1, 33, 200, 64], 0, 64),
                                                     ("v2lite", [300, 31], 3, 64), ("v2", [1, 95, 257], 0, 64),
                                                     ("v2", [257, 40], 2, 64), ("v2", [130, 3, 700], 0, 16),
-                                                    ("v2", [130, 3, 700], 4, 128), ("v2lite", [64, 128, 1], 0, 256)])
+                                                    ("v2", [130, 3, 700], 4, 128), ("v2lite", [64, 128, 1], 0, 256),
+                                                    ("v2", [3000, 700], 20, 64), ("v2", [3000, 1, 700], 0, 64),
+                                                    ("v2", [2500, 90], 24, 16)])
 def test_decode_attention_core_matches_oracle(name, lens, splits, block):
     """Kernel-isolated: queries and cache entries are random device values; the oracle reads the
     same values back.  Block sizes that are multiples of 64 take the tiled kernel, others the
-    general one."""
+    general one.  Small batches with automatic splits take the balanced units; 16 or more
+    partitions take the one-row-per-workgroup combine (with the tiled kernel's bf16 partials and
+    the general kernel's fp32 ones)."""
     dims = SMALL[name][0]
     layer = WL.DeviceLayer(dims, S.make_weights(dims))
     B = len(lens)
