@@ -201,6 +201,10 @@ int mla_prefill_chunk(const mla_dims *dims, const mla_weights *w, const mla_page
  *             max_ctx_len + 1 <= max_blocks_per_seq * block_size.
  *   num_splits (host): KV partitions per sequence (split-KV, combined by a log-sum-exp
  *             reduction); 0 = chosen from the sizes and the device's compute-unit count.
+ *             With 0 and fewer than 16 (sequence, 128-head group) units, the bf16 and fp8
+ *             paged kernels size their partitions on the device from ctx_lens (up to twice
+ *             the automatic count per sequence), so that ragged contexts load the compute
+ *             units evenly; otherwise each partition covers a fixed token range.
  *   u         [batch][d_model] output
  *   o_heads   NULL, or fp32 [batch][n_h][d_h] receiving o_{t,i}.
  */
@@ -224,7 +228,9 @@ int mla_decode_attention(const mla_dims *dims, const mla_paged_cache *cache, con
                          int32_t num_splits, void *o_hat, float *lse, void *workspace,
                          size_t ws_bytes, void *stream);
 
-/* The split count mla_decode uses for num_splits == 0 (host query; -1 on invalid sizes). */
+/* The split count mla_decode uses for num_splits == 0 with fixed partitions (host query; -1 on
+ * invalid sizes).  Small batches with num_splits == 0 use up to twice as many partition slots,
+ * balanced over the actual context lengths (see mla_decode). */
 int32_t mla_decode_auto_splits(const mla_dims *dims, int32_t batch, int32_t max_ctx_len);
 
 /* Static text for a status code. */
