@@ -283,8 +283,8 @@ def main():
         copy_only(args)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build "
-              f"(sharding across GPUs is described in DESIGN.md but not implemented)", file=sys.stderr)
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported: the library has no "
+              f"multi-GPU path (decode shards by batch, one independent process per GPU)", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch

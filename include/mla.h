@@ -53,7 +53,7 @@ extern "C" {
 typedef enum {
   MLA_OK = 0,
   MLA_ERR_INVALID_ARG = -1, /* NULL pointer, non-positive or inconsistent size */
-  MLA_ERR_UNSUPPORTED = -2, /* valid MLA sizes this build has no kernel for */
+  MLA_ERR_UNSUPPORTED = -2, /* valid MLA sizes the library has no kernel for */
   MLA_ERR_WORKSPACE = -3,   /* workspace NULL or smaller than mla_workspace_size() */
   MLA_ERR_HIP = -4          /* a HIP call or kernel launch failed */
 } mla_status;

@@ -544,7 +544,7 @@ const char* mla_status_string(int status) {
   switch (status) {
     case MLA_OK: return "MLA_OK";
     case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG: null pointer, non-positive or inconsistent size";
-    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: sizes without a kernel in this build";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: sizes the library has no kernel for";
     case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace missing or too small";
     case MLA_ERR_HIP: return "MLA_ERR_HIP: a HIP call or kernel launch failed";
     default: return "unknown mla_status";
