@@ -16,7 +16,9 @@ The plainest reading that an MI355X path can serve natively (the design notes li
   * attention reads value(code) * s; the quantiser's decisions are integers and are taken in
     fp32, the precision the kernels use.
 Pins: the code table and the encoder against torch's float8_e4m3fn conversion (a library
-routine), the error bound of the format, and the amax element mapping to +-448.
+routine), the error bound of the format, and the amax element mapping to +-448.  The decode step
+(mla_decode_fp8) is pinned against the plain decode step of mla_oracle on entries that quantise
+exactly, and its new codes against the quantised prefill row of the same token.
 """
 from __future__ import annotations
 
