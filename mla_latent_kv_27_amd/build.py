@@ -1,7 +1,9 @@
 """Builds libmla.so (the HIP kernels and the C ABI) in-tree for gfx950 with hipcc.
 
 Usage: python -m mla_latent_kv_27_amd.build   (or call build()).  Compiles every time it is
-called; objects go to mla_latent_kv_27_amd/_build/, the library to mla_latent_kv_27_amd/lib/.
+called; objects go to mla_latent_kv_27_amd/_build/, the libraries to mla_latent_kv_27_amd/lib/:
+libmla.so (the MLA kernels and the C ABI) and libmla_probe.so (the HBM streaming-ceiling probe
+the benchmark reports against; no part of the MLA computation).
 """
 import os
 import shutil
@@ -13,9 +15,11 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 LIB = os.path.join(PKG, "lib", "libmla.so")
+PROBE_LIB = os.path.join(PKG, "lib", "libmla_probe.so")
 ARCH = os.environ.get("MLA_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["gemm.hip", "rope.hip", "decode_attn.hip", "prefill_attn.hip", "latent_fp8.hip", "blas.cpp", "mla_api.cpp"]
+SOURCES = ["gemm.hip", "rope.hip", "decode_attn.hip", "prefill_attn.hip", "latent_fp8.hip", "mla_api.cpp"]
+PROBE_SOURCES = ["probe.hip"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
@@ -41,20 +45,26 @@ def _compile(src):
     return obj
 
 
+def _link(objs, out):
+    tmp = out + ".tmp"
+    cmd = [_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link of {os.path.basename(out)} failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, out)
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     os.makedirs(os.path.dirname(LIB), exist_ok=True)
-    jobs = min(len(SOURCES), max(1, min(8, os.cpu_count() or 1)))
+    srcs = SOURCES + PROBE_SOURCES
+    jobs = min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
     with ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-lhipblaslt", "-o", tmp]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PROBE_LIB)
     return LIB
 
 

@@ -235,15 +235,14 @@ DecodeWs carve_decode(Carve& cv, const mla_dims* d, int B, int max_ctx_len, int 
 struct PrefillWs {
   int32_t *seq, *pos;
   float2* rope;
-  void *cq, *qp, *kvd, *kva, *kp, *vt, *o;  // kva: chunked prefill's gathered keys (else kvd)
+  void *cq, *qc, *kvd, *kva, *kp, *vt, *o;  // kva: chunked prefill's gathered keys (else kvd)
+  float* qr;                               // [M][n_h*d_hr] un-rotated q^R, fp32
   float* partial;
-  void* blas;  // hipBLASLt workspace (bf16 layers), kBlasWs bytes
   GemmPlan kvq_p, q_p, kv_p, k_p, v_p, out_p;  // kvq_p: [W_DQ; W_DKV; W_KR] (d_cq > 0), else kv_p
   int Tk, Tp;  // key rows per sequence (T, or max_start + T when chunked), rounded up to 64
-  bool tm;     // the pipelined attention kernel runs: q^C, q^R (fp32) and k token-major
-  void *qc2;   // tm: [M][n_h*d_h] q^C, in qp's region
-  float* qr2;  // tm: [M][n_h*d_hr] un-rotated q^R, in qp's region after qc2
 };
+// Every intermediate is the plain output of one product: q^C and q^R token-major (q^R in fp32,
+// rotated by the attention kernel as it loads it), k^C token-major, v^T token-contiguous.
 // chunked: keys are the cached prefix plus the new rows, max_start + T per sequence
 PrefillWs carve_prefill(Carve& cv, const mla_dims* d, int S, int T, int cus, bool chunked = false,
                         int max_start = 0) {
@@ -264,11 +263,8 @@ PrefillWs carve_prefill(Carve& cv, const mla_dims* d, int S, int T, int cus, boo
   w.pos = cv.take<int32_t>((size_t)M * 4);
   w.rope = cv.take<float2>((size_t)M * (d->d_hr / 2) * sizeof(float2));
   w.cq = cv.take<char>((size_t)M * d->d_cq * es);
-  w.tm = prefill_pipelined(dt(d), S, w.Tk, d->n_h, d->d_h, d->d_hr, entry(d));
-  const size_t tm_bytes = w.tm ? (size_t)M * d->n_h * (d->d_h * es + d->d_hr * sizeof(float)) : 0;
-  w.qp = cv.take<char>(std::max((size_t)M * qw * es, tm_bytes));
-  w.qc2 = w.qp;
-  w.qr2 = w.qp ? reinterpret_cast<float*>(reinterpret_cast<char*>(w.qp) + (size_t)M * d->n_h * d->d_h * es) : nullptr;
+  w.qc = cv.take<char>((size_t)M * d->n_h * d->d_h * es);
+  w.qr = cv.take<float>((size_t)M * d->n_h * d->d_hr * sizeof(float));
   w.kvd = cv.take<char>((size_t)M * entry(d) * es);
   w.kva = chunked ? cv.take<char>((size_t)Mk * entry(d) * es) : w.kvd;
   w.kp = cv.take<char>((size_t)Mk * d->n_h * d->d_h * es);
@@ -281,7 +277,6 @@ PrefillWs carve_prefill(Carve& cv, const mla_dims* d, int S, int T, int cus, boo
                         gemm_partial_bound(M, d->d_model, d->n_h * d->d_h, 1, cus, sk(d))});
   if (d->d_cq > 0) mp = std::max(mp, gemm_partial_bound(M, d->d_cq + entry(d), d->d_model, 1, cus, sk(d)));
   w.partial = cv.take<float>(mp);
-  w.blas = cv.take<char>(dt(d) == DType::BF16 ? kBlasWs : 0);
   return w;
 }
 
@@ -442,30 +437,16 @@ int prefill_impl(const mla_dims* d, const mla_weights* w, const mla_paged_cache*
     g.epi = kv_epi;
     MLA_HIP(gemm_run(t, g, ws.kv_p, ws.partial, s));
   }
-  // With the pipelined attention kernel, q^C and the un-rotated q^R are plain products
-  // (hipBLASLt), token-major; the kernel rotates q^R as it loads it.
-  bool q_tm = false, k_tm = false;
-  if (ws.tm) {
-    hipError_t e = blas_gemm_nt(qin, qw, w->W_UQ, qw, ws.qc2, (int64_t)d->n_h * d->d_h, M, d->n_h * d->d_h, qw,
-                                ws.blas, kBlasWs, s);
-    if (e == hipSuccess)
-      e = blas_gemm_nt(qin, qw, w->W_QR, qw, ws.qr2, (int64_t)d->n_h * d->d_hr, M, d->n_h * d->d_hr, qw, ws.blas,
-                       kBlasWs, s, true);
-    if (e != hipSuccess && e != hipErrorNotSupported) return MLA_ERR_HIP;
-    q_tm = e == hipSuccess;
-  }
-  if (!q_tm) {  // [q^C | RoPE(q^R)] = [W_UQ; W_QR] c^q: q^C to columns [0, d_h) and q^R to
-                // [d_h, d_h + d_hr) of each head's row
+  {  // [q^C | q^R] = [W_UQ; W_QR] c^q in one launch: q^C token-major in the layer's type, q^R
+     // token-major in fp32 and not yet rotated (the attention kernel rotates it as it loads it)
     GemmParams g;
     g.A = qin; g.lda = qw; g.ldb = qw;
     g.B0 = w->W_UQ; g.N0 = d->n_h * d->d_h; g.B1 = w->W_QR;
     g.M = M; g.N = d->n_h * QD; g.K = qw;
-    g.epi = dense(ws.qp, (int64_t)d->n_h * QD);
-    g.epi.group = d->d_h; g.epi.group_stride = QD; g.epi.group_off = 0;
+    g.epi = dense(ws.qc, (int64_t)d->n_h * d->d_h);
     g.E0 = d->n_h * d->d_h;
-    g.epi2 = dense(ws.qp, (int64_t)d->n_h * QD);
-    g.epi2.group = d->d_hr; g.epi2.group_stride = QD; g.epi2.group_off = d->d_h;
-    g.epi2.rope_col0 = 0; g.epi2.d_hr = d->d_hr; g.epi2.rope_tab = ws.rope;
+    g.epi2 = dense(ws.qr, (int64_t)d->n_h * d->d_hr);
+    g.epi2.c_f32 = true;
     MLA_HIP(gemm_run(t, g, ws.q_p, ws.partial, s));
   }
   {
@@ -477,28 +458,14 @@ int prefill_impl(const mla_dims* d, const mla_weights* w, const mla_paged_cache*
       MLA_HIP(gather_entries(t, c->pool, fp8_cache(d) ? c->scales : nullptr, c->block_table, c->max_blocks_per_seq,
                              c->block_size, start, ws.kvd, T, batch, ws.Tk, E, d->d_c, ws.kva, s));
   }
-  if (ws.tm) {  // k^C = [W_UK_1; ...] c^KV token-major [Mk][n_h*d_h], a plain product
-    const hipError_t e = blas_gemm_nt(ws.kva, E, w->W_UK, d->d_c, ws.kp, (int64_t)d->n_h * d->d_h, Mk,
-                                      d->n_h * d->d_h, d->d_c, ws.blas, kBlasWs, s);
-    if (e != hipSuccess && e != hipErrorNotSupported) return MLA_ERR_HIP;
-    k_tm = e == hipSuccess;
-  }
-  if (!k_tm) {  // k^C_i = W_UK_i c^KV, stored head-major [n_h][M][d_h]
+  {  // k^C = [W_UK_1; ...; W_UK_n_h] c^KV, token-major [Mk][n_h*d_h]
     GemmParams g;
     g.A = ws.kva; g.lda = E; g.B0 = w->W_UK; g.ldb = d->d_c;
     g.M = Mk; g.N = d->n_h * d->d_h; g.K = d->d_c;
-    g.epi = dense(ws.kp, d->d_h);
-    g.epi.group = d->d_h; g.epi.group_stride = (int64_t)Mk * d->d_h;
+    g.epi = dense(ws.kp, (int64_t)d->n_h * d->d_h);
     MLA_HIP(gemm_run(t, g, ws.k_p, ws.partial, s));
   }
-  bool v_done = false;
-  if (t == DType::BF16 && ws.Tp == ws.Tk) {  // no padding columns: v^T is a plain product
-    const hipError_t e = blas_gemm_nt(w->W_UV, d->d_c, ws.kva, E, ws.vt, (int64_t)batch * ws.Tp, d->n_h * d->d_h,
-                                      Mk, d->d_c, ws.blas, kBlasWs, s);
-    if (e != hipSuccess && e != hipErrorNotSupported) return MLA_ERR_HIP;
-    v_done = e == hipSuccess;
-  }
-  if (!v_done) {  // v^T: rows (head, dim) of W_UV times c^KV^T, token-contiguous [n_h][d_h][S][Tp]
+  {  // v^T: rows (head, dim) of W_UV times c^KV^T, token-contiguous [n_h][d_h][S][Tp]
     GemmParams g;
     g.A = w->W_UV; g.lda = d->d_c; g.B0 = ws.kva; g.ldb = E;
     g.M = d->n_h * d->d_h; g.N = Mk; g.K = d->d_c;
@@ -508,30 +475,22 @@ int prefill_impl(const mla_dims* d, const mla_weights* w, const mla_paged_cache*
   }
   {
     PrefillAttnParams a{};
-    a.q = ws.qp; a.k = ws.kp; a.kr = ws.kva; a.ld_kr = E; a.kr_off = d->d_c; a.vt = ws.vt;
+    a.qc = ws.qc; a.qr = ws.qr; a.rope = ws.rope;
+    a.k = ws.kp; a.k_ld = (int64_t)d->n_h * d->d_h;
+    a.kr = ws.kva; a.ld_kr = E; a.kr_off = d->d_c; a.vt = ws.vt;
     a.o = ws.o; a.o_f32 = o_heads;
     a.S = batch; a.T = T; a.n_h = d->n_h; a.d_h = d->d_h; a.d_hr = d->d_hr;
     a.Tk = ws.Tk; a.q_off = start;
-    if (q_tm) {
-      a.qc = ws.qc2; a.qr = ws.qr2; a.rope = ws.rope;
-    }
-    if (k_tm) a.k_ld = (int64_t)d->n_h * d->d_h;
     a.scale_log2 = scale_of(d) * 1.4426950408889634f;
     MLA_HIP(prefill_attention(t, a, s));
   }
-  {  // u = W_O [o_1; ...; o_n_h]: a plain product (hipBLASLt for bf16)
+  {  // u = W_O [o_1; ...; o_n_h]
     const int64_t K = (int64_t)d->n_h * d->d_h;
-    hipError_t e = t == DType::BF16 ? blas_gemm_nt(ws.o, K, w->W_O, K, u, d->d_model, M, d->d_model, (int)K, ws.blas,
-                                                   kBlasWs, s)
-                                    : hipErrorNotSupported;
-    if (e == hipErrorNotSupported) {
-      GemmParams g;
-      g.A = ws.o; g.lda = K; g.B0 = w->W_O; g.ldb = K;
-      g.M = M; g.N = d->d_model; g.K = (int)K;
-      g.epi = dense(u, d->d_model);
-      e = gemm_run(t, g, ws.out_p, ws.partial, s);
-    }
-    MLA_HIP(e);
+    GemmParams g;
+    g.A = ws.o; g.lda = K; g.B0 = w->W_O; g.ldb = K;
+    g.M = M; g.N = d->d_model; g.K = (int)K;
+    g.epi = dense(u, d->d_model);
+    MLA_HIP(gemm_run(t, g, ws.out_p, ws.partial, s));
   }
   return MLA_OK;
 }

@@ -46,17 +46,33 @@ __global__ void __launch_bounds__(256) prefill_attn_kernel(PrefillAttnParams p) 
   const int qpos = off + qi;
   const int nk = off + p.T;                  // valid keys of this sequence
   const int Tk = p.Tk > 0 ? p.Tk : p.T;
-  const int64_t MT = (int64_t)p.S * Tk;
   const int Tp = (Tk + kBKV - 1) / kBKV * kBKV;
 
+  // [q^C | RoPE(q^R)] fragments: dims k .. k+7 of a chunk lie in one part (d_h and d_hr are
+  // multiples of 8); the rope ones are four pairs, rotated in fp32 and then rounded to T
   Frag8<T> q[KS];
   {
-    const T* qrow = reinterpret_cast<const T*>(p.q) + (((int64_t)s * p.T + min(qi, p.T - 1)) * p.n_h + head) * DQ;
+    const int64_t row = (int64_t)s * p.T + min(qi, p.T - 1);
+    const T* qrow = reinterpret_cast<const T*>(p.qc) + row * p.n_h * DH + (int64_t)head * DH;
+    const float* rrow = p.qr + row * p.n_h * DR + (int64_t)head * DR;
+    const float2* tab = p.rope + row * (DR / 2);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int k = ks * 16 + 8 * g;
-      if (qi < p.T && k < DQ) load8(q[ks], qrow + k);
-      else zero8(q[ks]);
+      if (qi >= p.T || k >= DQ) {
+        zero8(q[ks]);
+      } else if (k < DH) {
+        load8(q[ks], qrow + k);
+      } else {
+        const int d0 = k - DH;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x0 = rrow[d0 + 2 * i], x1 = rrow[d0 + 2 * i + 1];
+          const float2 cs = tab[d0 / 2 + i];
+          set8(q[ks], 2 * i, x0 * cs.x - x1 * cs.y);
+          set8(q[ks], 2 * i + 1, x1 * cs.x + x0 * cs.y);
+        }
+      }
     }
   }
   if (DQP > DQ) {
@@ -76,7 +92,7 @@ __global__ void __launch_bounds__(256) prefill_attn_kernel(PrefillAttnParams p) 
     for (int r = 0; r < 16; ++r) o[d][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  const T* kbase = reinterpret_cast<const T*>(p.k) + ((int64_t)head * MT + (int64_t)s * Tk) * DH;
+  const T* kbase = reinterpret_cast<const T*>(p.k) + (int64_t)s * Tk * p.k_ld + (int64_t)head * DH;
   const T* krbase = reinterpret_cast<const T*>(p.kr) + (int64_t)s * Tk * p.ld_kr + p.kr_off;
   const T* vbase = reinterpret_cast<const T*>(p.vt) + ((int64_t)head * DH * p.S + s) * Tp;  // row d at + d*S*Tp
   const int64_t vrow = (int64_t)p.S * Tp;
@@ -89,7 +105,7 @@ __global__ void __launch_bounds__(256) prefill_attn_kernel(PrefillAttnParams p) 
       const int r = c / (DQ / EPC), cc = (c % (DQ / EPC)) * EPC;
       const int j = j0 + r;
       Chunk16 v = zero16();
-      if (j < nk) v = cc < DH ? ld16(kbase + (int64_t)j * DH + cc) : ld16(krbase + (int64_t)j * p.ld_kr + (cc - DH));
+      if (j < nk) v = cc < DH ? ld16(kbase + (int64_t)j * p.k_ld + cc) : ld16(krbase + (int64_t)j * p.ld_kr + (cc - DH));
       st16(&Ks[r * LDK + cc], v);
     }
     for (int c = tid; c < DH * (kBKV / EPC); c += 256) {
@@ -394,20 +410,14 @@ __global__ void __launch_bounds__(512)
   const int qpos_last = off + min(qt * kQ + w * 32 + 31, p.T - 1);  // this wave's last query
   const int qpos_first = off + qt * kQ + w * 32;                     // and its first
   const int Tk = p.Tk > 0 ? p.Tk : p.T;
-  const int64_t MT = (int64_t)p.S * Tk;
   const int Tp = (Tk + kKV - 1) / kKV * kKV;
 
   Pf2Ctx c;
-  // spans below 2 GiB (checked by the launcher): offsets within them are 32-bit
-  if (p.k_ld > 0) {  // token-major keys: row j of head h at j * k_ld + h * d_h
-    c.k = dma_span(reinterpret_cast<const bf16*>(p.k) + (int64_t)sq * Tk * p.k_ld + (int64_t)head * kDH,
-                   (uint32_t)(((int64_t)(nk - 1) * p.k_ld + kDH) * 2));
-    c.krow = (int)(p.k_ld * 2);
-  } else {
-    c.k = dma_span(reinterpret_cast<const bf16*>(p.k) + ((int64_t)head * MT + (int64_t)sq * Tk) * kDH,
-                   (uint32_t)nk * kKRow);
-    c.krow = kKRow;
-  }
+  // spans below 2 GiB (checked by the launcher): offsets within them are 32-bit; key row j of
+  // head h at j * k_ld + h * d_h
+  c.k = dma_span(reinterpret_cast<const bf16*>(p.k) + (int64_t)sq * Tk * p.k_ld + (int64_t)head * kDH,
+                 (uint32_t)(((int64_t)(nk - 1) * p.k_ld + kDH) * 2));
+  c.krow = (int)(p.k_ld * 2);
   c.kr = dma_span(reinterpret_cast<const bf16*>(p.kr) + (int64_t)sq * Tk * p.ld_kr + p.kr_off,
                   (uint32_t)(((int64_t)(nk - 1) * p.ld_kr + kDR) * 2));
   c.ld_kr = (int)p.ld_kr;
@@ -417,7 +427,7 @@ __global__ void __launch_bounds__(512)
   c.T = nk;
 
   Frag8<bf16> q[12];
-  if (p.qc) {  // token-major q^C, and q^R rotated here: dims 16 (ks - 8) + 8g .. +7 are 4 pairs
+  {  // q^C, and q^R rotated here: dims 16 (ks - 8) + 8g .. +7 are 4 pairs
     const int64_t row = (int64_t)sq * p.T + min(qi, p.T - 1);
     const bf16* qrow = reinterpret_cast<const bf16*>(p.qc) + row * p.n_h * kDH + (int64_t)head * kDH;
     const float* rrow = p.qr + row * p.n_h * kDR + (int64_t)head * kDR;
@@ -440,13 +450,6 @@ __global__ void __launch_bounds__(512)
     if (qi >= p.T)
 #pragma unroll
       for (int ks = 0; ks < 12; ++ks) zero8(q[ks]);
-  } else {
-    const bf16* qrow = reinterpret_cast<const bf16*>(p.q) + (((int64_t)sq * p.T + min(qi, p.T - 1)) * p.n_h + head) * kDQ;
-#pragma unroll
-    for (int ks = 0; ks < 12; ++ks) {
-      if (qi < p.T) load8(q[ks], qrow + ks * 16 + 8 * g);
-      else zero8(q[ks]);
-    }
   }
   Pf2State s;
 #pragma unroll
@@ -506,19 +509,16 @@ hipError_t launch(const PrefillAttnParams& p, hipStream_t s) {
 // the pipelined kernel addresses each source span with 32-bit byte offsets
 static bool pf2_spans_fit(int64_t S, int64_t Tk, int64_t ld_kr, int64_t k_ld) {
   const int64_t Tp = (Tk + pf2::kKV - 1) / pf2::kKV * pf2::kKV;
-  const int64_t k_span = k_ld > 0 ? ((Tk - 1) * k_ld + pf2::kDH) * 2 : Tk * pf2::kKRow;
-  return k_span < (1LL << 31) && ((Tk - 1) * ld_kr + pf2::kDR) * 2 < (1LL << 31) &&
+  return ((Tk - 1) * k_ld + pf2::kDH) * 2 < (1LL << 31) && ((Tk - 1) * ld_kr + pf2::kDR) * 2 < (1LL << 31) &&
          ((int64_t)(pf2::kDH - 1) * S * Tp + Tp) * 2 < (1LL << 31);
-}
-
-bool prefill_pipelined(DType t, int S, int Tk, int n_h, int d_h, int d_hr, int64_t ld_kr) {
-  return t == DType::BF16 && d_h == 128 && d_hr == 64 && pf2_spans_fit(S, Tk, ld_kr, (int64_t)n_h * d_h);
 }
 
 hipError_t prefill_attention(DType t, const PrefillAttnParams& p, hipStream_t s) {
   const int64_t Tk = p.Tk > 0 ? p.Tk : p.T;
+  if (!p.qc || !p.qr || !p.rope || !p.k || p.k_ld < (int64_t)p.n_h * p.d_h) return hipErrorInvalidValue;
+  // the DeepSeek-V2 head sizes in bf16 take the pipelined kernel (unless a source span needs
+  // 64-bit offsets); every other supported size the synchronous one
   const bool pipelined = t == DType::BF16 && p.d_h == 128 && p.d_hr == 64 && pf2_spans_fit(p.S, Tk, p.ld_kr, p.k_ld);
-  if ((p.qc || p.k_ld > 0) && !pipelined) return hipErrorInvalidValue;  // token-major: pipelined kernel only
   if (pipelined) {
     const int nqt = (p.T + pf2::kQ - 1) / pf2::kQ;
     const int units = p.S * p.n_h;
