@@ -214,6 +214,27 @@ int mla_decode(const mla_dims *dims, const mla_weights *w, const mla_paged_cache
                void *stream);
 
 /*
+ * Allocation-free variant of mla_decode, for callers that cannot allocate device memory or hand
+ * over a workspace: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, results and validation as mla_decode, without the workspace.
+ *   - Scratch: the library's own device array of MLA_NOALLOC_SCRATCH_BYTES on each device,
+ *     reserved when the library's code object loads on that device and held until the process
+ *     ends; its address is looked up once per device, on the first call there.  Nothing in it
+ *     needs to start at zero.
+ *   - Calls whose sizes need more, i.e. mla_workspace_size(MLA_OP_DECODE, batch, 0, max_ctx_len,
+ *     num_splits) > MLA_NOALLOC_SCRATCH_BYTES, return MLA_ERR_WORKSPACE and launch nothing.
+ *     (DeepSeek-V2 sizes: batch 64 at any context up to 131072 fits.)
+ *   - Every call on one device uses that device's one array: calls that overlap in time on one
+ *     device (on different streams, or from threads without ordering) race and their results are
+ *     undefined.  Calls on one stream are ordered and safe.
+ *   - Allocates nothing (no hipMalloc / hipFree, no allocating library routine).
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)192 << 20)
+int mla_decode_noalloc(const mla_dims *dims, const mla_weights *w, const mla_paged_cache *cache,
+                       const void *h, int32_t batch, const int32_t *ctx_lens, int32_t max_ctx_len,
+                       int32_t num_splits, void *u, float *o_heads, void *stream);
+
+/*
  * Decode attention core only (the split-KV latent attention and its reduction), for timing and
  * kernel-level tests.  Inputs are the absorbed queries already formed:
  *   q        [batch][n_h][d_c + d_hr], dims->dtype: [q_hat_i | RoPE'd q^R_i] per head

@@ -24,9 +24,11 @@ MLA_FP8_E4M3 = 2
 OP_CACHE_APPEND, OP_PREFILL, OP_DECODE, OP_PREFILL_CHUNK = 0, 1, 2, 3
 
 EXPORTED = (
-    "mla_workspace_size", "mla_cache_append", "mla_prefill", "mla_prefill_chunk", "mla_decode", "mla_decode_attention",
-    "mla_decode_auto_splits", "mla_quantize_entries", "mla_status_string",
+    "mla_workspace_size", "mla_cache_append", "mla_prefill", "mla_prefill_chunk", "mla_decode", "mla_decode_noalloc",
+    "mla_decode_attention", "mla_decode_auto_splits", "mla_quantize_entries", "mla_status_string",
 )
+# bytes of the library's own scratch behind mla_decode_noalloc (MLA_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 192 << 20
 
 
 class MlaError(RuntimeError):
@@ -72,6 +74,7 @@ def lib() -> ctypes.CDLL:
         L.mla_prefill.argtypes = [D, W, C, P, I32, I32, P, P, P, SZ, P]
         L.mla_prefill_chunk.argtypes = [D, W, C, P, I32, I32, P, I32, P, P, P, SZ, P]
         L.mla_decode.argtypes = [D, W, C, P, I32, P, I32, I32, P, P, P, SZ, P]
+        L.mla_decode_noalloc.argtypes = [D, W, C, P, I32, P, I32, I32, P, P, P]
         L.mla_decode_attention.argtypes = [D, C, P, I32, P, I32, I32, P, P, P, SZ, P]
         L.mla_decode_auto_splits.argtypes = [D, I32, I32]
         L.mla_quantize_entries.argtypes = [D, P, I32, P, P, P]
@@ -80,7 +83,7 @@ def lib() -> ctypes.CDLL:
         L.mla_status_string.argtypes = [ctypes.c_int]
         L.mla_status_string.restype = ctypes.c_char_p
         for n in ("mla_workspace_size", "mla_cache_append", "mla_prefill", "mla_prefill_chunk", "mla_decode",
-                  "mla_decode_attention"):
+                  "mla_decode_noalloc", "mla_decode_attention"):
             getattr(L, n).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -174,6 +177,13 @@ def decode(dims, weights, cache, h, ctx_lens, max_ctx_len, u, workspace, num_spl
     _check(lib().mla_decode(ctypes.byref(dims), ctypes.byref(weights), ctypes.byref(cache), _ptr(h),
                             int(h.shape[0]), _ptr(ctx_lens), int(max_ctx_len), int(num_splits), _ptr(u),
                             _ptr(o_heads), p, n, _stream(stream)), "mla_decode")
+
+
+def decode_noalloc(dims, weights, cache, h, ctx_lens, max_ctx_len, u, num_splits=0, o_heads=None, stream=None):
+    """mla_decode on the library's own scratch (no workspace; see mla_decode_noalloc in mla.h)."""
+    _check(lib().mla_decode_noalloc(ctypes.byref(dims), ctypes.byref(weights), ctypes.byref(cache), _ptr(h),
+                                    int(h.shape[0]), _ptr(ctx_lens), int(max_ctx_len), int(num_splits), _ptr(u),
+                                    _ptr(o_heads), _stream(stream)), "mla_decode_noalloc")
 
 
 def decode_attention(dims, cache, q, kv_lens, max_kv_len, o_hat, workspace, num_splits=0, lse=None,

@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "mla.h"
 #include "internal.h"
@@ -495,6 +496,35 @@ int prefill_impl(const mla_dims* d, const mla_weights* w, const mla_paged_cache*
   return MLA_OK;
 }
 
+// ----------------------------------------------------------------------------- allocation-free decode
+// mla_decode_noalloc's scratch: one array per device, reserved when the code object loads there and
+// held until the process ends.  In host code `scratch` only names the symbol; its device address is
+// looked up once per device (with that device current) and used everywhere after that.
+constexpr size_t kNoAllocBytes = MLA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MLA_ERR_HIP;
+  if (dev >= kMaxDevices) return MLA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MLA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MLA_OK;
+}
+
+int decode_impl(const mla_dims* d, const mla_weights* w, const mla_paged_cache* c, const void* h, int32_t batch,
+                const int32_t* ctx_lens, int32_t max_ctx_len, int32_t num_splits, void* u, float* o_heads,
+                void* workspace, size_t ws_bytes, void* stream);
+
 }  // namespace
 
 extern "C" {
@@ -625,6 +655,25 @@ int mla_decode_attention(const mla_dims* d, const mla_paged_cache* c, const void
 int mla_decode(const mla_dims* d, const mla_weights* w, const mla_paged_cache* c, const void* h, int32_t batch,
                const int32_t* ctx_lens, int32_t max_ctx_len, int32_t num_splits, void* u, float* o_heads,
                void* workspace, size_t ws_bytes, void* stream) {
+  return decode_impl(d, w, c, h, batch, ctx_lens, max_ctx_len, num_splits, u, o_heads, workspace, ws_bytes, stream);
+}
+
+int mla_decode_noalloc(const mla_dims* d, const mla_weights* w, const mla_paged_cache* c, const void* h,
+                       int32_t batch, const int32_t* ctx_lens, int32_t max_ctx_len, int32_t num_splits, void* u,
+                       float* o_heads, void* stream) {
+  void* ws = nullptr;
+  const int st = noalloc_scratch(&ws);
+  if (st != MLA_OK) return st;
+  return decode_impl(d, w, c, h, batch, ctx_lens, max_ctx_len, num_splits, u, o_heads, ws, kNoAllocBytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int decode_impl(const mla_dims* d, const mla_weights* w, const mla_paged_cache* c, const void* h, int32_t batch,
+                const int32_t* ctx_lens, int32_t max_ctx_len, int32_t num_splits, void* u, float* o_heads,
+                void* workspace, size_t ws_bytes, void* stream) {
   int st = validate_dims(d);
   if (st != MLA_OK) return st;
   if ((st = validate_cache(d, c)) != MLA_OK) return st;
@@ -744,6 +793,10 @@ int mla_decode(const mla_dims* d, const mla_weights* w, const mla_paged_cache* c
   }
   return MLA_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 int mla_prefill(const mla_dims* d, const mla_weights* w, const mla_paged_cache* c, const void* h, int32_t batch,
                 int32_t T, void* u, float* o_heads, void* workspace, size_t ws_bytes, void* stream) {

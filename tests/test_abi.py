@@ -174,3 +174,13 @@ def test_workspace_for_max_sizes_serves_every_smaller_call():
     big = M.workspace_size(d, M.OP_DECODE, batch=4, max_ctx_len=131072, num_splits=7)
     for ctx in (1, 700, 22 * 32, 21 * 32, 131071):
         assert M.workspace_size(d, M.OP_DECODE, batch=4, max_ctx_len=ctx, num_splits=7) <= big
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define MLA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == M.NOALLOC_SCRATCH_BYTES
+    # the DeepSeek-V2 decode sizes the header promises fit
+    d = M.make_dims(5120, 128, 128, 512, 1536, 64, "bf16")
+    for B, ctx in ((64, 131072), (64, 8192), (4, 131072), (1, 131072)):
+        assert M.workspace_size(d, M.OP_DECODE, batch=B, max_ctx_len=ctx) <= M.NOALLOC_SCRATCH_BYTES, (B, ctx)
