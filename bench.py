@@ -33,17 +33,21 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    # the GPU's clocks take of the order of a hundred decode steps to settle; shorter warm-ups
-    # time the ramp (about 7% slower at 10 steps)
-    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    # After an idle spell the first few decode steps run fast and the next ~20 run 10-25% slower
+    # (the GPU's power management reacting to the burst) before the rate settles.  The steps are
+    # therefore run untimed for this long before the warm-up, so that the timed ones see the
+    # steady state whatever --warmup is; 0 disables it.
+    ap.add_argument("--settle-ms", type=float, default=300.0)
     ap.add_argument("--workload", default="v2_decode_b64_ctx8192")
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--replicas", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["attn", "copy"], default=None,
-                    help="profiling runs: only the attention core of the workload, or only a plain "
-                         "device copy of 1 GiB (the reference for HBM byte counters); prints one line")
+    ap.add_argument("--only", choices=["attn", "copy", "stream"], default=None,
+                    help="profiling runs: only the attention core of the workload, only a plain device copy "
+                         "of 1 GiB (the reference for HBM byte counters), or only the HBM streaming-ceiling "
+                         "probe (every variant); prints one line")
     return ap.parse_args()
 
 
@@ -65,6 +69,44 @@ def copy_only(args):
     ms = ev0.elapsed_time(ev1) / args.steps
     print(json.dumps({"only": "copy", "bytes_read": n, "bytes_written": n, "ms": round(ms, 5),
                       "GBps": round(2 * n / (ms / 1e3) / 1e9, 1)}))
+
+
+STREAM_BYTES = 2 << 30  # read passes over 2 GiB: eight times the 256 MB last-level cache
+STREAM_VARIANTS = {0: "regs x2", 1: "regs x4", 2: "regs x8", 3: "regs x16", 4: "lds ring 4", 5: "lds ring 8",
+                   6: "lds ring 16"}
+
+
+def stream_ceiling(variants=None, blocks=(256, 512, 1024, 2048), reps=5):
+    """Measured HBM read ceiling: the best GB/s over the probe's read-only passes (libmla_probe.so)
+    on a 2 GiB buffer, each configuration timed over `reps` passes after one untimed pass."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "mla_latent_kv_27_amd", "lib", "libmla_probe.so"))
+    lib.mla_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_void_p, ctypes.c_void_p]
+    lib.mla_probe_stream_read.restype = ctypes.c_int
+    buf = torch.empty(STREAM_BYTES, dtype=torch.uint8, device="cuda").fill_(3)
+    sink = torch.empty(max(blocks), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    res = {}
+    for v in (variants if variants is not None else STREAM_VARIANTS):
+        for nb in blocks:
+            def run():
+                rc = lib.mla_probe_stream_read(buf.data_ptr(), STREAM_BYTES, v, nb, sink.data_ptr(), stream.cuda_stream)
+                if rc != 0:
+                    raise RuntimeError(f"stream probe variant {v} blocks {nb}: status {rc}")
+            run()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                run()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            res[f"{STREAM_VARIANTS[v]}, {nb} blocks"] = round(STREAM_BYTES / (ms / 1e3) / 1e9, 1)
+    del buf
+    best = max(res, key=res.get)
+    return {"GBps": res[best], "best": best, "bytes_per_pass": STREAM_BYTES, "all": res}
 
 
 def entry_bytes(dims, cache="native"):
@@ -282,6 +324,11 @@ def main():
     if args.only == "copy":
         copy_only(args)
         return
+    if args.only == "stream":
+        import torch
+        torch.cuda.set_device(0)
+        print(json.dumps({"only": "stream", **stream_ceiling()}))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported: the library has no "
               f"multi-GPU path (decode shards by batch, one independent process per GPU)", file=sys.stderr)
@@ -329,23 +376,46 @@ def main():
             return f"auto (balanced units, up to {min(128, 2 * n)} partitions per sequence)"
         return f"auto ({n} partitions per sequence)"
 
-    def attn(i):
-        M.decode_attention(layer.cdims, reps[i % len(reps)][1].ccache, q, kv, max_ctx + 1, ohat, wss[0],
-                           num_splits=splits, stream=stream)
+    # the attention kernel alone, as the step runs it: the KV partitions of the step's automatic
+    # choice (fixed partitions; a small batch's step balances them over its lengths instead), left
+    # as partials (the step combines them inside the W_UV kernel)
+    att_splits = splits if splits > 0 else M.auto_splits(layer.cdims, B, max_ctx)
+    pm = torch.empty((B, att_splits, dims.n_h), dtype=torch.float32, device="cuda")
+    pl = torch.empty_like(pm)
+    po = torch.empty((B, att_splits, dims.n_h, dims.d_c), dtype=torch.bfloat16, device="cuda")
 
-    def timed(fn):
+    def attn(i):
+        M.decode_attention_partials(layer.cdims, reps[i % len(reps)][1].ccache, q, kv, max_ctx + 1, att_splits,
+                                    pm, pl, po, stream=stream)
+
+    def settle(fn):
+        """Untimed steps for --settle-ms of wall time; returns how many ran."""
+        n, t_end = 0, time.perf_counter() + args.settle_ms / 1e3
+        while time.perf_counter() < t_end:
+            for _ in range(32):
+                fn(n)
+                n += 1
+            torch.cuda.synchronize()
+        return n
+
+    def timed(fn, per_step=None):
+        """Mean ms over exactly --steps calls after --warmup untimed ones (events on the stream the
+        kernels run on, synchronised on both sides); per_step (a list) receives each call's ms."""
         for i in range(args.warmup):
             fn(i)
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        ev[0].record(stream)
         for i in range(args.steps):
             fn(i)
-        e1.record(stream)
+            ev[i + 1].record(stream)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / args.steps
+        if per_step is not None:
+            per_step.extend(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
+        return ev[0].elapsed_time(ev[-1]) / args.steps
 
     if args.only == "attn":
+        settle(attn)
         attn_ms = timed(attn)
         print(json.dumps({"only": "attn", "workload": w.name, "num_splits": splits, "ms": round(attn_ms, 5),
                           "algorithmic_bytes": attn_core_bytes(dims, lens, B, w.cache)}))
@@ -356,10 +426,14 @@ def main():
         M.decode(ly.cdims, ly.cweights, pl.ccache, h, ctx, max_ctx, outs[i % len(reps)], wss[i % len(reps)],
                  num_splits=splits, stream=stream)
 
-    ms = timed(step)
+    settled = settle(step)
+    per_step = []
+    ms = timed(step, per_step)
     value = B / (ms / 1e3)
     # dominant kernel: the latent attention core, timed on the same stream
+    settle(attn)
     attn_ms = timed(attn)
+    ceiling = stream_ceiling(variants=(2, 3), blocks=(256,), reps=5)
     core_bytes = attn_core_bytes(dims, lens, B, w.cache)
     achieved = core_bytes / (attn_ms / 1e3) / 1e9
     traffic = counters_for("decode_attn.hip", args.workload)
@@ -392,14 +466,21 @@ def main():
                    "cache": "fp8_e4m3 (per-token scales)" if fp8 else dims.dtype,
                    "latent_rmsnorm": bool(dims.latent_norm),
                    "yarn_scale": float(dims.rope_scale) if dims.rope_scale > 1 else None},
+        "settle_steps": settled,
+        "step_ms_p10_p50_p90": [round(float(np.percentile(per_step, x)), 5) for x in (10, 50, 90)],
         "step_GBps": round(step_bytes / (ms / 1e3) / 1e9, 1),
         "step_hbm_frac": round(step_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
         "step_bytes": step_bytes,
         "step_TFLOPs": round((attn_f + proj_f) / (ms / 1e3) / 1e12, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "kernel": "decode latent attention (+ split-KV combine when num_splits > 1)",
+                     "kernel": f"{'decode_attn_fp8_kernel' if fp8 else 'decode_attn_tiled_kernel'} "
+                               f"(mla_decode_attention_partials, {att_splits} KV "
+                               f"partitions per sequence, partials left for the W_UV kernel as in the step)",
                      "kernel_ms": round(attn_ms, 5), "algorithmic_bytes": core_bytes,
+                     "measured_peak": ceiling["GBps"],
+                     "frac_of_measured": round(achieved / ceiling["GBps"], 4),
+                     "measured_peak_probe": f"best read-only pass over {STREAM_BYTES >> 30} GiB ({ceiling['best']})",
                      "mfma_TFLOPs": round(attn_f / (attn_ms / 1e3) / 1e12, 1),
                      "mfma_frac": round(attn_f / (attn_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
         "cpu_baseline": cpu,

@@ -249,6 +249,32 @@ int mla_decode_attention(const mla_dims *dims, const mla_paged_cache *cache, con
                          int32_t num_splits, void *o_hat, float *lse, void *workspace,
                          size_t ws_bytes, void *stream);
 
+/*
+ * The decode attention core without the reduction of its KV partitions: the attention kernel that
+ * mla_decode runs, with each partition's result left in caller buffers.  For callers that reduce
+ * the partitions themselves (e.g. GPUs that hold different page ranges of one sequence, each
+ * contributing its partitions to one log-sum-exp reduction), and for timing the kernel alone.
+ *   q, kv_lens, max_kv_len: as mla_decode_attention.
+ *   num_splits (host) >= 1: the partition length is ceil(ceil(max_kv_len / 64) / num_splits) * 64
+ *             tokens; partition p of sequence b covers its tokens [p * length, (p + 1) * length).
+ *   *splits_out (host): P, the number of partitions (<= num_splits); the buffers below hold
+ *             batch * P rows of n_h heads.
+ *   part_m    [batch][P][n_h] fp32: a reference for the partition's scores x_j = scale * log2(e) *
+ *             (q . entry_j), within 8 of their maximum: max_j x_j - 8 <= part_m <= max_j x_j
+ *             (-inf for a partition with no tokens);
+ *   part_l    [batch][P][n_h] fp32: sum_j 2^(x_j - part_m);
+ *   part_o    [batch][P][n_h][d_c] bf16: sum_j 2^(x_j - part_m) c^KV_j / part_l (the partition's
+ *             normalised output; not written for a partition with no tokens).
+ *   The combined result is o_hat = sum_p w_p part_o_p / sum_p w_p with w_p = 2^(part_m_p - M)
+ *   part_l_p, M = max_p part_m_p.
+ * Requires dims->dtype MLA_BF16, d_c 512, d_hr 64 and block_size a multiple of 32 (else
+ * MLA_ERR_UNSUPPORTED).  Needs no workspace.
+ */
+int mla_decode_attention_partials(const mla_dims *dims, const mla_paged_cache *cache, const void *q,
+                                  int32_t batch, const int32_t *kv_lens, int32_t max_kv_len,
+                                  int32_t num_splits, float *part_m, float *part_l, void *part_o,
+                                  int32_t *splits_out, void *stream);
+
 /* The split count mla_decode uses for num_splits == 0 with fixed partitions (host query; -1 on
  * invalid sizes).  Small batches with num_splits == 0 use up to twice as many partition slots,
  * balanced over the actual context lengths (see mla_decode). */

@@ -25,7 +25,8 @@ OP_CACHE_APPEND, OP_PREFILL, OP_DECODE, OP_PREFILL_CHUNK = 0, 1, 2, 3
 
 EXPORTED = (
     "mla_workspace_size", "mla_cache_append", "mla_prefill", "mla_prefill_chunk", "mla_decode", "mla_decode_noalloc",
-    "mla_decode_attention", "mla_decode_auto_splits", "mla_quantize_entries", "mla_status_string",
+    "mla_decode_attention", "mla_decode_attention_partials", "mla_decode_auto_splits", "mla_quantize_entries",
+    "mla_status_string",
 )
 # bytes of the library's own scratch behind mla_decode_noalloc (MLA_NOALLOC_SCRATCH_BYTES)
 NOALLOC_SCRATCH_BYTES = 192 << 20
@@ -76,6 +77,7 @@ def lib() -> ctypes.CDLL:
         L.mla_decode.argtypes = [D, W, C, P, I32, P, I32, I32, P, P, P, SZ, P]
         L.mla_decode_noalloc.argtypes = [D, W, C, P, I32, P, I32, I32, P, P, P]
         L.mla_decode_attention.argtypes = [D, C, P, I32, P, I32, I32, P, P, P, SZ, P]
+        L.mla_decode_attention_partials.argtypes = [D, C, P, I32, P, I32, I32, P, P, P, ctypes.POINTER(I32), P]
         L.mla_decode_auto_splits.argtypes = [D, I32, I32]
         L.mla_quantize_entries.argtypes = [D, P, I32, P, P, P]
         L.mla_quantize_entries.restype = ctypes.c_int
@@ -83,7 +85,7 @@ def lib() -> ctypes.CDLL:
         L.mla_status_string.argtypes = [ctypes.c_int]
         L.mla_status_string.restype = ctypes.c_char_p
         for n in ("mla_workspace_size", "mla_cache_append", "mla_prefill", "mla_prefill_chunk", "mla_decode",
-                  "mla_decode_noalloc", "mla_decode_attention"):
+                  "mla_decode_noalloc", "mla_decode_attention", "mla_decode_attention_partials"):
             getattr(L, n).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -192,6 +194,18 @@ def decode_attention(dims, cache, q, kv_lens, max_kv_len, o_hat, workspace, num_
     _check(lib().mla_decode_attention(ctypes.byref(dims), ctypes.byref(cache), _ptr(q), int(q.shape[0]),
                                       _ptr(kv_lens), int(max_kv_len), int(num_splits), _ptr(o_hat), _ptr(lse),
                                       p, n, _stream(stream)), "mla_decode_attention")
+
+
+def decode_attention_partials(dims, cache, q, kv_lens, max_kv_len, num_splits, part_m, part_l, part_o,
+                              stream=None) -> int:
+    """The attention core's per-partition (max, sum, normalised output) without their reduction;
+    buffers sized for num_splits partitions; returns the number of partitions P."""
+    out = ctypes.c_int32(0)
+    _check(lib().mla_decode_attention_partials(ctypes.byref(dims), ctypes.byref(cache), _ptr(q), int(q.shape[0]),
+                                               _ptr(kv_lens), int(max_kv_len), int(num_splits), _ptr(part_m),
+                                               _ptr(part_l), _ptr(part_o), ctypes.byref(out), _stream(stream)),
+           "mla_decode_attention_partials")
+    return int(out.value)
 
 
 def quantize_entries(dims, entries, codes, scales, stream=None):

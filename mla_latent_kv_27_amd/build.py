@@ -26,6 +26,8 @@ FLAGS = [
     # packed fp32 ALU forms stay off: the compiler emits plain fp32 arithmetic
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
+    # the decode kernel sets M0 (the LDS destination of its copies) inside one asm statement
+    "-Wno-inline-asm",
 ]
 
 

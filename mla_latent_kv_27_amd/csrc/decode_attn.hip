@@ -294,7 +294,7 @@ constexpr int kRow = kCPR * 16;           // 1152 bytes per entry
 constexpr int kBytes = kT * kRow;         // 36864 per buffer
 constexpr int kWaves = 8;
 constexpr int kDmaTotal = kT * kCPR / 64;  // 36 one-KiB copies per tile: waves 0-3 issue 5, 4-7 issue 4
-__device__ __forceinline__ int dma_count(int w) { return w < 4 ? 5 : 4; }
+constexpr int kDmaPerWave = 5;             // copy instructions per wave and tile (4-7: one reads nothing)
 __device__ __forceinline__ int dma_first(int w) { return w < 4 ? 5 * w : 20 + 4 * (w - 4); }
 constexpr float kLazy = 8.f;              // log2 headroom before a rescale
 }  // namespace tiled
@@ -316,28 +316,53 @@ struct TiledCtx {
   int bs, kv_len;
 };
 
-// This wave's share (5 or 4) of the 36 direct-to-LDS copies of tile `tile` into buffer BUF.  block_size is a multiple
-// of the tile size, so a tile lies inside one block: one uniform block-table lookup, and every row copied
-// is a row of an allocated block (rows past the context are zeroed once the copies land).
+// This wave's share of the 36 direct-to-LDS copies of tile `tile` into buffer BUF: waves 0-3 copy
+// five 1-KiB pieces, waves 4-7 four plus a fifth that reads nothing (its offset is past the
+// resource) into a slot of their own, so that every wave issues the same five copies per tile and
+// a wait counts whole tiles.  block_size is a multiple of the tile size, so a tile lies inside one
+// block: one uniform block-table lookup, and every row copied is a row of an allocated block (rows
+// past the context are zeroed once the copies land).  A tile past the partition (live == false)
+// gets the same five copies, all reading nothing, so the count stays the same.
+__shared__ __attribute__((aligned(1024))) char g_dma_sink[4][1024];
+
+// The copy itself, written as one asm statement (M0 = the LDS destination): the compiler then does
+// not treat the ring's fragment reads as possibly waiting on these copies (with more copies in
+// flight than it tracks it would wait for most of them before every read).  The waits on them are
+// the kernel's own: each step waits until its tile's copies have landed, and nothing is read from
+// a buffer whose copies are still in flight; after the loop every copy is waited for.
+__device__ __forceinline__ void dma16_ring(__amdgpu_buffer_rsrc_t span, uint32_t off, const void* lds_dst) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds_dst;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(off), "s"(span), "s"(m0)
+               : "memory", "m0");
+}
+
 template <int BUF>
-__device__ __forceinline__ void issue_tile(const TiledCtx& c, int tile, int w, int lane) {
+__device__ __forceinline__ void issue_tile(const TiledCtx& c, int tile, bool live, int w, int lane) {
   using namespace tiled;
   char* dst = kv_buf<BUF>();
   const int tok0 = tile * kT;
   const int blk = tok0 / c.bs;
-  const char* base = c.pool + ((int64_t)c.bt[blk] * c.bs + (tok0 - blk * c.bs)) * kRow;
+  const char* base = c.pool + ((int64_t)c.bt[live ? blk : 0] * c.bs + (tok0 - blk * c.bs)) * kRow;
   int ln = lane;
   asm volatile("" : "+v"(ln));  // recompute the lane offsets here instead of keeping them live
-  const int first = dma_first(w), cnt = dma_count(w);
-  const __amdgpu_buffer_rsrc_t span = dma_span(base, kBytes);  // the tile: 32 consecutive rows
+  const int first = dma_first(w);
+  const __amdgpu_buffer_rsrc_t span = dma_span(base, live ? kBytes : 0);  // the tile: 32 consecutive rows
 #pragma unroll
-  for (int i = 0; i < 5; ++i) {
-    if (i < cnt) {
-      const int P = (first + i) * 64 + ln;
-      const int t = P / kCPR;
-      const int ch = (P - t * kCPR) ^ (t & 7);
-      dma16(span, t * kRow + ch * 16, (lds_void_t*)(dst + (first + i) * 1024));
-    }
+  for (int i = 0; i < 4; ++i) {
+    const int P = (first + i) * 64 + ln;
+    const int t = P / kCPR;
+    const int ch = (P - t * kCPR) ^ (t & 7);
+    dma16_ring(span, t * kRow + ch * 16, dst + (first + i) * 1024);
+  }
+  if (w < 4) {
+    const int P = (first + 4) * 64 + ln;
+    const int t = P / kCPR;
+    const int ch = (P - t * kCPR) ^ (t & 7);
+    dma16_ring(span, t * kRow + ch * 16, dst + (first + 4) * 1024);
+  } else {
+    dma16_ring(span, kBytes + ln * 16, &g_dma_sink[w - 4][0]);
   }
 }
 
@@ -382,9 +407,33 @@ __device__ __forceinline__ void tiled_pv(TiledState& st, const Frag8<bf16>& pf, 
   }
 }
 
+// ---- the bf16 kernel: S by head, P.V by latent column
+// The S^T = K Q^T product stays with the head's wave (Q is register-resident), but P.V is split by
+// latent columns: wave w accumulates O^T for dims 64w .. 64w+63 of all the workgroup's heads.  Its
+// A operand (V^T, 16 dims x 32 tokens) is then read once per tile and feeds one MFMA per 16-head
+// block, and each B operand (P^T, 32 tokens x 16 heads) one MFMA per 16-dim block, instead of every
+// wave reading the whole tile for its own 16 heads.  The probabilities cross waves through LDS, in
+// the B-operand layout: the S^T accumulators of lane (g, l16) hold head l16 at tokens
+// 16 (s/4) + 4g + s%4, which is exactly that lane's B fragment, so a wave stores its 16-byte
+// fragment at [g][head] and the P.V waves read it back with one 16-byte read per head block.
+// A raised softmax reference changes the scale of O rows that live in every wave: the S wave
+// publishes the factors of its heads and a per-wave flag with the probabilities, and the P.V waves
+// apply them before adding the tile (rare: the reference only moves by more than 2^8).
+__shared__ __attribute__((aligned(1024))) char g_pex[4 * 128 * 16];  // [lane group][head][8 bf16]
+__shared__ float g_alpha[128];                                        // factor of a raised reference
+__shared__ __attribute__((aligned(8))) unsigned char g_rescaled[8];  // per wave: factors published
+
+struct SplitState {
+  floatx4 o[4][8];  // O^T: latent dims 16 (4w + db) + 4g + j of head 16 hb + l16
+  float m_ref;      // S side: reference max of head 16w + l16 (log2 domain), shared by its lanes
+  float l_part;     // S side: this lane's partial normaliser
+};
+
+// S^T for this wave's 16 heads over the tile in buffer BUF, the lazy softmax, and the
+// probabilities (with the factors of a raised reference) published for the P.V waves.
 template <int BUF>
-__device__ __forceinline__ void tiled_compute(const Frag8<bf16> (&q)[18], TiledState& st, int t, int kv_len,
-                                              float scale_log2, int lane) {
+__device__ __forceinline__ void sp_scores(const Frag8<bf16> (&q)[18], SplitState& st, int t, int kv_len,
+                                          float scale_log2, int w, int lane) {
   using namespace tiled;
   const char* buf = kv_buf<BUF>();
   // the lane's LDS offsets are recomputed in every step (a few integer ops) rather than kept live
@@ -399,22 +448,22 @@ __device__ __forceinline__ void tiled_compute(const Frag8<bf16> (&q)[18], TiledS
     const int x = l16 & 7;
     const char* rb0 = buf + l16 * kRow + ((g) ^ x) * 16;
     const char* rb1 = buf + l16 * kRow + ((4 + g) ^ x) * 16;
-    Frag8<bf16> a[3][2];  // [stage][tb]: fragments two k-chunks ahead are in flight
+    Frag8<bf16> a[2][2];  // [stage][tb]: the next k-chunk's fragments are in flight
 #pragma unroll
-    for (int k0 = 0; k0 < 2; ++k0) {
-      const char* pn = (k0 & 1 ? rb1 : rb0);
+    for (int k0 = 0; k0 < 1; ++k0) {
+      const char* pn = rb0;
       a[k0][0].v = *reinterpret_cast<const bf16x8*>(pn);
       a[k0][1].v = *reinterpret_cast<const bf16x8*>(pn + 16 * kRow);
     }
 #pragma unroll
     for (int kc = 0; kc < 18; ++kc) {
-      if (kc + 2 < 18) {
-        const char* pn = ((kc + 2) & 1 ? rb1 : rb0) + 128 * ((kc + 2) >> 1);
-        a[(kc + 2) % 3][0].v = *reinterpret_cast<const bf16x8*>(pn);
-        a[(kc + 2) % 3][1].v = *reinterpret_cast<const bf16x8*>(pn + 16 * kRow);
+      if (kc + 1 < 18) {
+        const char* pn = ((kc + 1) & 1 ? rb1 : rb0) + 128 * ((kc + 1) >> 1);
+        a[(kc + 1) & 1][0].v = *reinterpret_cast<const bf16x8*>(pn);
+        a[(kc + 1) & 1][1].v = *reinterpret_cast<const bf16x8*>(pn + 16 * kRow);
       }
-      sc[0] = mma16(a[kc % 3][0], q[kc], sc[0]);
-      sc[1] = mma16(a[kc % 3][1], q[kc], sc[1]);
+      sc[0] = mma16(a[kc & 1][0], q[kc], sc[0]);
+      sc[1] = mma16(a[kc & 1][1], q[kc], sc[1]);
     }
   }
   // ---- lazy online softmax
@@ -429,51 +478,111 @@ __device__ __forceinline__ void tiled_compute(const Frag8<bf16> (&q)[18], TiledS
       sc[tb][j] = v;
       lmax = fmaxf(lmax, v);
     }
+  unsigned char raised = 0;
   if (__builtin_amdgcn_ballot_w64(lmax > st.m_ref + kLazy) != 0) {  // rare: raise the reference
     float hmax = wave_max_xor(lmax, 16);
     hmax = wave_max_xor(hmax, 32);
     const float m_new = fmaxf(st.m_ref, hmax);
     const float alpha = __builtin_amdgcn_exp2f(st.m_ref - m_new);  // -inf -> 0
     st.l_part *= alpha;
-#pragma unroll
-    for (int d = 0; d < 32; ++d) st.o[d] *= alpha;
+    // before the first reference no O row holds anything: nothing to rescale
+    if (__builtin_amdgcn_ballot_w64(st.m_ref != -INFINITY) != 0) {
+      if (g == 0) g_alpha[16 * w + l16] = alpha;
+      raised = 1;
+    }
     st.m_ref = m_new;
   }
-  Frag8<bf16> pf;  // slot s = token 16 (s/4) + 4g + s%4
+  if (lane == 0) g_rescaled[w] = raised;
+  bf16x8 pf;  // slot s = token 16 (s/4) + 4g + s%4
 #pragma unroll
   for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const bf16 e = (bf16)__builtin_amdgcn_exp2f(sc[tb][j] - st.m_ref);  // argument <= 8
       st.l_part += (float)e;
-      pf.v[tb * 4 + j] = e;
+      pf[tb * 4 + j] = e;
     }
-  tiled_pv<BUF>(st, pf, lane);
+  *reinterpret_cast<bf16x8*>(g_pex + ((g * 128) + 16 * w + l16) * 16) = pf;
 }
 
-// Two tiles per barrier: tiles t and t+1 sit in ring buffers B0 and B0+1 (B0 = 0 or 2), and the
-// only copies in flight are theirs.  Once they have landed and every wave is past the previous
-// pair, the copies of tiles t+2 and t+3 go into the other two buffers, then both tiles are
-// multiplied.  Half as many workgroup barriers as one per tile, and no pipeline drain between the
-// two tiles of a pair.
-template <int B0>
-__device__ __forceinline__ void tiled_pair(const TiledCtx& c, const Frag8<bf16> (&q)[18], TiledState& st, int t,
-                                           int t_end, float scale_log2, int w, int lane, int tid) {
+// O^T += V^T P^T for this wave's 64 latent dims and the nhb head blocks, over the tile in buffer
+// BUF; first the factors of any reference raised in this tile.
+template <int BUF, bool FULL>
+__device__ __forceinline__ void sp_pv(SplitState& st, int nhb_rt, int w, int lane) {
+  const int nhb = FULL ? 8 : nhb_rt;  // FULL: every head block of the group is present
   using namespace tiled;
-  MLA_TILE_BARRIER(waitcnt_vm(0));
-  if (t + 2 < t_end) issue_tile<(B0 + 2) % kNBuf>(c, t + 2, w, lane);
-  if (t + 3 < t_end) issue_tile<(B0 + 3) % kNBuf>(c, t + 3, w, lane);
-  const int last = min(t + 1, t_end - 1);  // only the sequence's last tile can be partial
-  const int valid = c.kv_len - last * kT;
-  if (valid < kT) {  // zero the rows past the end of the context (uniform branch)
-    char* buf = last == t ? kv_buf<B0>() : kv_buf<B0 + 1>();
+  const char* buf = kv_buf<BUF>();
+  asm volatile("" : "+v"(lane));
+  const int g = lane >> 4, l16 = lane & 15;
+  const uint64_t raised = *reinterpret_cast<const uint64_t*>(g_rescaled);
+  if (raised != 0) {  // rare, uniform
+#pragma unroll
+    for (int hb = 0; hb < 8; ++hb) {
+      if (hb < nhb && ((raised >> (8 * hb)) & 0xff)) {
+        const float a = g_alpha[16 * hb + l16];
+#pragma unroll
+        for (int db = 0; db < 4; ++db) st.o[db][hb] *= a;
+      }
+    }
+  }
+  // V^T fragments of dim blocks 4w .. 4w+3 (16 dims x 32 tokens each): lane group g reads tokens
+  // 4g + s/4 (+16 for the second read); source lane s supplies dims 16 d + 4 (s % 4) .. +3 = chunk
+  // 2d + (s%4)/2, byte (s % 2) * 8 of its token row, stored at slot chunk ^ (token & 7)
+  const int x = (4 * g + (l16 >> 2)) & 7;
+  const int clo = (l16 & 3) >> 1;
+  const char* row = buf + (4 * g + (l16 >> 2)) * kRow + (l16 & 1) * 8;
+  Frag8<bf16> va[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    const char* pv = row + ((2 * (4 * w + db) + clo) ^ x) * 16;
+    const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)pv);
+    const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)(pv + 16 * kRow));
+    va[db].v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+  // P^T fragments four head blocks at a time (the scheduler barrier keeps the second group's reads
+  // from being hoisted, which would need registers the queries and O occupy)
+  const char* pb = g_pex + (g * 128 + l16) * 16;
+#pragma unroll
+  for (int hq = 0; hq < 2; ++hq) {
+    Frag8<bf16> pf[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (FULL || 4 * hq + i < nhb) pf[i].v = *reinterpret_cast<const bf16x8*>(pb + 256 * (4 * hq + i));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (FULL || 4 * hq + i < nhb)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) st.o[db][4 * hq + i] = mma16(va[db], pf[i], st.o[db][4 * hq + i]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// One tile (in ring buffer BUF): wait until it has landed, this wave's copies of the two tiles
+// after it may still be in flight (waves 0-3 issue 5 copies per tile, 4-7 issue 4) and every
+// wave is done with the previous tile, whose buffer then takes tile t + 3.  Rows past the end of
+// the context are zeroed (only the sequence's last tile can be partial).  Then the S waves publish
+// the tile's probabilities and, after a second barrier, every wave adds its share of P.V.
+template <int BUF, bool FULL>
+__device__ __forceinline__ void sp_step(const TiledCtx& c, const Frag8<bf16> (&q)[18], SplitState& st, int t,
+                                        int t_end, float scale_log2, bool s_wave, int nhb, int w, int lane,
+                                        int tid) {
+  using namespace tiled;
+  // every wave has five copies per tile in flight: tile t has landed when at most those of the two
+  // tiles after it are outstanding
+  MLA_TILE_BARRIER(waitcnt_vm(2 * kDmaPerWave));
+  issue_tile<(BUF + 3) % kNBuf>(c, t + 3, t + 3 < t_end, w, lane);
+  const int valid = c.kv_len - t * kT;
+  if (valid < kT) {  // uniform
+    char* buf = kv_buf<BUF>();
     for (int i = tid; i < (kT - valid) * kCPR; i += 64 * kWaves) st16(buf + (valid * kCPR + i) * 16, zero16());
     MLA_TILE_BARRIER(kWaitLgkm0);
   }
-  tiled_compute<B0>(q, st, t, c.kv_len, scale_log2, lane);
-  if (t + 1 < t_end) tiled_compute<B0 + 1>(q, st, t + 1, c.kv_len, scale_log2, lane);
+  if (s_wave) sp_scores<BUF>(q, st, t, c.kv_len, scale_log2, w, lane);
+  MLA_TILE_BARRIER(kWaitLgkm0);  // the tile's probabilities, factors and flags are visible
+  sp_pv<BUF, FULL>(st, nhb, w, lane);
 }
 
+template <bool FULL>
 __global__ void __launch_bounds__(512)
     decode_attn_tiled_kernel(DecodeAttnParams p, int HG, const int32_t* __restrict__ block_table) {
   using namespace tiled;
@@ -496,9 +605,21 @@ __global__ void __launch_bounds__(512)
   }
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = lane >> 4;
-  const int head = hg * (16 * kWaves) + w * 16 + (lane & 15);
+  const int g = lane >> 4, l16 = lane & 15;
+  const int h0 = hg * (16 * kWaves);                  // the head group's first head
+  const int nhb = min(kWaves, (p.n_h - h0 + 15) / 16);  // its 16-head blocks
+  const bool s_wave = w < nhb;                        // this wave computes S for heads h0 + 16w ..
+  const int head = h0 + w * 16 + l16;
   const bool valid_head = head < p.n_h;
+
+  if (t_begin >= t_end) {  // an empty partition: only its max (-inf), which the combines skip
+    if (s_wave && valid_head && g == 0 && (p.splits > 1 || p.leave_partials)) {
+      const int64_t pi = ((int64_t)b * p.splits + split) * p.n_h + head;
+      p.part_m[pi] = -INFINITY;
+      p.part_l[pi] = 0.f;
+    }
+    return;
+  }
 
   TiledCtx c;
   c.pool = reinterpret_cast<const char*>(p.pool);
@@ -511,57 +632,69 @@ __global__ void __launch_bounds__(512)
     const bf16* qrow = reinterpret_cast<const bf16*>(p.q) + ((int64_t)b * p.n_h + (valid_head ? head : 0)) * kD;
 #pragma unroll
     for (int kc = 0; kc < 18; ++kc) {
-      if (valid_head) load8(q[kc], qrow + kc * 32 + 8 * g);
+      if (s_wave && valid_head) load8(q[kc], qrow + kc * 32 + 8 * g);
       else zero8(q[kc]);
     }
   }
-  TiledState st;
+  SplitState st;
 #pragma unroll
-  for (int d = 0; d < 32; ++d) st.o[d] = floatx4{0, 0, 0, 0};
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int hb = 0; hb < 8; ++hb) st.o[db][hb] = floatx4{0, 0, 0, 0};
   st.m_ref = -INFINITY;
   st.l_part = 0.f;
+  if (tid < kWaves) g_rescaled[tid] = 0;  // waves without heads never publish
+  // the queries first: with them still in flight the compiler would wait for every copy of the
+  // ring before the first tile
+  MLA_WAVE_WAIT(waitcnt_vm(0));
 
-  if (t_begin < t_end) issue_tile<0>(c, t_begin, w, lane);
-  if (t_begin + 1 < t_end) issue_tile<1>(c, t_begin + 1, w, lane);
+  issue_tile<0>(c, t_begin, true, w, lane);
+  issue_tile<1>(c, t_begin + 1, t_begin + 1 < t_end, w, lane);
+  issue_tile<2>(c, t_begin + 2, t_begin + 2 < t_end, w, lane);
   for (int t = t_begin; t < t_end; t += kNBuf) {
-    tiled_pair<0>(c, q, st, t, t_end, p.scale_log2, w, lane, tid);
-    if (t + 2 < t_end) tiled_pair<2>(c, q, st, t + 2, t_end, p.scale_log2, w, lane, tid);
+    sp_step<0, FULL>(c, q, st, t, t_end, p.scale_log2, s_wave, nhb, w, lane, tid);
+    if (t + 1 < t_end) sp_step<1, FULL>(c, q, st, t + 1, t_end, p.scale_log2, s_wave, nhb, w, lane, tid);
+    if (t + 2 < t_end) sp_step<2, FULL>(c, q, st, t + 2, t_end, p.scale_log2, s_wave, nhb, w, lane, tid);
+    if (t + 3 < t_end) sp_step<3, FULL>(c, q, st, t + 3, t_end, p.scale_log2, s_wave, nhb, w, lane, tid);
   }
+  // the copies past the partition (reading nothing) must land before the LDS is released
+  MLA_WAVE_WAIT(waitcnt_vm(0));
   // the four lane groups of a head hold partial sums over different tokens
   float l_run = wave_sum_xor(st.l_part, 16);
   l_run = wave_sum_xor(l_run, 32);
   const float m_run = st.m_ref;
-
-  if (!valid_head) return;
-  if (p.splits == 1) {
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    bf16* out = reinterpret_cast<bf16*>(p.o_hat) + ((int64_t)b * p.n_h + head) * kDC;
-#pragma unroll
-    for (int d = 0; d < 32; ++d) {
-      bf16x4 v;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = (bf16)(st.o[d][r] * inv);
-      *reinterpret_cast<bf16x4*>(out + d * 16 + 4 * g) = v;
+  MLA_TILE_BARRIER(kWaitLgkm0);  // every wave is done with the last tile's probabilities
+  float* inv_l = reinterpret_cast<float*>(g_pex);  // [head - h0]: 1 / l
+  if (s_wave && g == 0) inv_l[16 * w + l16] = l_run > 0.f ? 1.f / l_run : 0.f;
+  const bool partial = p.splits > 1 || p.leave_partials;  // else o_hat (and lse) directly
+  if (s_wave && valid_head && g == 0) {
+    if (!partial) {
+      if (p.lse) p.lse[(int64_t)b * p.n_h + head] = (m_run + log2f(l_run)) * 0.69314718055994531f;
+    } else {
+      const int64_t pi = ((int64_t)b * p.splits + split) * p.n_h + head;
+      p.part_m[pi] = m_run;
+      p.part_l[pi] = l_run;
     }
-    if (p.lse && g == 0) p.lse[(int64_t)b * p.n_h + head] = (m_run + log2f(l_run)) * 0.69314718055994531f;
-    return;
   }
-  const int64_t pi = ((int64_t)b * p.splits + split) * p.n_h + head;
-  if (g == 0) {
-    p.part_m[pi] = m_run;
-    p.part_l[pi] = l_run;
-  }
-  if (t_begin >= t_end) return;  // an empty partition: the combines skip it by its max (-inf)
-  // the partition's normalised output O_s / l_s (a convex combination of latent values) in bf16:
-  // half the partial traffic of fp32 for one more rounding of 2^-9 relative
-  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-  bf16* po = reinterpret_cast<bf16*>(p.part_o) + pi * kDC;
+  MLA_TILE_BARRIER(kWaitLgkm0);
+  // the normalised rows O / l (with several partitions, the partition's own O_s / l_s: a convex
+  // combination of latent values, stored in bf16 for half the partial traffic of fp32)
 #pragma unroll
-  for (int d = 0; d < 32; ++d) {
-    bf16x4 v;
+  for (int hb = 0; hb < 8; ++hb) {
+    const int hh = h0 + 16 * hb + l16;
+    if (hb < nhb && hh < p.n_h) {
+      const float inv = inv_l[16 * hb + l16];
+      bf16* out = !partial
+                      ? reinterpret_cast<bf16*>(p.o_hat) + ((int64_t)b * p.n_h + hh) * kDC
+                      : reinterpret_cast<bf16*>(p.part_o) + (((int64_t)b * p.splits + split) * p.n_h + hh) * kDC;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) v[r] = (bf16)(st.o[d][r] * inv);
-    *reinterpret_cast<bf16x4*>(po + d * 16 + 4 * g) = v;
+      for (int db = 0; db < 4; ++db) {
+        bf16x4 v;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = (bf16)(st.o[db][hb][r] * inv);
+        *reinterpret_cast<bf16x4*>(out + 16 * (4 * w + db) + 4 * g) = v;
+      }
+    }
   }
 }
 
@@ -974,7 +1107,7 @@ __global__ void __launch_bounds__(512)
 
   if (!valid_head) return;
   const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-  if (p.splits == 1) {
+  if (p.splits == 1 && !p.leave_partials) {
     bf16* out = reinterpret_cast<bf16*>(p.o_hat) + ((int64_t)b * p.n_h + head) * 512;
 #pragma unroll
     for (int d = 0; d < 32; ++d) {
@@ -1067,8 +1200,12 @@ hipError_t decode_attention(DType t, const DecodeAttnParams& p, hipStream_t s) {
     if (p.units) hipLaunchKernelGGL(decode_units_kernel, dim3(1), dim3(256), 0, s, p);
     const int units = p.B * p.splits + (p.units ? p.B : 0);  // with a table: + B idle entries
     const int blocks = (units + 7) / 8 * 8 * HG;
-    hipLaunchKernelGGL(decode_attn_tiled_kernel, dim3(blocks), dim3(64 * tiled::kWaves), 0, s, p, HG,
-                       p.block_table);
+    if (p.n_h % (16 * tiled::kWaves) == 0)  // every head group full: the P.V loop needs no guards
+      hipLaunchKernelGGL(decode_attn_tiled_kernel<true>, dim3(blocks), dim3(64 * tiled::kWaves), 0, s, p, HG,
+                         p.block_table);
+    else
+      hipLaunchKernelGGL(decode_attn_tiled_kernel<false>, dim3(blocks), dim3(64 * tiled::kWaves), 0, s, p, HG,
+                         p.block_table);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1 || p.leave_partials) return e;
     if (p.splits >= 16)

@@ -200,8 +200,9 @@ struct DecodeAttnParams {
   float* lse;             // optional [B][n_h], natural log
   bool fp8 = false;       // pool holds e4m3 codes, with per-token (s_c, s_r) in scales
   const float* scales = nullptr;  // [num_blocks][block_size][2]
-  bool leave_partials = false;    // splits > 1: skip the combine (the consumer combines; needs
-                                  // decode_bf16_partials), o_hat and lse are not written
+  bool leave_partials = false;    // write the partitions' (m, l, O_s / l_s) even with one partition,
+                                  // and skip the combine (needs decode_bf16_partials); o_hat and
+                                  // lse are not written
   int4* units = nullptr;          // set: balanced work units for the tiled kernels (scratch of
                                   // B * (splits + 1) entries, filled by decode_attention); null:
                                   // fixed partitions of tokens_per_split

@@ -652,6 +652,45 @@ int mla_decode_attention(const mla_dims* d, const mla_paged_cache* c, const void
   return MLA_OK;
 }
 
+int mla_decode_attention_partials(const mla_dims* d, const mla_paged_cache* c, const void* q, int32_t batch,
+                                  const int32_t* kv_lens, int32_t max_kv_len, int32_t num_splits, float* part_m,
+                                  float* part_l, void* part_o, int32_t* splits_out, void* stream) {
+  int st = validate_dims(d);
+  if (st != MLA_OK) return st;
+  if ((st = validate_cache(d, c)) != MLA_OK) return st;
+  if (!q || !kv_lens || !part_m || !part_l || !part_o || !splits_out || batch <= 0 || max_kv_len <= 0 ||
+      num_splits <= 0)
+    return MLA_ERR_INVALID_ARG;
+  if ((int64_t)max_kv_len > (int64_t)c->max_blocks_per_seq * c->block_size) return MLA_ERR_INVALID_ARG;
+  if (!decode_supported(d->d_c, d->d_hr)) return MLA_ERR_UNSUPPORTED;
+  DecodeAttnParams a{};
+  a.q = q;
+  a.pool = c->pool;
+  a.fp8 = fp8_cache(d);
+  a.scales = c->scales;
+  a.block_table = c->block_table;
+  a.max_blocks = c->max_blocks_per_seq;
+  a.block_size = c->block_size;
+  a.lens = kv_lens;
+  a.lens_plus_one = false;
+  a.B = batch;
+  a.n_h = d->n_h;
+  a.d_c = d->d_c;
+  a.d_hr = d->d_hr;
+  a.scale_log2 = scale_of(d) * 1.4426950408889634f;
+  a.splits = split_count(max_kv_len, num_splits, &a.tokens_per_split);
+  a.part_m = part_m;
+  a.part_l = part_l;
+  a.part_o = part_o;
+  a.units = nullptr;
+  a.cus = device_cus();
+  a.leave_partials = true;
+  if (!decode_bf16_partials(dt(d), a)) return MLA_ERR_UNSUPPORTED;
+  *splits_out = a.splits;
+  MLA_HIP(decode_attention(dt(d), a, reinterpret_cast<hipStream_t>(stream)));
+  return MLA_OK;
+}
+
 int mla_decode(const mla_dims* d, const mla_weights* w, const mla_paged_cache* c, const void* h, int32_t batch,
                const int32_t* ctx_lens, int32_t max_ctx_len, int32_t num_splits, void* u, float* o_heads,
                void* workspace, size_t ws_bytes, void* stream) {

@@ -315,3 +315,54 @@ def test_decode_step_equals_prefill_row(name):
     row = u[0, T].float().cpu().numpy()
     got = _decode_u(layer, pool, h[T:T + 1], [T], 0)[0]
     check(got, row, dims.dtype, f"{name} decode vs prefill row")
+
+
+@pytest.mark.parametrize("lens,splits,sharp", [([700, 1, 300], 3, False), ([257, 90], 1, False),
+                                               ([1000, 64], 4, True)])
+def test_decode_attention_partials_match_oracle_per_partition(lens, splits, sharp):
+    """mla_decode_attention_partials: each partition's (reference, normaliser, normalised output)
+    against the oracle's attention over that partition's tokens alone, and their log-sum-exp
+    combination against the whole context."""
+    dims = S.V2
+    layer = WL.DeviceLayer(dims, S.make_weights(dims))
+    B = len(lens)
+    rng = np.random.default_rng(21)
+    pool = WL.PagedPool(dims, lens, block_size=64)
+    for b, L in enumerate(lens):
+        pool.write_entries(b, WL.to_device(S.to_dtype(rng.standard_normal((L, dims.entry)).astype(np.float32),
+                                                      dims.dtype), dims))
+    q = (rng.standard_normal((B, dims.n_h, dims.entry)) * 0.3).astype(np.float32)
+    if sharp:
+        for b, L in enumerate(lens):
+            q[b] += np.geomspace(0.5, 24.0, dims.n_h)[:, None] * pool.read_entries(b, L)[rng.integers(0, L, dims.n_h)]
+    q = S.to_dtype(q, dims.dtype)
+    kv = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    pm = torch.empty((B, splits, dims.n_h), dtype=torch.float32, device="cuda")
+    pl = torch.empty_like(pm)
+    po = torch.empty((B, splits, dims.n_h, dims.d_c), dtype=torch.bfloat16, device="cuda")
+    P = M.decode_attention_partials(layer.cdims, pool.ccache, WL.to_device(q, dims), kv, max(lens), splits, pm, pl, po)
+    torch.cuda.synchronize()
+    chunks = (max(lens) + 63) // 64
+    length = -(-chunks // splits) * 64
+    assert P == -(-max(lens) // length)
+    m, l, o = pm.cpu().numpy(), pl.cpu().numpy(), po.float().cpu().numpy()
+    scale = O.softmax_scale(dims)
+    for b, L in enumerate(lens):
+        cache = pool.read_entries(b, L)
+        full, full_lse = O.latent_attention(q[b:b + 1], cache, [L], scale, dims.d_c)
+        acc, wsum, M_ = np.zeros((dims.n_h, dims.d_c)), np.zeros(dims.n_h), np.max(m[b, :P], axis=0)
+        for p_ in range(P):
+            lo, hi = p_ * length, min(L, (p_ + 1) * length)
+            if lo >= hi:
+                assert np.all(m[b, p_] == -np.inf)
+                continue
+            ref, ref_lse = O.latent_attention(q[b:b + 1], cache[lo:hi], [hi - lo], scale, dims.d_c)
+            x_max = np.max((q[b].astype(np.float64) @ cache[lo:hi].T.astype(np.float64)) * scale / np.log(2), axis=1)
+            assert np.all(m[b, p_] <= x_max + 1e-3) and np.all(m[b, p_] >= x_max - 8 - 1e-3)
+            got_lse = (m[b, p_] + np.log2(l[b, p_])) * np.log(2)
+            assert np.max(np.abs(got_lse - ref_lse[0])) < 2e-3 * max(1.0, np.max(np.abs(ref_lse)))
+            check(o[b, p_], ref[0], dims.dtype, f"partition {p_} of b={b}")
+            wgt = np.exp2(m[b, p_] - M_) * l[b, p_]
+            acc += wgt[:, None] * o[b, p_]
+            wsum += wgt
+        check(acc / wsum[:, None], full[0], dims.dtype, f"combined b={b}")
