@@ -260,7 +260,7 @@ int mla_decode_attention(const mla_dims *dims, const mla_paged_cache *cache, con
  *   *splits_out (host): P, the number of partitions (<= num_splits); the buffers below hold
  *             batch * P rows of n_h heads.
  *   part_m    [batch][P][n_h] fp32: a reference for the partition's scores x_j = scale * log2(e) *
- *             (q . entry_j), within 8 of their maximum: max_j x_j - 8 <= part_m <= max_j x_j
+ *             (q . entry_j), within 64 of their maximum: max_j x_j - 64 <= part_m <= max_j x_j
  *             (-inf for a partition with no tokens);
  *   part_l    [batch][P][n_h] fp32: sum_j 2^(x_j - part_m);
  *   part_o    [batch][P][n_h][d_c] bf16: sum_j 2^(x_j - part_m) c^KV_j / part_l (the partition's

@@ -134,6 +134,8 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t span, uint32_t off,
 // s_waitcnt immediates (gfx9 encoding): vmcnt in bits [3:0] and [15:14], expcnt [6:4],
 // lgkmcnt [11:8]; the unused counters are left at their maximum.
 constexpr int waitcnt_vm(int n) { return ((n >> 4) << 14) | (0xF << 8) | (0x7 << 4) | (n & 0xF); }
+// vmcnt(n) and lgkmcnt(0): the wave's LDS writes have completed as well
+constexpr int waitcnt_vm_lgkm0(int n) { return ((n >> 4) << 14) | (0x7 << 4) | (n & 0xF); }
 constexpr int kWaitLgkm0 = (0x3 << 14) | (0x7 << 4) | 0xF;
 
 // Workgroup barrier for the pipeline: waits only on what the caller asked for (unlike

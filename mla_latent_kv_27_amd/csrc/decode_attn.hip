@@ -267,12 +267,12 @@ __global__ void __launch_bounds__(256) decode_units_kernel(DecodeAttnParams p) {
 }
 
 // ----------------------------------------------------------------------------- tiled kernel
-// The DeepSeek-V2-sized bf16 case (d_c = 512, d_hr = 64).  A workgroup is eight waves of 16 heads
-// (two waves per SIMD hide each other's LDS and copy latency); with more than 128 heads the other
-// head groups' workgroups read the same tiles and get block ids on the same XCD, so their repeat
-// reads come from its L2.
-//   * Tiles of 32 tokens arrive by direct global->LDS copies into a ring of four buffers, three
-//     tiles ahead of the one being multiplied.
+// The DeepSeek-V2-sized cases (d_c = 512, d_hr = 64; the bf16 kernel and, with its own tiles, the
+// fp8 one).  A workgroup is eight waves (two per SIMD, hiding each other's LDS and copy latency)
+// and one (sequence, KV partition, group of 128 heads); with more than 128 heads the other head
+// groups' workgroups read the same tiles and get block ids on the same XCD, so their repeat reads
+// come from its L2.
+//   * Tiles of 32 tokens arrive by direct global->LDS copies into a ring of four buffers.
 //   * LDS row of a token = its 1152-byte cache entry as 72 16-byte chunks; chunk c of token t is
 //     stored at chunk slot t*72 + (c ^ (t & 7)) so that the 16 tokens of an MFMA operand read
 //     fall on different banks.
@@ -282,19 +282,17 @@ __global__ void __launch_bounds__(256) decode_units_kernel(DecodeAttnParams p) {
 //     token-major tile with the gfx950 LDS transpose read (ds_read_b64_tr_b16): within each
 //     16-lane group, source lane s supplies 4 consecutive dims of token 4j + s/4 and lane i
 //     receives dim i of those four tokens.
-//   * Softmax scaling is lazy: all lanes of a head share a reference max that is only raised (and
-//     O rescaled) when some score exceeds it by more than 2^8, so the common tile needs no
-//     cross-lane exchange; every lane keeps a partial sum that is combined once at the end.
+//   * The softmax keeps a per-head reference max that every lane of the head shares, so the common
+//     tile needs no cross-lane exchange; every lane keeps a partial sum combined once at the end.
 namespace tiled {
 constexpr int kT = 32;                    // tokens per tile
-constexpr int kNBuf = 4;                  // ring buffers (two tile pairs)
+constexpr int kNBuf = 4;                  // ring buffers
 constexpr int kD = 576, kDC = 512;        // entry width, latent width
 constexpr int kCPR = kD * 2 / 16;         // 72 chunks per entry
 constexpr int kRow = kCPR * 16;           // 1152 bytes per entry
 constexpr int kBytes = kT * kRow;         // 36864 per buffer
 constexpr int kWaves = 8;
 constexpr int kDmaTotal = kT * kCPR / 64;  // 36 one-KiB copies per tile: waves 0-3 issue 5, 4-7 issue 4
-constexpr int kDmaPerWave = 5;             // copy instructions per wave and tile (4-7: one reads nothing)
 __device__ __forceinline__ int dma_first(int w) { return w < 4 ? 5 * w : 20 + 4 * (w - 4); }
 constexpr float kLazy = 8.f;              // log2 headroom before a rescale
 }  // namespace tiled
@@ -316,20 +314,11 @@ struct TiledCtx {
   int bs, kv_len;
 };
 
-// This wave's share of the 36 direct-to-LDS copies of tile `tile` into buffer BUF: waves 0-3 copy
-// five 1-KiB pieces, waves 4-7 four plus a fifth that reads nothing (its offset is past the
-// resource) into a slot of their own, so that every wave issues the same five copies per tile and
-// a wait counts whole tiles.  block_size is a multiple of the tile size, so a tile lies inside one
-// block: one uniform block-table lookup, and every row copied is a row of an allocated block (rows
-// past the context are zeroed once the copies land).  A tile past the partition (live == false)
-// gets the same five copies, all reading nothing, so the count stays the same.
-__shared__ __attribute__((aligned(1024))) char g_dma_sink[4][1024];
-
 // The copy itself, written as one asm statement (M0 = the LDS destination): the compiler then does
 // not treat the ring's fragment reads as possibly waiting on these copies (with more copies in
 // flight than it tracks it would wait for most of them before every read).  The waits on them are
-// the kernel's own: each step waits until its tile's copies have landed, and nothing is read from
-// a buffer whose copies are still in flight; after the loop every copy is waited for.
+// the kernel's own: a tile is read only after every wave has waited for its own copies of it and
+// passed a barrier, and every copy is waited for before the workgroup ends.
 __device__ __forceinline__ void dma16_ring(__amdgpu_buffer_rsrc_t span, uint32_t off, const void* lds_dst) {
   const uint32_t m0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds_dst;
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
@@ -338,6 +327,13 @@ __device__ __forceinline__ void dma16_ring(__amdgpu_buffer_rsrc_t span, uint32_t
                : "memory", "m0");
 }
 
+// This wave's share of the 36 direct-to-LDS copies of tile `tile` into buffer BUF: waves 0-3 copy
+// five 1-KiB pieces, waves 4-7 four.  block_size is a multiple of the tile size, so a tile lies
+// inside one block: one uniform block-table lookup.  The buffer resource spans only the tile's rows
+// inside the context: rows past it read as zeros (an out-of-range buffer read returns zero, and the
+// copy writes those zeros), so a partial last tile needs no clearing.  A tile past the partition
+// (live == false) reads nothing at all; its copies are still issued so that every step of a wave
+// issues the same number.
 template <int BUF>
 __device__ __forceinline__ void issue_tile(const TiledCtx& c, int tile, bool live, int w, int lane) {
   using namespace tiled;
@@ -348,21 +344,16 @@ __device__ __forceinline__ void issue_tile(const TiledCtx& c, int tile, bool liv
   int ln = lane;
   asm volatile("" : "+v"(ln));  // recompute the lane offsets here instead of keeping them live
   const int first = dma_first(w);
-  const __amdgpu_buffer_rsrc_t span = dma_span(base, live ? kBytes : 0);  // the tile: 32 consecutive rows
+  const int rows = live ? min(kT, c.kv_len - tok0) : 0;
+  const __amdgpu_buffer_rsrc_t span = dma_span(base, (uint32_t)rows * kRow);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int P = (first + i) * 64 + ln;
-    const int t = P / kCPR;
-    const int ch = (P - t * kCPR) ^ (t & 7);
-    dma16_ring(span, t * kRow + ch * 16, dst + (first + i) * 1024);
-  }
-  if (w < 4) {
-    const int P = (first + 4) * 64 + ln;
-    const int t = P / kCPR;
-    const int ch = (P - t * kCPR) ^ (t & 7);
-    dma16_ring(span, t * kRow + ch * 16, dst + (first + 4) * 1024);
-  } else {
-    dma16_ring(span, kBytes + ln * 16, &g_dma_sink[w - 4][0]);
+  for (int i = 0; i < 5; ++i) {
+    if (i < 4 || w < 4) {
+      const int P = (first + i) * 64 + ln;
+      const int t = P / kCPR;
+      const int ch = (P - t * kCPR) ^ (t & 7);
+      dma16_ring(span, t * kRow + ch * 16, dst + (first + i) * 1024);
+    }
   }
 }
 
@@ -407,7 +398,7 @@ __device__ __forceinline__ void tiled_pv(TiledState& st, const Frag8<bf16>& pf, 
   }
 }
 
-// ---- the bf16 kernel: S by head, P.V by latent column
+// ---- the bf16 kernel: S by head, P.V by latent column, one barrier per tile
 // The S^T = K Q^T product stays with the head's wave (Q is register-resident), but P.V is split by
 // latent columns: wave w accumulates O^T for dims 64w .. 64w+63 of all the workgroup's heads.  Its
 // A operand (V^T, 16 dims x 32 tokens) is then read once per tile and feeds one MFMA per 16-head
@@ -416,12 +407,27 @@ __device__ __forceinline__ void tiled_pv(TiledState& st, const Frag8<bf16>& pf, 
 // the B-operand layout: the S^T accumulators of lane (g, l16) hold head l16 at tokens
 // 16 (s/4) + 4g + s%4, which is exactly that lane's B fragment, so a wave stores its 16-byte
 // fragment at [g][head] and the P.V waves read it back with one 16-byte read per head block.
-// A raised softmax reference changes the scale of O rows that live in every wave: the S wave
-// publishes the factors of its heads and a per-wave flag with the probabilities, and the P.V waves
-// apply them before adding the tile (rare: the reference only moves by more than 2^8).
-__shared__ __attribute__((aligned(1024))) char g_pex[4 * 128 * 16];  // [lane group][head][8 bf16]
-__shared__ float g_alpha[128];                                        // factor of a raised reference
-__shared__ __attribute__((aligned(8))) unsigned char g_rescaled[8];  // per wave: factors published
+//
+// Software pipeline: between two barriers a wave multiplies P.V of tile t-1 and then S of tile t, so
+// one barrier per tile publishes tile t's probabilities, retires tile t-1's buffer and makes tile
+// t+1 visible.  The probabilities alternate between two LDS buffers; the ring holds tiles t-1 (P.V),
+// t (S) and the copies of t+1 and t+2 in flight.
+//
+// The softmax reference of a head is fixed by the partition's first tile.  A later score more than
+// 2^kHeadroom above it (rare: P and O stay far from overflow below that) raises the reference, which
+// would leave O rows summed over two references in every wave; the partition then restarts from its
+// first tile with the raised references.  O therefore never passes through the vector ALU inside the
+// loop.  The restart flags of tile t's S waves travel in the rope-key bytes of tile t-1's buffer,
+// which nothing reads any more once tile t-1's S is done.
+namespace sp {
+constexpr float kHeadroom = 64.f;  // log2 units a score may exceed its head's reference by
+constexpr int kFlagOff = 1024;     // flags: bytes 1024 .. 1031 of a buffer (row 0's first rope chunk)
+}  // namespace sp
+
+__shared__ __attribute__((aligned(1024))) char g_pex0[4 * 128 * 16];  // [lane group][head][8 bf16]
+__shared__ __attribute__((aligned(1024))) char g_pex1[4 * 128 * 16];
+template <int PB>
+__device__ __forceinline__ char* pex_buf() { return PB == 0 ? g_pex0 : g_pex1; }
 
 struct SplitState {
   floatx4 o[4][8];  // O^T: latent dims 16 (4w + db) + 4g + j of head 16 hb + l16
@@ -429,10 +435,11 @@ struct SplitState {
   float l_part;     // S side: this lane's partial normaliser
 };
 
-// S^T for this wave's 16 heads over the tile in buffer BUF, the lazy softmax, and the
-// probabilities (with the factors of a raised reference) published for the P.V waves.
-template <int BUF>
-__device__ __forceinline__ void sp_scores(const Frag8<bf16> (&q)[18], SplitState& st, int t, int kv_len,
+// S^T for this wave's 16 heads over the tile in buffer BUF, the softmax against the fixed
+// references and the probabilities into P buffer PB.  Returns 1 when a reference had to be raised
+// (the same in every lane).
+template <int BUF, int PB>
+__device__ __forceinline__ unsigned char sp_scores(const Frag8<bf16> (&q)[18], SplitState& st, int t, int kv_len,
                                           float scale_log2, int w, int lane) {
   using namespace tiled;
   const char* buf = kv_buf<BUF>();
@@ -449,12 +456,8 @@ __device__ __forceinline__ void sp_scores(const Frag8<bf16> (&q)[18], SplitState
     const char* rb0 = buf + l16 * kRow + ((g) ^ x) * 16;
     const char* rb1 = buf + l16 * kRow + ((4 + g) ^ x) * 16;
     Frag8<bf16> a[2][2];  // [stage][tb]: the next k-chunk's fragments are in flight
-#pragma unroll
-    for (int k0 = 0; k0 < 1; ++k0) {
-      const char* pn = rb0;
-      a[k0][0].v = *reinterpret_cast<const bf16x8*>(pn);
-      a[k0][1].v = *reinterpret_cast<const bf16x8*>(pn + 16 * kRow);
-    }
+    a[0][0].v = *reinterpret_cast<const bf16x8*>(rb0);
+    a[0][1].v = *reinterpret_cast<const bf16x8*>(rb0 + 16 * kRow);
 #pragma unroll
     for (int kc = 0; kc < 18; ++kc) {
       if (kc + 1 < 18) {
@@ -466,7 +469,7 @@ __device__ __forceinline__ void sp_scores(const Frag8<bf16> (&q)[18], SplitState
       sc[1] = mma16(a[kc & 1][1], q[kc], sc[1]);
     }
   }
-  // ---- lazy online softmax
+  // ---- softmax against the head's reference (masked past the context on a partial tile)
   float lmax = -INFINITY;
   const bool full = (t + 1) * kT <= kv_len;
 #pragma unroll
@@ -478,53 +481,45 @@ __device__ __forceinline__ void sp_scores(const Frag8<bf16> (&q)[18], SplitState
       sc[tb][j] = v;
       lmax = fmaxf(lmax, v);
     }
-  unsigned char raised = 0;
-  if (__builtin_amdgcn_ballot_w64(lmax > st.m_ref + kLazy) != 0) {  // rare: raise the reference
+  unsigned char restart = 0;
+  if (__builtin_amdgcn_ballot_w64(lmax > st.m_ref + sp::kHeadroom) != 0) {  // the first tile, or rare
     float hmax = wave_max_xor(lmax, 16);
     hmax = wave_max_xor(hmax, 32);
-    const float m_new = fmaxf(st.m_ref, hmax);
-    const float alpha = __builtin_amdgcn_exp2f(st.m_ref - m_new);  // -inf -> 0
-    st.l_part *= alpha;
-    // before the first reference no O row holds anything: nothing to rescale
-    if (__builtin_amdgcn_ballot_w64(st.m_ref != -INFINITY) != 0) {
-      if (g == 0) g_alpha[16 * w + l16] = alpha;
-      raised = 1;
-    }
-    st.m_ref = m_new;
+    // a head whose reference was set already: its O rows hold sums over the old reference
+    if (__builtin_amdgcn_ballot_w64(st.m_ref != -INFINITY && lmax > st.m_ref + sp::kHeadroom) != 0) restart = 1;
+    st.m_ref = fmaxf(st.m_ref, hmax);
   }
-  if (lane == 0) g_rescaled[w] = raised;
   bf16x8 pf;  // slot s = token 16 (s/4) + 4g + s%4
 #pragma unroll
   for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const bf16 e = (bf16)__builtin_amdgcn_exp2f(sc[tb][j] - st.m_ref);  // argument <= 8
+      const bf16 e = (bf16)__builtin_amdgcn_exp2f(sc[tb][j] - st.m_ref);  // argument <= kHeadroom
       st.l_part += (float)e;
       pf[tb * 4 + j] = e;
     }
-  *reinterpret_cast<bf16x8*>(g_pex + ((g * 128) + 16 * w + l16) * 16) = pf;
+  *reinterpret_cast<bf16x8*>(pex_buf<PB>() + ((g * 128) + 16 * w + l16) * 16) = pf;
+  return restart;
 }
 
-// O^T += V^T P^T for this wave's 64 latent dims and the nhb head blocks, over the tile in buffer
-// BUF; first the factors of any reference raised in this tile.
-template <int BUF, bool FULL>
+// S of tile t in buffer BUF (S waves), probabilities into P buffer PB, and every wave's restart
+// flag (zero for waves without heads) into buffer FB.
+template <int BUF, int PB, int FB>
+__device__ __forceinline__ void sp_scores_flag(const Frag8<bf16> (&q)[18], SplitState& st, int t, int kv_len,
+                                               float scale_log2, bool s_wave, int w, int lane) {
+  const unsigned char r = s_wave ? sp_scores<BUF, PB>(q, st, t, kv_len, scale_log2, w, lane) : 0;
+  if (lane == 0) kv_buf<FB>()[sp::kFlagOff + w] = r;
+}
+
+// O^T += V^T P^T for this wave's 64 latent dims and the head blocks present, over the tile in
+// buffer BUF with the probabilities in P buffer PB.
+template <int BUF, int PB, bool FULL>
 __device__ __forceinline__ void sp_pv(SplitState& st, int nhb_rt, int w, int lane) {
-  const int nhb = FULL ? 8 : nhb_rt;  // FULL: every head block of the group is present
   using namespace tiled;
+  const int nhb = FULL ? 8 : nhb_rt;  // FULL: every head block of the group is present
   const char* buf = kv_buf<BUF>();
   asm volatile("" : "+v"(lane));
   const int g = lane >> 4, l16 = lane & 15;
-  const uint64_t raised = *reinterpret_cast<const uint64_t*>(g_rescaled);
-  if (raised != 0) {  // rare, uniform
-#pragma unroll
-    for (int hb = 0; hb < 8; ++hb) {
-      if (hb < nhb && ((raised >> (8 * hb)) & 0xff)) {
-        const float a = g_alpha[16 * hb + l16];
-#pragma unroll
-        for (int db = 0; db < 4; ++db) st.o[db][hb] *= a;
-      }
-    }
-  }
   // V^T fragments of dim blocks 4w .. 4w+3 (16 dims x 32 tokens each): lane group g reads tokens
   // 4g + s/4 (+16 for the second read); source lane s supplies dims 16 d + 4 (s % 4) .. +3 = chunk
   // 2d + (s%4)/2, byte (s % 2) * 8 of its token row, stored at slot chunk ^ (token & 7)
@@ -541,7 +536,7 @@ __device__ __forceinline__ void sp_pv(SplitState& st, int nhb_rt, int w, int lan
   }
   // P^T fragments four head blocks at a time (the scheduler barrier keeps the second group's reads
   // from being hoisted, which would need registers the queries and O occupy)
-  const char* pb = g_pex + (g * 128 + l16) * 16;
+  const char* pb = pex_buf<PB>() + (g * 128 + l16) * 16;
 #pragma unroll
   for (int hq = 0; hq < 2; ++hq) {
     Frag8<bf16> pf[4];
@@ -557,29 +552,29 @@ __device__ __forceinline__ void sp_pv(SplitState& st, int nhb_rt, int w, int lan
   }
 }
 
-// One tile (in ring buffer BUF): wait until it has landed, this wave's copies of the two tiles
-// after it may still be in flight (waves 0-3 issue 5 copies per tile, 4-7 issue 4) and every
-// wave is done with the previous tile, whose buffer then takes tile t + 3.  Rows past the end of
-// the context are zeroed (only the sequence's last tile can be partial).  Then the S waves publish
-// the tile's probabilities and, after a second barrier, every wave adds its share of P.V.
-template <int BUF, bool FULL>
-__device__ __forceinline__ void sp_step(const TiledCtx& c, const Frag8<bf16> (&q)[18], SplitState& st, int t,
-                                        int t_end, float scale_log2, bool s_wave, int nhb, int w, int lane,
-                                        int tid) {
+// Waits until this wave's copies of the next tile have landed, with those of the one after it still
+// in flight (waves 0-3 issue five copies per tile, 4-7 four), and until its LDS writes (the
+// probabilities and the restart flag it publishes) have completed; then the workgroup barrier.
+__device__ __forceinline__ void sp_barrier_next(int w) {
+  if (w < 4) MLA_TILE_BARRIER(waitcnt_vm_lgkm0(5));
+  else MLA_TILE_BARRIER(waitcnt_vm_lgkm0(4));
+}
+
+// The phase of tile t (buffer B = (t - t_begin) % 4; t == t_end: only tile t-1's P.V): read tile
+// t-1's restart flags, refill the buffer they sat in with tile t+2, P.V of tile t-1, S of tile t.
+// Returns the flags (nonzero: restart), the same in every wave.
+template <int B, bool FULL>
+__device__ __forceinline__ uint64_t sp_phase(const TiledCtx& c, const Frag8<bf16> (&q)[18], SplitState& st, int t,
+                                             int t_end, float scale_log2, bool s_wave, int nhb, int w, int lane) {
   using namespace tiled;
-  // every wave has five copies per tile in flight: tile t has landed when at most those of the two
-  // tiles after it are outstanding
-  MLA_TILE_BARRIER(waitcnt_vm(2 * kDmaPerWave));
-  issue_tile<(BUF + 3) % kNBuf>(c, t + 3, t + 3 < t_end, w, lane);
-  const int valid = c.kv_len - t * kT;
-  if (valid < kT) {  // uniform
-    char* buf = kv_buf<BUF>();
-    for (int i = tid; i < (kT - valid) * kCPR; i += 64 * kWaves) st16(buf + (valid * kCPR + i) * 16, zero16());
-    MLA_TILE_BARRIER(kWaitLgkm0);
-  }
-  if (s_wave) sp_scores<BUF>(q, st, t, c.kv_len, scale_log2, w, lane);
-  MLA_TILE_BARRIER(kWaitLgkm0);  // the tile's probabilities, factors and flags are visible
-  sp_pv<BUF, FULL>(st, nhb, w, lane);
+  constexpr int BPREV = (B + 3) % kNBuf, BNEXT2 = (B + 2) % kNBuf;
+  const uint64_t flags = *reinterpret_cast<const uint64_t*>(kv_buf<BNEXT2>() + sp::kFlagOff);
+  MLA_WAVE_WAIT(kWaitLgkm0);  // read before the buffer is refilled
+  issue_tile<BNEXT2>(c, t + 2, t + 2 < t_end, w, lane);
+  sp_pv<BPREV, (B + 1) & 1, FULL>(st, nhb, w, lane);
+  if (t < t_end) sp_scores_flag<B, B & 1, BPREV>(q, st, t, c.kv_len, scale_log2, s_wave, w, lane);
+  sp_barrier_next(w);
+  return flags;
 }
 
 template <bool FULL>
@@ -606,14 +601,15 @@ __global__ void __launch_bounds__(512)
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, l16 = lane & 15;
-  const int h0 = hg * (16 * kWaves);                  // the head group's first head
+  const int h0 = hg * (16 * kWaves);                    // the head group's first head
   const int nhb = min(kWaves, (p.n_h - h0 + 15) / 16);  // its 16-head blocks
-  const bool s_wave = w < nhb;                        // this wave computes S for heads h0 + 16w ..
+  const bool s_wave = w < nhb;                          // this wave computes S for heads h0 + 16w ..
   const int head = h0 + w * 16 + l16;
   const bool valid_head = head < p.n_h;
+  const bool partial = p.splits > 1 || p.leave_partials;  // else o_hat (and lse) directly
 
   if (t_begin >= t_end) {  // an empty partition: only its max (-inf), which the combines skip
-    if (s_wave && valid_head && g == 0 && (p.splits > 1 || p.leave_partials)) {
+    if (s_wave && valid_head && g == 0 && partial) {
       const int64_t pi = ((int64_t)b * p.splits + split) * p.n_h + head;
       p.part_m[pi] = -INFINITY;
       p.part_l[pi] = 0.f;
@@ -643,19 +639,39 @@ __global__ void __launch_bounds__(512)
     for (int hb = 0; hb < 8; ++hb) st.o[db][hb] = floatx4{0, 0, 0, 0};
   st.m_ref = -INFINITY;
   st.l_part = 0.f;
-  if (tid < kWaves) g_rescaled[tid] = 0;  // waves without heads never publish
   // the queries first: with them still in flight the compiler would wait for every copy of the
   // ring before the first tile
   MLA_WAVE_WAIT(waitcnt_vm(0));
 
-  issue_tile<0>(c, t_begin, true, w, lane);
-  issue_tile<1>(c, t_begin + 1, t_begin + 1 < t_end, w, lane);
-  issue_tile<2>(c, t_begin + 2, t_begin + 2 < t_end, w, lane);
-  for (int t = t_begin; t < t_end; t += kNBuf) {
-    sp_step<0, FULL>(c, q, st, t, t_end, p.scale_log2, s_wave, nhb, w, lane, tid);
-    if (t + 1 < t_end) sp_step<1, FULL>(c, q, st, t + 1, t_end, p.scale_log2, s_wave, nhb, w, lane, tid);
-    if (t + 2 < t_end) sp_step<2, FULL>(c, q, st, t + 2, t_end, p.scale_log2, s_wave, nhb, w, lane, tid);
-    if (t + 3 < t_end) sp_step<3, FULL>(c, q, st, t + 3, t_end, p.scale_log2, s_wave, nhb, w, lane, tid);
+  int t = t_begin;
+  while (t <= t_end) {
+    if (t == t_begin) {  // (re)start: tiles t_begin .. t_begin + 2 into buffers 0 .. 2, then S of the first
+      issue_tile<0>(c, t_begin, true, w, lane);
+      issue_tile<1>(c, t_begin + 1, t_begin + 1 < t_end, w, lane);
+      issue_tile<2>(c, t_begin + 2, t_begin + 2 < t_end, w, lane);
+      if (w < 4) MLA_TILE_BARRIER(waitcnt_vm(10));
+      else MLA_TILE_BARRIER(waitcnt_vm(8));
+      sp_scores_flag<0, 0, 3>(q, st, t_begin, c.kv_len, p.scale_log2, s_wave, w, lane);
+      sp_barrier_next(w);
+      t = t_begin + 1;
+    }
+    uint64_t fl = sp_phase<1, FULL>(c, q, st, t, t_end, p.scale_log2, s_wave, nhb, w, lane);
+    if (fl == 0 && t + 1 <= t_end) fl = sp_phase<2, FULL>(c, q, st, t + 1, t_end, p.scale_log2, s_wave, nhb, w, lane);
+    if (fl == 0 && t + 2 <= t_end) fl = sp_phase<3, FULL>(c, q, st, t + 2, t_end, p.scale_log2, s_wave, nhb, w, lane);
+    if (fl == 0 && t + 3 <= t_end) fl = sp_phase<0, FULL>(c, q, st, t + 3, t_end, p.scale_log2, s_wave, nhb, w, lane);
+    if (fl == 0) {
+      t += kNBuf;
+      continue;
+    }
+    // a reference was raised: start over from the first tile, keeping the raised references
+    MLA_WAVE_WAIT(waitcnt_vm(0));
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int hb = 0; hb < 8; ++hb) st.o[db][hb] = floatx4{0, 0, 0, 0};
+    st.l_part = 0.f;
+    MLA_TILE_BARRIER(kWaitLgkm0);
+    t = t_begin;
   }
   // the copies past the partition (reading nothing) must land before the LDS is released
   MLA_WAVE_WAIT(waitcnt_vm(0));
@@ -663,10 +679,9 @@ __global__ void __launch_bounds__(512)
   float l_run = wave_sum_xor(st.l_part, 16);
   l_run = wave_sum_xor(l_run, 32);
   const float m_run = st.m_ref;
-  MLA_TILE_BARRIER(kWaitLgkm0);  // every wave is done with the last tile's probabilities
-  float* inv_l = reinterpret_cast<float*>(g_pex);  // [head - h0]: 1 / l
+  MLA_TILE_BARRIER(kWaitLgkm0);  // every wave is done with the last probabilities
+  float* inv_l = reinterpret_cast<float*>(g_pex0);  // [head - h0]: 1 / l
   if (s_wave && g == 0) inv_l[16 * w + l16] = l_run > 0.f ? 1.f / l_run : 0.f;
-  const bool partial = p.splits > 1 || p.leave_partials;  // else o_hat (and lse) directly
   if (s_wave && valid_head && g == 0) {
     if (!partial) {
       if (p.lse) p.lse[(int64_t)b * p.n_h + head] = (m_run + log2f(l_run)) * 0.69314718055994531f;

@@ -358,7 +358,7 @@ def test_decode_attention_partials_match_oracle_per_partition(lens, splits, shar
                 continue
             ref, ref_lse = O.latent_attention(q[b:b + 1], cache[lo:hi], [hi - lo], scale, dims.d_c)
             x_max = np.max((q[b].astype(np.float64) @ cache[lo:hi].T.astype(np.float64)) * scale / np.log(2), axis=1)
-            assert np.all(m[b, p_] <= x_max + 1e-3) and np.all(m[b, p_] >= x_max - 8 - 1e-3)
+            assert np.all(m[b, p_] <= x_max + 1e-3) and np.all(m[b, p_] >= x_max - 64 - 1e-3)
             got_lse = (m[b, p_] + np.log2(l[b, p_])) * np.log(2)
             assert np.max(np.abs(got_lse - ref_lse[0])) < 2e-3 * max(1.0, np.max(np.abs(ref_lse)))
             check(o[b, p_], ref[0], dims.dtype, f"partition {p_} of b={b}")
