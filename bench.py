@@ -73,7 +73,7 @@ def copy_only(args):
 
 STREAM_BYTES = 2 << 30  # read passes over 2 GiB: eight times the 256 MB last-level cache
 STREAM_VARIANTS = {0: "regs x2", 1: "regs x4", 2: "regs x8", 3: "regs x16", 4: "lds ring 4", 5: "lds ring 8",
-                   6: "lds ring 16"}
+                   6: "lds ring 16", 7: "operand-shaped x8", 8: "operand-shaped x16"}
 
 
 def stream_ceiling(variants=None, blocks=(256, 512, 1024, 2048), reps=5):

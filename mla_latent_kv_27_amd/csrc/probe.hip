@@ -66,13 +66,44 @@ __global__ void __launch_bounds__(256) stream_read_lds(const char* __restrict__ 
   if (threadIdx.x == 0) sink[blockIdx.x] = x;
 }
 
+// MFMA-fragment-shaped reads of a row-major matrix of 2-byte elements, rows of `row_bytes`: a wave
+// owns 16 consecutive rows and reads them 32 elements (64 bytes) of each row per instruction, lane l
+// taking row l % 16 and 16 bytes at 16 (l / 16) of that 64-byte piece (the A-operand layout of a
+// 16x16x32 MFMA), with UNROLL instructions in flight.  Rows are dealt to waves round robin.
+template <int UNROLL>
+__global__ void __launch_bounds__(256) stream_read_frag(const char* __restrict__ src, int64_t bytes, int row_bytes,
+                                                        uint32_t* __restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  const int64_t nrows = bytes / row_bytes;
+  const int64_t groups = nrows / 16;
+  const int64_t waves = (int64_t)gridDim.x * 4;
+  const int per_row = row_bytes / 64;  // instructions per row group
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (int64_t grp = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); grp < groups; grp += waves) {
+    const char* base = src + (grp * 16 + (lane & 15)) * row_bytes + 16 * (lane >> 4);
+    int c = 0;
+    for (; c + UNROLL <= per_row; c += UNROLL) {
+      u32x4 v[UNROLL];
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (c + u) * 64));
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) acc ^= v[u];
+    }
+    for (; c < per_row; ++c) acc ^= *reinterpret_cast<const u32x4*>(base + c * 64);
+  }
+  uint32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+  for (int m = 32; m >= 1; m >>= 1) x ^= __shfl_xor(x, m, 64);
+  if (threadIdx.x == 0) sink[blockIdx.x] = x;
+}
+
 }  // namespace
 
 extern "C" {
 
 // One read pass over `bytes` bytes at `src` (device, 16-byte aligned, bytes a multiple of 1024).
 // variant: 0..3 register loads with 2, 4, 8, 16 loads in flight per lane; 4..6 direct-to-LDS
-// copies with rings of 4, 8, 16 slots per wave.  blocks: workgroups of 256 threads.  sink:
+// copies with rings of 4, 8, 16 slots per wave; 7, 8: MFMA-operand-shaped reads of 32-KiB rows
+// with 8, 16 loads in flight per lane.  blocks: workgroups of 256 threads.  sink:
 // device, >= blocks uint32.  Returns 0, or -1 on bad arguments, -4 on a launch failure.
 int mla_probe_stream_read(const void* src, int64_t bytes, int variant, int blocks, uint32_t* sink, void* stream) {
   if (!src || !sink || bytes <= 0 || bytes % 1024 || blocks <= 0) return -1;
@@ -88,6 +119,9 @@ int mla_probe_stream_read(const void* src, int64_t bytes, int variant, int block
     case 4: hipLaunchKernelGGL(stream_read_lds<4>, dim3(blocks), dim3(256), 0, s, c, bytes, sink); break;
     case 5: hipLaunchKernelGGL(stream_read_lds<8>, dim3(blocks), dim3(256), 0, s, c, bytes, sink); break;
     case 6: hipLaunchKernelGGL(stream_read_lds<16>, dim3(blocks), dim3(256), 0, s, c, bytes, sink); break;
+    // weight-matrix shaped reads: rows of 32 KiB (16384 bf16, the longest DeepSeek-V2 weight row)
+    case 7: hipLaunchKernelGGL(stream_read_frag<8>, dim3(blocks), dim3(256), 0, s, c, bytes, 32768, sink); break;
+    case 8: hipLaunchKernelGGL(stream_read_frag<16>, dim3(blocks), dim3(256), 0, s, c, bytes, 32768, sink); break;
     default: return -1;
   }
   return hipGetLastError() == hipSuccess ? 0 : -4;
