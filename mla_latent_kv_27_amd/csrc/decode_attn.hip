@@ -292,8 +292,8 @@ constexpr int kCPR = kD * 2 / 16;         // 72 chunks per entry
 constexpr int kRow = kCPR * 16;           // 1152 bytes per entry
 constexpr int kBytes = kT * kRow;         // 36864 per buffer
 constexpr int kWaves = 8;
-constexpr int kDmaTotal = kT * kCPR / 64;  // 36 one-KiB copies per tile: waves 0-3 issue 5, 4-7 issue 4
-__device__ __forceinline__ int dma_first(int w) { return w < 4 ? 5 * w : 20 + 4 * (w - 4); }
+constexpr int kDmaTotal = kT * kCPR / 64;  // 36 one-KiB copies per tile, nine from each of waves 0-3
+constexpr int kDmaPerWave = kDmaTotal / 4;
 constexpr float kLazy = 8.f;              // log2 headroom before a rescale
 }  // namespace tiled
 
@@ -328,7 +328,10 @@ __device__ __forceinline__ void dma16_ring(__amdgpu_buffer_rsrc_t span, uint32_t
 }
 
 // This wave's share of the 36 direct-to-LDS copies of tile `tile` into buffer BUF: waves 0-3 copy
-// five 1-KiB pieces, waves 4-7 four.  block_size is a multiple of the tile size, so a tile lies
+// nine 1-KiB pieces each (rows 8w .. 8w+7), waves 4-7 none.  Issued all by half of the waves, the
+// copies hold up only those (measured: 169.5 against 175.6 us with every wave issuing its share,
+// and slower again with the copies spread through the multiply): the other wave of each SIMD
+// starts its products at once and has the matrix core to itself meanwhile.  block_size is a multiple of the tile size, so a tile lies
 // inside one block: one uniform block-table lookup.  The buffer resource spans only the tile's rows
 // inside the context: rows past it read as zeros (an out-of-range buffer read returns zero, and the
 // copy writes those zeros), so a partial last tile needs no clearing.  A tile past the partition
@@ -343,12 +346,12 @@ __device__ __forceinline__ void issue_tile(const TiledCtx& c, int tile, bool liv
   const char* base = c.pool + ((int64_t)c.bt[live ? blk : 0] * c.bs + (tok0 - blk * c.bs)) * kRow;
   int ln = lane;
   asm volatile("" : "+v"(ln));  // recompute the lane offsets here instead of keeping them live
-  const int first = dma_first(w);
+  const int first = kDmaPerWave * w;
   const int rows = live ? min(kT, c.kv_len - tok0) : 0;
   const __amdgpu_buffer_rsrc_t span = dma_span(base, (uint32_t)rows * kRow);
 #pragma unroll
-  for (int i = 0; i < 5; ++i) {
-    if (i < 4 || w < 4) {
+  for (int i = 0; i < kDmaPerWave; ++i) {
+    if (w < 4) {
       const int P = (first + i) * 64 + ln;
       const int t = P / kCPR;
       const int ch = (P - t * kCPR) ^ (t & 7);
@@ -417,11 +420,15 @@ __device__ __forceinline__ void tiled_pv(TiledState& st, const Frag8<bf16>& pf, 
 // 2^kHeadroom above it (rare: P and O stay far from overflow below that) raises the reference, which
 // would leave O rows summed over two references in every wave; the partition then restarts from its
 // first tile with the raised references.  O therefore never passes through the vector ALU inside the
-// loop.  The restart flags of tile t's S waves travel in the rope-key bytes of tile t-1's buffer,
-// which nothing reads any more once tile t-1's S is done.
+// loop.  The restart request travels with the probabilities themselves: a wave that raised a
+// reference writes the value -1 (bf16 0xBF80) as the first probability of each of its fragments, a
+// value no probability takes (2^x is never negative, and a NaN from a corrupt cache entry has an
+// all-ones exponent, so it cannot pose as a request and restart the partition forever).  Every wave,
+// reading every head block's fragments for its P.V, sees the request in the next phase; its O is
+// discarded by the restart, so the replaced values do no harm.  Nothing else in LDS carries it, so no
+// copy into the ring can overwrite a request before every wave has read it.
 namespace sp {
 constexpr float kHeadroom = 64.f;  // log2 units a score may exceed its head's reference by
-constexpr int kFlagOff = 1024;     // flags: bytes 1024 .. 1031 of a buffer (row 0's first rope chunk)
 }  // namespace sp
 
 __shared__ __attribute__((aligned(1024))) char g_pex0[4 * 128 * 16];  // [lane group][head][8 bf16]
@@ -498,23 +505,23 @@ __device__ __forceinline__ unsigned char sp_scores(const Frag8<bf16> (&q)[18], S
       st.l_part += (float)e;
       pf[tb * 4 + j] = e;
     }
+  if (restart) pf[0] = (bf16)-1.f;  // the request: a value no probability takes
   *reinterpret_cast<bf16x8*>(pex_buf<PB>() + ((g * 128) + 16 * w + l16) * 16) = pf;
   return restart;
 }
 
-// S of tile t in buffer BUF (S waves), probabilities into P buffer PB, and every wave's restart
-// flag (zero for waves without heads) into buffer FB.
-template <int BUF, int PB, int FB>
-__device__ __forceinline__ void sp_scores_flag(const Frag8<bf16> (&q)[18], SplitState& st, int t, int kv_len,
+// S of tile t in buffer BUF by the waves that own heads, probabilities into P buffer PB.
+template <int BUF, int PB>
+__device__ __forceinline__ void sp_scores_wave(const Frag8<bf16> (&q)[18], SplitState& st, int t, int kv_len,
                                                float scale_log2, bool s_wave, int w, int lane) {
-  const unsigned char r = s_wave ? sp_scores<BUF, PB>(q, st, t, kv_len, scale_log2, w, lane) : 0;
-  if (lane == 0) kv_buf<FB>()[sp::kFlagOff + w] = r;
+  if (s_wave) sp_scores<BUF, PB>(q, st, t, kv_len, scale_log2, w, lane);
 }
 
 // O^T += V^T P^T for this wave's 64 latent dims and the head blocks present, over the tile in
-// buffer BUF with the probabilities in P buffer PB.
+// buffer BUF with the probabilities in P buffer PB.  Returns nonzero (the same in every wave) when
+// one of those probabilities carries a restart request.
 template <int BUF, int PB, bool FULL>
-__device__ __forceinline__ void sp_pv(SplitState& st, int nhb_rt, int w, int lane) {
+__device__ __forceinline__ uint64_t sp_pv(SplitState& st, int nhb_rt, int w, int lane) {
   using namespace tiled;
   const int nhb = FULL ? 8 : nhb_rt;  // FULL: every head block of the group is present
   const char* buf = kv_buf<BUF>();
@@ -537,6 +544,7 @@ __device__ __forceinline__ void sp_pv(SplitState& st, int nhb_rt, int w, int lan
   // P^T fragments four head blocks at a time (the scheduler barrier keeps the second group's reads
   // from being hoisted, which would need registers the queries and O occupy)
   const char* pb = pex_buf<PB>() + (g * 128 + l16) * 16;
+  bool req = false;  // a fragment's first value is the request value
 #pragma unroll
   for (int hq = 0; hq < 2; ++hq) {
     Frag8<bf16> pf[4];
@@ -545,36 +553,37 @@ __device__ __forceinline__ void sp_pv(SplitState& st, int nhb_rt, int w, int lan
       if (FULL || 4 * hq + i < nhb) pf[i].v = *reinterpret_cast<const bf16x8*>(pb + 256 * (4 * hq + i));
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (FULL || 4 * hq + i < nhb)
+      if (FULL || 4 * hq + i < nhb) {
 #pragma unroll
         for (int db = 0; db < 4; ++db) st.o[db][4 * hq + i] = mma16(va[db], pf[i], st.o[db][4 * hq + i]);
+        req |= ((uint32_t)__builtin_bit_cast(intx4, pf[i].v)[0] & 0xFFFFu) == 0xBF80u;
+      }
     __builtin_amdgcn_sched_barrier(0);
   }
+  return __builtin_amdgcn_ballot_w64(req);
 }
 
 // Waits until this wave's copies of the next tile have landed, with those of the one after it still
-// in flight (waves 0-3 issue five copies per tile, 4-7 four), and until its LDS writes (the
-// probabilities and the restart flag it publishes) have completed; then the workgroup barrier.
+// in flight (waves 0-3 issue nine copies per tile, 4-7 none), and until its LDS writes (the
+// probabilities it publishes) have completed; then the workgroup barrier.
 __device__ __forceinline__ void sp_barrier_next(int w) {
-  if (w < 4) MLA_TILE_BARRIER(waitcnt_vm_lgkm0(5));
-  else MLA_TILE_BARRIER(waitcnt_vm_lgkm0(4));
+  if (w < 4) MLA_TILE_BARRIER(waitcnt_vm_lgkm0(tiled::kDmaPerWave));
+  else MLA_TILE_BARRIER(waitcnt_vm_lgkm0(0));
 }
 
-// The phase of tile t (buffer B = (t - t_begin) % 4; t == t_end: only tile t-1's P.V): read tile
-// t-1's restart flags, refill the buffer they sat in with tile t+2, P.V of tile t-1, S of tile t.
-// Returns the flags (nonzero: restart), the same in every wave.
+// The phase of tile t (buffer B = (t - t_begin) % 4; t == t_end: only tile t-1's P.V): refill the
+// buffer tile t-2 left with tile t+2, P.V of tile t-1, S of tile t.  Returns nonzero, the same in
+// every wave, when tile t-1's probabilities carry a restart request.
 template <int B, bool FULL>
 __device__ __forceinline__ uint64_t sp_phase(const TiledCtx& c, const Frag8<bf16> (&q)[18], SplitState& st, int t,
                                              int t_end, float scale_log2, bool s_wave, int nhb, int w, int lane) {
   using namespace tiled;
   constexpr int BPREV = (B + 3) % kNBuf, BNEXT2 = (B + 2) % kNBuf;
-  const uint64_t flags = *reinterpret_cast<const uint64_t*>(kv_buf<BNEXT2>() + sp::kFlagOff);
-  MLA_WAVE_WAIT(kWaitLgkm0);  // read before the buffer is refilled
   issue_tile<BNEXT2>(c, t + 2, t + 2 < t_end, w, lane);
-  sp_pv<BPREV, (B + 1) & 1, FULL>(st, nhb, w, lane);
-  if (t < t_end) sp_scores_flag<B, B & 1, BPREV>(q, st, t, c.kv_len, scale_log2, s_wave, w, lane);
+  const uint64_t req = sp_pv<BPREV, (B + 1) & 1, FULL>(st, nhb, w, lane);
+  if (t < t_end) sp_scores_wave<B, B & 1>(q, st, t, c.kv_len, scale_log2, s_wave, w, lane);
   sp_barrier_next(w);
-  return flags;
+  return req;
 }
 
 template <bool FULL>
@@ -649,9 +658,9 @@ __global__ void __launch_bounds__(512)
       issue_tile<0>(c, t_begin, true, w, lane);
       issue_tile<1>(c, t_begin + 1, t_begin + 1 < t_end, w, lane);
       issue_tile<2>(c, t_begin + 2, t_begin + 2 < t_end, w, lane);
-      if (w < 4) MLA_TILE_BARRIER(waitcnt_vm(10));
-      else MLA_TILE_BARRIER(waitcnt_vm(8));
-      sp_scores_flag<0, 0, 3>(q, st, t_begin, c.kv_len, p.scale_log2, s_wave, w, lane);
+      if (w < 4) MLA_TILE_BARRIER(waitcnt_vm(2 * kDmaPerWave));  // the first tile landed
+      else MLA_TILE_BARRIER(waitcnt_vm(0));
+      sp_scores_wave<0, 0>(q, st, t_begin, c.kv_len, p.scale_log2, s_wave, w, lane);
       sp_barrier_next(w);
       t = t_begin + 1;
     }

@@ -366,3 +366,38 @@ def test_decode_attention_partials_match_oracle_per_partition(lens, splits, shar
             acc += wgt[:, None] * o[b, p_]
             wsum += wgt
         check(acc / wsum[:, None], full[0], dims.dtype, f"combined b={b}")
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+def test_decode_attention_corrupt_entry_finishes(splits):
+    """A NaN with its sign bit set (bf16 0xFFFF) in an attended cache entry of one sequence: the
+    kernel still finishes (the partition-restart request of the online softmax is an exact value
+    that no NaN can pose as), that sequence's outputs are NaN, and the clean sequence next to it
+    still matches the oracle."""
+    dims = S.V2
+    layer = WL.DeviceLayer(dims, S.make_weights(dims))
+    lens = [700, 300]
+    B = len(lens)
+    rng = np.random.default_rng(31)
+    pool = WL.PagedPool(dims, lens, block_size=64)
+    for b, L in enumerate(lens):
+        pool.write_entries(b, WL.to_device(S.to_dtype(rng.standard_normal((L, dims.entry)).astype(np.float32),
+                                                      dims.dtype), dims))
+    bad = 650  # token of sequence 0: in its last partition for every split count here
+    blk = int(pool.table_np[0, bad // pool.block_size])
+    pool.pool.view(torch.int16)[blk, bad % pool.block_size, :] = -1
+    q = S.to_dtype((rng.standard_normal((B, dims.n_h, dims.entry)) * 0.3).astype(np.float32), dims.dtype)
+    kv = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    pm = torch.empty((B, splits, dims.n_h), dtype=torch.float32, device="cuda")
+    pl = torch.empty_like(pm)
+    po = torch.empty((B, splits, dims.n_h, dims.d_c), dtype=torch.bfloat16, device="cuda")
+    P = M.decode_attention_partials(layer.cdims, pool.ccache, WL.to_device(q, dims), kv, max(lens), splits, pm, pl, po)
+    ws = WL.ws_tensor(M.workspace_size(layer.cdims, M.OP_DECODE, batch=B, max_ctx_len=max(lens) - 1,
+                                       num_splits=splits))
+    ohat = torch.empty((B, dims.n_h, dims.d_c), dtype=WL.torch_dtype(dims), device="cuda")
+    M.decode_attention(layer.cdims, pool.ccache, WL.to_device(q, dims), kv, max(lens), ohat, ws, num_splits=splits)
+    torch.cuda.synchronize()
+    assert np.isnan(po[0, P - 1].float().cpu().numpy()).all()
+    assert np.isnan(ohat[0].float().cpu().numpy()).all()
+    ref, _ = O.latent_attention(q[1:2], pool.read_entries(1, lens[1]), [lens[1]], O.softmax_scale(dims), dims.d_c)
+    check(ohat[1].float().cpu().numpy(), ref[0], dims.dtype, "clean sequence next to a corrupt one")
