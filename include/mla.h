@@ -36,7 +36,10 @@
  *     call returns without synchronising.
  *   - Host-side validation runs before anything is enqueued and returns a negative mla_status;
  *     on error nothing has been launched.  Device-side preconditions (block ids < num_blocks,
- *     ctx_lens[b] <= max_ctx_len, positions inside the block table) are the caller's duty.
+ *     ctx_lens[b] <= max_ctx_len, positions inside the block table) are the caller's duty; the
+ *     MLA_DEBUG build of the library (libmla_debug.so) checks them too, by reading the tables
+ *     back before launching (MLA_ERR_INVALID_ARG, with a message on stderr), and synchronises
+ *     the device after every launch group (a failing kernel: MLA_ERR_HIP from its own call).
  *   - Accumulation is always fp32.  In MLA_BF16 mode the intermediates handed between kernels
  *     (c^q, q^C, the absorbed query, attention outputs) are stored as bf16.
  */

@@ -11,7 +11,9 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "lib", "libmla.so")
+# MLA_LIBRARY selects another build of the same library (the debug or sanitizer variants that
+# build.py makes beside it); the default is the release build
+LIB_PATH = os.environ.get("MLA_LIBRARY") or os.path.join(PKG, "lib", "libmla.so")
 
 MLA_OK = 0
 MLA_ERR_INVALID_ARG = -1

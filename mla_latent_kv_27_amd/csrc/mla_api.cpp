@@ -5,7 +5,9 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdio>
 #include <mutex>
+#include <vector>
 
 #include "mla.h"
 #include "internal.h"
@@ -101,6 +103,79 @@ int validate_cache(const mla_dims* d, const mla_paged_cache* c) {
   if (!c || !c->pool || !c->block_table) return MLA_ERR_INVALID_ARG;
   if (c->num_blocks <= 0 || c->block_size <= 0 || c->max_blocks_per_seq <= 0) return MLA_ERR_INVALID_ARG;
   if (fp8_cache(d) && !c->scales) return MLA_ERR_INVALID_ARG;
+  return MLA_OK;
+}
+
+// ----------------------------------------------------------------------------- debug builds
+// Built with -DMLA_DEBUG (build.py --variant debug), the library also checks the preconditions
+// that a release build leaves to the caller, because checking them means reading device memory
+// on the host: every context length inside its bound and its block table row, and every block id
+// that a sequence's tokens use inside the pool.  The tables are copied to the host (synchronously)
+// before anything is launched; a violation prints what it found and returns MLA_ERR_INVALID_ARG.
+// Every launch group is followed by a device synchronisation, so that a kernel that fails is
+// reported (MLA_ERR_HIP) by the call that launched it.
+#ifdef MLA_DEBUG
+constexpr bool kDebug = true;
+#else
+constexpr bool kDebug = false;
+#endif
+
+// Sequence b (of batch) uses tokens 0 .. len_b - 1, len_b = (lens ? lens[b] : 0) + extra
+// (+ start[b] for a chunk); lens (device, may be null) each in [0, max_len].
+[[maybe_unused]] int debug_check_tokens(const mla_paged_cache* c, const int32_t* lens, int batch, int extra, int max_len,
+                       const int32_t* start = nullptr) {
+  std::vector<int32_t> len(batch, 0), st(batch, 0), row(c->max_blocks_per_seq);
+  if (lens && hipMemcpy(len.data(), lens, sizeof(int32_t) * batch, hipMemcpyDeviceToHost) != hipSuccess)
+    return MLA_ERR_HIP;
+  if (start && hipMemcpy(st.data(), start, sizeof(int32_t) * batch, hipMemcpyDeviceToHost) != hipSuccess)
+    return MLA_ERR_HIP;
+  for (int b = 0; b < batch; ++b) {
+    if (len[b] < 0 || (lens && len[b] > max_len) || st[b] < 0) {
+      std::fprintf(stderr, "mla debug: sequence %d: length %d (bound %d), start %d\n", b, len[b], max_len, st[b]);
+      return MLA_ERR_INVALID_ARG;
+    }
+    const int64_t tokens = (int64_t)st[b] + len[b] + extra;
+    const int64_t blocks = (tokens + c->block_size - 1) / c->block_size;
+    if (blocks > c->max_blocks_per_seq) {
+      std::fprintf(stderr, "mla debug: sequence %d: %lld tokens need %lld blocks, the table row has %d\n", b,
+                   (long long)tokens, (long long)blocks, c->max_blocks_per_seq);
+      return MLA_ERR_INVALID_ARG;
+    }
+    if (blocks == 0) continue;
+    if (hipMemcpy(row.data(), c->block_table + (int64_t)b * c->max_blocks_per_seq, sizeof(int32_t) * blocks,
+                  hipMemcpyDeviceToHost) != hipSuccess)
+      return MLA_ERR_HIP;
+    for (int64_t k = 0; k < blocks; ++k)
+      if (row[k] < 0 || row[k] >= c->num_blocks) {
+        std::fprintf(stderr, "mla debug: sequence %d: logical block %lld maps to block %d of %d\n", b, (long long)k,
+                     row[k], c->num_blocks);
+        return MLA_ERR_INVALID_ARG;
+      }
+  }
+  return MLA_OK;
+}
+
+// Appended token i goes to position pos[i] of sequence seq_idx[i] (both device).
+[[maybe_unused]] int debug_check_slots(const mla_paged_cache* c, const int32_t* seq_idx, const int32_t* pos, int n) {
+  std::vector<int32_t> sq(n), ps(n);
+  if (hipMemcpy(sq.data(), seq_idx, sizeof(int32_t) * n, hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemcpy(ps.data(), pos, sizeof(int32_t) * n, hipMemcpyDeviceToHost) != hipSuccess)
+    return MLA_ERR_HIP;
+  for (int i = 0; i < n; ++i) {
+    if (sq[i] < 0 || ps[i] < 0 || ps[i] / c->block_size >= c->max_blocks_per_seq) {
+      std::fprintf(stderr, "mla debug: token %d: sequence %d position %d outside the table\n", i, sq[i], ps[i]);
+      return MLA_ERR_INVALID_ARG;
+    }
+    int32_t blk = 0;
+    if (hipMemcpy(&blk, c->block_table + (int64_t)sq[i] * c->max_blocks_per_seq + ps[i] / c->block_size,
+                  sizeof(int32_t), hipMemcpyDeviceToHost) != hipSuccess)
+      return MLA_ERR_HIP;
+    if (blk < 0 || blk >= c->num_blocks) {
+      std::fprintf(stderr, "mla debug: token %d: position %d of sequence %d maps to block %d of %d\n", i, ps[i],
+                   sq[i], blk, c->num_blocks);
+      return MLA_ERR_INVALID_ARG;
+    }
+  }
   return MLA_OK;
 }
 
@@ -281,9 +356,11 @@ PrefillWs carve_prefill(Carve& cv, const mla_dims* d, int S, int T, int cus, boo
   return w;
 }
 
-#define MLA_HIP(x)                                  \
-  do {                                              \
-    if ((x) != hipSuccess) return MLA_ERR_HIP;      \
+#define MLA_HIP(x)                                                                      \
+  do {                                                                                  \
+    if ((x) != hipSuccess) return MLA_ERR_HIP;                                          \
+    if (kDebug && (hipDeviceSynchronize() != hipSuccess || hipGetLastError() != hipSuccess)) \
+      return MLA_ERR_HIP;                                                               \
   } while (0)
 
 // Plain row-major output epilogue.
@@ -406,6 +483,7 @@ int prefill_impl(const mla_dims* d, const mla_weights* w, const mla_paged_cache*
   Carve sz(nullptr);
   carve_prefill(sz, d, batch, T, cus, chunked, max_start);
   if (!workspace || ws_bytes < sz.off) return MLA_ERR_WORKSPACE;
+  if (kDebug && (st = debug_check_tokens(c, nullptr, batch, T, 0, start)) != MLA_OK) return st;
   Carve cv(workspace);
   PrefillWs ws = carve_prefill(cv, d, batch, T, cus, chunked, max_start);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -588,6 +666,7 @@ int mla_cache_append(const mla_dims* d, const mla_weights* w, const mla_paged_ca
   Carve sz(nullptr);
   carve_append(sz, d, n, cus);
   if (!workspace || ws_bytes < sz.off) return MLA_ERR_WORKSPACE;
+  if (kDebug && (st = debug_check_slots(c, seq_idx, pos, n)) != MLA_OK) return st;
   Carve cv(workspace);
   AppendWs ws = carve_append(cv, d, n, cus);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -622,6 +701,7 @@ int mla_decode_attention(const mla_dims* d, const mla_paged_cache* c, const void
   Carve sz(nullptr);
   carve_decode(sz, d, batch, max_kv_len - 1, num_splits, cus);
   if (!workspace || ws_bytes < sz.off) return MLA_ERR_WORKSPACE;
+  if (kDebug && (st = debug_check_tokens(c, kv_lens, batch, 0, max_kv_len)) != MLA_OK) return st;
   Carve cv(workspace);
   DecodeWs ws = carve_decode(cv, d, batch, max_kv_len - 1, num_splits, cus);
   DecodeAttnParams a{};
@@ -686,6 +766,7 @@ int mla_decode_attention_partials(const mla_dims* d, const mla_paged_cache* c, c
   a.cus = device_cus();
   a.leave_partials = true;
   if (!decode_bf16_partials(dt(d), a)) return MLA_ERR_UNSUPPORTED;
+  if (kDebug && (st = debug_check_tokens(c, kv_lens, batch, 0, max_kv_len)) != MLA_OK) return st;
   *splits_out = a.splits;
   MLA_HIP(decode_attention(dt(d), a, reinterpret_cast<hipStream_t>(stream)));
   return MLA_OK;
@@ -726,6 +807,8 @@ int decode_impl(const mla_dims* d, const mla_weights* w, const mla_paged_cache* 
   Carve sz(nullptr);
   carve_decode(sz, d, batch, max_ctx_len, num_splits, cus);
   if (!workspace || ws_bytes < sz.off) return MLA_ERR_WORKSPACE;
+  // the new token goes to position ctx_lens[b]: ctx_lens[b] + 1 tokens per sequence
+  if (kDebug && (st = debug_check_tokens(c, ctx_lens, batch, 1, max_ctx_len)) != MLA_OK) return st;
   Carve cv(workspace);
   DecodeWs ws = carve_decode(cv, d, batch, max_ctx_len, num_splits, cus);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
