@@ -298,10 +298,7 @@ constexpr int a_after_b(int q) {
 
 __shared__ __attribute__((aligned(1024))) char g_sk_a0[64 * skinny::kAChunkRow];
 __shared__ __attribute__((aligned(1024))) char g_sk_a1[64 * skinny::kAChunkRow];
-__shared__ __attribute__((aligned(1024))) char g_sk_b0[skinny::kWaves * skinny::kStage];
-__shared__ __attribute__((aligned(1024))) char g_sk_b1[skinny::kWaves * skinny::kStage];
-__shared__ __attribute__((aligned(1024))) char g_sk_b2[skinny::kWaves * skinny::kStage];
-static_assert(skinny::kNS == 3, "one LDS array per stage");
+__shared__ __attribute__((aligned(1024))) char g_sk_b[skinny::kNS][skinny::kWaves * skinny::kStage];
 
 __device__ __forceinline__ uint32_t lds_addr(const char* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
@@ -309,7 +306,7 @@ __device__ __forceinline__ uint32_t lds_addr(const char* p) {
 template <int AB>
 __device__ __forceinline__ char* sk_abuf() { return AB == 0 ? g_sk_a0 : g_sk_a1; }
 template <int ST>
-__device__ __forceinline__ char* sk_bbuf() { return ST == 0 ? g_sk_b0 : (ST == 1 ? g_sk_b1 : g_sk_b2); }
+__device__ __forceinline__ char* sk_bbuf() { return g_sk_b[ST]; }
 
 struct SkinnyCtx {
   const bf16* a;        // activation row 0 of this batch at k = kb
@@ -418,6 +415,15 @@ __device__ __forceinline__ void sk_step(const SkinnyCtx& x, int s, floatx16 (&ac
   }
 }
 
+// The first kNS - 1 weight stages.
+template <int ST>
+__device__ __forceinline__ void sk_prologue_b(const SkinnyCtx& x) {
+  if constexpr (ST < skinny::kNS - 1) {
+    sk_issue_b<ST>(x, ST);
+    sk_prologue_b<ST + 1>(x);
+  }
+}
+
 // Steps s .. s + kPeriod - 1 with compile-time ring, buffer and chunk positions.
 template <int MB, int U>
 __device__ __forceinline__ void sk_period(const SkinnyCtx& x, int s, floatx16 (&acc)[MB]) {
@@ -473,9 +479,7 @@ __global__ void __launch_bounds__(256)
 
   if (x.nsteps > 0) {
     sk_issue_a<MB, 0>(x, 0);
-    sk_issue_b<0>(x, 0);
-    sk_issue_b<1>(x, 1);
-    static_assert(kNS == 3, "prologue fills kNS - 1 stages");
+    sk_prologue_b<0>(x);
     for (int s = 0; s < x.nsteps; s += kPeriod) sk_period<MB, 0>(x, s, acc);
     // the ring's last copies (re-reads past the end) must land before the LDS is released
     MLA_WAVE_WAIT(waitcnt_vm(0));
