@@ -563,25 +563,29 @@ __device__ __forceinline__ uint64_t sp_pv(SplitState& st, int nhb_rt, int w, int
   return __builtin_amdgcn_ballot_w64(req);
 }
 
-// Waits until this wave's copies of the next tile have landed, with those of the one after it still
-// in flight (waves 0-3 issue nine copies per tile, 4-7 none), and until its LDS writes (the
-// probabilities it publishes) have completed; then the workgroup barrier.
+// Waits until this wave's copies of the next tile have landed, with those of the one after it (issued
+// at the end of this phase) still in flight (waves 0-3 issue nine copies per tile, 4-7 none), and
+// until its LDS writes (the probabilities it publishes) have completed; then the workgroup barrier.
 __device__ __forceinline__ void sp_barrier_next(int w) {
   if (w < 4) MLA_TILE_BARRIER(waitcnt_vm_lgkm0(tiled::kDmaPerWave));
   else MLA_TILE_BARRIER(waitcnt_vm_lgkm0(0));
 }
 
-// The phase of tile t (buffer B = (t - t_begin) % 4; t == t_end: only tile t-1's P.V): refill the
-// buffer tile t-2 left with tile t+2, P.V of tile t-1, S of tile t.  Returns nonzero, the same in
-// every wave, when tile t-1's probabilities carry a restart request.
+// The phase of tile t (buffer B = (t - t_begin) % 4; t == t_end: only tile t-1's P.V): P.V of tile
+// t-1, S of tile t, then the copies of tile t+2 into the buffer tile t-2 left.  The copies go out
+// at the end of the phase: the copying waves (0-3) finish their products before the others, which
+// share their SIMDs, so the issue overlaps the others' last products instead of delaying the
+// copying waves' first ones (measured: 174.5 against 177.0 us); tile t+2 still has a whole phase
+// to land.  Returns nonzero, the same in every wave, when tile t-1's probabilities carry a restart
+// request.
 template <int B, bool FULL>
 __device__ __forceinline__ uint64_t sp_phase(const TiledCtx& c, const Frag8<bf16> (&q)[18], SplitState& st, int t,
                                              int t_end, float scale_log2, bool s_wave, int nhb, int w, int lane) {
   using namespace tiled;
   constexpr int BPREV = (B + 3) % kNBuf, BNEXT2 = (B + 2) % kNBuf;
-  issue_tile<BNEXT2>(c, t + 2, t + 2 < t_end, w, lane);
   const uint64_t req = sp_pv<BPREV, (B + 1) & 1, FULL>(st, nhb, w, lane);
   if (t < t_end) sp_scores_wave<B, B & 1>(q, st, t, c.kv_len, scale_log2, s_wave, w, lane);
+  issue_tile<BNEXT2>(c, t + 2, t + 2 < t_end, w, lane);
   sp_barrier_next(w);
   return req;
 }
