@@ -1169,13 +1169,14 @@ __global__ void __launch_bounds__(64 * NW) uv_kernel(const bf16* __restrict__ oh
 
 bool uv_ok(DType t, int d_h, int d_c) { return t == DType::BF16 && d_c == uvk::kDc && d_h % uvk::kCols == 0; }
 bool uv_parts_ok(DType t, int d_h, int d_c) { return uv_ok(t, d_h, d_c) && d_h == 16 * uvk::kWavesParts; }
+int uv_parts_workgroups(int B, int n_h) { return (n_h + 7) / 8 * 8 * ((B + uvk::kMBParts - 1) / uvk::kMBParts); }
 
 hipError_t uv_run(const void* ohat, const void* w_uv, void* o, float* o32, int B, int n_h, int d_h,
                   hipStream_t s, const UvPartials* parts) {
   if (B == 0) return hipSuccess;
   if (parts) {
     if (d_h != 16 * uvk::kWavesParts || parts->splits < 1) return hipErrorInvalidValue;
-    const int blocks = (n_h + 7) / 8 * 8 * ((B + uvk::kMBParts - 1) / uvk::kMBParts);
+    const int blocks = uv_parts_workgroups(B, n_h);
     hipLaunchKernelGGL((uv_kernel<uvk::kWavesParts, true>), dim3(blocks), dim3(64 * uvk::kWavesParts), 0, s,
                        nullptr, *parts, reinterpret_cast<const bf16*>(w_uv), reinterpret_cast<bf16*>(o), o32, B,
                        n_h, d_h);

@@ -119,6 +119,8 @@ struct UvPartials {
 };
 bool uv_ok(DType t, int d_h, int d_c);
 bool uv_parts_ok(DType t, int d_h, int d_c);
+// Workgroups of the W_UV kernel that combines the partitions itself, for B rows of n_h heads.
+int uv_parts_workgroups(int B, int n_h);
 hipError_t uv_run(const void* ohat, const void* w_uv, void* o, float* o32, int B, int n_h, int d_h,
                   hipStream_t s, const UvPartials* parts = nullptr);
 // fp8 cache quantiser (latent_fp8.hip).  Destination of entry row r: dense row r of `codes` /

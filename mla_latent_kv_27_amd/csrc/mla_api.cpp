@@ -886,8 +886,13 @@ int decode_impl(const mla_dims* d, const mla_weights* w, const mla_paged_cache* 
     a.part_m = ws.attn.pm; a.part_l = ws.attn.pl; a.part_o = ws.attn.po;
     a.units = ws.attn.balanced ? ws.attn.units : nullptr; a.cus = cus;
     a.o_hat = ws.ohat; a.lse = nullptr;
-    // with several partitions and the W_UV kernel that combines them, the combine pass is skipped
-    a.leave_partials = a.splits > 1 && uv_parts_ok(t, d->d_h, d->d_c) && decode_bf16_partials(t, a);
+    // with several partitions and the W_UV kernel that combines them, the combine pass is skipped;
+    // not when many partitions meet few workgroups of that kernel (a small batch with few heads):
+    // the combine kernel's workgroup per row then spreads the partition reads over the chip
+    // (measured: V2-Lite, batch 8, up to 128 partitions: 69.4 against 77.7 us per step; the
+    // 128-head long-context batch keeps the fused combine, 192.5 against 209.2 us)
+    const bool fused_combine = a.splits < 16 || uv_parts_workgroups(B, d->n_h) >= cus / 2;
+    a.leave_partials = a.splits > 1 && fused_combine && uv_parts_ok(t, d->d_h, d->d_c) && decode_bf16_partials(t, a);
     MLA_HIP(decode_attention(t, a, s));
     parts.m = a.part_m; parts.l = a.part_l; parts.o = a.part_o;
     parts.splits = a.leave_partials ? a.splits : 0;

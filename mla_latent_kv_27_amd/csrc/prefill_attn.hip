@@ -289,7 +289,6 @@ __device__ __forceinline__ void pf2_compute(const Frag8<bf16> (&q)[12], Pf2State
                                             bool masked, float scale_log2, int lane) {
   using namespace pf2;
   const char* st = pf_stage<ST>();
-  asm volatile("" : "+v"(lane));
   const int g = lane >> 5, l32 = lane & 31, x = vswz(l32);
   const int j0 = kt * kKV;
   floatx16 sc[2];
