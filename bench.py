@@ -474,7 +474,7 @@ def main():
         "step_TFLOPs": round((attn_f + proj_f) / (ms / 1e3) / 1e12, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "kernel": f"{'decode_attn_fp8_kernel' if fp8 else 'decode_attn_tiled_kernel'} "
+                     "kernel": f"decode_attn_tiled_kernel{' over the fp8 cache' if fp8 else ''} "
                                f"(mla_decode_attention_partials, {att_splits} KV "
                                f"partitions per sequence, partials left for the W_UV kernel as in the step)",
                      "kernel_ms": round(attn_ms, 5), "algorithmic_bytes": core_bytes,

@@ -129,3 +129,34 @@ def test_fp8_decode_end_to_end(name, lens):
     check(u.float().cpu().numpy(), ref["u"], dims.dtype, f"{name} fp8 decode u")
     new_codes = np.stack([pool.read_codes(b, L + 1)[0][L] for b, L in enumerate(lens)])
     assert np.mean(new_codes == ref["codes"]) >= 0.99, f"{name}: new entries' codes"
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+def test_fp8_attention_corrupt_scale_finishes(splits):
+    """A NaN latent scale on one attended token of one sequence: the kernel still finishes (a NaN
+    probability cannot pose as the partition-restart request), that sequence's outputs are NaN,
+    and the clean sequence next to it still matches the oracle."""
+    dims = S.V2
+    cd = M.make_dims(dims.d_model, dims.n_h, dims.d_h, dims.d_c, dims.d_cq, dims.d_hr, dims.dtype,
+                     dims.softmax_scale, dims.rope_base, "fp8")
+    lens = [700, 300]
+    B = len(lens)
+    pool = WL.PagedPool(dims, lens, block_size=64, fp8=True)
+    deq = []
+    for b, L in enumerate(lens):
+        codes = S.fp8_codes(L, dims.entry, seed=500 + b)
+        scales = S.fp8_scales(L, seed=600 + b)
+        if b == 0:
+            scales[650, 0] = np.nan  # in the last partition for every split count here
+        pool.write_codes(b, torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda())
+        deq.append(F.dequantize(codes, scales, dims.d_c))
+    rng = np.random.default_rng(8)
+    q = S.to_dtype((rng.standard_normal((B, dims.n_h, dims.entry)) * 0.5).astype(np.float32), dims.dtype)
+    kv = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    ws = WL.ws_tensor(M.workspace_size(cd, M.OP_DECODE, batch=B, max_ctx_len=max(lens) - 1, num_splits=splits))
+    oh = torch.empty((B, dims.n_h, dims.d_c), dtype=torch.bfloat16, device="cuda")
+    M.decode_attention(cd, pool.ccache, WL.to_device(q, dims), kv, max(lens), oh, ws, num_splits=splits)
+    torch.cuda.synchronize()
+    assert np.isnan(oh[0].float().cpu().numpy()).all()
+    ref, _ = O.latent_attention(q[1:2], deq[1], np.array([lens[1]]), O.softmax_scale(dims), dims.d_c)
+    check(oh[1].float().cpu().numpy(), ref[0], dims.dtype, "clean sequence next to a corrupt one")
