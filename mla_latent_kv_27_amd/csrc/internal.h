@@ -104,8 +104,11 @@ GemmPlan gemm_plan(int M, int N, int K, int batch, int cus, bool skinny_ok);
 // W_UK absorption for bf16 (d_h == 128, d_c a multiple of 128):
 // qhat[b*out_ld + h*out_hs + c] = sum_k qc[(b*n_h + h)*d_h + k] * w_uk[(h*d_h + k)*d_c + c].
 bool absorb_ok(DType t, int d_h, int d_c);
+struct QuantJob;
+// With qj (a decode step over the fp8 cache), the same launch also quantises the step's new entries
+// (qj->n rows) in workgroups of its own, which saves the quantiser its launch.
 hipError_t absorb_run(const void* qc, const void* w_uk, void* qhat, int B, int n_h, int d_h, int d_c,
-                      int64_t out_ld, int64_t out_hs, hipStream_t s);
+                      int64_t out_ld, int64_t out_hs, hipStream_t s, const QuantJob* qj = nullptr);
 // o = W_UV per head for bf16 (d_c == 512, d_h a multiple of 64):
 // o[(b*n_h + h)*d_h + d] = sum_c w_uv[(h*d_h + d)*512 + c] * ohat[(b*n_h + h)*512 + c]; o32 (may be
 // null) receives the same values in fp32.
@@ -134,6 +137,17 @@ struct QuantDst {
   const int32_t* row_pos = nullptr;
 };
 bool fp8_cache_ok(int d_c, int d_hr);
+// n staged bf16 entries (rows src_ld elements apart) to quantise into dst, with the arguments of
+// quantize_entries_run, for a launch that does it on the side (absorb_run).
+struct QuantJob {
+  void* src = nullptr;
+  int64_t src_ld = 0;
+  int n = 0;
+  QuantDst dst;
+  const void* gain = nullptr;
+  float eps = 0.f;
+  bool writeback = false;
+};
 // Quantises n bf16 entries (rows src_ld elements apart) into dst; with gain, their latent part is
 // RMS-normalised first (and written back into src when writeback).
 hipError_t quantize_entries_run(const void* src, int64_t src_ld, int n, const QuantDst& dst, hipStream_t s,

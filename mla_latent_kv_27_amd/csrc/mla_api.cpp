@@ -417,11 +417,14 @@ inline bool staged_entries(const mla_dims* d, const mla_weights* w) { return fp8
 // Staged rows -> their cache slots (seq == nullptr: row r belongs to sequence r): the c^KV norm
 // in place, then quantised (fp8) or copied into the pages.  cq (n_q rows), when given, gets the
 // c^q norm in the same launch on the bf16/fp32 path.
+// quant_later: the fp8 quantisation is left to a later launch (the decode step's W_UK absorption).
 int finish_entries(const mla_dims* d, const mla_weights* w, const mla_paged_cache* c, void* staged, int n,
-                   const int32_t* seq, const int32_t* pos, hipStream_t s, void* cq = nullptr, int n_q = 0) {
+                   const int32_t* seq, const int32_t* pos, hipStream_t s, void* cq = nullptr, int n_q = 0,
+                   bool quant_later = false) {
   const bool q_norm = cq && w->g_cq;
   if (fp8_cache(d)) {
-    MLA_HIP(quantize_entries_run(staged, entry(d), n, quant_dst(c, seq, pos), s, w->g_ckv, eps_of(d), true));
+    if (!quant_later)
+      MLA_HIP(quantize_entries_run(staged, entry(d), n, quant_dst(c, seq, pos), s, w->g_ckv, eps_of(d), true));
     if (q_norm) MLA_HIP(rmsnorm_rows(dt(d), cq, n_q, d->d_cq, d->d_cq, w->g_cq, eps_of(d), s));
     return MLA_OK;
   }
@@ -816,6 +819,9 @@ int decode_impl(const mla_dims* d, const mla_weights* w, const mla_paged_cache* 
   const int B = batch, E = entry(d), qw = q_in(d);
 
   const void* qin = h;
+  // over the fp8 cache the new entries are quantised by the W_UK absorption's launch (workgroups of
+  // its own; the attention, which reads them, comes after it)
+  const bool quant_in_absorb = fp8_cache(d) && absorb_ok(t, d->d_h, d->d_c);
   {  // [c^q | c^KV | k^R] = [W_DQ; W_DKV; W_KR] h: c^q to the workspace, the new token's cache
      // entry to position ctx_lens[b] of its sequence
     GemmParams g;
@@ -842,7 +848,8 @@ int decode_impl(const mla_dims* d, const mla_weights* w, const mla_paged_cache* 
     }
     MLA_HIP(gemm_run(t, g, ws.gm.kvq, ws.partial, s));
     if (staged_entries(d, w)) {  // entries to their pages; the c^q norm rides along
-      const int rc = finish_entries(d, w, c, ws.staged, B, nullptr, ctx_lens, s, d->d_cq > 0 ? ws.cq : nullptr, B);
+      const int rc = finish_entries(d, w, c, ws.staged, B, nullptr, ctx_lens, s, d->d_cq > 0 ? ws.cq : nullptr, B,
+                                    quant_in_absorb);
       if (rc != MLA_OK) return rc;
     } else if (w->g_cq) {
       MLA_HIP(rmsnorm_rows(t, ws.cq, B, d->d_cq, d->d_cq, w->g_cq, eps_of(d), s));
@@ -863,7 +870,14 @@ int decode_impl(const mla_dims* d, const mla_weights* w, const mla_paged_cache* 
     MLA_HIP(gemm_run(t, g, ws.gm.q, ws.partial, s));
   }
   if (absorb_ok(t, d->d_h, d->d_c)) {  // q_hat_i = W_UK_i^T q^C_i -> columns [0, d_c) of each head's row
-    MLA_HIP(absorb_run(ws.qc, w->W_UK, ws.qcat, B, d->n_h, d->d_h, d->d_c, (int64_t)d->n_h * E, E, s));
+    QuantJob qj;
+    if (quant_in_absorb) {
+      qj.src = ws.staged; qj.src_ld = E; qj.n = B;
+      qj.dst = quant_dst(c, nullptr, ctx_lens);
+      qj.gain = w->g_ckv; qj.eps = eps_of(d); qj.writeback = true;
+    }
+    MLA_HIP(absorb_run(ws.qc, w->W_UK, ws.qcat, B, d->n_h, d->d_h, d->d_c, (int64_t)d->n_h * E, E, s,
+                       quant_in_absorb ? &qj : nullptr));
   } else {
     GemmParams g;
     g.A = ws.qc; g.lda = (int64_t)d->n_h * d->d_h; g.strideA = d->d_h;
