@@ -497,9 +497,16 @@ constexpr int kScales = kT * 8;             // 256: (s_c, s_r) per token
 constexpr int kBuf = kCodes + kScales;
 constexpr int kCodeCopies = kCodes / 1024;  // 18 one-KiB copies per tile
 constexpr int kDmaPerWave = 5;              // waves 0-2: five code copies; wave 3: three and the scales
-// chunk c of token row t sits at slot c ^ swz(t): the 16 rows of a K fragment read, and the 32 rows
-// of a V^T transpose read, fall in distinct banks
-__device__ __forceinline__ int swz(int t) { return ((t >> 2) & 3) ^ (((t >> 4) & 1) << 1); }
+// Chunk c of token row t sits at slot c ^ swz_lat(t) for the 32 latent chunks and c ^ swz_rope(t) for
+// the 4 rope chunks (each a permutation within its part of the row).  LDS serves a 16-byte read 8
+// lanes at a time and an 8-byte read 16 lanes at a time over 32 banks (128 bytes); rows are 576
+// bytes = 16 banks apart, so a chunk's bank group (of 4) is (4 (t & 1) + slot) mod 8.  With these
+// swizzles every read of the kernel takes its minimum number of passes: a K fragment read
+// (8 consecutive rows, one chunk: u(t) = swz_lat(t) ^ 4 (t & 1) takes 8 distinct values on them), a
+// rope read (8 consecutive rows, one chunk: (t & 1, (t >> 1) & 3) distinct) and a V^T transpose read
+// (the tokens 4g .. 4g+3 and 16 + 4g .. +3 of a lane group: u distinct on them as well).
+__device__ __forceinline__ int swz_lat(int t) { return (t & 3) | ((((t >> 4) ^ (t >> 2) ^ t) & 1) << 2); }
+__device__ __forceinline__ int swz_rope(int t) { return (t >> 1) & 3; }
 }  // namespace tiled8
 
 typedef int intx2 __attribute__((ext_vector_type(2)));
@@ -545,7 +552,7 @@ __device__ __forceinline__ void issue_tile8(const TiledCtx& c, int tile, bool li
       if (P < kCodeCopies) {
         const int byte = P * 1024 + ln * 16;
         const int t = byte / kRow, sl = (byte - t * kRow) >> 4;
-        dma16_ring(codes, t * kRow + ((sl ^ swz(t)) << 4), dst + P * 1024);
+        dma16_ring(codes, t * kRow + ((sl ^ (sl < 32 ? swz_lat(t) : swz_rope(t))) << 4), dst + P * 1024);
       } else if (P == kCodeCopies) {
         dma4_ring(dma_span(c.scales + 2 * slot0, rows * 8), ln * 4, dst + kCodes);
       }
@@ -558,18 +565,18 @@ struct QBf16 {
 };
 struct QFp8 {
   intx8 c_hi[4], c_lo[4];  // latent part, chunk kc: codes of dims 128 kc + 32 g .. +31
-  long r_hi[2], r_lo[2];   // rope part, chunk kr: codes of rope dims 32 kr + 8 g .. +7
+  long r_hi[2], r_lo[2];   // rope part, MFMA kr: codes of rope dims 16 g + 8 kr .. +7
   float s;                 // the head's query scale
 };
 
 // The head's query as hi + lo e4m3 codes with one scale: s = amax / 448 over the head's 576 values
 // (its four lane groups), hi = e4m3(q / s), lo = e4m3(q / s - hi).
 __device__ __forceinline__ void load_q_fp8(QFp8& q, const bf16* qrow, bool live, int g) {
-  Frag8<bf16> qv[18];  // 0..15: latent dims 128 (i / 4) + 32 g + 8 (i % 4); 16, 17: rope dims 32 kr + 8 g
+  Frag8<bf16> qv[18];  // 0..15: latent dims 128 (i / 4) + 32 g + 8 (i % 4); 16, 17: rope dims 16 g + 8 kr
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < 18; ++i) {
-    const int off = i < 16 ? 128 * (i >> 2) + 32 * g + 8 * (i & 3) : 512 + 32 * (i - 16) + 8 * g;
+    const int off = i < 16 ? 128 * (i >> 2) + 32 * g + 8 * (i & 3) : 512 + 16 * g + 8 * (i - 16);
     if (live) load8(qv[i], qrow + off);
     else zero8(qv[i]);
 #pragma unroll
@@ -630,7 +637,7 @@ __device__ __forceinline__ void sp8_scores(const QFp8& q, SplitState& st, int t,
   floatx4 scr[2] = {floatx4{0, 0, 0, 0}, floatx4{0, 0, 0, 0}};
   {
     const char* rows[2] = {buf + l16 * kRow, buf + (16 + l16) * kRow};
-    const int sw[2] = {swz(l16), swz(16 + l16)};
+    const int sw[2] = {swz_lat(l16), swz_lat(16 + l16)};
     auto kfrag = [&](int kc, int tb) {
       const int ch = 8 * kc + 2 * g;
       const intx4 x = *reinterpret_cast<const intx4*>(rows[tb] + ((ch ^ sw[tb]) << 4));
@@ -646,16 +653,20 @@ __device__ __forceinline__ void sp8_scores(const QFp8& q, SplitState& st, int t,
       acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i & 1], q.c_hi[i >> 1], acc, 0, 0, 0, 127, 0, 127);
       acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i & 1], q.c_lo[i >> 1], acc, 0, 0, 0, 127, 0, 127);
     }
-    // rope part: 8 codes of dims 32 kr + 8 g: half (g & 1) of slot 32 + 2 kr + (g >> 1)
+    // rope part: the k split of the two 16x16x32 MFMAs is again free as long as both operands
+    // follow it: lane group g takes rope dims 16 g + 8 kr .. +7 in MFMA kr, so one 16-byte read of
+    // chunk 32 + g serves both
 #pragma unroll
-    for (int kr = 0; kr < 2; ++kr)
+    for (int tb = 0; tb < 2; ++tb) {
+      const int r = 16 * tb + l16;
+      const intx4 k16 = *reinterpret_cast<const intx4*>(rows[tb] + (((32 + g) ^ swz_rope(r)) << 4));
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        const int ch = 32 + 2 * kr + (g >> 1);
-        const long k8 = *reinterpret_cast<const long*>(rows[tb] + ((ch ^ sw[tb]) << 4) + (g & 1) * 8);
+      for (int kr = 0; kr < 2; ++kr) {
+        const long k8 = (long)(((uint64_t)(uint32_t)k16[2 * kr + 1] << 32) | (uint32_t)k16[2 * kr]);
         scr[tb] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(k8, q.r_hi[kr], scr[tb], 0, 0, 0);
         scr[tb] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(k8, q.r_lo[kr], scr[tb], 0, 0, 0);
       }
+    }
   }
   // ---- per-token and per-head scales; softmax against the head's reference (masked past the
   // context on a partial tile)
@@ -735,11 +746,11 @@ __device__ __forceinline__ uint64_t sp_pv(SplitState& st, int nhb_rt, int w, int
     // l16 / 2, so lane i of group g receives dim i of exactly the tokens its P fragment holds; the
     // codes (exact in bf16) are converted in registers, the token's s_c being folded into P
     const int tok = 16 * (l16 >> 3) + 4 * g + ((l16 >> 1) & 3);
-    const int sw = g ^ ((l16 >> 3) << 1);  // swz(tok)
-    const char* row = buf + tok * kRow + 64 * w + 8 * (l16 & 1);
+    const int sw = swz_lat(tok);
+    const char* row = buf + tok * kRow + 8 * (l16 & 1);
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-      const intx2 c8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_intx2_t*)(row + 16 * (db ^ sw)));
+      const intx2 c8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_intx2_t*)(row + 16 * ((4 * w + db) ^ sw)));
       const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c8[0], 1.f, false);
       const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c8[0], 1.f, true);
       const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c8[1], 1.f, false);
