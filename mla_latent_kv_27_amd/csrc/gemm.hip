@@ -28,6 +28,13 @@ __device__ __forceinline__ void rope_pair(const Epilogue& e, int row, int col, f
   }
 }
 
+// Offset of column c within its output row: groups of e.group columns, group_stride apart.
+__device__ __forceinline__ int64_t epi_col(const Epilogue& e, int c) {
+  int j = c % e.group;
+  if (e.perm16) j = (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1);  // pieces 1 and 2 of 16 swap
+  return (int64_t)(c / e.group) * e.group_stride + e.group_off + j;
+}
+
 template <typename T>
 __device__ __forceinline__ void epi_store(const Epilogue& e, int z, int row, int col, float v) {
   int64_t rbase;
@@ -40,8 +47,7 @@ __device__ __forceinline__ void epi_store(const Epilogue& e, int z, int row, int
   } else {
     rbase = (int64_t)row * e.ldc;
   }
-  const int64_t idx = (int64_t)z * e.batch_stride + rbase + (int64_t)(col / e.group) * e.group_stride +
-                      e.group_off + col % e.group;
+  const int64_t idx = (int64_t)z * e.batch_stride + rbase + epi_col(e, col);
   if (e.c_f32)
     reinterpret_cast<float*>(e.C)[idx] = v;
   else
@@ -70,7 +76,7 @@ __device__ __forceinline__ void out_quad(const GemmParams& p, int z, int row, in
   const bool hi = col >= p.E0;
   const Epilogue& e = hi ? p.epi2 : p.epi;
   const int c = hi ? col - p.E0 : col;
-  if (c % e.group + 3 < e.group && !e.c_f32 && !e.C2 && sizeof(T) == 2 &&
+  if (c % e.group + 3 < e.group && (!e.perm16 || c % e.group % 4 == 0) && !e.c_f32 && !e.C2 && sizeof(T) == 2 &&
       (reinterpret_cast<uintptr_t>(e.C) & 7) == 0) {
     int64_t rbase;
     if (e.block_table) {
@@ -80,8 +86,7 @@ __device__ __forceinline__ void out_quad(const GemmParams& p, int z, int row, in
     } else {
       rbase = (int64_t)row * e.ldc;
     }
-    const int64_t idx = (int64_t)z * e.batch_stride + rbase + (int64_t)(c / e.group) * e.group_stride + e.group_off +
-                        c % e.group;
+    const int64_t idx = (int64_t)z * e.batch_stride + rbase + epi_col(e, c);
     bf16x4 q = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
     *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(e.C) + idx) = q;
     return;
@@ -682,10 +687,7 @@ __global__ void __launch_bounds__(512) gemm_big_kernel(GemmParams p) {
   const bool hi = col >= p.E0;
   const int c = hi ? col - p.E0 : col;
   // this lane's epilogue fields, picked once (the two epilogues are kernel arguments)
-  const int e_group = hi ? p.epi2.group : p.epi.group;
-  const int64_t col_off = (int64_t)z * (hi ? p.epi2.batch_stride : p.epi.batch_stride) +
-                          (int64_t)(c / e_group) * (hi ? p.epi2.group_stride : p.epi.group_stride) +
-                          (hi ? p.epi2.group_off : p.epi.group_off) + c % e_group;
+  const int64_t col_off = (int64_t)z * (hi ? p.epi2.batch_stride : p.epi.batch_stride) + epi_col(hi ? p.epi2 : p.epi, c);
   const int e_rope0 = hi ? p.epi2.rope_col0 : p.epi.rope_col0, e_dhr = hi ? p.epi2.d_hr : p.epi.d_hr;
   const float2* e_tab = hi ? p.epi2.rope_tab : p.epi.rope_tab;
   const bool rot = c >= e_rope0;
@@ -708,8 +710,7 @@ __global__ void __launch_bounds__(512) gemm_big_kernel(GemmParams p) {
   const bool v_hi = v_col >= p.E0;
   const int v_c = v_hi ? v_col - p.E0 : v_col;
   const Epilogue& ve = v_hi ? p.epi2 : p.epi;
-  const int64_t v_off = (int64_t)z * ve.batch_stride + (int64_t)(v_c / ve.group) * ve.group_stride +
-                        ve.group_off + v_c % ve.group;
+  const int64_t v_off = (int64_t)z * ve.batch_stride + epi_col(ve, v_c);  // 4 columns stay together
   const bool v_rot = ve.rope_tab != nullptr && v_c >= ve.rope_col0;
   const int v_dhr = ve.d_hr;
   const int v_rk = v_rot ? ((v_c - ve.rope_col0) % v_dhr) >> 1 : 0;

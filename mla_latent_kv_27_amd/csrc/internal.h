@@ -59,6 +59,9 @@ struct Epilogue {
   int64_t ldc = 0, batch_stride = 0;
   int group = 1 << 30;
   int64_t group_stride = 0, group_off = 0;
+  // the 4-column pieces of every 16 columns of a group are stored in the order 0, 2, 1, 3 (the
+  // pipelined prefill attention's V^T rows: a lane's 8 keys of a 16-key step then lie together)
+  bool perm16 = false;
   int rope_col0 = 1 << 30;
   int d_hr = 0;
   const float2* rope_tab = nullptr;
@@ -245,7 +248,8 @@ struct PrefillAttnParams {
   const void* kr;     // [S*Tk] rows of ld_kr elements; k^R at column kr_off
   int64_t ld_kr;
   int kr_off;
-  const void* vt;     // [n_h][d_h][S][Tkp]       (W_UV_i c^KV, token-contiguous; Tkp = Tk rounded up to 64)
+  const void* vt;     // [n_h][d_h][S][Tkp]       (W_UV_i c^KV, token-contiguous; Tkp = Tk rounded up to 64;
+                      //  for the pipelined kernel with the key pieces of Epilogue::perm16)
   void* o;            // [S*T][n_h][d_h]
   float* o_f32;       // optional fp32 copy
   int S, T, n_h, d_h, d_hr;
@@ -254,6 +258,9 @@ struct PrefillAttnParams {
   float scale_log2;
 };
 bool prefill_supported(int d_h, int d_hr);
+// Whether prefill_attention takes the pipelined kernel for these sizes (its V^T rows then carry the
+// key order of Epilogue::perm16).
+bool prefill_pipelined(DType t, int d_h, int d_hr, int64_t S, int64_t Tk, int64_t ld_kr, int64_t k_ld);
 hipError_t prefill_attention(DType t, const PrefillAttnParams& p, hipStream_t s);
 
 }  // namespace mla

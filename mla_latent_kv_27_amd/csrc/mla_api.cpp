@@ -553,6 +553,7 @@ int prefill_impl(const mla_dims* d, const mla_weights* w, const mla_paged_cache*
     g.M = d->n_h * d->d_h; g.N = Mk; g.K = d->d_c;
     g.epi = dense(ws.vt, (int64_t)batch * ws.Tp);
     g.epi.group = ws.Tk; g.epi.group_stride = ws.Tp;
+    g.epi.perm16 = prefill_pipelined(t, d->d_h, d->d_hr, batch, ws.Tk, E, (int64_t)d->n_h * d->d_h);
     MLA_HIP(gemm_run(t, g, ws.v_p, ws.partial, s));
   }
   {

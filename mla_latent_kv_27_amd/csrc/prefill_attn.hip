@@ -223,10 +223,14 @@ constexpr int kCopies = kKCopies + kRCopies + kVCopies;
 // 16-byte chunk c of a row r sits at slot c ^ swizzle: 16 consecutive rows then cover all banks
 __device__ __forceinline__ int kslot(int r, int c) { return c ^ (r & 15); }         // 16-chunk rows
 __device__ __forceinline__ int rslot(int r, int c) { return c ^ ((r >> 1) & 7); }   // 8-chunk rows
-// V^T rows (128 bytes: 8 chunks): the 32 rows of a fragment read share parity in pairs of bank
-// halves, so the chunk is XORed with (row >> 1) & 7: each slot of a half serves two rows, the
-// least a 32-lane 8-byte read of 32 rows can do (row & 7 would give four)
-__device__ __forceinline__ int vswz(int d) { return (d >> 1) & 7; }
+// V^T rows (128 bytes: 8 chunks of 8 keys).  The rows arrive with the 4-key pieces of every 16 keys
+// in the order 0, 2, 1, 3 (the epilogue of the V^T product stores them so), which puts the 8 keys a
+// lane group takes in one 16-key step (4g .. 4g+3 and 8 + 4g .. +3) in one chunk.  A fragment read
+// is then one 16-byte read; LDS serves those 8 lanes (8 consecutive rows, one chunk) at a time, and
+// rows 128 bytes apart share banks, so the chunk is XORed with row & 7.
+__device__ __forceinline__ int vswz(int d) { return d & 7; }
+// position of key k in a V^T row
+__device__ __forceinline__ int vpos(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
 }  // namespace pf2
 
 __shared__ __attribute__((aligned(1024))) char g_pf_s0[pf2::kStage];
@@ -341,9 +345,10 @@ __device__ __forceinline__ void pf2_compute(const Frag8<bf16> (&q)[12], Pf2State
       s.l_part += e;
       sc[kb][r] = e;
     }
-  // O^T += V^T P^T: lane (dim 32 d + l32, group g) reads keys 16 (2kb + half) + 4g + 0..3 and
-  // + 8 + 0..3, i.e. chunk 4kb + 2half (+1) of its row, byte 8g
-  const char* vrow = st + kVOff + l32 * kVRow + 8 * g;
+  // O^T += V^T P^T: lane (dim 32 d + l32, group g) takes keys 16 (2kb + half) + 4g + 0..3 and
+  // + 8 + 0..3: chunk 4kb + 2half + g of its row
+  const char* vrow = st + kVOff + l32 * kVRow;
+  const int gx = g ^ x;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -351,14 +356,11 @@ __device__ __forceinline__ void pf2_compute(const Frag8<bf16> (&q)[12], Pf2State
       Frag8<bf16> pfr;
 #pragma unroll
       for (int e = 0; e < 8; ++e) pfr.v[e] = (bf16)sc[kb][8 * half + e];
-      const int c0 = 4 * kb + 2 * half;
+      const int cx = (4 * kb + 2 * half) ^ gx;  // (4kb + 2half + g) ^ x
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        const char* vr = vrow + d * 32 * kVRow;
-        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr + ((c0 ^ x) * 16));
-        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vr + (((c0 + 1) ^ x) * 16));
         Frag8<bf16> a;
-        a.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        a.v = *reinterpret_cast<const bf16x8*>(vrow + d * 32 * kVRow + cx * 16);
         s.o[d] = mma32(a, pfr, s.o[d]);
       }
     }
@@ -379,9 +381,9 @@ __device__ __forceinline__ void pf2_step(const Pf2Ctx& c, const Frag8<bf16> (&q)
   if (valid < kKV) {  // uniform: V^T columns of keys >= T (padding, uninitialised) -> 0
     char* v = pf_stage<ST>() + kVOff;
     for (int i = tid; i < kDH * (kKV - valid); i += 64 * kWaves) {
-      const int d = i / (kKV - valid), key = valid + i % (kKV - valid);
-      const int slot = (key >> 3) ^ vswz(d);
-      *reinterpret_cast<bf16*>(v + d * kVRow + slot * 16 + (key & 7) * 2) = (bf16)0.f;
+      const int d = i / (kKV - valid), pos = vpos(valid + i % (kKV - valid));
+      const int slot = (pos >> 3) ^ vswz(d);
+      *reinterpret_cast<bf16*>(v + d * kVRow + slot * 16 + (pos & 7) * 2) = (bf16)0.f;
     }
     MLA_TILE_BARRIER(kWaitLgkm0);
   }
@@ -512,12 +514,16 @@ static bool pf2_spans_fit(int64_t S, int64_t Tk, int64_t ld_kr, int64_t k_ld) {
          ((int64_t)(pf2::kDH - 1) * S * Tp + Tp) * 2 < (1LL << 31);
 }
 
+bool prefill_pipelined(DType t, int d_h, int d_hr, int64_t S, int64_t Tk, int64_t ld_kr, int64_t k_ld) {
+  return t == DType::BF16 && d_h == 128 && d_hr == 64 && pf2_spans_fit(S, Tk, ld_kr, k_ld);
+}
+
 hipError_t prefill_attention(DType t, const PrefillAttnParams& p, hipStream_t s) {
   const int64_t Tk = p.Tk > 0 ? p.Tk : p.T;
   if (!p.qc || !p.qr || !p.rope || !p.k || p.k_ld < (int64_t)p.n_h * p.d_h) return hipErrorInvalidValue;
   // the DeepSeek-V2 head sizes in bf16 take the pipelined kernel (unless a source span needs
   // 64-bit offsets); every other supported size the synchronous one
-  const bool pipelined = t == DType::BF16 && p.d_h == 128 && p.d_hr == 64 && pf2_spans_fit(p.S, Tk, p.ld_kr, p.k_ld);
+  const bool pipelined = prefill_pipelined(t, p.d_h, p.d_hr, p.S, Tk, p.ld_kr, p.k_ld);
   if (pipelined) {
     const int nqt = (p.T + pf2::kQ - 1) / pf2::kQ;
     const int units = p.S * p.n_h;
