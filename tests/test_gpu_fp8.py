@@ -160,3 +160,40 @@ def test_fp8_attention_corrupt_scale_finishes(splits):
     assert np.isnan(oh[0].float().cpu().numpy()).all()
     ref, _ = O.latent_attention(q[1:2], deq[1], np.array([lens[1]]), O.softmax_scale(dims), dims.d_c)
     check(oh[1].float().cpu().numpy(), ref[0], dims.dtype, "clean sequence next to a corrupt one")
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+def test_fp8_attention_reference_raise_restarts(splits):
+    """As the bf16 test of the same name, over the fp8 cache: one late entry aligned with head 0's
+    query passes its partition's first-tile reference by far more than the headroom, so the kernel
+    restarts the partition with the raised reference; the result still matches the oracle on the
+    dequantised cache."""
+    dims = S.V2
+    cd = M.make_dims(dims.d_model, dims.n_h, dims.d_h, dims.d_c, dims.d_cq, dims.d_hr, dims.dtype,
+                     dims.softmax_scale, dims.rope_base, "fp8")
+    lens = [700, 300]
+    B = len(lens)
+    rng = np.random.default_rng(43)
+    q = S.to_dtype((rng.standard_normal((B, dims.n_h, dims.entry)) * 0.3).astype(np.float32), dims.dtype)
+    spike = 600  # partition 0 of 1 (first tile 0..31) or partition 2 of 3 (first tile 512..543)
+    scale = O.softmax_scale(dims)
+    pool = WL.PagedPool(dims, lens, block_size=64, fp8=True)
+    deq = []
+    for b, L in enumerate(lens):
+        e = S.to_dtype(rng.standard_normal((L, dims.entry)).astype(np.float32), dims.dtype)
+        if b == 0:
+            e[spike] = S.to_dtype(20.0 * q[0, 0].astype(np.float32), dims.dtype)
+        codes, scales = F.quantize_entries(e.astype(np.float64), dims.d_c)
+        pool.write_codes(b, torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda())
+        deq.append(F.dequantize(codes, scales, dims.d_c))
+    s0 = deq[0] @ q[0, 0].astype(np.float64) * scale / np.log(2)
+    for p0 in (0, 512):
+        assert s0[spike] - np.max(s0[p0:p0 + 32]) > 70
+    kv = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    ws = WL.ws_tensor(M.workspace_size(cd, M.OP_DECODE, batch=B, max_ctx_len=max(lens) - 1, num_splits=splits))
+    oh = torch.empty((B, dims.n_h, dims.d_c), dtype=torch.bfloat16, device="cuda")
+    M.decode_attention(cd, pool.ccache, WL.to_device(q, dims), kv, max(lens), oh, ws, num_splits=splits)
+    torch.cuda.synchronize()
+    for b, L in enumerate(lens):
+        ref, _ = O.latent_attention(q[b:b + 1], deq[b], np.array([L]), scale, dims.d_c)
+        check(oh[b].float().cpu().numpy(), ref[0], dims.dtype, f"fp8 b={b} with a raised reference")

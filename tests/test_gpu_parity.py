@@ -199,6 +199,33 @@ def test_prefill_matches_oracle(name, batch, T):
         check(u[b].float().cpu().numpy(), ref["u"], dims.dtype, f"{name} u b={b}")
 
 
+def test_prefill_score_spike():
+    """Token 600's hidden state is scaled by 3 (then rounded to bf16, the input both sides see): for
+    many (query, head) pairs after it the score of key 600 passes the maximum over the keys before
+    its tile by up to 17 log2 units, past the prefill kernel's lazy-softmax threshold (8), so the
+    reference is raised and O rescaled in place mid-row.  Larger factors are no use: with a score
+    that large the bf16 rounding of the per-head keys alone moves the result past the bf16
+    tolerance (a CPU emulation of those roundings gives 0.75% of max|ref| at 3, 1.1% at 4, 8.9% at
+    64).  Rows before the spike and rows after it are checked apart."""
+    dims, recipe = SMALL["v2"]
+    W = S.make_weights(dims)
+    layer = WL.DeviceLayer(dims, W)
+    T, spike = 1000, 600
+    pool = WL.PagedPool(dims, [T], block_size=64)
+    hs = S.hidden_history(dims, 0, T, recipe)
+    hs[spike] = S.to_dtype((hs[spike] * 3.0).astype(np.float32), dims.dtype)
+    h = WL.to_device(hs[None], dims)
+    u = torch.empty((1, T, dims.d_model), dtype=WL.torch_dtype(dims), device="cuda")
+    oh = torch.empty((1, T, dims.n_h, dims.d_h), dtype=torch.float32, device="cuda")
+    ws = WL.prefill_workspace(layer, 1, T)
+    M.prefill(layer.cdims, layer.cweights, pool.ccache, h, u, ws, o_heads=oh)
+    torch.cuda.synchronize()
+    ref = O.mla_prefill(W, dims, hs)
+    o = oh[0].cpu().numpy()
+    check(o[:spike], ref["o"][:spike], dims.dtype, "o before the spike")
+    check(o[spike:], ref["o"][spike:], dims.dtype, "o from the spike on")
+
+
 def test_tiny_prefill_then_four_decode_steps():
     """The tiny fp32 workload: causal prefill of 16 tokens, then 4 decode steps."""
     dims = S.TINY
@@ -401,3 +428,42 @@ def test_decode_attention_corrupt_entry_finishes(splits):
     assert np.isnan(ohat[0].float().cpu().numpy()).all()
     ref, _ = O.latent_attention(q[1:2], pool.read_entries(1, lens[1]), [lens[1]], O.softmax_scale(dims), dims.d_c)
     check(ohat[1].float().cpu().numpy(), ref[0], dims.dtype, "clean sequence next to a corrupt one")
+
+
+def _spike_case(lens, spike, q, entries, scale, partition_starts):
+    """Checks on the CPU that the planted entry really passes the reference of its partition's first
+    tile by more than the kernels' headroom (64 log2 units), for head 0 of sequence 0."""
+    s = entries[0].astype(np.float64) @ q[0, 0].astype(np.float64) * scale / np.log(2)
+    for p0 in partition_starts:
+        assert s[spike] - np.max(s[p0:p0 + 32]) > 70, (p0, s[spike], np.max(s[p0:p0 + 32]))
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+def test_decode_attention_reference_raise_restarts(splits):
+    """One late cache entry of sequence 0 is aligned with head 0's query so that its score passes the
+    reference set by its partition's first tile by far more than the kernel's headroom: the kernel
+    must raise the reference and restart the partition, and still match the oracle (head 0's
+    softmax then sits almost entirely on that entry).  Random inputs never reach this path."""
+    dims = S.V2
+    layer = WL.DeviceLayer(dims, S.make_weights(dims))
+    lens = [700, 300]
+    B = len(lens)
+    rng = np.random.default_rng(41)
+    q = S.to_dtype((rng.standard_normal((B, dims.n_h, dims.entry)) * 0.3).astype(np.float32), dims.dtype)
+    entries = [S.to_dtype(rng.standard_normal((L, dims.entry)).astype(np.float32), dims.dtype) for L in lens]
+    spike = 600  # partition 0 of 1 (first tile 0..31) or partition 2 of 3 (first tile 512..543)
+    entries[0][spike] = S.to_dtype(20.0 * q[0, 0].astype(np.float32), dims.dtype)
+    scale = O.softmax_scale(dims)
+    _spike_case(lens, spike, q, entries, scale, [0, 512])
+    pool = WL.PagedPool(dims, lens, block_size=64)
+    for b in range(B):
+        pool.write_entries(b, WL.to_device(entries[b], dims))
+    kv = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    ws = WL.ws_tensor(M.workspace_size(layer.cdims, M.OP_DECODE, batch=B, max_ctx_len=max(lens) - 1,
+                                       num_splits=splits))
+    ohat = torch.empty((B, dims.n_h, dims.d_c), dtype=WL.torch_dtype(dims), device="cuda")
+    M.decode_attention(layer.cdims, pool.ccache, WL.to_device(q, dims), kv, max(lens), ohat, ws, num_splits=splits)
+    torch.cuda.synchronize()
+    for b, L in enumerate(lens):
+        ref, _ = O.latent_attention(q[b:b + 1], pool.read_entries(b, L), [L], scale, dims.d_c)
+        check(ohat[b].float().cpu().numpy(), ref[0], dims.dtype, f"b={b} with a raised reference")
