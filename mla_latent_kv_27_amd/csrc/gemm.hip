@@ -521,7 +521,8 @@ __global__ void __launch_bounds__(256)
 // Prefill-sized bf16 "NT" products (M in the thousands).  A workgroup of eight waves computes a
 // 256 x 256 tile, each wave 128 x 64 (4 x 2 blocks of 32x32x16 MFMA).  Both operands arrive by
 // direct global->LDS copies into two 64-k stages (the next stage's copies in flight while the
-// current one is multiplied), one barrier per stage.  LDS rows are 128 bytes (eight 16-byte
+// current one is multiplied), one barrier per stage; inside a stage the fragment reads of its
+// second half run while its first half is multiplied.  LDS rows are 128 bytes (eight 16-byte
 // chunks); chunk c of row r sits in slot c ^ ((r >> 1) & 7), which keeps the 16-byte fragment
 // reads free of bank conflicts.
 namespace big {
@@ -546,6 +547,17 @@ struct BigCtx {
   int w, lane;
 };
 
+// The copy as one asm statement (M0 = the LDS destination), which the compiler does not track: the
+// fragment reads of the other stage then need no wait for these copies (the barrier's own wait on
+// the vector memory counter covers them).
+__device__ __forceinline__ void big_copy(const void* src, const void* lds_dst) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds_dst;
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(m0)
+               : "memory", "m0");
+}
+
 template <int ST>
 __device__ __forceinline__ void big_issue(const BigCtx& x, int step) {
   using namespace big;
@@ -554,14 +566,13 @@ __device__ __forceinline__ void big_issue(const BigCtx& x, int step) {
 #pragma unroll
   for (int i = 0; i < kCopies; ++i) {
     const int P = i * kWaves + x.w;
-    __builtin_amdgcn_global_load_lds((const void*)(x.a[i] + k), (lds_void_t*)(st + P * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((const void*)(x.b[i] + k), (lds_void_t*)(st + kOp + P * 1024), 16, 0, 0);
+    big_copy(x.a[i] + k, st + P * 1024);
+    big_copy(x.b[i] + k, st + kOp + P * 1024);
   }
 }
 
-// Fragments of two 16-k sub-steps (2h, 2h + 1) of stage ST.  The reads and their wait are one asm
-// block: with the other stage's copies in flight the compiler would otherwise wait for all of
-// them before the first LDS read.
+// Fragments of two 16-k sub-steps (2h, 2h + 1) of stage ST, as plain LDS reads (the copies are
+// untracked asm, so the compiler's waits concern these reads only).
 struct BigHalf {
   bf16x8 a[2][big::kFM], b[2][big::kFN];
 };
@@ -572,21 +583,20 @@ __device__ __forceinline__ void big_read(const BigCtx& x, int h, BigHalf& f) {
   asm volatile("" : "+v"(lane));
   const int g = lane >> 5, l32 = lane & 31, sw = swz(l32);
   const int wm = x.w >> 2, wn = x.w & 3;
-  const uint32_t st = lds_addr(big_stage<ST>());
-  const uint32_t s0 = ((4 * h + g) ^ sw) * 16, s1 = ((4 * h + 2 + g) ^ sw) * 16;
-  const uint32_t pa = st + (wm * 128 + l32) * kRowB, pb = st + kOp + (wn * 64 + l32) * kRowB;
-  asm volatile(
-      "ds_read_b128 %0, %12\n\tds_read_b128 %1, %12 offset:4096\n\t"
-      "ds_read_b128 %2, %12 offset:8192\n\tds_read_b128 %3, %12 offset:12288\n\t"
-      "ds_read_b128 %4, %13\n\tds_read_b128 %5, %13 offset:4096\n\t"
-      "ds_read_b128 %6, %13 offset:8192\n\tds_read_b128 %7, %13 offset:12288\n\t"
-      "ds_read_b128 %8, %14\n\tds_read_b128 %9, %14 offset:4096\n\t"
-      "ds_read_b128 %10, %15\n\tds_read_b128 %11, %15 offset:4096\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(f.a[0][0]), "=&v"(f.a[0][1]), "=&v"(f.a[0][2]), "=&v"(f.a[0][3]), "=&v"(f.a[1][0]),
-        "=&v"(f.a[1][1]), "=&v"(f.a[1][2]), "=&v"(f.a[1][3]), "=&v"(f.b[0][0]), "=&v"(f.b[0][1]),
-        "=&v"(f.b[1][0]), "=&v"(f.b[1][1])
-      : "v"(pa + s0), "v"(pa + s1), "v"(pb + s0), "v"(pb + s1));
+  const char* st = big_stage<ST>();
+  const int s0 = ((4 * h + g) ^ sw) * 16, s1 = ((4 * h + 2 + g) ^ sw) * 16;
+  const char* pa = st + (wm * 128 + l32) * kRowB;
+  const char* pb = st + kOp + (wn * 64 + l32) * kRowB;
+#pragma unroll
+  for (int fm = 0; fm < kFM; ++fm) {
+    f.a[0][fm] = *reinterpret_cast<const bf16x8*>(pa + fm * 4096 + s0);
+    f.a[1][fm] = *reinterpret_cast<const bf16x8*>(pa + fm * 4096 + s1);
+  }
+#pragma unroll
+  for (int fn = 0; fn < kFN; ++fn) {
+    f.b[0][fn] = *reinterpret_cast<const bf16x8*>(pb + fn * 4096 + s0);
+    f.b[1][fn] = *reinterpret_cast<const bf16x8*>(pb + fn * 4096 + s1);
+  }
 }
 __device__ __forceinline__ void big_mfma(const BigHalf& f, floatx16 (&acc)[big::kFM][big::kFN]) {
 #pragma unroll
@@ -602,16 +612,16 @@ __device__ __forceinline__ void big_mfma(const BigHalf& f, floatx16 (&acc)[big::
       }
 }
 
-// One 64-k stage: half the stage's fragments are read, multiplied, then the other half.
+// One 64-k stage: the second half's fragments are read while the first half is multiplied.
 template <int ST>
 __device__ __forceinline__ void big_step(const BigCtx& x, int s, int nsteps, floatx16 (&acc)[big::kFM][big::kFN]) {
-  MLA_TILE_BARRIER(waitcnt_vm(0));  // this stage's copies have landed, the other stage is free
+  MLA_TILE_BARRIER(waitcnt_vm_lgkm0(0));  // this stage's copies have landed, the other stage is free
   if (s + 1 < nsteps) big_issue<1 - ST>(x, s + 1);
-  BigHalf f;
-  big_read<ST>(x, 0, f);
-  big_mfma(f, acc);
-  big_read<ST>(x, 1, f);
-  big_mfma(f, acc);
+  BigHalf f0, f1;
+  big_read<ST>(x, 0, f0);
+  big_read<ST>(x, 1, f1);
+  big_mfma(f0, acc);
+  big_mfma(f1, acc);
 }
 
 // Row base (element offset of the row's start) of an epilogue.
