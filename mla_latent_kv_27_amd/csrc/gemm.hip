@@ -634,7 +634,10 @@ __device__ __forceinline__ int64_t epi_row_base(const Epilogue& e, int row) {
   return (int64_t)row * e.ldc;
 }
 
-__global__ void __launch_bounds__(512) gemm_big_kernel(GemmParams p) {
+// With splits > 1, workgroup z-index `split` multiplies k in [split kps, (split + 1) kps) and stores
+// its raw fp32 sums into partial[split][batch][M][N] for the split-K reduce pass, which runs the
+// epilogue.
+__global__ void __launch_bounds__(512) gemm_big_kernel(GemmParams p, int splits, int kps, float* __restrict__ partial) {
   using namespace big;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -657,7 +660,8 @@ __global__ void __launch_bounds__(512) gemm_big_kernel(GemmParams p) {
     n_t = in / gm;
   }
   const int m0 = m_t * kTileM, n0 = n_t * kTileN;
-  const int z = blockIdx.y;
+  const int z = blockIdx.y, split = blockIdx.z;
+  const int k0 = split * kps, k1 = min(p.K, k0 + kps);  // a multiple of kStepK each
   BigCtx x;
   x.w = w;
   x.lane = lane;
@@ -667,8 +671,8 @@ __global__ void __launch_bounds__(512) gemm_big_kernel(GemmParams p) {
     for (int i = 0; i < kCopies; ++i) {
       const int row = (i * kWaves + w) * 8 + (lane >> 3);  // tile row of this lane's copy
       const int ch = (lane & 7) ^ swz(row);                 // source chunk landing in slot lane & 7
-      x.a[i] = A + (int64_t)min(m0 + row, p.M - 1) * p.lda + ch * 8;
-      x.b[i] = b_row<bf16>(p, z, min(n0 + row, p.N - 1)) + ch * 8;
+      x.a[i] = A + (int64_t)min(m0 + row, p.M - 1) * p.lda + k0 + ch * 8;
+      x.b[i] = b_row<bf16>(p, z, min(n0 + row, p.N - 1)) + k0 + ch * 8;
     }
   }
   floatx16 acc[kFM][kFN];
@@ -678,13 +682,30 @@ __global__ void __launch_bounds__(512) gemm_big_kernel(GemmParams p) {
     for (int j = 0; j < kFN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  const int nsteps = p.K / kStepK;
+  const int nsteps = (k1 - k0) / kStepK;
   big_issue<0>(x, 0);
   for (int s = 0; s < nsteps; s += 2) {
     big_step<0>(x, s, nsteps, acc);
     if (s + 1 < nsteps) big_step<1>(x, s + 1, nsteps, acc);
   }
 
+  if (splits > 1) {  // the raw sums (uniform: the whole workgroup returns here)
+    const int g = lane >> 5, l32 = lane & 31;
+    const int wm = w >> 2, wn = w & 3;
+    float* out = partial + ((int64_t)split * p.batch + z) * p.M * p.N;
+#pragma unroll
+    for (int fm = 0; fm < kFM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < kFN; ++fn) {
+        const int col = n0 + wn * 64 + fn * 32 + l32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + wm * 128 + fm * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (row < p.M && col < p.N) out[(int64_t)row * p.N + col] = acc[fm][fn][r];
+        }
+      }
+    return;
+  }
   // Epilogue through LDS, half a wave block (64 x 64) at a time, in the wave's own 16 KiB: the
   // accumulators are only ever indexed by constants (a loop over them that is too long to unroll
   // would move them to scratch memory).  On the way out each lane owns one column, so the column's
@@ -1249,8 +1270,10 @@ hipError_t run_t(const GemmParams& p_in, const GemmPlan& plan, float* partial, h
     case 0: err = launch_cfg<T, 0>(p, plan, partial, s); break;
     case 1: err = launch_cfg<T, 1>(p, plan, partial, s); break;
     case 5: {
-      dim3 grid(((p.M + big::kTileM - 1) / big::kTileM) * ((p.N + big::kTileN - 1) / big::kTileN), p.batch);
-      hipLaunchKernelGGL(gemm_big_kernel, grid, dim3(64 * big::kWaves), 0, s, p);
+      dim3 grid(((p.M + big::kTileM - 1) / big::kTileM) * ((p.N + big::kTileN - 1) / big::kTileN), p.batch,
+                plan.splits);
+      hipLaunchKernelGGL(gemm_big_kernel, grid, dim3(64 * big::kWaves), 0, s, p, plan.splits, plan.k_per_split,
+                         partial);
       err = hipGetLastError();
       break;
     }
@@ -1310,17 +1333,27 @@ GemmPlan gemm_plan_skinny(int M, int N, int K, int batch, int cus) {
 
 GemmPlan gemm_plan(int M, int N, int K, int batch, int cus, bool skinny_ok) {
   if (skinny_ok && M <= 64 && K % skinny::kKS == 0 && N % 2 == 0) return gemm_plan_skinny(M, N, K, batch, cus);
-  // large products: 256 x 256 tiles, one k range (enough tiles to fill the compute units)
-  if (skinny_ok && K % big::kStepK == 0 && N % 2 == 0 &&
-      (int64_t)((M + big::kTileM - 1) / big::kTileM) * ((N + big::kTileN - 1) / big::kTileN) * batch >= cus) {
-    GemmPlan pl;
-    pl.cfg = 5;
-    pl.bm = big::kTileM;
-    pl.bn = big::kTileN;
-    pl.splits = 1;
-    pl.k_per_split = K;
-    pl.partial_bytes = 0;
-    return pl;
+  // large products: 256 x 256 tiles, one k range when there are enough tiles to fill the compute
+  // units, else the k range split into at most ceil(cus / tiles) pieces of at least four 64-k steps
+  // (measured on 512-row products: 0.19 PFLOP/s on the generic tiles, split 256 x 256 tiles and a
+  // reduce pass instead).  Too few tiles even then (a short K): the generic tiles.
+  if (skinny_ok && K % big::kStepK == 0 && N % 2 == 0) {
+    const int64_t tiles =
+        (int64_t)((M + big::kTileM - 1) / big::kTileM) * ((N + big::kTileN - 1) / big::kTileN) * batch;
+    const int ksteps = K / big::kStepK;
+    int splits = tiles >= cus ? 1 : (int)std::min<int64_t>((cus + tiles - 1) / tiles, std::max(1, ksteps / 4));
+    const int per = (ksteps + splits - 1) / splits;
+    splits = (ksteps + per - 1) / per;
+    if (tiles * splits >= cus / 2) {
+      GemmPlan pl;
+      pl.cfg = 5;
+      pl.bm = big::kTileM;
+      pl.bn = big::kTileN;
+      pl.splits = splits;
+      pl.k_per_split = per * big::kStepK;
+      pl.partial_bytes = splits > 1 ? (size_t)splits * batch * M * N * sizeof(float) : 0;
+      return pl;
+    }
   }
   GemmPlan pl;
   pl.cfg = M <= 32 ? 0 : (M <= 64 ? 1 : 2);
