@@ -750,6 +750,25 @@ __global__ void __launch_bounds__(512) gemm_big_kernel(GemmParams p, int splits,
   float* v_C2 = ve.C2;
   const bool v_f32 = ve.c_f32;
   const bool v_ok = v_col < p.N;
+  // Eight columns per lane (one 16-byte store, 8 rows per instruction) where the layout allows it:
+  // bf16 outputs without an fp32 copy or the Vt key order, every group of 8 columns in one range.
+  const bool vec8 = vec4 && p.N % 8 == 0 && (p.E0 >= p.N || p.E0 % 8 == 0) && p.epi.group % 8 == 0 &&
+                    p.epi2.group % 8 == 0 && p.epi.ldc % 8 == 0 && p.epi2.ldc % 8 == 0 &&
+                    p.epi.group_stride % 8 == 0 && p.epi2.group_stride % 8 == 0 && p.epi.group_off % 8 == 0 &&
+                    p.epi2.group_off % 8 == 0 && p.epi.batch_stride % 8 == 0 && p.epi2.batch_stride % 8 == 0 &&
+                    (p.epi.rope_tab == nullptr || p.epi.rope_col0 % 8 == 0) &&
+                    (p.epi2.rope_tab == nullptr || p.epi2.rope_col0 % 8 == 0) && p.epi.d_hr % 8 == 0 &&
+                    p.epi2.d_hr % 8 == 0 && !p.epi.perm16 && !p.epi2.perm16 && !p.epi.c_f32 && !p.epi2.c_f32 &&
+                    !p.epi.C2 && !p.epi2.C2 && (reinterpret_cast<uintptr_t>(p.epi.C) & 15) == 0 &&
+                    (p.E0 >= p.N || (reinterpret_cast<uintptr_t>(p.epi2.C) & 15) == 0);
+  const int w_col = n0 + wn * 64 + 8 * (lane & 7);
+  const bool w_hi = w_col >= p.E0;
+  const int w_c = w_hi ? w_col - p.E0 : w_col;
+  const Epilogue& we = w_hi ? p.epi2 : p.epi;
+  const int64_t w_off = (int64_t)z * we.batch_stride + epi_col(we, w_c);
+  const bool w_rot = we.rope_tab != nullptr && w_c >= we.rope_col0;
+  const int w_rk = w_rot ? ((w_c - we.rope_col0) % we.d_hr) >> 1 : 0;
+  const bool w_ok = w_col < p.N;
   // element (lr, lc) at lr*64 + (lc ^ 32*((lr >> 2) & 1)): the two row groups one write covers
   // land in different banks
 #pragma unroll
@@ -767,6 +786,36 @@ __global__ void __launch_bounds__(512) gemm_big_kernel(GemmParams p, int splits,
     __builtin_amdgcn_wave_barrier();
     const int row0 = m0 + wm * 128 + h * 64;
     const int nrows = min(64, p.M - row0);
+    if (vec8) {
+      const int rq = lane >> 3, cq = 8 * (lane & 7);
+      for (int lr = rq; lr < nrows; lr += 8) {
+        const int sw = ((lr >> 2) & 1) << 5;
+        floatx4 a = *reinterpret_cast<const floatx4*>(&ep[lr * 64 + (cq ^ sw)]);
+        floatx4 b = *reinterpret_cast<const floatx4*>(&ep[lr * 64 + ((cq + 4) ^ sw)]);
+        const int row = row0 + lr;
+        if (w_rot) {
+          const float2* tb = we.rope_tab + (int64_t)row * (we.d_hr >> 1) + w_rk;
+          const float4 c0 = *reinterpret_cast<const float4*>(tb), c1 = *reinterpret_cast<const float4*>(tb + 2);
+          a = floatx4{a[0] * c0.x - a[1] * c0.y, a[1] * c0.x + a[0] * c0.y, a[2] * c0.z - a[3] * c0.w,
+                      a[3] * c0.z + a[2] * c0.w};
+          b = floatx4{b[0] * c1.x - b[1] * c1.y, b[1] * c1.x + b[0] * c1.y, b[2] * c1.z - b[3] * c1.w,
+                      b[3] * c1.z + b[2] * c1.w};
+        }
+        if (w_ok) {
+          const int64_t idx = epi_row_base(we, row) + w_off;
+          bf16x8 o;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            o[i] = from_f32<bf16>(a[i]);
+            o[4 + i] = from_f32<bf16>(b[i]);
+          }
+          *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(we.C) + idx) = o;
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      __builtin_amdgcn_wave_barrier();
+      continue;
+    }
     if (vec4) {
       // four consecutive columns and one of four rows per lane: 8- (or 16-) byte stores, RoPE
       // pairs inside the lane
