@@ -20,12 +20,17 @@ namespace mla {
 
 constexpr int kBK = 32;  // k elements staged per iteration
 
+// Rotation of one element of a RoPE pair by (cos, sin) = cs; partner is the pair's other element.
+__device__ __forceinline__ float rope_rot(float v, float partner, float2 cs, bool odd) {
+  return odd ? (partner * cs.y + v * cs.x) : (v * cs.x - partner * cs.y);
+}
+// (cos, sin) of RoPE column col (col >= e.rope_col0) in row `row`.
+__device__ __forceinline__ float2 rope_cs(const Epilogue& e, int row, int col) {
+  const int k = ((col - e.rope_col0) % e.d_hr) >> 1;
+  return e.rope_tab[(int64_t)row * (e.d_hr >> 1) + k];
+}
 __device__ __forceinline__ void rope_pair(const Epilogue& e, int row, int col, float& v, float partner) {
-  if (col >= e.rope_col0) {
-    const int k = ((col - e.rope_col0) % e.d_hr) >> 1;
-    const float2 cs = e.rope_tab[(int64_t)row * (e.d_hr >> 1) + k];
-    v = (col & 1) ? (partner * cs.y + v * cs.x) : (v * cs.x - partner * cs.y);
-  }
+  if (col >= e.rope_col0) v = rope_rot(v, partner, rope_cs(e, row, col), col & 1);
 }
 
 // Offset of column c within its output row: groups of e.group columns, group_stride apart.
@@ -70,9 +75,11 @@ __device__ __forceinline__ void out_elem(const GemmParams& p, int z, int row, in
 
 // Four consecutive columns col .. col+3 (col % 4 == 0) of one row through the epilogue; the
 // values are already rotated.  One 8- or 16-byte store when the four land next to each other
-// (no column group boundary inside), else element by element.
+// (no column group boundary inside), else element by element.  A paged epilogue's row position
+// and sequence may be passed in (pos >= 0), read by the caller ahead of its other loads.
 template <typename T>
-__device__ __forceinline__ void out_quad(const GemmParams& p, int z, int row, int col, const float (&v)[4]) {
+__device__ __forceinline__ void out_quad(const GemmParams& p, int z, int row, int col, const float (&v)[4],
+                                         int pos = -1, int seq = 0) {
   const bool hi = col >= p.E0;
   const Epilogue& e = hi ? p.epi2 : p.epi;
   const int c = hi ? col - p.E0 : col;
@@ -80,7 +87,7 @@ __device__ __forceinline__ void out_quad(const GemmParams& p, int z, int row, in
       (reinterpret_cast<uintptr_t>(e.C) & 7) == 0) {
     int64_t rbase;
     if (e.block_table) {
-      const int sq = e.row_seq ? e.row_seq[row] : row, ps = e.row_pos[row];
+      const int sq = pos >= 0 ? seq : (e.row_seq ? e.row_seq[row] : row), ps = pos >= 0 ? pos : e.row_pos[row];
       rbase = ((int64_t)e.block_table[(int64_t)sq * e.max_blocks + ps / e.block_size] * e.block_size +
                ps % e.block_size) * e.ldc;
     } else {
@@ -210,11 +217,15 @@ __global__ void __launch_bounds__(64 * WM * WN)
 
 // Sums the split-K partials [splits][batch][M][N] and runs the epilogue; a thread owns an even
 // number of consecutive columns so that RoPE pairs stay together.
-template <typename T, int V>
+template <typename T, int V, int NF>
 __global__ void __launch_bounds__(128)
     splitk_reduce_kernel(GemmParams p, int splits, const float* __restrict__ partial) {
-  // one thread per V consecutive columns of one row; the splits are summed in order, eight
-  // partial loads in flight at a time
+  // one thread per V consecutive columns of one row; the splits are summed in order.  All the
+  // partial loads of up to NF splits are issued before the first add: with a loop over a run-time
+  // split count each load would wait for the previous add, one memory round trip per split (a
+  // 14-way split then takes seven times the latency of one).  NF is the smallest of 2, 4, 8, 16
+  // that covers the split count, so the registers, and with them the occupancy, follow it.
+  constexpr int kInFlight = NF;
   typedef float vec_t __attribute__((ext_vector_type(V)));
   const int64_t groups = (int64_t)p.batch * p.M * (p.N / V);
   const int64_t stride = (int64_t)p.M * p.N * p.batch;
@@ -225,30 +236,44 @@ __global__ void __launch_bounds__(128)
     const int row = (int)(zr % p.M), z = (int)(zr / p.M);
     const int col = V * cg;
     const float* src = partial + ((int64_t)z * p.M + row) * p.N + col;
-    vec_t acc = {};
-    int s = 0;
-    for (; s + 8 <= splits; s += 8) {
-      vec_t v[8];
+    // the RoPE factors of the quad's two pairs are loaded ahead of the partials, so that their
+    // round trip overlaps the partials' instead of following it
+    float2 cs[2] = {};
+    bool rot[2] = {false, false};
+    int pos = -1, seq = 0;  // a paged epilogue's row position and sequence, read with them too
+    if constexpr (V == 4) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = *reinterpret_cast<const vec_t*>(src + (s + i) * stride);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc += v[i];
+      for (int i = 0; i < 2; ++i) {
+        const bool hi = col + 2 * i >= p.E0;
+        const Epilogue& e = hi ? p.epi2 : p.epi;
+        const int c = hi ? col + 2 * i - p.E0 : col + 2 * i;
+        rot[i] = c >= e.rope_col0;
+        if (rot[i]) cs[i] = rope_cs(e, row, c);
+      }
+      const Epilogue& e = col >= p.E0 ? p.epi2 : p.epi;
+      if (e.block_table) {
+        pos = e.row_pos[row];
+        seq = e.row_seq ? e.row_seq[row] : row;
+      }
     }
-    for (; s < splits; ++s) acc += *reinterpret_cast<const vec_t*>(src + s * stride);
+    vec_t acc = {};
+    for (int s = 0; s < splits; s += kInFlight) {
+      vec_t v[kInFlight];
+#pragma unroll
+      for (int i = 0; i < kInFlight; ++i)
+        if (s + i < splits) v[i] = *reinterpret_cast<const vec_t*>(src + (s + i) * stride);
+#pragma unroll
+      for (int i = 0; i < kInFlight; ++i)
+        if (s + i < splits) acc += v[i];
+    }
     if constexpr (V == 4) {
       float v[4];
 #pragma unroll
       for (int i = 0; i < 4; i += 2) {
-        const bool hi = col + i >= p.E0;
-        const Epilogue& e = hi ? p.epi2 : p.epi;
-        const int c = hi ? col + i - p.E0 : col + i;
-        float v0 = acc[i], v1 = acc[i + 1];
-        rope_pair(e, row, c, v0, acc[i + 1]);
-        rope_pair(e, row, c + 1, v1, acc[i]);
-        v[i] = v0;
-        v[i + 1] = v1;
+        v[i] = rot[i / 2] ? rope_rot(acc[i], acc[i + 1], cs[i / 2], false) : acc[i];
+        v[i + 1] = rot[i / 2] ? rope_rot(acc[i + 1], acc[i], cs[i / 2], true) : acc[i + 1];
       }
-      out_quad<T>(p, z, row, col, v);
+      out_quad<T>(p, z, row, col, v, pos, seq);
     } else {
 #pragma unroll
       for (int i = 0; i < V; i += 2) {
@@ -1302,6 +1327,14 @@ hipError_t launch_cfg(const GemmParams& p, const GemmPlan& plan, float* partial,
   return hipGetLastError();
 }
 
+template <typename T, int V>
+void launch_reduce(const GemmParams& p, int splits, const float* partial, int blocks, hipStream_t s) {
+  auto k = splits <= 2 ? splitk_reduce_kernel<T, V, 2>
+           : splits <= 4 ? splitk_reduce_kernel<T, V, 4>
+           : splits <= 8 ? splitk_reduce_kernel<T, V, 8> : splitk_reduce_kernel<T, V, 16>;
+  hipLaunchKernelGGL(k, dim3(blocks), dim3(128), 0, s, p, splits, partial);
+}
+
 template <typename T>
 hipError_t run_t(const GemmParams& p_in, const GemmPlan& plan, float* partial, hipStream_t s) {
   hipError_t err;
@@ -1343,11 +1376,11 @@ hipError_t run_t(const GemmParams& p_in, const GemmPlan& plan, float* partial, h
   if (p.N % 4 == 0 && p.E0 % 4 == 0) {
     const int64_t groups = (int64_t)p.batch * p.M * (p.N / 4);
     const int blocks = (int)std::min<int64_t>((groups + 127) / 128, 16384);
-    hipLaunchKernelGGL((splitk_reduce_kernel<T, 4>), dim3(blocks), dim3(128), 0, s, p, plan.splits, partial);
+    launch_reduce<T, 4>(p, plan.splits, partial, blocks, s);
   } else {
     const int64_t groups = (int64_t)p.batch * p.M * (p.N / 2);
     const int blocks = (int)std::min<int64_t>((groups + 127) / 128, 16384);
-    hipLaunchKernelGGL((splitk_reduce_kernel<T, 2>), dim3(blocks), dim3(128), 0, s, p, plan.splits, partial);
+    launch_reduce<T, 2>(p, plan.splits, partial, blocks, s);
   }
   return hipGetLastError();
 }
