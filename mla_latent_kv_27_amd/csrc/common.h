@@ -131,6 +131,12 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t span, uint32_t off,
   __builtin_amdgcn_raw_ptr_buffer_load_lds(span, dst, 16, off, 0, 0, 0);
 }
 
+// The value lane `src` (the same in every lane) holds, read with v_readlane: a scalar result, no
+// LDS round trip as a shuffle would take.
+__device__ __forceinline__ float lane_value(float x, int src) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), src));
+}
+
 // s_waitcnt immediates (gfx9 encoding): vmcnt in bits [3:0] and [15:14], expcnt [6:4],
 // lgkmcnt [11:8]; the unused counters are left at their maximum.
 constexpr int waitcnt_vm(int n) { return ((n >> 4) << 14) | (0xF << 8) | (0x7 << 4) | (n & 0xF); }

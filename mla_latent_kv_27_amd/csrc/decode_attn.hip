@@ -1000,9 +1000,9 @@ __global__ void __launch_bounds__(512)
 template <typename T, typename PT, int DC, bool COOP>
 __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeAttnParams p) {
   constexpr int V = DC >= 64 ? DC / 64 : 1;  // dims per thread
-  const int wv = threadIdx.x >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // b * n_h + head: one wave per row, or (COOP, many partitions) one workgroup per row, its four
-  // waves taking every fourth chunk of 64 partitions and adding up in LDS
+  // waves taking every fourth group of partitions and adding up in LDS
   const int bh = COOP ? blockIdx.x : blockIdx.x * 4 + wv;
   if (bh >= p.B * p.n_h) return;
   const int lane = threadIdx.x & 63;
@@ -1010,48 +1010,71 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeAttnParams p)
   const int b = bh / p.n_h, head = bh % p.n_h;
   const int64_t base = (int64_t)b * p.splits * p.n_h + head;  // partition s at base + s * n_h
   const int d = V * lane;
-  // M: the partitions' maxima one per lane, then a wave reduction
-  float M = -INFINITY;
-  for (int c = 0; c < p.splits; c += 64)
-    if (c + lane < p.splits) M = fmaxf(M, p.part_m[base + (int64_t)(c + lane) * p.n_h]);
+  // Two memory round trips: every partition's (max, normaliser), two per lane (partitions lane and
+  // 64 + lane; beyond 128 read where needed; M by a wave reduction), then the output rows of the
+  // non-empty partitions of two groups of kG at once.  With COOP the four waves take the groups in
+  // turn (wave w: groups w, w + 4, ...); alone, a wave takes them all, in order.
+  constexpr int kG = 8, NWv = COOP ? 4 : 1;
+  const int w = COOP ? wv : 0;
+  const int S = p.splits;
+  float m2[2], l2[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int sp = 64 * j + lane;
+    m2[j] = sp < S ? p.part_m[base + (int64_t)sp * p.n_h] : -INFINITY;
+    l2[j] = sp < S ? p.part_l[base + (int64_t)sp * p.n_h] : 0.f;
+  }
+  float M = fmaxf(m2[0], m2[1]);
+  for (int c = 128; c < S; c += 64)
+    if (c + lane < S) M = fmaxf(M, p.part_m[base + (int64_t)(c + lane) * p.n_h]);
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
   float L = 0.f;
   float acc[V];
 #pragma unroll
   for (int i = 0; i < V; ++i) acc[i] = 0.f;
-  // 64 partitions' (max, normaliser) at a time sit one per lane; a group of kG is skipped when
-  // all are empty, else the output rows of its non-empty partitions are loaded together
-  constexpr int kG = 16;
-  for (int c0 = COOP ? 64 * wv : 0; c0 < p.splits; c0 += COOP ? 256 : 64) {
-    const int64_t pl = base + (int64_t)(c0 + lane) * p.n_h;
-    const float m_l = c0 + lane < p.splits ? p.part_m[pl] : -INFINITY;
-    const float l_l = c0 + lane < p.splits ? p.part_l[pl] : 0.f;
-    const uint64_t used = __builtin_amdgcn_ballot_w64(m_l > -INFINITY);
-    for (int s0 = c0; s0 < min(p.splits, c0 + 64); s0 += kG) {
-      if (((used >> (s0 - c0)) & ((1ull << kG) - 1)) == 0) continue;
-      float ms[kG], ls[kG];
-      PT v[kG][V];
+  for (int s0 = kG * w; s0 < S; s0 += 2 * kG * NWv) {
+    float ms[2][kG], ls[2][kG];
+    PT v[2][kG][V];
+    // a group lies wholly below partition 128 (values from the lanes that hold them) or wholly
+    // above it (read here): one path per group, so that no row load waits on another
 #pragma unroll
-      for (int u = 0; u < kG; ++u) {
-        ms[u] = __shfl(m_l, s0 - c0 + u, 64);
-        ls[u] = __shfl(l_l, s0 - c0 + u, 64);
-        if (ms[u] > -INFINITY) {  // (-inf past the last partition too)
-          const PT* src = reinterpret_cast<const PT*>(p.part_o) + (base + (int64_t)(s0 + u) * p.n_h) * DC + d;
+    for (int q = 0; q < 2; ++q) {
+      const int g0 = s0 + q * kG * NWv;  // the same in every lane
+      if (g0 < 128) {
 #pragma unroll
-          for (int i = 0; i < V; ++i) v[u][i] = has_dims ? src[i] : PT(0.f);
+        for (int u = 0; u < kG; ++u) {
+          ms[q][u] = lane_value(g0 < 64 ? m2[0] : m2[1], (g0 + u) & 63);
+          ls[q][u] = lane_value(g0 < 64 ? l2[0] : l2[1], (g0 + u) & 63);
         }
-      }
+      } else {
 #pragma unroll
-      for (int u = 0; u < kG; ++u) {
-        if (ms[u] > -INFINITY) {
-          const float ws = exp2f(ms[u] - M) * ls[u];
-          L += ws;
-#pragma unroll
-          for (int i = 0; i < V; ++i) acc[i] += ws * to_f32(v[u][i]);
+        for (int u = 0; u < kG; ++u) {
+          ms[q][u] = g0 + u < S ? p.part_m[base + (int64_t)(g0 + u) * p.n_h] : -INFINITY;
+          ls[q][u] = g0 + u < S ? p.part_l[base + (int64_t)(g0 + u) * p.n_h] : 0.f;
         }
       }
     }
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int u = 0; u < kG; ++u)
+        if (ms[q][u] > -INFINITY) {  // (-inf past the last partition too)
+          const PT* src =
+              reinterpret_cast<const PT*>(p.part_o) + (base + (int64_t)(s0 + q * kG * NWv + u) * p.n_h) * DC + d;
+#pragma unroll
+          for (int i = 0; i < V; ++i) v[q][u][i] = has_dims ? src[i] : PT(0.f);
+        }
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int u = 0; u < kG; ++u)
+        if (ms[q][u] > -INFINITY) {
+          const float ws = exp2f(ms[q][u] - M) * ls[q][u];
+          L += ws;
+#pragma unroll
+          for (int i = 0; i < V; ++i) acc[i] += ws * to_f32(v[q][u][i]);
+        }
   }
   if constexpr (COOP) {
     __shared__ float red[4][V + 1][64];

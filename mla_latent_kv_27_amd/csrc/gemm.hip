@@ -1097,14 +1097,17 @@ __global__ void __launch_bounds__(64 * NW) uv_kernel(const bf16* __restrict__ oh
       __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(la + r * kRowB), 16, 0, 0);
     }
   };
-  // rows r = i NW + wv of the block, kRowsInFlight at a time: lane holds dims 8 lane .. +7.  The
-  // partitions' maxima are read one per lane (M by a wave reduction), and a partition's output
-  // row is loaded only when its max is finite (empty partitions write none).  The loads of a
-  // group, four partitions of every row, are all issued before any is used.
+  // rows r = i NW + wv of the block, kRowsInFlight at a time: lane holds dims 8 lane .. +7.  Lane u
+  // reads partition u's max and normaliser (fewer than 16 partitions here; M by a wave reduction);
+  // the output rows go four partitions at a time.  The maxima, the normalisers and the first four
+  // partitions' rows are all issued before any of them is used, one memory round trip instead of
+  // one per dependent load.  A row is read whether or not its partition is empty (an empty one
+  // writes only its max, -inf, and its row is then never added: the loads stay inside the
+  // partials, and skipping them would cost another round trip).
   auto combine_a = [&](int m0) {
     const int S = parts.splits;
     for (int i0 = 0; i0 < MB / NW; i0 += kRowsInFlight) {
-      float M[kRowsInFlight], L[kRowsInFlight], acc[kRowsInFlight][8];
+      float M[kRowsInFlight], L[kRowsInFlight], acc[kRowsInFlight][8], m_l[kRowsInFlight], l_l[kRowsInFlight];
       int64_t base[kRowsInFlight];
       bool live[kRowsInFlight];  // rows past B are not read (their products are never stored)
 #pragma unroll
@@ -1112,46 +1115,47 @@ __global__ void __launch_bounds__(64 * NW) uv_kernel(const bf16* __restrict__ oh
         const int m = m0 + (i0 + k) * NW + wv;
         live[k] = m < B;
         base[k] = (int64_t)min(m, B - 1) * S * n_h + h;  // partition s at base + s n_h
-        float mx = -INFINITY;
-        if (live[k])
-          for (int c = 0; c < S; c += 64)
-            if (c + lane < S) mx = fmaxf(mx, parts.m[base[k] + (int64_t)(c + lane) * n_h]);
-        M[k] = wave_max_xor(wave_max_xor(wave_max_xor(mx, 1), 2), 4);
-        M[k] = wave_max_xor(wave_max_xor(wave_max_xor(M[k], 8), 16), 32);
+        const bool in = live[k] && lane < S;
+        m_l[k] = in ? parts.m[base[k] + (int64_t)lane * n_h] : -INFINITY;
+        l_l[k] = in ? parts.l[base[k] + (int64_t)lane * n_h] : 0.f;
         L[k] = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[k][e] = 0.f;
       }
-      auto part = [&](int k, int sp, float& ms, float& ls, bf16x8& v) {
-        const int64_t pi = base[k] + (int64_t)sp * n_h;
-        ms = parts.m[pi];
-        if (ms > -INFINITY) {  // uniform
-          ls = parts.l[pi];
-          v = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(parts.o) + pi * kDc + 8 * lane);
-        }
-      };
-      auto add = [&](int k, float ms, float ls, const bf16x8& v) {
-        if (ms > -INFINITY) {
-          const float ws = exp2f(ms - M[k]) * ls;
-          L[k] += ws;
+      auto load_group = [&](int s0, bf16x8 (&v)[kRowsInFlight][4]) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[k][e] += ws * (float)v[e];
-        }
+        for (int k = 0; k < kRowsInFlight; ++k)
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (live[k] && s0 + u < S)
+              v[k][u] = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(parts.o) +
+                                                        (base[k] + (int64_t)(s0 + u) * n_h) * kDc + 8 * lane);
       };
-      for (int s0 = 0; s0 < S; s0 += 4) {
-        float ms[kRowsInFlight][4], ls[kRowsInFlight][4];
-        bf16x8 v[kRowsInFlight][4];
+      auto add_group = [&](int s0, const bf16x8 (&v)[kRowsInFlight][4]) {
 #pragma unroll
         for (int k = 0; k < kRowsInFlight; ++k)
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
-            ms[k][u] = -INFINITY;
-            if (live[k] && s0 + u < S) part(k, s0 + u, ms[k][u], ls[k][u], v[k][u]);
+            const float ms = lane_value(m_l[k], s0 + u), ls = lane_value(l_l[k], s0 + u);
+            if (s0 + u < S && ms > -INFINITY) {
+              const float ws = exp2f(ms - M[k]) * ls;
+              L[k] += ws;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) acc[k][e] += ws * (float)v[k][u][e];
+            }
           }
+      };
+      bf16x8 v[kRowsInFlight][4];
+      load_group(0, v);
 #pragma unroll
-        for (int k = 0; k < kRowsInFlight; ++k)
-#pragma unroll
-          for (int u = 0; u < 4; ++u) add(k, ms[k][u], ls[k][u], v[k][u]);
+      for (int k = 0; k < kRowsInFlight; ++k) {
+        M[k] = wave_max_xor(wave_max_xor(wave_max_xor(m_l[k], 1), 2), 4);
+        M[k] = wave_max_xor(wave_max_xor(wave_max_xor(M[k], 8), 16), 32);
+      }
+      add_group(0, v);
+      for (int s0 = 4; s0 < S; s0 += 4) {
+        load_group(s0, v);
+        add_group(s0, v);
       }
 #pragma unroll
       for (int k = 0; k < kRowsInFlight; ++k) {
@@ -1166,14 +1170,24 @@ __global__ void __launch_bounds__(64 * NW) uv_kernel(const bf16* __restrict__ oh
   };
   // With many partitions (16 or more: long contexts, small batches) every wave takes part in
   // every row: wave w walks the row's groups w, w + NW, ... of eight partitions, and the waves'
-  // partial sums meet in LDS, where the row's owner normalises them into the A block.
+  // partial sums meet in LDS, where the row's owner normalises them into the A block.  Every
+  // partition's (max, normaliser) is read first, two per lane (partitions lane and 64 + lane;
+  // beyond 128 read where needed), so that each group then takes one round trip for its non-empty
+  // partitions' rows (the weights held in registers leave room for one group in flight).
   auto combine_coop = [&](int m0, float* red) {
-    constexpr int kCoopG = 8;  // partitions per wave and pass (their loads in flight together)
+    constexpr int kCoopG = 8;  // partitions per wave and group
     const int S = parts.splits;
     for (int r = 0; r < MB && m0 + r < B; ++r) {
       const int64_t base = (int64_t)(m0 + r) * S * n_h + h;
-      float M = -INFINITY;
-      for (int c = 0; c < S; c += 64)
+      float m2[2], l2[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int sp = 64 * j + lane;
+        m2[j] = sp < S ? parts.m[base + (int64_t)sp * n_h] : -INFINITY;
+        l2[j] = sp < S ? parts.l[base + (int64_t)sp * n_h] : 0.f;
+      }
+      float M = fmaxf(m2[0], m2[1]);
+      for (int c = 128; c < S; c += 64)
         if (c + lane < S) M = fmaxf(M, parts.m[base + (int64_t)(c + lane) * n_h]);
 #pragma unroll
       for (int d = 1; d < 64; d <<= 1) M = fmaxf(M, __shfl_xor(M, d, 64));
@@ -1181,21 +1195,28 @@ __global__ void __launch_bounds__(64 * NW) uv_kernel(const bf16* __restrict__ oh
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] = 0.f;
       for (int s0 = kCoopG * wv; s0 < S; s0 += kCoopG * NW) {
-        const int64_t pl = base + (int64_t)(s0 + (lane % kCoopG)) * n_h;
-        const bool in = s0 + (lane % kCoopG) < S;
-        const float m_l = in ? parts.m[pl] : -INFINITY;
-        const float l_l = in ? parts.l[pl] : 0.f;
-        if (__builtin_amdgcn_ballot_w64(m_l > -INFINITY) == 0) continue;
+        // a group lies wholly below partition 128 (values from the lanes that hold them) or wholly
+        // above it (read here): one path per group, so that no row load waits on another
         float ms[kCoopG], ls[kCoopG];
         bf16x8 v[kCoopG];
+        if (s0 < 128) {
 #pragma unroll
-        for (int u = 0; u < kCoopG; ++u) {
-          ms[u] = __shfl(m_l, u, 64);
-          ls[u] = __shfl(l_l, u, 64);
-          if (ms[u] > -INFINITY)
+          for (int u = 0; u < kCoopG; ++u) {
+            ms[u] = lane_value(s0 < 64 ? m2[0] : m2[1], (s0 + u) & 63);
+            ls[u] = lane_value(s0 < 64 ? l2[0] : l2[1], (s0 + u) & 63);
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < kCoopG; ++u) {
+            ms[u] = s0 + u < S ? parts.m[base + (int64_t)(s0 + u) * n_h] : -INFINITY;
+            ls[u] = s0 + u < S ? parts.l[base + (int64_t)(s0 + u) * n_h] : 0.f;
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kCoopG; ++u)
+          if (ms[u] > -INFINITY)  // (-inf past the last partition too)
             v[u] = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(parts.o) +
                                                     (base + (int64_t)(s0 + u) * n_h) * kDc + 8 * lane);
-        }
 #pragma unroll
         for (int u = 0; u < kCoopG; ++u)
           if (ms[u] > -INFINITY) {
