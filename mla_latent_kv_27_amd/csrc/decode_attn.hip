@@ -23,6 +23,7 @@
 
 #include "common.h"
 #include "internal.h"
+#include "units.h"
 
 namespace mla {
 
@@ -189,83 +190,8 @@ __global__ void __launch_bounds__(64 * NW) decode_attn_kernel(DecodeAttnParams p
 }
 
 // ----------------------------------------------------------------------------- balanced units
-// Work units of the tiled kernels for small batches, where contexts of different lengths would
-// leave most fixed-length partitions of the short sequences empty.  Each sequence has p.splits
-// partition slots; sequence b takes n_b = ceil(tiles_b / tps) of them.  tps starts at the
-// shortest length that fits the longest sequence in its slots and is raised while that lowers
-// the finish time, counted in rounds of p.cus units (one per compute unit) times tps.  The table
-// lists the partitions in sequence order, then the slots no partition uses (p >= n_b: they get
-// an empty partial, max -inf and no output rows), then B idle units: (b, p, first tile, end
-// tile), b = -1 when idle.  One workgroup builds it from the lengths in device memory (B <= 64),
-// so the host needs only B and splits.
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int o = __shfl_up(v, d, 64);
-    if (lane >= d) v += o;
-  }
-  return v;
-}
-
-__device__ __forceinline__ int wave_sum_int(int v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
-  return v;
-}
-
-__global__ void __launch_bounds__(256) decode_units_kernel(DecodeAttnParams p) {
-  const int lane = threadIdx.x & 63;
-  const int plus = p.lens_plus_one ? 1 : 0, S = p.splits, T = kTile;
-  const int C = max(1, p.cus);
-  // one lane per sequence (B <= 64)
-  const int my_tiles = lane < p.B ? (p.lens[lane] + plus + T - 1) / T : 0;
-  const int tot = wave_sum_int(my_tiles);
-  int mx = my_tiles;
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) mx = max(mx, __shfl_xor(mx, d, 64));
-  // partition length: the shortest one that fits every sequence in its S slots, or a longer one
-  // when that finishes sooner; the finish time counts rounds of C units (one per compute unit)
-  const int tmin = max(1, (mx + S - 1) / S);
-  int tps = tmin;
-  long best = -1;
-  for (int k = 0; k <= 9; ++k) {
-    const int cand = k < 9 ? tmin + tmin * k / 8 : max(tmin, (tot + C - 1) / C);
-    const int used = wave_sum_int((my_tiles + cand - 1) / cand);
-    const long cost = (long)((used + C - 1) / C) * cand;
-    if (best < 0 || cost < best) {
-      best = cost;
-      tps = cand;
-    }
-  }
-  // per-sequence partition counts and their prefix sums (B <= 64 here), then every thread fills
-  // table entries
-  __shared__ int s_tiles[64], s_pend[64], s_fend[64];  // tiles, partitions / free slots up to b
-  if (threadIdx.x < 64) {
-    const int tiles = my_tiles;
-    const int n = lane < p.B ? (tiles + tps - 1) / tps : 0;
-    s_tiles[lane] = tiles;
-    s_pend[lane] = wave_incl_scan(n, lane);
-    s_fend[lane] = wave_incl_scan(lane < p.B ? S - n : 0, lane);
-  }
-  __syncthreads();
-  const int np = s_pend[p.B - 1];
-  for (int j = threadIdx.x; j < p.B * S + p.B; j += blockDim.x) {
-    int4 e = make_int4(-1, 0, 0, 0);
-    if (j < np) {
-      int i = 0;
-      while (s_pend[i] <= j) ++i;
-      const int k = j - (i ? s_pend[i - 1] : 0);
-      e = make_int4(i, k, k * tps, min(s_tiles[i], (k + 1) * tps));
-    } else if (j < p.B * S) {
-      const int f = j - np;
-      int i = 0;
-      while (s_fend[i] <= f) ++i;
-      const int n_i = s_pend[i] - (i ? s_pend[i - 1] : 0);
-      e = make_int4(i, n_i + f - (i ? s_fend[i - 1] : 0), 0, 0);
-    }
-    p.units[j] = e;
-  }
-}
+// (the table builder is in units.h: the W_UK absorption launch can run it as well)
+__global__ void __launch_bounds__(256) decode_units_kernel(DecodeAttnParams p) { build_decode_units(p); }
 
 // ----------------------------------------------------------------------------- tiled kernel
 // The DeepSeek-V2-sized cases (d_c = 512, d_hr = 64; the bf16 kernel and, with its own tiles, the
@@ -1146,7 +1072,7 @@ hipError_t decode_attention(DType t, const DecodeAttnParams& p, hipStream_t s) {
     const int HG = (p.n_h + 16 * tiled::kWaves - 1) / (16 * tiled::kWaves);
     if (p.B == 0) return hipSuccess;
     if (p.units && p.B > 64) return hipErrorInvalidValue;  // the table builder takes B <= 64
-    if (p.units) hipLaunchKernelGGL(decode_units_kernel, dim3(1), dim3(256), 0, s, p);
+    if (p.units && !p.units_ready) hipLaunchKernelGGL(decode_units_kernel, dim3(1), dim3(256), 0, s, p);
     const int units = p.B * p.splits + (p.units ? p.B : 0);  // with a table: + B idle entries
     const int blocks = (units + 7) / 8 * 8 * HG;
     const bool full = p.n_h % (16 * tiled::kWaves) == 0;  // every head group full: the P.V loop needs no guards

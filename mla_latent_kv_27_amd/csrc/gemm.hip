@@ -15,6 +15,7 @@
 #include "common.h"
 #include "internal.h"
 #include "quant.h"
+#include "units.h"
 
 namespace mla {
 
@@ -922,24 +923,32 @@ __device__ __forceinline__ int wslot(int r, int c) { return c ^ ((r & 3) << 1); 
 __device__ __forceinline__ int qslot(int m, int c) { return c ^ (m & 15); }
 }  // namespace absorb
 
-// Rows y < q_rows of the grid are the quantiser's: wave wv of workgroup (x, y) quantises new entry
-// (y gridDim.x + x) kWaves + wv of the job.
+// With a units job (u_rows == 1) grid row 0 builds the decode attention's balanced work-unit table
+// (workgroup x = 0; the others of the row return).  The next q_rows rows are the quantiser's: wave
+// wv of workgroup (x, y) quantises new entry (y' gridDim.x + x) kWaves + wv of the job, y' = y -
+// u_rows.  Both kinds of rows come first, so that their few workgroups start with the launch
+// instead of trailing it.
 __global__ void __launch_bounds__(256) absorb_kernel(const bf16* __restrict__ qc, const bf16* __restrict__ w,
                                                      bf16* __restrict__ out, int B, int n_h, int d_c,
-                                                     int64_t out_ld, int64_t out_hs, QuantJob qj, int q_rows) {
+                                                     int64_t out_ld, int64_t out_hs, QuantJob qj, int q_rows,
+                                                     DecodeAttnParams uj, int u_rows) {
   using namespace absorb;
   __shared__ __attribute__((aligned(1024))) char lw[kDh * kRowB];
   __shared__ __attribute__((aligned(1024))) char lq[kMB * kRowB];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if ((int)blockIdx.y < q_rows) {  // the whole workgroup: no barrier below is reached
-    const int row = ((int)blockIdx.y * (int)gridDim.x + (int)blockIdx.x) * kWaves + wv;
+  if ((int)blockIdx.y < u_rows) {  // the whole workgroup (one synchronisation inside)
+    if (blockIdx.x == 0) build_decode_units(uj);
+    return;
+  }
+  if ((int)blockIdx.y < u_rows + q_rows) {  // the whole workgroup: no barrier below is reached
+    const int row = (((int)blockIdx.y - u_rows) * (int)gridDim.x + (int)blockIdx.x) * kWaves + wv;
     if (row < qj.n)
       quant::quantize_entry(reinterpret_cast<bf16*>(qj.src) + (int64_t)row * qj.src_ld, row, qj.dst,
                             reinterpret_cast<const bf16*>(qj.gain), qj.eps, qj.writeback, lane);
     return;
   }
-  const int c0 = blockIdx.x * kCols, h = blockIdx.y - q_rows;
+  const int c0 = blockIdx.x * kCols, h = blockIdx.y - q_rows - u_rows;
   const int sub = lane >> 4, sl = lane & 15;  // copy lane: row 4P + sub, slot sl (1 KiB = 4 rows)
   // the weight slice: 32 copies, 8 per wave
 #pragma unroll
@@ -1023,17 +1032,20 @@ bool absorb_ok(DType t, int d_h, int d_c) {
 }
 
 hipError_t absorb_run(const void* qc, const void* w_uk, void* qhat, int B, int n_h, int d_h, int d_c,
-                      int64_t out_ld, int64_t out_hs, hipStream_t s, const QuantJob* qj) {
+                      int64_t out_ld, int64_t out_hs, hipStream_t s, const QuantJob* qj,
+                      const DecodeAttnParams* units) {
   const QuantJob job = qj ? *qj : QuantJob{};
-  if (B == 0 && job.n <= 0) return hipSuccess;
-  // the quantiser's rows first: its few workgroups start with the launch instead of trailing it
+  if (units && (!units->units || units->B > 64 || units->B < 1)) return hipErrorInvalidValue;
+  if (B == 0 && job.n <= 0 && !units) return hipSuccess;
+  // the units table's row, then the quantiser's rows, then the heads
+  const int u_rows = units ? 1 : 0;
   const int per_row = d_c / absorb::kCols * absorb::kWaves;  // entries per grid row
   const int q_rows = job.n > 0 ? (job.n + per_row - 1) / per_row : 0;
-  dim3 grid(d_c / absorb::kCols, (B > 0 ? n_h : 0) + q_rows);
+  dim3 grid(d_c / absorb::kCols, (B > 0 ? n_h : 0) + q_rows + u_rows);
   (void)d_h;  // == absorb::kDh (absorb_ok)
   hipLaunchKernelGGL(absorb_kernel, grid, dim3(64 * absorb::kWaves), 0, s, reinterpret_cast<const bf16*>(qc),
                      reinterpret_cast<const bf16*>(w_uk), reinterpret_cast<bf16*>(qhat), B, n_h, d_c, out_ld, out_hs,
-                     job, q_rows);
+                     job, q_rows, units ? *units : DecodeAttnParams{}, u_rows);
   return hipGetLastError();
 }
 

@@ -108,10 +108,14 @@ GemmPlan gemm_plan(int M, int N, int K, int batch, int cus, bool skinny_ok);
 // qhat[b*out_ld + h*out_hs + c] = sum_k qc[(b*n_h + h)*d_h + k] * w_uk[(h*d_h + k)*d_c + c].
 bool absorb_ok(DType t, int d_h, int d_c);
 struct QuantJob;
+struct DecodeAttnParams;
 // With qj (a decode step over the fp8 cache), the same launch also quantises the step's new entries
-// (qj->n rows) in workgroups of its own, which saves the quantiser its launch.
+// (qj->n rows) in workgroups of its own, which saves the quantiser its launch.  With units (a decode
+// attention's parameters with a balanced-units table, B <= 64), one workgroup of the launch builds
+// that table, which saves the table builder its launch (the attention is then told units_ready).
 hipError_t absorb_run(const void* qc, const void* w_uk, void* qhat, int B, int n_h, int d_h, int d_c,
-                      int64_t out_ld, int64_t out_hs, hipStream_t s, const QuantJob* qj = nullptr);
+                      int64_t out_ld, int64_t out_hs, hipStream_t s, const QuantJob* qj = nullptr,
+                      const DecodeAttnParams* units = nullptr);
 // o = W_UV per head for bf16 (d_c == 512, d_h a multiple of 64):
 // o[(b*n_h + h)*d_h + d] = sum_c w_uv[(h*d_h + d)*512 + c] * ohat[(b*n_h + h)*512 + c]; o32 (may be
 // null) receives the same values in fp32.
@@ -226,6 +230,7 @@ struct DecodeAttnParams {
                                   // B * (splits + 1) entries, filled by decode_attention); null:
                                   // fixed partitions of tokens_per_split
   int cus = 256;                  // compute units, for the balanced units' finish time
+  bool units_ready = false;       // the table is already built (by an earlier launch on the stream)
 };
 
 // true when the kernel decode_attention picks writes bf16 partition outputs

@@ -870,6 +870,19 @@ int decode_impl(const mla_dims* d, const mla_weights* w, const mla_paged_cache* 
     g.epi2.rope_col0 = 0; g.epi2.d_hr = d->d_hr; g.epi2.rope_tab = ws.rope;
     MLA_HIP(gemm_run(t, g, ws.gm.q, ws.partial, s));
   }
+  // the latent attention's parameters (over ctx_lens[b] + 1 entries); with balanced work units the
+  // absorption launch builds their table
+  DecodeAttnParams a{};
+  a.q = ws.qcat; a.pool = c->pool; a.block_table = c->block_table;
+  a.fp8 = fp8_cache(d); a.scales = c->scales;
+  a.max_blocks = c->max_blocks_per_seq; a.block_size = c->block_size;
+  a.lens = ctx_lens; a.lens_plus_one = true;
+  a.B = B; a.n_h = d->n_h; a.d_c = d->d_c; a.d_hr = d->d_hr;
+  a.scale_log2 = scale_of(d) * 1.4426950408889634f;
+  a.splits = ws.attn.splits; a.tokens_per_split = ws.attn.tps;
+  a.part_m = ws.attn.pm; a.part_l = ws.attn.pl; a.part_o = ws.attn.po;
+  a.units = ws.attn.balanced ? ws.attn.units : nullptr; a.cus = cus;
+  a.o_hat = ws.ohat; a.lse = nullptr;
   if (absorb_ok(t, d->d_h, d->d_c)) {  // q_hat_i = W_UK_i^T q^C_i -> columns [0, d_c) of each head's row
     QuantJob qj;
     if (quant_in_absorb) {
@@ -877,8 +890,10 @@ int decode_impl(const mla_dims* d, const mla_weights* w, const mla_paged_cache* 
       qj.dst = quant_dst(c, nullptr, ctx_lens);
       qj.gain = w->g_ckv; qj.eps = eps_of(d); qj.writeback = true;
     }
+    const bool units_here = a.units && B <= 64;
     MLA_HIP(absorb_run(ws.qc, w->W_UK, ws.qcat, B, d->n_h, d->d_h, d->d_c, (int64_t)d->n_h * E, E, s,
-                       quant_in_absorb ? &qj : nullptr));
+                       quant_in_absorb ? &qj : nullptr, units_here ? &a : nullptr));
+    a.units_ready = units_here;
   } else {
     GemmParams g;
     g.A = ws.qc; g.lda = (int64_t)d->n_h * d->d_h; g.strideA = d->d_h;
@@ -890,17 +905,6 @@ int decode_impl(const mla_dims* d, const mla_weights* w, const mla_paged_cache* 
   }
   UvPartials parts;
   {  // latent attention over ctx_lens[b] + 1 entries
-    DecodeAttnParams a{};
-    a.q = ws.qcat; a.pool = c->pool; a.block_table = c->block_table;
-    a.fp8 = fp8_cache(d); a.scales = c->scales;
-    a.max_blocks = c->max_blocks_per_seq; a.block_size = c->block_size;
-    a.lens = ctx_lens; a.lens_plus_one = true;
-    a.B = B; a.n_h = d->n_h; a.d_c = d->d_c; a.d_hr = d->d_hr;
-    a.scale_log2 = scale_of(d) * 1.4426950408889634f;
-    a.splits = ws.attn.splits; a.tokens_per_split = ws.attn.tps;
-    a.part_m = ws.attn.pm; a.part_l = ws.attn.pl; a.part_o = ws.attn.po;
-    a.units = ws.attn.balanced ? ws.attn.units : nullptr; a.cus = cus;
-    a.o_hat = ws.ohat; a.lse = nullptr;
     // with several partitions and the W_UV kernel that combines them, the combine pass is skipped;
     // not when many partitions meet few workgroups of that kernel (a small batch with few heads):
     // the combine kernel's workgroup per row then spreads the partition reads over the chip
