@@ -308,6 +308,46 @@ def test_split_count_invariance_and_page_permutation_invariance():
         assert np.array_equal(_decode_u(layer, pool2.clone(), h, lens, sp), _decode_u(layer, pool.clone(), h, lens, sp))
 
 
+def test_more_than_128_partitions():
+    """160 partitions of 64 tokens: the 9000-token sequence fills 141 of them, the short ones
+    leave most empty.  Both log-sum-exp combines hold the (max, normaliser) of partitions 0..127
+    in lanes and read the later ones on a path of their own: the combine kernel behind
+    mla_decode_attention against the oracle, and the W_UV kernel's combine inside mla_decode
+    against the same step with one partition (the un-absorbed oracle over 9000 tokens is too slow
+    for a test)."""
+    dims, recipe = SMALL["v2"]
+    lens, splits = [9000, 700, 130], 160
+    B = len(lens)
+    layer = WL.DeviceLayer(dims, S.make_weights(dims))
+    rng = np.random.default_rng(17)
+    pool = WL.PagedPool(dims, lens, block_size=64)
+    ent = S.to_dtype(rng.standard_normal((pool.pool.shape[0] * pool.pool.shape[1], dims.entry)).astype(np.float32),
+                     dims.dtype)
+    pool.pool.copy_(WL.to_device(ent, dims).view(pool.pool.shape))
+    q = S.to_dtype((rng.standard_normal((B, dims.n_h, dims.entry)) * 0.3).astype(np.float32), dims.dtype)
+    kv = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    ws = WL.ws_tensor(M.workspace_size(layer.cdims, M.OP_DECODE, batch=B, max_ctx_len=max(lens) - 1,
+                                       num_splits=splits))
+    ohat = torch.empty((B, dims.n_h, dims.d_c), dtype=WL.torch_dtype(dims), device="cuda")
+    lse = torch.empty((B, dims.n_h), dtype=torch.float32, device="cuda")
+    M.decode_attention(layer.cdims, pool.ccache, WL.to_device(q, dims), kv, max(lens), ohat, ws, num_splits=splits,
+                       lse=lse)
+    torch.cuda.synchronize()
+    for b in range(B):
+        ref, ref_lse = O.latent_attention(q[b:b + 1], pool.read_entries(b, lens[b]), [lens[b]], O.softmax_scale(dims),
+                                          dims.d_c)
+        check(ohat[b].float().cpu().numpy(), ref[0], dims.dtype, f"o_hat b={b} with {splits} partitions")
+        assert np.max(np.abs(lse[b].cpu().numpy() - ref_lse[0])) < 2e-3 * max(1.0, np.max(np.abs(ref_lse)))
+
+    W = S.make_weights(dims)
+    layer = WL.DeviceLayer(dims, W)
+    pool = WL.PagedPool(dims, [L + 1 for L in lens])
+    WL.build_context(layer, pool, lens, recipe)
+    h = S.hidden_step(dims, B, recipe)
+    base = _decode_u(layer, pool.clone(), h, lens, 1)
+    check(_decode_u(layer, pool.clone(), h, lens, splits), base, dims.dtype, f"u with {splits} partitions")
+
+
 def test_checkpoint_restore_continues_bit_identically():
     """The caller-owned cache is the only state: copy pool and table to the host, restore them
     into fresh device buffers and keep decoding; outputs equal the uninterrupted run bit for bit."""
