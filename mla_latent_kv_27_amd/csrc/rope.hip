@@ -8,6 +8,8 @@
 // theta_k above beta turns, is slowed to theta_k / s below alpha turns, and is blended linearly
 // in r_k between.  The angle is formed and reduced modulo 2*pi in fp64 so that positions near
 // 1.3e5 keep full fp32 accuracy in cos/sin.
+#include <initializer_list>
+
 #include "common.h"
 #include "internal.h"
 
@@ -49,16 +51,90 @@ __global__ void __launch_bounds__(256)
   for (int i = lane; i < W; i += 64) r[i] = from_f32<T>(to_f32(r[i]) * inv * to_f32(g[i]));
 }
 
+// The same on 16-byte chunks with every load of a row in flight at once: lane l holds chunks l,
+// l + 64, ... (at most NC of them) in registers.  Rows of L elements; the first W are normalised
+// (gain g, when set), the rest (an entry's rope part) pass unchanged.  The loops above issue one
+// element per lane and iteration over a run-time width, so each load waits for the previous add
+// (24 dependent round trips for a 1536-wide c^q row).
+template <typename T, int NC>
+struct RowChunks {
+  static constexpr int kEV = 16 / sizeof(T);  // elements per chunk
+  typedef T vec_t __attribute__((ext_vector_type(kEV)));
+  vec_t v[NC];
+  __device__ __forceinline__ bool has(int k, int lane, int L) const { return (lane + 64 * k) * kEV < L; }
+  __device__ __forceinline__ void load(const T* x, int L, int lane) {
+#pragma unroll
+    for (int k = 0; k < NC; ++k)
+      if (has(k, lane, L)) v[k] = *reinterpret_cast<const vec_t*>(x + (lane + 64 * k) * kEV);
+  }
+  __device__ __forceinline__ void store(T* x, int L, int lane) const {
+#pragma unroll
+    for (int k = 0; k < NC; ++k)
+      if (has(k, lane, L)) *reinterpret_cast<vec_t*>(x + (lane + 64 * k) * kEV) = v[k];
+  }
+  // x[i] <- x[i] / rms(x[0..W)) * g[i] for i < W, with gv holding g's chunks
+  __device__ __forceinline__ void normalise(const RowChunks& gv, int W, float eps, int lane) {
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < NC; ++k)
+      if (has(k, lane, W))
+#pragma unroll
+        for (int e = 0; e < kEV; ++e) {
+          const float a = to_f32(v[k][e]);
+          ss += a * a;
+        }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) ss = wave_sum_xor(ss, m);
+    const float inv = 1.0f / sqrtf(ss / (float)W + eps);
+#pragma unroll
+    for (int k = 0; k < NC; ++k)
+      if (has(k, lane, W))
+#pragma unroll
+        for (int e = 0; e < kEV; ++e) v[k][e] = from_f32<T>(to_f32(v[k][e]) * inv * to_f32(gv.v[k][e]));
+  }
+};
+constexpr int kRowChunks = 4;  // chunks per lane: rows up to 2048 bf16 or 1024 fp32 values
+
+template <typename T>
+__global__ void __launch_bounds__(256)
+    rmsnorm_rows_vec_kernel(T* __restrict__ x, int n, int W, int64_t ld, const T* __restrict__ g, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= n) return;
+  RowChunks<T, kRowChunks> v, gv;
+  v.load(x + row * ld, W, lane);
+  gv.load(g, W, lane);
+  v.normalise(gv, W, eps, lane);
+  v.store(x + row * ld, W, lane);
+}
+
+// Whether rows of these widths and pointers take the 16-byte chunks.
+template <typename T>
+bool chunked_rows_ok(std::initializer_list<int64_t> widths, std::initializer_list<const void*> ptrs) {
+  constexpr int ev = 16 / sizeof(T);
+  for (int64_t w : widths)
+    if (w % ev != 0 || w > (int64_t)64 * kRowChunks * ev) return false;
+  for (const void* p : ptrs)
+    if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return false;
+  return true;
+}
+
+template <typename T>
+hipError_t rmsnorm_rows_t(void* x, int n, int W, int64_t ld, const void* gain, float eps, hipStream_t s) {
+  const dim3 grid((n + 3) / 4), block(256);
+  if (chunked_rows_ok<T>({W, ld}, {x, gain}))
+    hipLaunchKernelGGL(rmsnorm_rows_vec_kernel<T>, grid, block, 0, s, reinterpret_cast<T*>(x), n, W, ld,
+                       reinterpret_cast<const T*>(gain), eps);
+  else
+    hipLaunchKernelGGL(rmsnorm_rows_kernel<T>, grid, block, 0, s, reinterpret_cast<T*>(x), n, W, ld,
+                       reinterpret_cast<const T*>(gain), eps);
+  return hipGetLastError();
+}
+
 hipError_t rmsnorm_rows(DType t, void* x, int n, int W, int64_t ld, const void* gain, float eps, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  const dim3 grid((n + 3) / 4), block(256);
-  if (t == DType::BF16)
-    hipLaunchKernelGGL(rmsnorm_rows_kernel<bf16>, grid, block, 0, s, reinterpret_cast<bf16*>(x), n, W, ld,
-                       reinterpret_cast<const bf16*>(gain), eps);
-  else
-    hipLaunchKernelGGL(rmsnorm_rows_kernel<float>, grid, block, 0, s, reinterpret_cast<float*>(x), n, W, ld,
-                       reinterpret_cast<const float*>(gain), eps);
-  return hipGetLastError();
+  return t == DType::BF16 ? rmsnorm_rows_t<bf16>(x, n, W, ld, gain, eps, s)
+                          : rmsnorm_rows_t<float>(x, n, W, ld, gain, eps, s);
 }
 
 // One wave per row: rows < n_e are new cache entries (normalise the latent part, store in place
@@ -92,15 +168,53 @@ __global__ void __launch_bounds__(256) latent_finish_kernel(LatentFinish f) {
   for (int i = lane; i < f.E; i += 64) dst[i] = x[i];  // this lane's own writes above: no barrier needed
 }
 
+// The same on 16-byte chunks (RowChunks): an entry's page position is read first, with the row,
+// so that its block-table read overlaps the row's; the row is read once, normalised in registers,
+// stored in place and into its page.
+template <typename T>
+__global__ void __launch_bounds__(256) latent_finish_vec_kernel(LatentFinish f) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= f.n_e + f.n_q) return;
+  const bool entry = row < f.n_e;
+  T* x = entry ? reinterpret_cast<T*>(f.entries) + (int64_t)row * f.E
+               : reinterpret_cast<T*>(f.cq) + (int64_t)(row - f.n_e) * f.d_cq;
+  const int W = entry ? f.d_c : f.d_cq, L = entry ? f.E : f.d_cq;
+  const T* g = reinterpret_cast<const T*>(entry ? f.g_ckv : f.g_cq);
+  int sq = 0, ps = 0;
+  if (entry) {
+    sq = f.seq ? f.seq[row] : row;
+    ps = f.pos[row];
+  }
+  RowChunks<T, kRowChunks> v, gv;
+  v.load(x, L, lane);
+  if (g) gv.load(g, W, lane);
+  int64_t slot = 0;
+  if (entry)
+    slot = (int64_t)f.block_table[(int64_t)sq * f.max_blocks + ps / f.block_size] * f.block_size + ps % f.block_size;
+  if (g) {
+    v.normalise(gv, W, f.eps, lane);
+    v.store(x, W, lane);
+  }
+  if (entry) v.store(reinterpret_cast<T*>(f.pool) + slot * f.E, L, lane);
+}
+
+template <typename T>
+hipError_t latent_finish_t(const LatentFinish& f, hipStream_t s) {
+  const dim3 grid((f.n_e + f.n_q + 3) / 4), block(256);
+  const bool vec = chunked_rows_ok<T>({f.E, f.d_c, f.n_q > 0 ? f.d_cq : 0},
+                                      {f.entries, f.g_ckv, f.pool, f.n_q > 0 ? f.cq : nullptr, f.g_cq});
+  if (vec)
+    hipLaunchKernelGGL(latent_finish_vec_kernel<T>, grid, block, 0, s, f);
+  else
+    hipLaunchKernelGGL(latent_finish_kernel<T>, grid, block, 0, s, f);
+  return hipGetLastError();
+}
+
 hipError_t latent_finish(DType t, const LatentFinish& f, hipStream_t s) {
   const int rows = f.n_e + f.n_q;
   if (rows <= 0) return hipSuccess;
-  const dim3 grid((rows + 3) / 4), block(256);
-  if (t == DType::BF16)
-    hipLaunchKernelGGL(latent_finish_kernel<bf16>, grid, block, 0, s, f);
-  else
-    hipLaunchKernelGGL(latent_finish_kernel<float>, grid, block, 0, s, f);
-  return hipGetLastError();
+  return t == DType::BF16 ? latent_finish_t<bf16>(f, s) : latent_finish_t<float>(f, s);
 }
 
 __global__ void __launch_bounds__(256)
