@@ -2,6 +2,8 @@
 reading is pinned in test_rmsnorm_oracle.py) through the C ABI: the cache writer, decode and
 prefill with the c^q and c^KV norms, on V2, V2-Lite (no query compression: the c^KV norm only)
 and the fp32 tiny layer, plus the fp8 cache, whose quantiser takes the normalised entries."""
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -120,3 +122,42 @@ def test_fp8_cache_quantises_the_normalised_entries():
         step = np.maximum(np.abs(F.dequantize(ref_codes, ref_scales, dims.d_c)) * 2.0 ** -3,
                           np.repeat(ref_scales, [dims.d_c, dims.d_hr], axis=1) * 2.0 ** -9)
         assert np.all(d <= 1.05 * step + 1e-30), b
+
+
+
+def test_norms_on_rows_wider_than_the_chunked_kernels():
+    """Decode and prefill on V2 dims with both latent norms and a 2560-wide c^q: rows wider than
+    2048 bf16 values take the norms' element-per-lane kernels instead of the 16-byte-chunk ones
+    (the decode step's c^q rows and the entries through one launch, the prefill's c^q rows
+    through the row-norm launch), against the oracle."""
+    base, recipe, block = CASES["v2"]
+    dims = dataclasses.replace(base, d_cq=2560)
+    W = S.make_weights(dims)
+    layer = WL.DeviceLayer(dims, W)
+    lens = [63, 200]
+    B = len(lens)
+    pool = WL.PagedPool(dims, [L + 1 for L in lens], block_size=block)
+    WL.build_context(layer, pool, lens, recipe)
+    h = S.hidden_step(dims, B, recipe)
+    u = torch.empty((B, dims.d_model), dtype=WL.torch_dtype(dims), device="cuda")
+    ctx = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    M.decode(layer.cdims, layer.cweights, pool.ccache, WL.to_device(h, dims), ctx, max(lens), u,
+             WL.decode_workspace(layer, B, max(lens)))
+    torch.cuda.synchronize()
+    caches = [O.latent_entries(W, dims, S.hidden_history(dims, b, L, recipe), np.arange(L))
+              for b, L in enumerate(lens)]
+    ref = O.mla_decode(W, dims, h, caches)
+    check(u.float().cpu().numpy(), ref["u"], dims.dtype, "wide c^q decode u")
+    new = np.stack([pool.read_entries(b, L + 1)[L] for b, L in enumerate(lens)])
+    check(new, ref["entry"], dims.dtype, "wide c^q decode new entries")
+
+    T = 130
+    pool = WL.PagedPool(dims, [T], block_size=block)
+    hs = S.hidden_history(dims, 0, T, recipe)
+    u = torch.empty((1, T, dims.d_model), dtype=WL.torch_dtype(dims), device="cuda")
+    M.prefill(layer.cdims, layer.cweights, pool.ccache, WL.to_device(hs[None], dims), u,
+              WL.prefill_workspace(layer, 1, T))
+    torch.cuda.synchronize()
+    ref = O.mla_prefill(W, dims, hs)
+    check(pool.read_entries(0, T), ref["cache"], dims.dtype, "wide c^q prefill cache")
+    check(u[0].float().cpu().numpy(), ref["u"], dims.dtype, "wide c^q prefill u")
