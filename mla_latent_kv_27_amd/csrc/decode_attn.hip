@@ -387,11 +387,14 @@ __device__ __forceinline__ unsigned char sp_scores(const Frag8<bf16> (&q)[18], S
 #pragma unroll
   for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const bf16 e = (bf16)__builtin_amdgcn_exp2f(sc[tb][j] - st.m_ref);  // argument <= kHeadroom
-      st.l_part += (float)e;
-      pf[tb * 4 + j] = e;
-    }
+    for (int j = 0; j < 4; ++j)
+      pf[tb * 4 + j] = (bf16)__builtin_amdgcn_exp2f(sc[tb][j] - st.m_ref);  // argument <= kHeadroom
+  // the normaliser sums the probabilities as P.V multiplies them (rounded to bf16): one bf16 dot
+  // product with (1, 1) per pair instead of a widening and an add per value
+  const bf16x2 one = {(bf16)1.f, (bf16)1.f};
+#pragma unroll
+  for (int i = 0; i < 8; i += 2)
+    st.l_part = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[i], pf[i + 1]}, one, st.l_part, false);
   if (restart) pf[0] = (bf16)-1.f;  // the request: a value no probability takes
   *reinterpret_cast<bf16x8*>(pex_buf<PB>() + ((g * 128) + 16 * w + l16) * 16) = pf;
   return restart;
